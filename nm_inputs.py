@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for the N:M sparse GEMM workloads.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the method's arithmetic (no pruning, packing or products),
+so both the CPU oracle's tests and the GPU path's tests, bench and smoke run
+draw their inputs from here.
+
+Recipe (the same everywhere):
+  * generator: numpy PCG64 seeded with the sequence [workload_id, tensor_id,
+    variant]; tensor_id 0 = weight W, 1 = activations, 2 = permutation;
+  * W and activations: float32 standard normal times sigma, then rounded to
+    the storage type with round-to-nearest-even (fp16 through numpy's cast,
+    bf16 through the bit routine below);
+  * permutation: a uniform random permutation of 0..K-1 (int32).
+
+Half-precision arrays are returned as their raw uint16 bit patterns, the form
+every consumer (oracle, C ABI) takes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    Standard bias-and-truncate method: add 0x7FFF plus the lowest kept bit,
+    then drop the low 16 bits.  Inputs here are finite normals (no NaN).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def to_half_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F16:
+        return f32_to_f16_bits(x)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown half dtype {dtype!r}")
+
+
+def rng_for(workload_id: int, tensor_id: int, variant: int = 0) -> np.random.Generator:
+    return np.random.default_rng([int(workload_id), int(tensor_id), int(variant)])
+
+
+def normal_half(shape, sigma: float, dtype: str, workload_id: int, tensor_id: int,
+                variant: int = 0) -> np.ndarray:
+    """uint16 bits of N(0, sigma^2) samples rounded to `dtype`."""
+    rng = rng_for(workload_id, tensor_id, variant)
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)
+    return to_half_bits(x, dtype)
+
+
+def integer_half(shape, lo: int, hi: int, dtype: str, workload_id: int, tensor_id: int,
+                 variant: int = 0) -> np.ndarray:
+    """uint16 bits of uniform integers in [lo, hi] (exact in fp16 and bf16)."""
+    rng = rng_for(workload_id, tensor_id, variant)
+    x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return to_half_bits(x, dtype)
+
+
+def random_permutation(k: int, workload_id: int, variant: int = 0) -> np.ndarray:
+    return rng_for(workload_id, 2, variant).permutation(int(k)).astype(np.int32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: W is R x K, activations are T x K (K-contiguous)."""
+    wid: int
+    name: str
+    R: int
+    K: int
+    Ts: tuple
+    patterns: tuple  # (n, m) pairs
+    dtype: str
+    sigma_w: float
+    sigma_x: float = 1.0
+    permuted: bool = False
+    note: str = ""
+
+    def weights(self) -> np.ndarray:
+        return normal_half((self.R, self.K), self.sigma_w, self.dtype, self.wid, 0)
+
+    def activations(self, T: int | None = None) -> np.ndarray:
+        T = self.Ts[0] if T is None else T
+        return normal_half((T, self.K), self.sigma_x, self.dtype, self.wid, 1, T)
+
+    def permutation(self) -> np.ndarray | None:
+        return random_permutation(self.K, self.wid) if self.permuted else None
+
+
+# The five workloads (sizes R x K x T).  Shapes follow the layers the pages
+# measure: a small 2:4 example, a LLaMA-2-7B projection at prefill and at
+# decode, the general 1:4 / 1:8 forms, and a ViT-B/16 MLP fc1 over 64 images
+# of 197 tokens with a learned column permutation.
+WORKLOADS = {
+    1: Workload(1, "small-2of4-fp16", 256, 256, (64,), ((2, 4),), F16, 1.0,
+                note="2:4 fp16 small case"),
+    2: Workload(2, "llama2-7b-proj-prefill-2of4-bf16", 4096, 4096, (2048,), ((2, 4),), BF16, 0.02,
+                note="2:4 bf16 prefill, MFMA-bound"),
+    3: Workload(3, "llama2-7b-mlp-decode-2of4-bf16", 11008, 4096, (1, 8, 16), ((2, 4),), BF16, 0.02,
+                note="2:4 bf16 decode, HBM-bound"),
+    4: Workload(4, "general-1of4-1of8-fp16", 4096, 4096, (512,), ((1, 4), (1, 8)), F16, 1.0,
+                note="1:4 and 1:8 fp16"),
+    5: Workload(5, "vit-b16-fc1-perm-2of4-fp16", 3072, 768, (12608,), ((2, 4),), F16, 0.02,
+                permuted=True, note="2:4 fp16 with column permutation, 197 tokens x 64 images"),
+}

@@ -1,0 +1,242 @@
+"""CPU oracle for N:M structured weight sparsity: prune, pack, decompress, GEMM.
+
+TEST INFRASTRUCTURE ONLY.  This module exists to check the GPU library; only
+the test suite, the smoke check and the CPU-baseline leg of the benchmark may
+import it.  The library itself never calls into it and there is no CPU
+fallback through it.  It shares no code with the HIP path.
+
+Plain NumPy, written for a reader to check against the pages by eye:
+
+* Definition (COE-592 lecture 04-2, "M:N sparsity on NVIDIA tensor cores",
+  opening section): along each row of W, every group of M consecutive weights
+  keeps N of them; the worked row has survivor positions [[0, 3], [1, 2]];
+  a pattern is written survivors:block-size.  The groups run along the row of
+  W, which is the reduction axis of the GEMM.
+* Pruning rule (same page, section "The recipe", step 2): in each group keep
+  the weights with the largest absolute value, zero the others.
+* Storage (same page, section "Where this sits among the three case
+  studies"): survivors of a row are pushed left into a contiguous block of
+  values; a small index per survivor records which slot of its group it came
+  from (2 bits for groups of four).
+* GEMM (same section): sparse weight matrix times dense matrix gives a dense
+  matrix; only the weight operand is compressed.
+* Permuted layer (SHUFFLESPARSE technical summary, section 2 "Methodologie"
+  and the "Efficiency at inference" item of "Belangrijke Technische
+  Componenten"): y = (W Pi) x, where the hardened permutation is applied as a
+  precomputed index map on the input reads.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  R1  exactly N slots are stored per group (a slot may hold a zero);
+  R2  magnitude is compared on the stored 16-bit value: key = bits & 0x7FFF,
+      the sign bit dropped; equal keys go to the lower position;
+  R3  positions inside a group are stored in ascending order;
+  R4  index width b = ceil(log2 M) bits (2 for M = 4, 3 for M = 8);
+  R5  each row's indices form an LSB-first bitstream: survivor s occupies bits
+      [s*b, s*b + b); the row is zero-padded to whole little-endian uint32
+      words;
+  R6  activations arrive as act[T, K] (K-contiguous) and X = act^T;
+  R7  with a permutation, y[r, t] = sum_k W[r, k] * act[t, perm[k]].
+
+Parity pins: every function here is pinned by tests under tests/ (worked
+row, 36-bit group cost, brute-force top-N, exhaustive ties, worked K = 8
+product, identity and integer GEMMs, dense N = M case, explicit-matrix
+permutation route).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+
+# --------------------------------------------------------------------------
+# 16-bit storage types
+# --------------------------------------------------------------------------
+
+def half_bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of fp16 / bf16 bit patterns (uint16)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def magnitude_keys(bits: np.ndarray) -> np.ndarray:
+    """Reading R2: |w| as an integer key.
+
+    fp16 and bf16 keep the sign in bit 15; for non-negative IEEE values the
+    unsigned bit order is the magnitude order, so dropping the sign bit gives
+    a key whose order is the order of |w| (+0 and -0 share key 0).
+    """
+    return (np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Format arithmetic
+# --------------------------------------------------------------------------
+
+def index_bits(m: int) -> int:
+    """Reading R4: bits needed to name one of M slots."""
+    return max(1, int(m - 1).bit_length())
+
+
+def survivors_per_row(K: int, n: int, m: int) -> int:
+    return K // m * n
+
+
+def idx_words_per_row(K: int, n: int, m: int) -> int:
+    """uint32 words holding one row's index bitstream (reading R5)."""
+    nbits = survivors_per_row(K, n, m) * index_bits(m)
+    return (nbits + 31) // 32
+
+
+# --------------------------------------------------------------------------
+# Prune: choose the survivors of every group
+# --------------------------------------------------------------------------
+
+def select_survivors(w_bits: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Positions (0..m-1) of the n kept weights of each group, ascending.
+
+    Returns int64 [R, K/m, n].  Within a group the weights are ranked by key
+    (largest first); a stable sort of the negated keys leaves equal keys in
+    position order, so ties go to the lower position (R2).  The first n of
+    that ranking are kept and then put back in ascending order (R3).
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    R, K = w_bits.shape
+    if K % m:
+        raise ValueError("K must be a multiple of m")
+    keys = magnitude_keys(w_bits).reshape(R, K // m, m)
+    ranking = np.argsort(-keys, axis=-1, kind="stable")
+    kept = np.sort(ranking[..., :n], axis=-1)
+    return kept.astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Pack: values pushed left, indices into a per-row bitstream
+# --------------------------------------------------------------------------
+
+def pack_values(w_bits: np.ndarray, positions: np.ndarray, m: int) -> np.ndarray:
+    """values[r, g*n + j] = bits of W[r, g*m + positions[r, g, j]] (no arithmetic)."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    R, K = w_bits.shape
+    G, n = positions.shape[1], positions.shape[2]
+    groups = w_bits.reshape(R, G, m)
+    vals = np.take_along_axis(groups, positions, axis=-1)
+    return vals.reshape(R, G * n).copy()
+
+
+def pack_indices(positions: np.ndarray, m: int) -> np.ndarray:
+    """Reading R5: row bitstream, survivor s at bits [s*b, s*b+b), LSB first.
+
+    Built as an explicit bit array: bit j of survivor s's position goes to
+    stream bit s*b + j; the stream is zero-padded to 32-bit words and word w
+    collects stream bits [32w, 32w + 32) with stream bit 32w + i at weight 2^i.
+    """
+    R = positions.shape[0]
+    pos = positions.reshape(R, -1).astype(np.int64)
+    S = pos.shape[1]
+    b = index_bits(m)
+    nwords = (S * b + 31) // 32
+    stream = np.zeros((R, nwords * 32), dtype=np.uint64)
+    for j in range(b):
+        stream[:, j:S * b:b] = (pos >> j) & 1
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    words = (stream.reshape(R, nwords, 32) * weights).sum(axis=-1)
+    return words.astype(np.uint32)
+
+
+def prune_pack(w_bits: np.ndarray, n: int, m: int):
+    """Magnitude top-n-of-m prune, then pack.  Returns (values uint16 [R, S], idx uint32 [R, W])."""
+    positions = select_survivors(w_bits, n, m)
+    return pack_values(w_bits, positions, m), pack_indices(positions, m)
+
+
+# --------------------------------------------------------------------------
+# Unpack / decompress
+# --------------------------------------------------------------------------
+
+def unpack_indices(idx: np.ndarray, S: int, m: int) -> np.ndarray:
+    """Inverse of pack_indices: positions [R, S] read back from the bitstream."""
+    idx = np.asarray(idx, dtype=np.uint32)
+    R = idx.shape[0]
+    b = index_bits(m)
+    start = np.arange(S, dtype=np.int64) * b
+    pos = np.zeros((R, S), dtype=np.int64)
+    for j in range(b):
+        bit = start + j
+        word = idx[:, bit // 32].astype(np.int64)
+        pos |= ((word >> (bit % 32)) & 1) << j
+    return pos
+
+
+def decompress(values: np.ndarray, idx: np.ndarray, K: int, n: int, m: int) -> np.ndarray:
+    """Dense bit patterns [R, K]: each stored value back at g*m + position, zeros elsewhere."""
+    values = np.asarray(values, dtype=np.uint16)
+    R, S = values.shape
+    if S != survivors_per_row(K, n, m):
+        raise ValueError("values width does not match K*n/m")
+    pos = unpack_indices(idx, S, m)
+    group = np.arange(S, dtype=np.int64) // n
+    cols = group[None, :] * m + pos
+    dense = np.zeros((R, K), dtype=np.uint16)
+    rows = np.broadcast_to(np.arange(R)[:, None], (R, S))
+    dense[rows, cols] = values
+    return dense
+
+
+# --------------------------------------------------------------------------
+# GEMM
+# --------------------------------------------------------------------------
+
+def spmm_ref(values, idx, K: int, n: int, m: int, act_bits, dtype: str, perm=None) -> np.ndarray:
+    """Y = W_nm X in float64, returned as [R, T].
+
+    W_nm is the decompressed weight; X = act^T (R6).  With a permutation the
+    input rows are read through the index map, X_perm[k, :] = X[perm[k], :]
+    (R7), which is (W Pi) x for Pi[k, perm[k]] = 1.
+    """
+    wd = half_bits_to_f64(decompress(values, idx, K, n, m), dtype)
+    x = half_bits_to_f64(np.asarray(act_bits, dtype=np.uint16), dtype).T  # [K, T]
+    if perm is not None:
+        x = x[np.asarray(perm, dtype=np.int64), :]
+    return wd @ x
+
+
+def spmm_rows_ref(values, idx, K: int, n: int, m: int, act_bits, dtype: str, rows, cols,
+                  perm=None) -> np.ndarray:
+    """Y[rows[i], cols[i]] one at a time, for sampled checks at full size."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    wd = half_bits_to_f64(decompress(values[np.unique(rows)], idx[np.unique(rows)], K, n, m), dtype)
+    where = {r: i for i, r in enumerate(np.unique(rows))}
+    out = np.empty(len(rows), dtype=np.float64)
+    act = np.asarray(act_bits, dtype=np.uint16)
+    p = None if perm is None else np.asarray(perm, dtype=np.int64)
+    for i, (r, t) in enumerate(zip(rows, cols)):
+        xt = half_bits_to_f64(act[t], dtype)
+        if p is not None:
+            xt = xt[p]
+        out[i] = float(np.dot(wd[where[int(r)]], xt))
+    return out
+
+
+def relative_error(y: np.ndarray, yref: np.ndarray):
+    """(max floored relative error, normwise relative error).
+
+    Element error is |y - yref| / max(|yref|, rms(yref)); the floor keeps the
+    ratio bounded where yref is near zero.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    yref = np.asarray(yref, dtype=np.float64)
+    if yref.size == 0:
+        return 0.0, 0.0
+    rms = float(np.sqrt(np.mean(yref * yref)))
+    floor = np.maximum(np.abs(yref), rms if rms > 0 else 1.0)
+    max_rel = float(np.max(np.abs(y - yref) / floor))
+    den = float(np.linalg.norm(yref))
+    norm_rel = float(np.linalg.norm(y - yref) / den) if den > 0 else float(np.linalg.norm(y - yref))
+    return max_rel, norm_rel
