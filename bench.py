@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the N:M sparse GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+nm_compress (magnitude prune + pack of W) followed by nm_spmm (Y = W_nm X),
+with every input resident in HBM before the timed region starts.
+
+Default workload: a LLaMA-2-7B projection at prefill, W 4096 x 4096 bf16
+N(0, 0.02) pruned 2:4 along K, activations 2048 x 4096 bf16 N(0, 1), fp32 Y.
+
+Prints one JSON line (rank 0, N = 1):
+  value        dense-equivalent TFLOP/s of the step, 2*R*K*T / t_step
+  roofline     the sparse GEMM kernel against the MI355X dense MFMA peak for
+               its dtype: achieved = algorithmic FLOP (2*R*S*T, S = K*N/M
+               stored weights per row) / mean kernel duration from HIP events
+               recorded around each launch on its stream inside the timed loop
+  cpu_baseline the CPU oracle (NumPy, fp64) timed on this host over the same
+               workload
+  kernels      per-kernel means (sparse GEMM, compress, dense hipBLASLt GEMM
+               of the same shape) and the speedup over the dense GEMM
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "2:4 sparse GEMM dense-equivalent TFLOP/s and HBM GB/s; speedup vs dense"
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: prefill 4096x4096x2048)")
+    ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
+    ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="copies of the inputs cycled through (defeats the 256 MB last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key, hsh):
+    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != hsh:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n, m, T, reps):
+    """The oracle as it stands, timed on the host: prune+pack, decompress, fp64 GEMM."""
+    import numpy as np
+    from oracle import nm_oracle as O
+    w = wl.weights()
+    act = wl.activations(T)
+    perm = wl.permutation()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        vals, idx = O.prune_pack(w, n, m)
+        O.spmm_ref(vals, idx, wl.K, n, m, act, wl.dtype, perm=perm)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            cores = min(cores, int(os.environ[var]))
+            break
+    flops = 2.0 * wl.R * wl.K * T
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload ({wl.R}x{wl.K}x{T}, {n}:{m}): prune+pack, decompress and "
+                      f"fp64 matmul; median of {reps} runs, {t:.2f} s each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU kernel is what --gpus 1 times); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nm_inputs
+    import structured_sparse_gemm_nm_amd as nm
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    nm.lib()  # fails loudly if the library is not built
+
+    wl = nm_inputs.WORKLOADS[args.workload]
+    T = args.T if args.T is not None else wl.Ts[-1] if args.workload == 3 else wl.Ts[0]
+    if args.pattern:
+        n, m = (int(v) for v in args.pattern.split(":"))
+    else:
+        n, m = wl.patterns[0]
+    R, K = wl.R, wl.K
+    S = K // m * n
+    dt = wl.dtype
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    out_dtype = torch.float32 if args.out_dtype == "f32" else tdt
+    nm.nm_set_variant(args.variant)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+    W = dev(wl.weights())
+    act = dev(wl.activations(T))
+    perm_np = wl.permutation()
+    perm = torch.from_numpy(perm_np).cuda() if perm_np is not None else None
+    vb, ib, words = nm.nm_packed_sizes(R, K, n, m, nm.NM_F16 if dt == "f16" else nm.NM_BF16)
+    ybytes = T * R * (4 if out_dtype == torch.float32 else 2)
+    step_bytes = vb + ib + T * K * 2 + ybytes  # the GEMM's algorithmic bytes
+
+    # Rotation: enough copies that one pass over them exceeds the 256 MB cache.
+    rotate = args.rotate if args.rotate is not None else (1 if args.workload == 2 else
+                                                          max(1, min(64, -(-320_000_000 // step_bytes))))
+    copies = []
+    for c in range(rotate):
+        Wc = W if c == 0 else W.clone()
+        Ac = act if c == 0 else act.clone()
+        vals = torch.empty((R, S), dtype=tdt, device="cuda")
+        idx = torch.empty((R, words), dtype=torch.int32, device="cuda")
+        Y = torch.empty((T, R), dtype=out_dtype, device="cuda")
+        copies.append((Wc, Ac, vals, idx, Y))
+
+    def gemm(c):
+        _, Ac, vals, idx, Y = copies[c]
+        if perm is None:
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=Y)
+        else:
+            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=Y)
+
+    def compress(c):
+        Wc, _, vals, idx, _ = copies[c]
+        nm.nm_compress(Wc, n, m, values=vals, idx=idx)
+
+    # ---- warmup
+    for i in range(args.warmup):
+        compress(i % rotate)
+        gemm(i % rotate)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        compress(i % rotate)
+        ev[i][0].record()
+        gemm(i % rotate)
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    gemm_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    gemm_mean_us = statistics.fmean(gemm_us)
+
+    # ---- per-kernel breakdown (back-to-back launches of one kernel)
+    def time_loop(fn, iters):
+        for i in range(5):
+            fn(i % rotate)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            fn(i % rotate)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    iters = max(20, args.steps)
+    gemm_loop_us = time_loop(gemm, iters)
+    compress_us = time_loop(compress, iters)
+    dense = []
+    for c in range(rotate):
+        dense.append(nm.nm_decompress(copies[c][2], copies[c][3], K, n, m))
+    actp = [copies[c][1] if perm is None else copies[c][1][:, perm.long()].contiguous()
+            for c in range(rotate)]
+
+    def dense_gemm(c):
+        torch.nn.functional.linear(actp[c], dense[c])
+
+    dense_us = time_loop(dense_gemm, iters)
+    y_half = torch.empty((T, R), dtype=tdt, device="cuda")
+
+    def gemm_half(c):
+        _, Ac, vals, idx, _ = copies[c]
+        if perm is None:
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=tdt, out=y_half)
+        else:
+            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half)
+
+    gemm_half_us = time_loop(gemm_half, iters)
+
+    dense_eq_flop = 2.0 * R * K * T
+    alg_flop = 2.0 * R * S * T
+    achieved_tflops = alg_flop / (gemm_mean_us * 1e-6) / 1e12
+    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
+               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
+    hsh = source_hash(lib_src)
+    kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{args.out_dtype}"
+    roofline_bound = "mfma" if args.workload in (1, 2, 4) else "hbm"
+    if roofline_bound == "mfma":
+        roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_MFMA_TFLOPS[dt],
+                    "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_MFMA_TFLOPS[dt],
+                    "traffic": traffic_from_profile(kernel_key, hsh)}
+    else:
+        gbps = step_bytes / (gemm_mean_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(kernel_key, hsh)}
+    roofline["kernel"] = "nm_spmm" if perm is None else "nm_spmm_perm"
+    roofline["per_launch"] = {"flop": alg_flop, "bytes": step_bytes, "mean_us": gemm_mean_us}
+
+    out = {
+        "metric": METRIC,
+        "value": dense_eq_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,sigma) inputs of the workload's shapes)",
+        "config": {"workload": wl.name, "R": R, "K": K, "T": T, "pattern": f"{n}:{m}",
+                   "out_dtype": args.out_dtype, "permuted": perm is not None, "rotate": rotate,
+                   "step": "nm_compress + nm_spmm", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {
+            "nm_spmm_us_in_step": gemm_mean_us,
+            "nm_spmm_us_loop": gemm_loop_us,
+            "nm_spmm_dense_eq_tflops": dense_eq_flop / (gemm_loop_us * 1e-6) / 1e12,
+            "nm_spmm_packed_gbps": (vb + ib) / (gemm_loop_us * 1e-6) / 1e9,
+            "nm_spmm_alg_gbps": step_bytes / (gemm_loop_us * 1e-6) / 1e9,
+            "nm_spmm_half_out_us": gemm_half_us,
+            "nm_compress_us": compress_us,
+            "nm_compress_gbps": (R * K * 2 + vb + ib) / (compress_us * 1e-6) / 1e9,
+            "dense_linear_us": dense_us,
+            "speedup_vs_dense_half_out": dense_us / gemm_half_us,
+            "speedup_vs_dense_f32_out": dense_us / gemm_loop_us,
+        },
+        "wall_s_timed": wall,
+        "source_hash": hsh,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, n, m, T, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * nmsparse.h -- N:M structured weight sparsity on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over plain pointers and sizes.  Every device pointer is HIP device
+ * memory owned by the caller; the library allocates nothing on these paths
+ * and keeps no state between calls.  Streams are passed as `void*` holding a
+ * hipStream_t (NULL = the legacy default stream).
+ *
+ * Notation.  W is R x K (rows = output features, K = the reduction axis).
+ * An N:M pattern keeps N of every M consecutive weights along a row of W;
+ * S = K*N/M survivors per row; b = ceil(log2 M) index bits per survivor.
+ *
+ * Sources.  "M:N sparsity on NVIDIA tensor cores" (COE-592 lecture 04-2):
+ * the opening section defines the pattern (groups along rows, survivor
+ * positions per group) and the survivors:block notation; section "Where this
+ * sits among the three case studies" gives the storage format (survivors
+ * pushed left, small per-survivor indices), the product rule (only the weight
+ * operand is compressed; sparse times dense is dense) and the shape rule (the
+ * reduction dimension a multiple of 16 for 16-bit types, other layers stay
+ * dense); section "The recipe" gives the pruning rule (keep the largest
+ * magnitudes).  "SHUFFLESPARSE" technical summary, section 2 and its item on
+ * inference efficiency: y = (W Pi) x with the hardened permutation applied as
+ * a precomputed index map on the input reads.
+ *
+ * Error behaviour.  Every entry point validates its arguments on the host
+ * before any HIP call and returns a status; on failure nothing is enqueued
+ * and nm_last_error() describes the problem.  NM_OK means the work was
+ * enqueued on `stream` (asynchronous, stream-ordered); device-side faults
+ * surface at the caller's next synchronisation.  No exception or abort
+ * crosses this boundary.  Results are bitwise reproducible (no atomics).
+ */
+#ifndef NMSPARSE_H
+#define NMSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  NM_ERR_SHAPE = 2,        /* R, K or T out of range; K % 16 or K % M non-zero    */
+  NM_ERR_UNSUPPORTED = 3,  /* (n, m) pair or dtype combination not provided       */
+  NM_ERR_STRIDE = 4,       /* leading dimension smaller than the row width        */
+  NM_ERR_ALIAS = 5,        /* output overlaps an input                            */
+  NM_ERR_HIP = 6,          /* a HIP call failed (launch error, no device, ...)    */
+  NM_ERR_ALIGN = 7         /* pointer or leading dimension misaligned (see below) */
+} nm_status;
+
+typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2 } nm_dtype;
+
+/* Version of this ABI (major * 100 + minor). */
+int nm_version(void);
+
+/* Short fixed text for a status code (never NULL). */
+const char* nm_status_string(int status);
+
+/* Detail for the last failing call on this thread (empty string if none). */
+const char* nm_last_error(void);
+
+/*
+ * Sizes of the packed format.  Pure host arithmetic, no device access.
+ *   values_bytes  = R * S * 2            (values [R, S], same 16-bit type as W)
+ *   idx_row_words = ceil(S * b / 32)     (uint32 words per row)
+ *   idx_bytes     = R * idx_row_words * 4
+ * Any output pointer may be NULL.  Same validation as nm_compress.
+ *
+ * Packed format (the canonical one every entry point reads and writes):
+ *   values[r, g*N + j]  the j-th survivor of group g of row r, survivors of a
+ *                       group in ascending position order, bits copied
+ *                       unchanged from W;
+ *   idx row r           an LSB-first bitstream: the in-group position (0..M-1)
+ *                       of survivor s = g*N + j sits in bits [s*b, s*b + b);
+ *                       stream bit i is bit (i % 32) of word (i / 32); words
+ *                       are little-endian uint32, the tail is zero-padded.
+ * With 2:4, one group of four 16-bit weights costs 2*16 + 2*2 = 36 bits
+ * (+ per-row padding to a whole word when S*b is not a multiple of 32).
+ */
+nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype,
+                          size_t* values_bytes, size_t* idx_bytes, int64_t* idx_row_words);
+
+/*
+ * Prune + pack (magnitude top-N of every M along the rows of W).
+ *   W       device, [R, K] row-major, leading dimension ldw >= K (elements),
+ *           dtype NM_F16 or NM_BF16.
+ *   values  device, [R, S] contiguous, same dtype (written).
+ *   idx     device, [R, idx_row_words] uint32 contiguous (written, padding
+ *           bits zero).
+ * Selection: magnitude is compared on the stored 16-bit pattern with the sign
+ * bit cleared (bits & 0x7FFF), so +0/-0 tie and +x/-x tie; the N largest keys
+ * of a group are kept, equal keys going to the lower position.  Exactly N
+ * slots are stored per group even when the group holds fewer non-zeros.
+ * Supported (n, m): (2, 4), (1, 4), (1, 8).  K % 16 == 0 and K % m == 0.
+ * Alignment: W, values and idx 16-byte aligned; ldw % 8 == 0.
+ */
+nm_status nm_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, int n, int m,
+                      void* values, uint32_t* idx, void* stream);
+
+/*
+ * Decompress: dense W_nm [R, K] (leading dimension ldw) with the survivors
+ * back in place and zeros elsewhere.  Same format rules as nm_compress.
+ */
+nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n,
+                        int m, int dtype, void* W_out, int64_t ldw, void* stream);
+
+/*
+ * Sparse GEMM  Y = W_nm X,  X = act^T.
+ *   values, idx  packed W (see nm_packed_sizes), dtype NM_F16 or NM_BF16.
+ *   act          device, [T, K] row-major (each token's K features contiguous),
+ *                leading dimension ldx >= K, same dtype as values.
+ *   Y            device, [T, R] row-major, leading dimension ldy >= R, i.e. the
+ *                transpose of Y = W_nm X (the layout of a linear layer's output);
+ *                out_dtype NM_F32 (default) or the input dtype (RNE rounded).
+ *   Y[t, r] = sum_k W_nm[r, k] * act[t, k], products and sums in fp32.
+ * Shapes: R >= 1, T >= 0 (T == 0 enqueues nothing), K >= 16, K % 16 == 0,
+ * K % m == 0.  Alignment: every pointer 16-byte aligned, ldx % 8 == 0,
+ * ldy % 4 == 0.  Y must not overlap values, idx or act (NM_ERR_ALIAS).
+ */
+nm_status nm_spmm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
+                  int dtype, const void* act, int64_t T, int64_t ldx, void* Y, int64_t ldy,
+                  int out_dtype, void* stream);
+
+/*
+ * Permuted sparse GEMM  y = (W Pi) x:  Y[t, r] = sum_k W_nm[r, k] * act[t, perm[k]].
+ *   perm  device int32 [K], a permutation of 0..K-1 (precondition, not checked
+ *         on the hot path; out-of-range entries are undefined behaviour).
+ * All other arguments as nm_spmm.  The permutation is applied while X is read;
+ * no permuted copy of X is made.
+ */
+nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
+                       int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
+                       void* Y, int64_t ldy, int out_dtype, void* stream);
+
+/*
+ * Host-side check that perm is a permutation of 0..K-1 (copies perm to the
+ * host and synchronises `stream`).  NM_ERR_SHAPE if it is not.  Debug aid.
+ */
+nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
+
+/*
+ * Kernel variant for nm_spmm / nm_spmm_perm.  0 = automatic (default),
+ * 1 = sparse MFMA (v_smfmac) path, 2 = dense MFMA on decompressed LDS tiles.
+ * Process-wide; meant for ablations and tests.
+ */
+nm_status nm_set_variant(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NMSPARSE_H */

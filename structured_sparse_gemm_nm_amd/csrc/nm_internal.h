@@ -1,0 +1,46 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nmsparse.h"
+
+namespace nm {
+
+// Launchers (defined next to their kernels).  Arguments are already
+// validated; each returns the hipError_t of its launch.
+hipError_t launch_prune_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                             uint16_t* values, uint32_t* idx, int64_t idx_row_words,
+                             hipStream_t s);
+
+hipError_t launch_decompress(const uint16_t* values, const uint32_t* idx, int64_t R, int64_t K,
+                             int n, int m, int64_t idx_row_words, uint16_t* W, int64_t ldw,
+                             hipStream_t s);
+
+struct SpmmArgs {
+  const uint16_t* values;
+  const uint32_t* idx;
+  int64_t R, K;
+  int n, m;
+  int dtype;             // NM_F16 / NM_BF16
+  const uint16_t* act;   // [T, K], ldx
+  int64_t T, ldx;
+  const int32_t* perm;   // nullptr: identity
+  void* Y;               // [T, R], ldy
+  int64_t ldy;
+  int out_dtype;         // NM_F32 or dtype
+  int64_t idx_row_words;
+  int variant;           // 0 auto, 1 smfmac, 2 decompressed dense MFMA
+};
+
+hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
+
+inline int index_bits(int m) {
+  int b = 0;
+  while ((1 << b) < m) ++b;
+  return b < 1 ? 1 : b;
+}
+
+}  // namespace nm

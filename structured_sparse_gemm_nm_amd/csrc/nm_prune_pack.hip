@@ -1,0 +1,223 @@
+// Prune + pack and decompress kernels for N:M structured sparsity (gfx950).
+//
+// Prune rule: "M:N sparsity on NVIDIA tensor cores" (COE-592 lecture 04-2),
+// section "The recipe", step 2 -- in every group of M weights along a row keep
+// the N with the largest absolute value.  Magnitude is compared on the stored
+// 16-bit pattern with the sign cleared; equal magnitudes go to the lower
+// position.  Storage (same page, "Where this sits among the three case
+// studies"): survivors pushed left into contiguous values; each survivor's
+// in-group position stored as a b-bit field of an LSB-first per-row bitstream
+// padded to whole 32-bit words.
+//
+// Thread mapping.  One lane owns one 16-byte chunk (8 consecutive weights) of
+// a row, so a wavefront reads 1 KiB of W contiguously.  A lane produces
+// 8*N/M survivors and BPL = 8*N/M*b index bits.  The smallest run of lanes
+// whose bits fill whole words (L = 32 / gcd(BPL, 32) lanes -> L*BPL/32 words)
+// assembles its words with an OR-reduction over cross-lane shuffles; rows are
+// padded to a multiple of L lanes so a run never spans two rows.
+#include "nm_internal.h"
+
+namespace nm {
+namespace {
+
+template <int N, int M>
+struct PackShape {
+  static constexpr int B = (M <= 2) ? 1 : (M <= 4) ? 2 : 3;      // index bits
+  static constexpr int GPL = 8 / M;                              // groups per lane
+  static constexpr int SPL = GPL * N;                            // survivors per lane
+  static constexpr int BPL = SPL * B;                            // index bits per lane
+  static constexpr int GCD = (BPL % 32 == 0) ? 32 : (BPL % 16 == 0) ? 16 : (BPL % 8 == 0) ? 8
+                             : (BPL % 4 == 0) ? 4 : (BPL % 2 == 0) ? 2 : 1;
+  static constexpr int L = 32 / GCD;                             // lanes per word run
+  static constexpr int WPR = L * BPL / 32;                       // words per run
+};
+
+// Select the N largest of M keys (ties -> lower position); positions ascending.
+template <int N, int M>
+__device__ inline void select_group(const uint32_t* key, int* pos) {
+  // Composite keys (key << 3 | (M-1-i)) are all distinct and larger means
+  // "wins"; an element is kept when fewer than N others beat it.  The kept
+  // set becomes a bit mask whose set bits, lowest first, are the positions.
+  uint32_t ck[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) ck[i] = (key[i] << 3) | uint32_t(M - 1 - i);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    int beaten = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) beaten += (ck[j] > ck[i]) ? 1 : 0;
+    mask |= (beaten < N) ? (1u << i) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    pos[j] = __builtin_ctz(mask);
+    mask &= mask - 1u;
+  }
+}
+
+template <int N, int M>
+__global__ __launch_bounds__(256) void prune_pack_kernel(const uint16_t* __restrict__ W, int64_t R,
+                                                         int64_t K, int64_t ldw, int64_t lanes_per_row,
+                                                         uint16_t* __restrict__ values,
+                                                         uint32_t* __restrict__ idx,
+                                                         int64_t idx_row_words) {
+  using PS = PackShape<N, M>;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t r = gid / lanes_per_row;
+  const int64_t c = gid - r * lanes_per_row;  // chunk index inside the row
+  const int64_t chunks = K / 8;
+  const bool live = (r < R) && (c < chunks);
+
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (live) {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + r * ldw + c * 8);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  uint32_t bits[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bits[2 * i] = w[i] & 0xFFFFu;
+    bits[2 * i + 1] = w[i] >> 16;
+  }
+
+  uint32_t lane_idx = 0;        // this lane's BPL index bits, survivor order
+  uint16_t kept[PS::SPL];
+#pragma unroll
+  for (int g = 0; g < PS::GPL; ++g) {
+    uint32_t key[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) key[i] = bits[g * M + i] & 0x7FFFu;
+    int pos[N];
+    select_group<N, M>(key, pos);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      // pos[j] < M; pick the bits with a short unrolled select (no dynamic
+      // register indexing).
+      uint32_t val = 0;
+#pragma unroll
+      for (int i = 0; i < M; ++i) val = (pos[j] == i) ? bits[g * M + i] : val;
+      kept[g * N + j] = uint16_t(val);
+      lane_idx |= uint32_t(pos[j]) << ((g * N + j) * PS::B);
+    }
+  }
+
+  // Values: SPL consecutive halves at survivor offset c*SPL of the row.
+  if (live) {
+    const int64_t S = K / M * N;
+    uint16_t* dst = values + r * S + c * PS::SPL;
+    if constexpr (PS::SPL == 4) {
+      uint2 o;
+      o.x = uint32_t(kept[0]) | (uint32_t(kept[1]) << 16);
+      o.y = uint32_t(kept[2]) | (uint32_t(kept[3]) << 16);
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else if constexpr (PS::SPL == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = uint32_t(kept[0]) | (uint32_t(kept[1]) << 16);
+    } else {
+      *dst = kept[0];
+    }
+  }
+
+  // Index words: OR-reduce each word's contributions over the L-lane run.
+  const int li = int(c % PS::L);           // lane position inside its run
+  const int off = li * PS::BPL;            // bit offset inside the run
+  const uint32_t mine = live ? lane_idx : 0u;
+#pragma unroll
+  for (int wd = 0; wd < PS::WPR; ++wd) {
+    const int sh = off - 32 * wd;
+    uint32_t part = 0;
+    if (sh >= 0 && sh < 32) part = mine << sh;
+    else if (sh < 0 && sh > -PS::BPL) part = mine >> (-sh);
+#pragma unroll
+    for (int d = 1; d < PS::L; d <<= 1) part |= uint32_t(__shfl_xor(int(part), d, 64));
+    if (li == wd && r < R) {
+      const int64_t word = (c - li) * PS::BPL / 32 + wd;
+      if (word < idx_row_words) idx[r * idx_row_words + word] = part;
+    }
+  }
+}
+
+// Decompress: one lane writes one 16-byte chunk (8 dense positions).
+template <int N, int M>
+__global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restrict__ values,
+                                                         const uint32_t* __restrict__ idx, int64_t R,
+                                                         int64_t K, int64_t idx_row_words,
+                                                         uint16_t* __restrict__ Wout, int64_t ldw) {
+  using PS = PackShape<N, M>;
+  const int64_t chunks = K / 8;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t r = gid / chunks;
+  const int64_t c = gid - r * chunks;
+  if (r >= R) return;
+  const int64_t S = K / M * N;
+  const uint32_t* irow = idx + r * idx_row_words;
+  const int64_t bit0 = c * PS::BPL;
+  const int64_t wi = bit0 >> 5;
+  const int sh = int(bit0 & 31);
+  uint64_t both = irow[wi];
+  if (sh + PS::BPL > 32 && wi + 1 < idx_row_words) both |= uint64_t(irow[wi + 1]) << 32;
+  const uint32_t lane_idx = uint32_t(both >> sh);
+  uint32_t outv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < PS::SPL; ++s) {
+    const int g = s / N;
+    const int p = int((lane_idx >> (s * PS::B)) & ((1u << PS::B) - 1));
+    const uint32_t v = values[r * S + c * PS::SPL + s];
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (p == i) outv[g * M + i] = v;
+  }
+  uint4 o;
+  o.x = outv[0] | (outv[1] << 16);
+  o.y = outv[2] | (outv[3] << 16);
+  o.z = outv[4] | (outv[5] << 16);
+  o.w = outv[6] | (outv[7] << 16);
+  *reinterpret_cast<uint4*>(Wout + r * ldw + c * 8) = o;
+}
+
+template <int N, int M>
+hipError_t prune_pack_t(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, uint16_t* values,
+                        uint32_t* idx, int64_t idx_row_words, hipStream_t s) {
+  using PS = PackShape<N, M>;
+  const int64_t chunks = K / 8;
+  const int64_t lanes_per_row = (chunks + PS::L - 1) / PS::L * PS::L;
+  const int64_t threads = R * lanes_per_row;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prune_pack_kernel<N, M>), dim3(unsigned(blocks)), dim3(256), 0, s, W, R, K,
+                     ldw, lanes_per_row, values, idx, idx_row_words);
+  return hipGetLastError();
+}
+
+template <int N, int M>
+hipError_t decompress_t(const uint16_t* values, const uint32_t* idx, int64_t R, int64_t K,
+                        int64_t idx_row_words, uint16_t* W, int64_t ldw, hipStream_t s) {
+  const int64_t threads = R * (K / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decompress_kernel<N, M>), dim3(unsigned(blocks)), dim3(256), 0, s, values, idx,
+                     R, K, idx_row_words, W, ldw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prune_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                             uint16_t* values, uint32_t* idx, int64_t idx_row_words,
+                             hipStream_t s) {
+  if (n == 2 && m == 4) return prune_pack_t<2, 4>(W, R, K, ldw, values, idx, idx_row_words, s);
+  if (n == 1 && m == 4) return prune_pack_t<1, 4>(W, R, K, ldw, values, idx, idx_row_words, s);
+  if (n == 1 && m == 8) return prune_pack_t<1, 8>(W, R, K, ldw, values, idx, idx_row_words, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decompress(const uint16_t* values, const uint32_t* idx, int64_t R, int64_t K,
+                             int n, int m, int64_t idx_row_words, uint16_t* W, int64_t ldw,
+                             hipStream_t s) {
+  if (n == 2 && m == 4) return decompress_t<2, 4>(values, idx, R, K, idx_row_words, W, ldw, s);
+  if (n == 1 && m == 4) return decompress_t<1, 4>(values, idx, R, K, idx_row_words, W, ldw, s);
+  if (n == 1 && m == 8) return decompress_t<1, 8>(values, idx, R, K, idx_row_words, W, ldw, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nm

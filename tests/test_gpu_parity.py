@@ -1,0 +1,244 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Pack: values and index words bit-exact.  GEMM: max floored relative error
+<= 1e-2 against the fp64 oracle, and every element inside the fp32
+summation bound; exact-arithmetic cases bit-exact.
+"""
+import numpy as np
+import pytest
+
+import nm_inputs
+import structured_sparse_gemm_nm_amd as nm
+from oracle import nm_oracle as O
+from gpu_util import (assert_close, bits_of, error_bound, log, oracle_pack, to_dev, words_of)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W_CASES = [(1, 2, 4), (2, 2, 4), (3, 2, 4), (4, 1, 4), (4, 1, 8), (5, 2, 4)]
+
+
+def gpu_compress(w_bits, dt, n, m, ldw=None):
+    R, K = w_bits.shape
+    if ldw is not None and ldw != K:
+        big = np.zeros((R, ldw), dtype=np.uint16)
+        big[:, :K] = w_bits
+        Wd = to_dev(big, dt)[:, :K]
+    else:
+        Wd = to_dev(w_bits, dt)
+    vals, idx = nm.nm_compress(Wd, n, m)
+    torch.cuda.synchronize()
+    return vals, idx
+
+
+# ---------------------------------------------------------------------------
+# prune + pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wid,n,m", W_CASES)
+def test_compress_workloads_bit_exact(wid, n, m):
+    wl = nm_inputs.WORKLOADS[wid]
+    log(f"compress workload {wid} {wl.R}x{wl.K} {n}:{m} {wl.dtype}")
+    w, ref_vals, ref_idx = oracle_pack(wid, n, m)
+    vals, idx = gpu_compress(w, wl.dtype, n, m)
+    assert np.array_equal(bits_of(vals), ref_vals)
+    assert np.array_equal(words_of(idx), ref_idx)
+
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("R,K,ldw", [(1, 16, 16), (3, 48, 56), (37, 80, 80), (129, 1040, 1048),
+                                     (5, 272, 272), (64, 256, 320)])
+def test_compress_ragged_and_ties(R, K, ldw, n, m, dt):
+    if K % m:
+        pytest.skip("K not a multiple of m")
+    log(f"compress ragged R={R} K={K} ldw={ldw} {n}:{m} {dt}")
+    # small integers with random signs: ties everywhere, +-0 included
+    w = nm_inputs.integer_half((R, K), -3, 3, dt, 40, 0, R * 7 + K)
+    vals, idx = gpu_compress(w, dt, n, m, ldw=ldw)
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    assert np.array_equal(bits_of(vals), ref_vals)
+    assert np.array_equal(words_of(idx), ref_idx)
+    # and a normal draw
+    w2 = nm_inputs.normal_half((R, K), 0.02, dt, 41, 0, R + K)
+    vals, idx = gpu_compress(w2, dt, n, m, ldw=ldw)
+    ref_vals, ref_idx = O.prune_pack(w2, n, m)
+    assert np.array_equal(bits_of(vals), ref_vals)
+    assert np.array_equal(words_of(idx), ref_idx)
+
+
+def test_compress_worked_row():
+    log("compress worked row")
+    row = [0.5, 0.0, 0.0, -2.0, 0.0, 3.0, -1.0, 0.0] * 2
+    w = np.asarray([row], dtype=np.float16).view(np.uint16)
+    vals, idx = gpu_compress(w, "f16", 2, 4)
+    assert words_of(idx)[0, 0] & 0xFF == 0x9C
+    assert np.array_equal(words_of(idx), O.prune_pack(w, 2, 4)[1])
+
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+def test_decompress_round_trip(n, m):
+    log(f"decompress {n}:{m}")
+    w = nm_inputs.normal_half((70, 208), 1.0, "bf16", 42, 0, m)
+    vals, idx = gpu_compress(w, "bf16", n, m)
+    dense = nm.nm_decompress(vals, idx, 208, n, m)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    assert np.array_equal(bits_of(dense), O.decompress(ref_vals, ref_idx, 208, n, m))
+
+
+# ---------------------------------------------------------------------------
+# GEMM on the five workloads
+# ---------------------------------------------------------------------------
+
+def run_workload(wid, n, m, T, out_dtype=None):
+    wl = nm_inputs.WORKLOADS[wid]
+    w, ref_vals, ref_idx = oracle_pack(wid, n, m)
+    act = wl.activations(T)
+    perm = wl.permutation()
+    log(f"spmm workload {wid} R={wl.R} K={wl.K} T={T} {n}:{m} {wl.dtype} perm={perm is not None} out={out_dtype}")
+    vals, idx = gpu_compress(w, wl.dtype, n, m)
+    A = to_dev(act, wl.dtype)
+    if perm is None:
+        y = nm.nm_spmm(vals, idx, A, wl.K, n, m, out_dtype=out_dtype)
+    else:
+        y = nm.nm_spmm_perm(vals, idx, A, torch.from_numpy(perm).cuda(), wl.K, n, m,
+                            out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    yref = O.spmm_ref(ref_vals, ref_idx, wl.K, n, m, act, wl.dtype, perm=perm)
+    bound = error_bound(ref_vals, ref_idx, wl.K, n, m, act, wl.dtype, perm=perm)
+    return y, yref, bound, wl
+
+
+@pytest.mark.parametrize("wid,n,m,T", [(1, 2, 4, 64), (2, 2, 4, 2048), (3, 2, 4, 1), (3, 2, 4, 8),
+                                       (3, 2, 4, 16), (4, 1, 4, 512), (4, 1, 8, 512),
+                                       (5, 2, 4, 12608)])
+def test_spmm_workloads(wid, n, m, T):
+    y, yref, bound, wl = run_workload(wid, n, m, T)
+    max_rel, norm_rel = assert_close(y, yref, bound)
+    log(f"  max_rel={max_rel:.3e} norm_rel={norm_rel:.3e}")
+
+
+@pytest.mark.parametrize("wid,n,m,T", [(1, 2, 4, 64), (4, 1, 8, 512), (3, 2, 4, 16)])
+def test_spmm_half_output(wid, n, m, T):
+    wl = nm_inputs.WORKLOADS[wid]
+    od = torch.float16 if wl.dtype == "f16" else torch.bfloat16
+    y, yref, bound, wl = run_workload(wid, n, m, T, out_dtype=od)
+    assert y.dtype == od
+    assert_close(y, yref, bound, out_half=wl.dtype)
+
+
+# ---------------------------------------------------------------------------
+# exact-arithmetic cases: bit-exact regardless of summation order
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_identity_activations_exact(n, m, dt):
+    # act = I (T = K): Y^T = W_nm^T exactly; every index decides one output
+    R, K = 96, 256
+    log(f"identity X {n}:{m} {dt}")
+    w = nm_inputs.normal_half((R, K), 1.0, dt, 43, 0, m)
+    vals, idx = gpu_compress(w, dt, n, m)
+    eye = nm_inputs.to_half_bits(np.eye(K, dtype=np.float32), dt)
+    y = nm.nm_spmm(vals, idx, to_dev(eye, dt), K, n, m)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    want = O.half_bits_to_f64(O.decompress(ref_vals, ref_idx, K, n, m), dt)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64).T, want)
+
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("R,K,T", [(256, 4096, 256), (100, 80, 37), (33, 16, 5), (300, 1024, 130)])
+def test_integer_gemm_exact(R, K, T, n, m):
+    if K % m:
+        pytest.skip("K not a multiple of m")
+    log(f"integer gemm R={R} K={K} T={T} {n}:{m}")
+    w = nm_inputs.integer_half((R, K), -3, 3, "f16", 44, 0, K)
+    act = nm_inputs.integer_half((T, K), -2, 2, "f16", 44, 1, K)
+    vals, idx = gpu_compress(w, "f16", n, m)
+    y = nm.nm_spmm(vals, idx, to_dev(act, "f16"), K, n, m)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "f16")
+    assert np.array_equal(y.cpu().numpy().astype(np.float64).T, yref)
+
+
+# ---------------------------------------------------------------------------
+# permutation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+def test_perm_properties(n, m):
+    R, K, T = 200, 768, 300
+    log(f"perm properties {n}:{m}")
+    w = nm_inputs.normal_half((R, K), 0.02, "f16", 45, 0, m)
+    act = nm_inputs.normal_half((T, K), 1.0, "f16", 45, 1, m)
+    perm = nm_inputs.random_permutation(K, 45, m)
+    vals, idx = gpu_compress(w, "f16", n, m)
+    A = to_dev(act, "f16")
+    P = torch.from_numpy(perm).cuda()
+    nm.nm_check_perm(P)
+    y_perm = nm.nm_spmm_perm(vals, idx, A, P, K, n, m)
+    ident = torch.arange(K, dtype=torch.int32, device="cuda")
+    y_id = nm.nm_spmm_perm(vals, idx, A, ident, K, n, m)
+    y_plain = nm.nm_spmm(vals, idx, A, K, n, m)
+    A_perm = A[:, P.long()].contiguous()
+    y_gathered = nm.nm_spmm(vals, idx, A_perm, K, n, m)
+    torch.cuda.synchronize()
+    assert torch.equal(y_id, y_plain)                 # identity map = plain product
+    assert torch.equal(y_perm, y_gathered)            # index map = reading a permuted copy
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "f16", perm=perm)
+    assert_close(y_perm, yref, error_bound(ref_vals, ref_idx, K, n, m, act, "f16", perm=perm))
+
+
+def test_check_perm_rejects_non_permutation():
+    bad = torch.tensor([0, 1, 1, 3] * 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(nm.NMError):
+        nm.nm_check_perm(bad)
+
+
+# ---------------------------------------------------------------------------
+# ragged shapes, strides, canaries, determinism
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("R,K,T", [(1, 16, 1), (17, 48, 3), (255, 80, 129), (258, 208, 65),
+                                   (513, 1040, 17), (64, 64, 200), (1000, 512, 2)])
+def test_spmm_ragged(R, K, T, n, m):
+    if K % m:
+        pytest.skip("K not a multiple of m")
+    log(f"spmm ragged R={R} K={K} T={T} {n}:{m}")
+    dt = "bf16"
+    w = nm_inputs.normal_half((R, K), 0.5, dt, 46, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 46, 1, R + K + T)
+    vals, idx = gpu_compress(w, dt, n, m)
+    # act with a wider leading dimension, Y with padding columns holding a canary
+    ldx = K + 24
+    big = np.zeros((T, ldx), dtype=np.uint16)
+    big[:, :K] = act
+    A = to_dev(big, dt)[:, :K]
+    ldy = (R + 3) // 4 * 4 + 8
+    Yfull = torch.full((T, ldy), 12345.0, dtype=torch.float32, device="cuda")
+    Y = Yfull[:, :R]
+    nm.nm_spmm(vals, idx, A, K, n, m, out=Y)
+    torch.cuda.synchronize()
+    assert torch.all(Yfull[:, R:] == 12345.0), "write outside the output"
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt)
+    assert_close(Y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt))
+
+
+def test_spmm_deterministic_and_empty():
+    log("determinism")
+    wl = nm_inputs.WORKLOADS[1]
+    w, _, _ = oracle_pack(1, 2, 4)
+    vals, idx = gpu_compress(w, "f16", 2, 4)
+    A = to_dev(wl.activations(), "f16")
+    y1 = nm.nm_spmm(vals, idx, A, wl.K, 2, 4)
+    y2 = nm.nm_spmm(vals, idx, A, wl.K, 2, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    empty = nm.nm_spmm(vals, idx, A[:0], wl.K, 2, 4)
+    assert empty.shape == (0, wl.R)
