@@ -116,8 +116,8 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
  *                out_dtype NM_F32 (default) or the input dtype (RNE rounded).
  *   Y[t, r] = sum_k W_nm[r, k] * act[t, k], products and sums in fp32.
  * Shapes: R >= 1, T >= 0 (T == 0 enqueues nothing), K >= 16, K % 16 == 0,
- * K % m == 0.  Alignment: every pointer 16-byte aligned, ldx % 8 == 0,
- * ldy % 4 == 0.  Y must not overlap values, idx or act (NM_ERR_ALIAS).
+ * K % m == 0.  Alignment: every pointer 16-byte aligned, ldx % 8 == 0 (ldy
+ * is free).  Y must not overlap values, idx or act (NM_ERR_ALIAS).
  */
 nm_status nm_spmm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                   int dtype, const void* act, int64_t T, int64_t ldx, void* Y, int64_t ldy,

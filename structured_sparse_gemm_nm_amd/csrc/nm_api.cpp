@@ -99,7 +99,6 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   if (!values || !idx || !act || !Y || (want_perm && !perm))
     return fail(NM_ERR_NULL, "values, idx, act, Y%s must be non-NULL", want_perm ? ", perm" : "");
   if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of 8", (long long)ldx);
-  if (ldy % 4) return fail(NM_ERR_ALIGN, "ldy = %lld is not a multiple of 4", (long long)ldy);
   if (!aligned16(values) || !aligned16(idx) || !aligned16(act) || !aligned16(Y) ||
       (want_perm && !aligned16(perm)))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");

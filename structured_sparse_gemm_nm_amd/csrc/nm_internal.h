@@ -37,6 +37,14 @@ struct SpmmArgs {
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
 
+// Pipelined large-tile kernel (nm_spmm_pipe.hip) and the shapes it takes.
+bool spmm_pipe_applies(const SpmmArgs& a);
+hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s);
+
+// All-LDS 2:4 kernel (nm_spmm_lds.hip) and the shapes it takes.
+bool spmm_lds_applies(const SpmmArgs& a);
+hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);
+
 inline int index_bits(int m) {
   int b = 0;
   while ((1 << b) < m) ++b;

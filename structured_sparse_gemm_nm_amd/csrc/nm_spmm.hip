@@ -333,6 +333,7 @@ __global__ __launch_bounds__(256) void spmm_kernel(const uint16_t* __restrict__ 
   }
 
   // ---- epilogue: lane holds Y^T[t][r .. r+3] for each fragment
+  const bool vec_ok = (ldy & 3) == 0;  // 4-element row pieces stay aligned
 #pragma unroll
   for (int i = 0; i < C::FR; ++i) {
     const int r = R0 + wr * (BR / WR) + i * 16 + lq * 4;
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(256) void spmm_kernel(const uint16_t* __restrict__ 
       const f32x4 v = acc[i][j];
       if constexpr (OUT == NM_F32) {
         float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
-        if (r + 3 < R) {
+        if (vec_ok && r + 3 < R) {
           *reinterpret_cast<f32x4*>(y) = v;
         } else {
           for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void spmm_kernel(const uint16_t* __restrict__ 
         uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
         const uint16_t h0 = to_half_bits<DT>(v[0]), h1 = to_half_bits<DT>(v[1]);
         const uint16_t h2 = to_half_bits<DT>(v[2]), h3 = to_half_bits<DT>(v[3]);
-        if (r + 3 < R) {
+        if (vec_ok && r + 3 < R) {
           *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h0) | (uint32_t(h1) << 16),
                                                     uint32_t(h2) | (uint32_t(h3) << 16));
         } else {
@@ -411,6 +412,8 @@ hipError_t pick_dtype(const SpmmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
+  if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
+  if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
   if (a.n == 2 && a.m == 4) return pick_dtype<0>(a, s);
   if (a.n == 1 && a.m == 4) return pick_dtype<1>(a, s);
   if (a.n == 1 && a.m == 8) return pick_dtype<2>(a, s);

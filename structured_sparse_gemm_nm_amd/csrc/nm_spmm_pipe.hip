@@ -1,0 +1,334 @@
+// Pipelined sparse GEMM for large tiles (prefill shapes) on gfx950.
+//
+// Same product as nm_spmm.hip (Y^T[t, r] = sum_k W_nm[r, k] act[t, k], on
+// v_smfmac_f32_16x16x64), organised to keep several K steps of loads in flight:
+//
+//   * a workgroup (4 waves) owns a 256 x BT tile of Y^T; wave w owns rows
+//     [64w, 64w + 64) and all BT tokens, so its packed-A fragments are private
+//     and go straight from global memory into registers in the operand layout
+//     the instruction wants (16 bytes of values + 16 index bits per lane for
+//     2:4), NS - 1 steps ahead of use;
+//   * the activation tile (BT tokens x 64 K per step) is shared by the four
+//     waves through an NS-stage LDS ring filled with direct global->LDS loads;
+//     slot (token, 16-byte chunk c) sits at token*8 + (c ^ (token & 7)) so the
+//     fragment reads of 8 consecutive tokens hit distinct banks;
+//   * one barrier per step: it both publishes stage s and retires stage s - 1,
+//     whose slot the step's new loads then reuse.
+// The permuted product is not handled here (it gathers X through the index
+// map); shapes with K % 64 != 0 fall back as well.
+#include "nm_internal.h"
+
+namespace nm {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+constexpr int pat_n(int P) { return P == 0 ? 2 : 1; }
+constexpr int pat_m(int P) { return P == 2 ? 8 : 4; }
+
+template <int DT>
+__device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
+  if constexpr (DT == NM_F16) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
+                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, 0);
+  } else {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
+                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, 0);
+  }
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <int DT>
+__device__ inline uint16_t to_half_bits(float f) {
+  if constexpr (DT == NM_F16) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  } else {
+    return f32_to_bf16_rne(f);
+  }
+}
+
+// One lane's share of one 16-row A fragment for one K step.
+struct AFrag {
+  uint32_t v[4];  // packed values (pattern-dependent count used)
+  uint32_t ib;    // index bits of this lane's slice
+};
+
+// Issue the loads of lane (row, lq) for step s.  Rows past R load nothing.
+template <int P>
+__device__ inline void load_afrag(AFrag& f, const uint16_t* __restrict__ values,
+                                  const uint32_t* __restrict__ idx, int64_t S, int64_t words, int row,
+                                  int R, int s, int lq) {
+  if (row >= R) {
+    f.v[0] = f.v[1] = f.v[2] = f.v[3] = 0u;
+    f.ib = 0u;
+    return;
+  }
+  const uint16_t* vrow = values + int64_t(row) * S;
+  const unsigned char* irow = reinterpret_cast<const unsigned char*>(idx + int64_t(row) * words);
+  if constexpr (P == 0) {  // 2:4: 8 values (16 B), 16 index bits
+    const uint4 t = *reinterpret_cast<const uint4*>(vrow + s * 32 + lq * 8);
+    f.v[0] = t.x; f.v[1] = t.y; f.v[2] = t.z; f.v[3] = t.w;
+    f.ib = *reinterpret_cast<const uint16_t*>(irow + s * 8 + lq * 2);
+  } else if constexpr (P == 1) {  // 1:4: 4 values (8 B), 8 index bits
+    const uint2 t = *reinterpret_cast<const uint2*>(vrow + s * 16 + lq * 4);
+    f.v[0] = t.x; f.v[1] = t.y; f.v[2] = 0u; f.v[3] = 0u;
+    f.ib = irow[s * 4 + lq];
+  } else {  // 1:8: 2 values (4 B), 6 index bits at bit 24 s + 6 lq
+    f.v[0] = *reinterpret_cast<const uint32_t*>(vrow + s * 8 + lq * 2);
+    f.v[1] = f.v[2] = f.v[3] = 0u;
+    const int bit = 6 * lq;
+    const int byte = s * 3 + (bit >> 3);
+    uint32_t b = irow[byte];
+    if ((bit & 7) + 6 > 8) b |= uint32_t(irow[byte + 1]) << 8;
+    f.ib = b >> (bit & 7);
+  }
+}
+
+// Widen to the 2:4 smfmac operand (see nm_spmm.hip for the 1:4 / 1:8 rules).
+template <int P>
+__device__ inline void widen(const AFrag& f, u32x4& a, uint32_t& idx16) {
+  if constexpr (P == 0) {
+    a[0] = f.v[0]; a[1] = f.v[1]; a[2] = f.v[2]; a[3] = f.v[3];
+    idx16 = f.ib;
+  } else if constexpr (P == 1) {
+    a[0] = f.v[0] & 0xFFFFu; a[1] = f.v[0] >> 16; a[2] = f.v[1] & 0xFFFFu; a[3] = f.v[1] >> 16;
+    const uint32_t ib = f.ib;
+    const uint32_t t = (ib & 0x3u) | ((ib & 0xCu) << 2) | ((ib & 0x30u) << 4) | ((ib & 0xC0u) << 6);
+    idx16 = t | (t << 2);
+  } else {
+    const uint32_t v0 = f.v[0] & 0xFFFFu, v1 = f.v[0] >> 16;
+    const uint32_t p0 = f.ib & 7u, p1 = (f.ib >> 3) & 7u;
+    const bool h0 = p0 >= 4, h1 = p1 >= 4;
+    a[0] = h0 ? 0u : v0; a[1] = h0 ? v0 : 0u;
+    a[2] = h1 ? 0u : v1; a[3] = h1 ? v1 : 0u;
+    const uint32_t f0 = (p0 & 3u) * 5u, f1 = (p1 & 3u) * 5u;
+    idx16 = (h0 ? (f0 << 4) : f0) | (h1 ? (f1 << 12) : (f1 << 8));
+  }
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds: the fence
+// would wait for every outstanding global load (vmcnt(0)) and drain the
+// prefetch pipeline.  Callers wait for exactly the loads they need first; the
+// empty asm statements keep the compiler from moving LDS accesses across.
+__device__ inline void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int P, int DT, int OUT, int BT, int NS>
+__global__ __launch_bounds__(256, 1) void spmm_pipe_kernel(
+    const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K,
+    int64_t words, const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y,
+    int64_t ldy, int tilesR, int tilesT, int group_r) {
+  constexpr int BR = 256;
+  constexpr int FR = 4;                 // 16-row fragments per wave
+  constexpr int FT = BT / 16;           // 16-token fragments
+  constexpr int STAGE = BT * 128;       // bytes of one activation stage (BT x 64 halves)
+  constexpr int BLOADS = BT / 32;       // 16-byte direct loads per thread per stage
+  constexpr int ALOADS = FR * 2;        // A loads per thread per step (values + index)
+  constexpr int PER_STEP = BLOADS + ALOADS;
+  static_assert(NS >= 2, "at least double buffering");
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
+
+  // ---- tile: XCD-aware remap, then groups of group_r row tiles
+  const int ntiles = tilesR * tilesT;
+  int b = blockIdx.x;
+  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+  const int per_group = group_r * tilesT;
+  const int grp = b / per_group;
+  const int rem = b - grp * per_group;
+  const int rows_in_grp = min(group_r, tilesR - grp * group_r);
+  const int tr = grp * group_r + rem % rows_in_grp;
+  const int tt = rem / rows_in_grp;
+  const int R0 = tr * BR, T0 = tt * BT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lq = lane >> 4;
+  const int64_t S = int64_t(K) / pat_m(P) * pat_n(P);
+  const int nsteps = K >> 6;
+
+  // activation slots this thread fills each stage: instruction j covers slots
+  // [(wave*BLOADS + j)*64, +64), lane l takes slot base + l
+  const uint16_t* bsrc[BLOADS];
+#pragma unroll
+  for (int j = 0; j < BLOADS; ++j) {
+    const int slot = (wave * BLOADS + j) * 64 + lane;
+    const int tok = slot >> 3;
+    const int chunk = (slot & 7) ^ (tok & 7);
+    const int t = min(T0 + tok, T - 1);  // rows past T read a valid row; their outputs are dropped
+    bsrc[j] = act + int64_t(t) * ldx + chunk * 8;
+  }
+
+  auto issue_b = [&](int s, int stage) {
+#pragma unroll
+    for (int j = 0; j < BLOADS; ++j) {
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(bsrc[j] + s * 64),
+          (lds_byte*)(smem + stage * STAGE + (wave * BLOADS + j) * 1024), 16, 0, 0);
+    }
+  };
+
+  AFrag ar[NS][FR];
+  const int row0 = R0 + wave * 64 + li;
+  auto issue_a = [&](int s, AFrag* dst) {
+#pragma unroll
+    for (int i = 0; i < FR; ++i) load_afrag<P>(dst[i], values, idx, S, words, row0 + i * 16, R, s, lq);
+  };
+
+  f32x4 acc[FR][FT];
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- prologue: steps 0 .. NS-2 in flight
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (p < nsteps) {
+      issue_b(p, p);
+      issue_a(p, ar[p]);
+    }
+  }
+
+  for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int s = s0 + u;
+      if (s < nsteps) {
+        // step s's loads are done once at most the later steps' loads remain
+        if (s + NS - 2 < nsteps) wait_vmcnt<(NS - 2) * PER_STEP>();
+        else wait_vmcnt<0>();
+        barrier_no_fence();
+        if (s + NS - 1 < nsteps) {
+          issue_b(s + NS - 1, (u + NS - 1) % NS);
+          issue_a(s + NS - 1, ar[(u + NS - 1) % NS]);
+        }
+        const unsigned char* st = smem + u * STAGE;
+        u32x4 a[FR];
+        uint32_t ix[FR];
+#pragma unroll
+        for (int i = 0; i < FR; ++i) widen<P>(ar[u][i], a[i], ix[i]);
+        u32x8 bf[FT];
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          const int tok = j * 16 + li;
+          const int sw = tok & 7;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(st + (tok * 8 + (lq ^ sw)) * 16);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(st + (tok * 8 + ((lq + 4) ^ sw)) * 16);
+          bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+#pragma unroll
+          for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
+        // Schedule: the first half of the step's LDS fragment reads, the
+        // prefetch loads, two MFMAs, the second half of the reads (hidden
+        // behind the first half's MFMAs), then the remaining MFMAs.  Halves
+        // keep the outstanding LDS count within the 4-bit counter, so each
+        // MFMA waits only for its own fragment.
+        __builtin_amdgcn_sched_group_barrier(0x100, FT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, PER_STEP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FR * FT - 2, 0);
+      }
+    }
+  }
+
+  // ---- epilogue
+  const bool vec_ok = (ldy & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FR; ++i) {
+    const int r = R0 + wave * 64 + i * 16 + lq * 4;
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int t = T0 + j * 16 + li;
+      if (t >= T || r >= R) continue;
+      const f32x4 v = acc[i][j];
+      if constexpr (OUT == NM_F32) {
+        float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
+        if (vec_ok && r + 3 < R) {
+          *reinterpret_cast<f32x4*>(y) = v;
+        } else {
+          for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
+        }
+      } else {
+        uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
+        const uint16_t h0 = to_half_bits<DT>(v[0]), h1 = to_half_bits<DT>(v[1]);
+        const uint16_t h2 = to_half_bits<DT>(v[2]), h3 = to_half_bits<DT>(v[3]);
+        if (vec_ok && r + 3 < R) {
+          *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h0) | (uint32_t(h1) << 16),
+                                                    uint32_t(h2) | (uint32_t(h3) << 16));
+        } else {
+          const uint16_t hh[4] = {h0, h1, h2, h3};
+          for (int e = 0; e < 4 && r + e < R; ++e) y[e] = hh[e];
+        }
+      }
+    }
+  }
+}
+
+template <int P, int DT, int OUT, int BT, int NS>
+hipError_t launch_pipe(const SpmmArgs& a, hipStream_t s) {
+  const int tilesR = int((a.R + 255) / 256);
+  const int tilesT = int((a.T + BT - 1) / BT);
+  const int64_t ntiles = int64_t(tilesR) * tilesT;
+  if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int group_r = tilesR < 4 ? tilesR : 4;
+  hipLaunchKernelGGL((spmm_pipe_kernel<P, DT, OUT, BT, NS>), dim3(unsigned(ntiles)), dim3(256), 0, s,
+                     a.values, a.idx, int(a.R), int(a.K), a.idx_row_words, a.act, int(a.T), a.ldx,
+                     a.Y, a.ldy, tilesR, tilesT, group_r);
+  return hipGetLastError();
+}
+
+template <int P, int DT, int OUT>
+hipError_t pipe_tile(const SpmmArgs& a, hipStream_t s) {
+  return launch_pipe<P, DT, OUT, 128, 4>(a, s);
+}
+
+template <int P, int DT>
+hipError_t pipe_out(const SpmmArgs& a, hipStream_t s) {
+  return a.out_dtype == NM_F32 ? pipe_tile<P, DT, NM_F32>(a, s) : pipe_tile<P, DT, DT>(a, s);
+}
+
+template <int P>
+hipError_t pipe_dtype(const SpmmArgs& a, hipStream_t s) {
+  return a.dtype == NM_F16 ? pipe_out<P, NM_F16>(a, s) : pipe_out<P, NM_BF16>(a, s);
+}
+
+}  // namespace
+
+bool spmm_pipe_applies(const SpmmArgs& a) {
+  return a.perm == nullptr && (a.K % 64) == 0 && a.T >= 128 && a.R >= 256 && a.variant != 2;
+}
+
+hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s) {
+  if (a.n == 2 && a.m == 4) return pipe_dtype<0>(a, s);
+  if (a.n == 1 && a.m == 4) return pipe_dtype<1>(a, s);
+  if (a.n == 1 && a.m == 8) return pipe_dtype<2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nm

@@ -119,7 +119,7 @@ def test_spmm_workloads(wid, n, m, T):
     log(f"  max_rel={max_rel:.3e} norm_rel={norm_rel:.3e}")
 
 
-@pytest.mark.parametrize("wid,n,m,T", [(1, 2, 4, 64), (4, 1, 8, 512), (3, 2, 4, 16)])
+@pytest.mark.parametrize("wid,n,m,T", [(1, 2, 4, 64), (4, 1, 8, 512), (3, 2, 4, 16), (2, 2, 4, 2048)])
 def test_spmm_half_output(wid, n, m, T):
     wl = nm_inputs.WORKLOADS[wid]
     od = torch.float16 if wl.dtype == "f16" else torch.bfloat16
@@ -205,7 +205,8 @@ def test_check_perm_rejects_non_permutation():
 
 @pytest.mark.parametrize("n,m", nm.PATTERNS)
 @pytest.mark.parametrize("R,K,T", [(1, 16, 1), (17, 48, 3), (255, 80, 129), (258, 208, 65),
-                                   (513, 1040, 17), (64, 64, 200), (1000, 512, 2)])
+                                   (513, 1040, 17), (64, 64, 200), (1000, 512, 2),
+                                   (300, 1152, 257), (520, 1088, 300), (256, 128, 128)])
 def test_spmm_ragged(R, K, T, n, m):
     if K % m:
         pytest.skip("K not a multiple of m")
