@@ -41,6 +41,10 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
 bool spmm_pipe_applies(const SpmmArgs& a);
 hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s);
 
+// Few-token kernel (nm_spmm_decode.hip) and the shapes it takes.
+bool spmm_decode_applies(const SpmmArgs& a);
+hipError_t launch_spmm_decode(const SpmmArgs& a, hipStream_t s);
+
 // All-LDS 2:4 kernel (nm_spmm_lds.hip) and the shapes it takes.
 bool spmm_lds_applies(const SpmmArgs& a);
 hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);

@@ -412,6 +412,7 @@ hipError_t pick_dtype(const SpmmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
+  if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
   if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
   if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
   if (a.n == 2 && a.m == 4) return pick_dtype<0>(a, s);

@@ -243,3 +243,32 @@ def test_spmm_deterministic_and_empty():
     assert torch.equal(y1, y2)
     empty = nm.nm_spmm(vals, idx, A[:0], wl.K, 2, 4)
     assert empty.shape == (0, wl.R)
+
+
+# ---------------------------------------------------------------------------
+# few tokens (the decode kernel): ragged rows, odd T, a partial last K step,
+# with and without the permutation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("R,K,T,permuted", [(100, 4096, 13, False), (77, 336, 7, True),
+                                            (1030, 1024, 16, True), (5, 16, 1, False),
+                                            (600, 2064, 4, False)])
+def test_spmm_few_tokens(R, K, T, permuted, n, m):
+    if K % m:
+        pytest.skip("K not a multiple of m")
+    log(f"few tokens R={R} K={K} T={T} perm={permuted} {n}:{m}")
+    dt = "f16"
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 47, 0, R + K)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 47, 1, R + K)
+    vals, idx = gpu_compress(w, dt, n, m)
+    A = to_dev(act, dt)
+    perm = nm_inputs.random_permutation(K, 47, R) if permuted else None
+    if perm is None:
+        y = nm.nm_spmm(vals, idx, A, K, n, m)
+    else:
+        y = nm.nm_spmm_perm(vals, idx, A, torch.from_numpy(perm).cuda(), K, n, m)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt, perm=perm)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt, perm=perm))
