@@ -51,6 +51,9 @@ def parse():
                     help="copies of the inputs cycled through (defeats the 256 MB last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy, the reference a counter "
+                         "profile of this command scales HBM byte counters against")
     return ap.parse_args()
 
 
@@ -283,6 +286,12 @@ def main():
         "wall_s_timed": wall,
         "source_hash": hsh,
     }
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, n, m, T, args.cpu_reps)
     print(json.dumps(out), flush=True)

@@ -141,9 +141,16 @@ nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64
 nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
 
 /*
- * Kernel variant for nm_spmm / nm_spmm_perm.  0 = automatic (default),
- * 1 = sparse MFMA (v_smfmac) path, 2 = dense MFMA on decompressed LDS tiles.
- * Process-wide; meant for ablations and tests.
+ * Kernel family for nm_spmm / nm_spmm_perm, process-wide (ablations, tests).
+ *   0  choose by shape (default)
+ *   1  generic tiled kernel (LDS-staged operands, any shape)
+ *   2  register-prefetch pipelined kernel (K % 64 == 0, T >= 64, R >= 128)
+ *   3  all-LDS direct-load kernels (2:4; K % 128 == 0; the permuted one also
+ *      K <= 768)
+ *   4  few-token kernel (T <= 16, K <= 4096)
+ * A forced family that does not take the shape falls back to the choice by
+ * shape.  Every family computes the same product; all but 4 add the K steps
+ * in the same order and give the same bits.  NM_ERR_UNSUPPORTED outside 0..4.
  */
 nm_status nm_set_variant(int variant);
 

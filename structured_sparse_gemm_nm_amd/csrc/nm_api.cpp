@@ -239,7 +239,8 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream) {
 }
 
 nm_status nm_set_variant(int variant) {
-  if (variant < 0 || variant > 2) return fail(NM_ERR_UNSUPPORTED, "variant %d", variant);
+  if (variant < 0 || variant > nm::NM_VARIANT_MAX)
+    return fail(NM_ERR_UNSUPPORTED, "variant %d", variant);
   g_variant.store(variant, std::memory_order_relaxed);
   return ok();
 }

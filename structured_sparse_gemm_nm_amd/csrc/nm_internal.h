@@ -9,6 +9,9 @@
 
 namespace nm {
 
+enum { NM_VARIANT_AUTO = 0, NM_VARIANT_GENERIC = 1, NM_VARIANT_PIPE = 2, NM_VARIANT_LDS = 3,
+       NM_VARIANT_DECODE = 4, NM_VARIANT_MAX = 4 };
+
 // Launchers (defined next to their kernels).  Arguments are already
 // validated; each returns the hipError_t of its launch.
 hipError_t launch_prune_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
@@ -32,7 +35,7 @@ struct SpmmArgs {
   int64_t ldy;
   int out_dtype;         // NM_F32 or dtype
   int64_t idx_row_words;
-  int variant;           // 0 auto, 1 smfmac, 2 decompressed dense MFMA
+  int variant;           // NM_VARIANT_* (0 = choose by shape)
 };
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
@@ -44,6 +47,10 @@ hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s);
 // Few-token kernel (nm_spmm_decode.hip) and the shapes it takes.
 bool spmm_decode_applies(const SpmmArgs& a);
 hipError_t launch_spmm_decode(const SpmmArgs& a, hipStream_t s);
+
+// Permuted 2:4 kernel gathering from LDS (nm_spmm_perm.hip) and its shapes.
+bool spmm_perm_lds_applies(const SpmmArgs& a);
+hipError_t launch_spmm_perm_lds(const SpmmArgs& a, hipStream_t s);
 
 // All-LDS 2:4 kernel (nm_spmm_lds.hip) and the shapes it takes.
 bool spmm_lds_applies(const SpmmArgs& a);

@@ -411,14 +411,35 @@ hipError_t pick_dtype(const SpmmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
-  if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
-  if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
-  if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
+hipError_t launch_generic(const SpmmArgs& a, hipStream_t s) {
   if (a.n == 2 && a.m == 4) return pick_dtype<0>(a, s);
   if (a.n == 1 && a.m == 4) return pick_dtype<1>(a, s);
   if (a.n == 1 && a.m == 8) return pick_dtype<2>(a, s);
   return hipErrorInvalidValue;
+}
+
+// Kernel choice.  variant 0 picks by shape; 1..4 force one kernel family when
+// the shape allows it (ablations, tests), else fall back to the choice by shape.
+hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
+  switch (a.variant) {
+    case NM_VARIANT_GENERIC: return launch_generic(a, s);
+    case NM_VARIANT_PIPE:
+      if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
+      break;
+    case NM_VARIANT_LDS:
+      if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
+      if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
+      break;
+    case NM_VARIANT_DECODE:
+      if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
+      break;
+    default: break;
+  }
+  if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
+  if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
+  if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
+  if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
+  return launch_generic(a, s);
 }
 
 }  // namespace nm

@@ -540,7 +540,7 @@ hipError_t pick_dt(const SpmmArgs& a, hipStream_t s) {
 }  // namespace
 
 bool spmm_decode_applies(const SpmmArgs& a) {
-  return a.T <= 16 && a.K <= 8 * 8 * 64 && a.variant != 2;
+  return a.T <= 16 && a.K <= 8 * 8 * 64;
 }
 
 hipError_t launch_spmm_decode(const SpmmArgs& a, hipStream_t s) {

@@ -279,7 +279,7 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
 
 bool spmm_lds_applies(const SpmmArgs& a) {
   if (!(a.perm == nullptr && a.n == 2 && a.m == 4 && (a.K % 128) == 0 && a.T >= 128 &&
-        a.R >= 256 && a.variant != 2))
+        a.R >= 256))
     return false;
   // needs a workgroup LDS allocation of kLds bytes
   static int max_lds = -1;

@@ -66,16 +66,14 @@ struct AFrag {
   uint32_t ib;    // index bits of this lane's slice
 };
 
-// Issue the loads of lane (row, lq) for step s.  Rows past R load nothing.
+// Issue the loads of lane (row, lq) for step s.  Every lane issues them (rows
+// past R reread row R - 1 and their outputs are dropped), so each wave issues
+// exactly ALOADS_PER_FRAG loads per fragment: the counted waits rely on it.
 template <int P>
 __device__ inline void load_afrag(AFrag& f, const uint16_t* __restrict__ values,
                                   const uint32_t* __restrict__ idx, int64_t S, int64_t words, int row,
                                   int R, int s, int lq) {
-  if (row >= R) {
-    f.v[0] = f.v[1] = f.v[2] = f.v[3] = 0u;
-    f.ib = 0u;
-    return;
-  }
+  row = min(row, R - 1);
   const uint16_t* vrow = values + int64_t(row) * S;
   const unsigned char* irow = reinterpret_cast<const unsigned char*>(idx + int64_t(row) * words);
   if constexpr (P == 0) {  // 2:4: 8 values (16 B), 16 index bits
@@ -89,6 +87,9 @@ __device__ inline void load_afrag(AFrag& f, const uint16_t* __restrict__ values,
   } else {  // 1:8: 2 values (4 B), 6 index bits at bit 24 s + 6 lq
     f.v[0] = *reinterpret_cast<const uint32_t*>(vrow + s * 8 + lq * 2);
     f.v[1] = f.v[2] = f.v[3] = 0u;
+    // The 6 bits of lane lq sit in byte 3s + (6lq >> 3); lanes lq = 1, 2 also
+    // need the next byte (inside the step's 3 bytes).  Every wave holds all
+    // four lq values, so the second load is issued by every wave.
     const int bit = 6 * lq;
     const int byte = s * 3 + (bit >> 3);
     uint32_t b = irow[byte];
@@ -96,6 +97,9 @@ __device__ inline void load_afrag(AFrag& f, const uint16_t* __restrict__ values,
     f.ib = b >> (bit & 7);
   }
 }
+
+// Loads each wave issues per A fragment per step (see load_afrag).
+constexpr int aloads_per_frag(int P) { return P == 2 ? 3 : 2; }
 
 // Widen to the 2:4 smfmac operand (see nm_spmm.hip for the 1:4 / 1:8 rules).
 template <int P>
@@ -136,19 +140,20 @@ __device__ inline void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
-template <int P, int DT, int OUT, int BT, int NS>
-__global__ __launch_bounds__(256, 1) void spmm_pipe_kernel(
+template <int P, int DT, int OUT, int BR, int BT, int NS>
+__global__ __launch_bounds__(256) void spmm_pipe_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K,
     int64_t words, const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y,
     int64_t ldy, int tilesR, int tilesT, int group_r) {
-  constexpr int BR = 256;
-  constexpr int FR = 4;                 // 16-row fragments per wave
+  constexpr int WROWS = BR / 4;         // rows per wave
+  constexpr int FR = WROWS / 16;        // 16-row fragments per wave
   constexpr int FT = BT / 16;           // 16-token fragments
   constexpr int STAGE = BT * 128;       // bytes of one activation stage (BT x 64 halves)
   constexpr int BLOADS = BT / 32;       // 16-byte direct loads per thread per stage
-  constexpr int ALOADS = FR * 2;        // A loads per thread per step (values + index)
+  constexpr int ALOADS = FR * aloads_per_frag(P);  // A loads per wave per step
   constexpr int PER_STEP = BLOADS + ALOADS;
   static_assert(NS >= 2, "at least double buffering");
+  static_assert((NS - 2) * (BT / 32 + (BR / 64) * aloads_per_frag(P)) < 64, "vmcnt range");
   __shared__ __align__(16) unsigned char smem[NS * STAGE];
 
   // ---- tile: XCD-aware remap, then groups of group_r row tiles
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void spmm_pipe_kernel(
   };
 
   AFrag ar[NS][FR];
-  const int row0 = R0 + wave * 64 + li;
+  const int row0 = R0 + wave * WROWS + li;
   auto issue_a = [&](int s, AFrag* dst) {
 #pragma unroll
     for (int i = 0; i < FR; ++i) load_afrag<P>(dst[i], values, idx, S, words, row0 + i * 16, R, s, lq);
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void spmm_pipe_kernel(
   const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FR; ++i) {
-    const int r = R0 + wave * 64 + i * 16 + lq * 4;
+    const int r = R0 + wave * WROWS + i * 16 + lq * 4;
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
       const int t = T0 + j * 16 + li;
@@ -290,14 +295,14 @@ __global__ __launch_bounds__(256, 1) void spmm_pipe_kernel(
   }
 }
 
-template <int P, int DT, int OUT, int BT, int NS>
+template <int P, int DT, int OUT, int BR, int BT, int NS>
 hipError_t launch_pipe(const SpmmArgs& a, hipStream_t s) {
-  const int tilesR = int((a.R + 255) / 256);
+  const int tilesR = int((a.R + BR - 1) / BR);
   const int tilesT = int((a.T + BT - 1) / BT);
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int group_r = tilesR < 4 ? tilesR : 4;
-  hipLaunchKernelGGL((spmm_pipe_kernel<P, DT, OUT, BT, NS>), dim3(unsigned(ntiles)), dim3(256), 0, s,
+  hipLaunchKernelGGL((spmm_pipe_kernel<P, DT, OUT, BR, BT, NS>), dim3(unsigned(ntiles)), dim3(256), 0, s,
                      a.values, a.idx, int(a.R), int(a.K), a.idx_row_words, a.act, int(a.T), a.ldx,
                      a.Y, a.ldy, tilesR, tilesT, group_r);
   return hipGetLastError();
@@ -305,7 +310,11 @@ hipError_t launch_pipe(const SpmmArgs& a, hipStream_t s) {
 
 template <int P, int DT, int OUT>
 hipError_t pipe_tile(const SpmmArgs& a, hipStream_t s) {
-  return launch_pipe<P, DT, OUT, 128, 4>(a, s);
+  // 256 x 128 tiles when they cover the chip's 256 CUs, else 128 x 64
+  const int64_t big = ((a.R + 255) / 256) * ((a.T + 127) / 128);
+  if (big >= 256) return launch_pipe<P, DT, OUT, 256, 128, 4>(a, s);
+  // small tiles do little MFMA work per step: keep 7 steps of loads in flight
+  return launch_pipe<P, DT, OUT, 128, 64, 8>(a, s);
 }
 
 template <int P, int DT>
@@ -321,7 +330,7 @@ hipError_t pipe_dtype(const SpmmArgs& a, hipStream_t s) {
 }  // namespace
 
 bool spmm_pipe_applies(const SpmmArgs& a) {
-  return a.perm == nullptr && (a.K % 64) == 0 && a.T >= 128 && a.R >= 256 && a.variant != 2;
+  return a.perm == nullptr && (a.K % 64) == 0 && a.T >= 64 && a.R >= 128;
 }
 
 hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s) {

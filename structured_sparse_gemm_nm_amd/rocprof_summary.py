@@ -1,0 +1,90 @@
+"""Summarise rocprofv3 result databases (rocpd SQLite) for this library's kernels.
+
+    python -m structured_sparse_gemm_nm_amd.rocprof_summary trace  <dir>
+    python -m structured_sparse_gemm_nm_amd.rocprof_summary counters <dir>...
+
+`trace`: per-kernel call count and mean duration from a --kernel-trace run.
+`counters`: per-kernel mean of every collected counter (one directory per
+--pmc pass).  With FETCH_SIZE / WRITE_SIZE passes that include the plain
+256 MiB copy of `bench.py --copy-calibration`, it also prints the HBM bytes
+per launch of each kernel scaled by the copy's bytes / counter ratio.
+"""
+from __future__ import annotations
+
+import collections
+import glob
+import os
+import sqlite3
+import sys
+
+COPY_BYTES = 64 * 1024 * 1024 * 4
+
+
+def _dbs(path):
+    return sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+
+
+def short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name.split("(")[0] if "(" in name else name
+
+
+def trace(path):
+    rows = collections.defaultdict(list)
+    for db in _dbs(path):
+        con = sqlite3.connect(db)
+        for name, start, end in con.execute("select name, start, end from kernels"):
+            rows[name].append((end - start) / 1000.0)
+    out = []
+    for name, d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        out.append((short(name), len(d), sum(d) / len(d)))
+    return out
+
+
+def counters(paths):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for db in _dbs(path):
+            con = sqlite3.connect(db)
+            q = "select dispatch_id, kernel_name, counter_name, value from counters_collection"
+            per = collections.defaultdict(float)
+            names = {}
+            for did, kname, cname, val in con.execute(q):
+                per[(did, cname)] += val
+                names[did] = kname
+            for (did, cname), val in per.items():
+                agg[short(names[did])][cname].append(val)
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in agg.items()}
+
+
+def main(argv):
+    if len(argv) < 2 or argv[0] not in ("trace", "counters"):
+        print(__doc__)
+        return 2
+    if argv[0] == "trace":
+        print(f"{'kernel':70s} {'calls':>6s} {'mean_us':>10s}")
+        for name, n, us in trace(argv[1]):
+            print(f"{name[:70]:70s} {n:6d} {us:10.3f}")
+        return 0
+    res = counters(argv[1:])
+    copy = next((v for k, v in res.items() if "copyBuffer" in k or "copy" in k.lower()), None)
+    scale = {}
+    if copy:
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if copy.get(c):
+                scale[c] = COPY_BYTES / (copy[c] * 1024.0)
+    for k, d in sorted(res.items()):
+        line = ", ".join(f"{c}={v:.1f}" for c, v in sorted(d.items()))
+        print(f"{k[:90]}: {line}")
+        hbm = [d[c] * 1024.0 * scale[c] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in d and c in scale]
+        if len(hbm) == 2:
+            print(f"    HBM bytes per launch (copy-scaled): read {hbm[0]/1e6:.2f} MB, "
+                  f"write {hbm[1]/1e6:.2f} MB, total {sum(hbm)/1e6:.2f} MB")
+    if scale:
+        print("copy calibration (bytes per counter byte): " +
+              ", ".join(f"{c} x{v:.3f}" for c, v in scale.items()))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

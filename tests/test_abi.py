@@ -145,6 +145,9 @@ def test_decompress_and_misc_errors():
     assert L.nm_check_perm(None, 16, None) == 1
     assert L.nm_check_perm(FAKE, 0, None) == 2
     assert L.nm_set_variant(7) == 3
+    assert L.nm_set_variant(-1) == 3
+    for v in range(5):
+        assert L.nm_set_variant(v) == 0
     assert L.nm_set_variant(0) == 0
 
 

@@ -272,3 +272,62 @@ def test_spmm_few_tokens(R, K, T, permuted, n, m):
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt, perm=perm)
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt, perm=perm))
+
+
+# ---------------------------------------------------------------------------
+# permuted 2:4 prefill path (X tile gathered through perm from LDS)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("R,K,T", [(300, 768, 100), (512, 128, 64), (256, 640, 130), (3072, 768, 197)])
+def test_perm_prefill(R, K, T, dt):
+    log(f"perm prefill R={R} K={K} T={T} {dt}")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 48, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 48, 1, R + K + T)
+    perm = nm_inputs.random_permutation(K, 48, R + T)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    P = torch.from_numpy(perm).cuda()
+    y = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4)
+    # every prefill kernel adds the K steps in order from zero, so reading a
+    # permuted copy must give the same bits
+    y_copy = nm.nm_spmm(vals, idx, A[:, P.long()].contiguous(), K, 2, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_copy)
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
+
+
+# ---------------------------------------------------------------------------
+# every kernel family on the same inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+def test_kernel_families_agree(n, m):
+    R, K, T = 512, 1024, 256
+    log(f"kernel families {n}:{m}")
+    w = nm_inputs.normal_half((R, K), 0.02, "bf16", 49, 0, m)
+    act = nm_inputs.normal_half((T, K), 1.0, "bf16", 49, 1, m)
+    vals, idx = gpu_compress(w, "bf16", n, m)
+    A = to_dev(act, "bf16")
+    outs = {}
+    try:
+        for v in (1, 2, 3):
+            nm.nm_set_variant(v)
+            outs[v] = nm.nm_spmm(vals, idx, A, K, n, m)
+        nm.nm_set_variant(4)
+        y_few = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m)
+        nm.nm_set_variant(1)
+        y_few_ref = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m)
+    finally:
+        nm.nm_set_variant(0)
+    torch.cuda.synchronize()
+    # families that add the K steps in order from zero give identical bits
+    assert torch.equal(outs[1], outs[2]) and torch.equal(outs[1], outs[3])
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "bf16")
+    assert_close(outs[1], yref, error_bound(ref_vals, ref_idx, K, n, m, act, "bf16"))
+    # the few-token family splits K: same product within the summation bound
+    assert_close(y_few, yref[:, :16], error_bound(ref_vals, ref_idx, K, n, m, act[:16], "bf16"))
+    assert_close(y_few_ref, yref[:, :16])
