@@ -3,24 +3,27 @@
 //
 // Same product as nm_spmm.hip (Y^T[t, r] = sum_k W_nm[r, k] act[t, k] on
 // v_smfmac_f32_16x16x64).  What this kernel is organised around is the cost
-// of L2 requests: every 64-lane load instruction is pointed at whole 128-byte
-// lines.  A direct load deposits lane l's 16 bytes at slot base + l of LDS, so
-// the LDS layout is chosen by which global address each lane reads:
+// of L2 requests: no lane loads fewer than 16 bytes and every instruction
+// reads 64- or 128-byte runs.  A direct load deposits lane l's 16 bytes at
+// slot base + l of LDS, so the LDS layout is chosen by which global address
+// each lane reads:
 //
-//   packed values  stage = 2 K steps; slot (row, step u, quarter q) at
-//                  (row*2 + u)*4 + (q ^ ((row >> 1) & 3)): one instruction
-//                  covers 8 rows x 128 contiguous bytes, and a fragment read
-//                  (16 rows, one quarter) hits 8 distinct bank groups per
-//                  8 lanes;
-//   activations    stage = 2 K steps; slot (u, token, chunk c) at
-//                  (u*BT + token)*8 + (c ^ (token & 7)): 8 tokens x 128 bytes
-//                  per instruction;
+//   packed values  one K step per stage; slot (row, quarter q) at
+//                  row*4 + (q ^ ((row >> 2) & 3)): an instruction covers 16 rows
+//                  x 64 bytes, and a fragment read by 8 consecutive rows hits
+//                  distinct bank groups;
+//   activations    one K step per stage; slot (token, chunk c) at
+//                  token*8 + (c ^ (token & 7)): 8 tokens x 128 bytes per
+//                  instruction;
 //   index bits     block = 8 K steps (64 bytes per row); slot (row, chunk) at
 //                  row*4 + (chunk ^ ((row >> 2) & 3)).
 //
-// A workgroup (4 waves) owns a 256 x BT tile; wave w owns rows [64w, 64w+64).
-// Stages are double buffered: after one barrier per stage the next stage's
-// loads are issued and the current stage's two steps are computed.
+// A workgroup (4 waves) owns a 256 x 128 tile; waves are 2 x 2, each owning
+// 128 rows x 64 tokens (8 x 4 fragments: the fragment-read volume per MFMA is
+// lowest for this split).  Stages form a 4-deep ring, so three K steps of
+// loads are in flight while one is computed; each step waits (counted vmcnt)
+// for exactly its own loads and passes one fence-free barrier, which both
+// publishes it and retires the slot the step's new loads reuse.
 #include "nm_internal.h"
 
 namespace nm {
@@ -79,21 +82,29 @@ __device__ inline void dma16(const void* src, unsigned char* lds_dst) {
 
 constexpr int kBR = 256;
 constexpr int kBT = 128;
-constexpr int kStageB = 2 * kBT * 128;   // activations, 2 steps
-constexpr int kStageA = kBR * 2 * 64;    // packed values, 2 steps
-constexpr int kBlockI = kBR * 64;        // index bits, 8 steps
-constexpr int kLds = 2 * (kStageB + kStageA) + 2 * kBlockI;
+constexpr int kNS = 4;                     // one-K-step stages in the ring
+constexpr int kStageB = kBT * 128;         // activations, one step
+constexpr int kStageA = kBR * 64;          // packed values, one step
+constexpr int kBlockI = kBR * 64;          // index bits, 8 steps
+constexpr int kLds = kNS * (kStageB + kStageA) + 2 * kBlockI;
+constexpr int kPerStep = 8;                // direct loads per wave per step (4 B + 4 A)
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 template <int DT, int OUT>
 __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K,
     const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y, int64_t ldy,
     int tilesR, int tilesT, int group_r) {
-  constexpr int FR = 4, FT = kBT / 16;
+  constexpr int FR = 8, FT = kBT / 32;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* bbuf = smem;                          // [2][kStageB]
-  unsigned char* abuf = smem + 2 * kStageB;            // [2][kStageA]
-  unsigned char* ibuf = smem + 2 * (kStageB + kStageA);  // [2][kBlockI]
+  unsigned char* bbuf = smem;                              // [kNS][kStageB]
+  unsigned char* abuf = smem + kNS * kStageB;              // [kNS][kStageA]
+  unsigned char* ibuf = smem + kNS * (kStageB + kStageA);  // [2][kBlockI]
 
   // ---- tile: XCD-aware remap, then groups of group_r row tiles sharing X
   const int ntiles = tilesR * tilesT;
@@ -110,37 +121,34 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
+  const int wr = wave >> 1, wt = wave & 1;
   const int nsteps = K >> 6;                 // K % 128 == 0 on this path
-  const int nstages = nsteps >> 1;
   const int S = K >> 1;                      // packed values per row
   const int irow_bytes = K >> 3;             // index bytes per row (2 bits per survivor)
 
-  // Per-thread source pointers for the direct loads.  Instruction j of a
-  // wave fills slots [(wave*8 + j)*64, +64); lane l takes slot base + l.
-  // Activations: slot -> (u, token, chunk)
-  const unsigned char* bsrc[8];
+  // Per-lane source pointers.  Instruction j of a wave fills slots
+  // [(wave*4 + j)*64, +64); lane l takes slot base + l.
+  // Activations, one step: slot (token, chunk) at token*8 + (c ^ (token & 7)).
+  const unsigned char* bsrc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int slot = (wave * 8 + j) * 64 + lane;
-    const int u = slot / (kBT * 8);
-    const int rest = slot % (kBT * 8);
-    const int tok = rest >> 3;
-    const int c = (rest & 7) ^ (tok & 7);
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int tok = slot >> 3;
+    const int c = (slot & 7) ^ (tok & 7);
     const int t = min(T0 + tok, T - 1);
-    bsrc[j] = reinterpret_cast<const unsigned char*>(act + int64_t(t) * ldx + u * 64 + c * 8);
+    bsrc[j] = reinterpret_cast<const unsigned char*>(act + int64_t(t) * ldx + c * 8);
   }
-  // Packed values: slot -> (row, u, quarter)
-  const unsigned char* asrc[8];
+  // Packed values, one step: slot (row, quarter) at row*4 + (q ^ ((row >> 2) & 3)).
+  const unsigned char* asrc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int slot = (wave * 8 + j) * 64 + lane;
-    const int row = slot >> 3;
-    const int u = (slot >> 2) & 1;
-    const int q = (slot & 3) ^ ((row >> 1) & 3);
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int row = slot >> 2;
+    const int q = (slot & 3) ^ ((row >> 2) & 3);
     const int r = min(R0 + row, R - 1);
-    asrc[j] = reinterpret_cast<const unsigned char*>(values + int64_t(r) * S + u * 32 + q * 8);
+    asrc[j] = reinterpret_cast<const unsigned char*>(values + int64_t(r) * S + q * 8);
   }
-  // Index bits: slot -> (row, chunk); 4 instructions per wave per block
+  // Index bits, 8 steps: slot (row, chunk) at row*4 + (c ^ ((row >> 2) & 3)).
   const unsigned char* isrc[4];
   int ichunk[4];
 #pragma unroll
@@ -153,23 +161,23 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     isrc[j] = reinterpret_cast<const unsigned char*>(idx) + int64_t(r) * irow_bytes + c * 16;
   }
 
-  // Stage p covers K steps 2p and 2p + 1 (K % 128 == 0 on this path).
-  auto issue_stage = [&](int p, int buf) {
+  auto issue_step = [&](int s) {
+    const int buf = s & (kNS - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      dma16(bsrc[j] + int64_t(p) * 256, bbuf + buf * kStageB + (wave * 8 + j) * 1024);
+    for (int j = 0; j < 4; ++j)
+      dma16(bsrc[j] + int64_t(s) * 128, bbuf + buf * kStageB + (wave * 4 + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      dma16(asrc[j] + int64_t(p) * 128, abuf + buf * kStageA + (wave * 8 + j) * 1024);
+    for (int j = 0; j < 4; ++j)
+      dma16(asrc[j] + int64_t(s) * 64, abuf + buf * kStageA + (wave * 4 + j) * 1024);
   };
-  auto issue_index = [&](int q, int buf) {
+  auto issue_index = [&](int q) {
     const int steps_left = nsteps - 8 * q;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // chunk c holds steps 2c, 2c+1 of the block (steps_left is even); past
       // the row's end the lane rereads chunk 0 of the block
       const int back = (2 * ichunk[j] < steps_left) ? 0 : ichunk[j] * 16;
-      dma16(isrc[j] + int64_t(q) * 64 - back, ibuf + buf * kBlockI + (wave * 4 + j) * 1024);
+      dma16(isrc[j] + int64_t(q) * 64 - back, ibuf + (q & 1) * kBlockI + (wave * 4 + j) * 1024);
     }
   };
 
@@ -179,57 +187,67 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
 #pragma unroll
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_index(0, 0);
-  issue_stage(0, 0);
+  // ---- prologue: index block 0, then steps 0 .. kNS-2
+  issue_index(0);
+#pragma unroll
+  for (int p = 0; p < kNS - 1; ++p)
+    if (p < nsteps) issue_step(p);
 
-  for (int p = 0; p < nstages; ++p) {
-    wait_all_vm();
-    barrier_no_fence();
-    if (p + 1 < nstages) issue_stage(p + 1, (p + 1) & 1);
-    if ((p & 3) == 0 && 8 * (p / 4 + 1) < nsteps) issue_index(p / 4 + 1, (p / 4 + 1) & 1);
-    const unsigned char* sb = bbuf + (p & 1) * kStageB;
-    const unsigned char* sa = abuf + (p & 1) * kStageA;
-    const unsigned char* si = ibuf + ((p >> 2) & 1) * kBlockI;
+  for (int s = 0; s < nsteps; ++s) {
+    // Step s has landed once at most the loads issued after it remain: those
+    // of steps s+1, s+2 (an index block issued in between only makes the
+    // wait stricter).
+    if (s + 2 < nsteps) wait_vmcnt<2 * kPerStep>();
+    else if (s + 1 < nsteps) wait_vmcnt<kPerStep>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();  // publishes step s, retires step s - 1
+    if (s + kNS - 1 < nsteps) issue_step(s + kNS - 1);
+    if ((s & 7) == 0 && s + 8 < nsteps) issue_index((s >> 3) + 1);
+
+    const unsigned char* sb = bbuf + (s & (kNS - 1)) * kStageB;
+    const unsigned char* sa = abuf + (s & (kNS - 1)) * kStageA;
+    const unsigned char* si = ibuf + ((s >> 3) & 1) * kBlockI;
+    const int u8 = s & 7;
+    u32x4 a[FR];
+    uint32_t ix[FR];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int u8 = (2 * p + u) & 7;  // step inside the index block
-      u32x4 a[FR];
-      uint32_t ix[FR];
-#pragma unroll
-      for (int i = 0; i < FR; ++i) {
-        const int row = wave * 64 + i * 16 + li;
-        a[i] = *reinterpret_cast<const u32x4*>(sa + ((row * 2 + u) * 4 + (lq ^ ((row >> 1) & 3))) * 16);
-        const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
-        ix[i] = *reinterpret_cast<const uint16_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8 + lq * 2);
-      }
-      u32x8 bf[FT];
-#pragma unroll
-      for (int j = 0; j < FT; ++j) {
-        const int tok = u * kBT + j * 16 + li;
-        const int sw = tok & 7;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + (lq ^ sw)) * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4) ^ sw)) * 16);
-        bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < FT; ++j)
-#pragma unroll
-        for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FR + FT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, FT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, FR * FT - 2, 0);
+    for (int i = 0; i < FR; ++i) {
+      const int row = wr * 128 + i * 16 + li;
+      a[i] = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 2) & 3))) * 16);
+      const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
+      ix[i] = *reinterpret_cast<const uint16_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8 + lq * 2);
     }
+    u32x8 bf[FT];
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int tok = wt * (kBT / 2) + j * 16 + li;
+      const int sw = tok & 7;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + (lq ^ sw)) * 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4) ^ sw)) * 16);
+      bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < FT; ++j)
+#pragma unroll
+      for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
+    // Schedule: the A reads and the first B fragment, then MFMAs with the
+    // remaining B reads spread between them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FR + 2, 0);
+    for (int k = 0; k < 2 * FT - 2; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FR * FT - 2 * (2 * FT - 2), 0);
   }
 
   // ---- epilogue
   const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FR; ++i) {
-    const int r = R0 + wave * 64 + i * 16 + lq * 4;
+    const int r = R0 + wr * 128 + i * 16 + lq * 4;
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      const int t = T0 + j * 16 + li;
+      const int t = T0 + wt * (kBT / 2) + j * 16 + li;
       if (t >= T || r >= R) continue;
       const f32x4 v = acc[i][j];
       if constexpr (OUT == NM_F32) {
