@@ -26,6 +26,12 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
                 "-Wall", "-Wno-unused-function"]
+# Translation units whose MFMA loops hold every accumulator in VGPRs: without
+# this the register allocator moves some accumulators between AGPRs and VGPRs
+# every K step, and each move waits for the MFMA that wrote the value.
+PER_SOURCE_FLAGS = {
+    "nm_spmm_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:
@@ -45,7 +51,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = PER_SOURCE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", *DEVICE_FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -2,28 +2,30 @@
 // by direct global->LDS loads (gfx950 global_load_lds_dwordx4).
 //
 // Same product as nm_spmm.hip (Y^T[t, r] = sum_k W_nm[r, k] act[t, k] on
-// v_smfmac_f32_16x16x64).  What this kernel is organised around is the cost
-// of L2 requests: no lane loads fewer than 16 bytes and every instruction
-// reads 64- or 128-byte runs.  A direct load deposits lane l's 16 bytes at
-// slot base + l of LDS, so the LDS layout is chosen by which global address
-// each lane reads:
+// v_smfmac_f32_16x16x64).  No lane loads fewer than 16 bytes and every load
+// instruction reads 64- or 128-byte runs.  A direct load deposits lane l's 16
+// bytes at slot base + l of LDS, so the LDS layout is chosen by which global
+// address each lane reads.  The XOR swizzles below were picked by measuring
+// the LDS bank-conflict counter for the exact fragment reads of this kernel;
+// each layout reads without conflicts.  A lane reads the 8 index bytes of its
+// row's step (8-byte reads cost half of what 2-byte reads do) and keeps its
+// own 2 bytes:
 //
 //   packed values  one K step per stage; slot (row, quarter q) at
-//                  row*4 + (q ^ ((row >> 2) & 3)): an instruction covers 16 rows
-//                  x 64 bytes, and a fragment read by 8 consecutive rows hits
-//                  distinct bank groups;
+//                  row*4 + (q ^ ((row >> 1) & 3)): a load covers 16 rows x 64 B;
 //   activations    one K step per stage; slot (token, chunk c) at
-//                  token*8 + (c ^ (token & 7)): 8 tokens x 128 bytes per
-//                  instruction;
+//                  token*8 + (c ^ (token & 7)): 8 tokens x 128 B per load;
 //   index bits     block = 8 K steps (64 bytes per row); slot (row, chunk) at
 //                  row*4 + (chunk ^ ((row >> 2) & 3)).
 //
 // A workgroup (4 waves) owns a 256 x 128 tile; waves are 2 x 2, each owning
 // 128 rows x 64 tokens (8 x 4 fragments: the fragment-read volume per MFMA is
 // lowest for this split).  Stages form a 4-deep ring, so three K steps of
-// loads are in flight while one is computed; each step waits (counted vmcnt)
-// for exactly its own loads and passes one fence-free barrier, which both
-// publishes it and retires the slot the step's new loads reuse.
+// loads are in flight while one is read.  Fragments go through two register
+// sets: the LDS reads of step s+1 are issued between the MFMAs of step s.
+// Each step waits (counted vmcnt) for exactly the loads of the step it is
+// about to read and passes one fence-free barrier, which both publishes that
+// step and retires the slot the new loads reuse.
 #include "nm_internal.h"
 
 namespace nm {
@@ -76,8 +78,20 @@ __device__ inline void wait_all_vm() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
 
-__device__ inline void dma16(const void* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_byte*)lds_dst, 16, 0, 0);
+__device__ inline void wait_lgkm0() {
+  // lgkmcnt(0), vmcnt/expcnt untouched (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
+}
+
+// Buffer resource over [base, base + 4 GiB): raw (stride 0) 32-bit data, no
+// range check in practice (every offset used here is clamped by the caller).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+// 16 bytes per lane from base + voff + soff into LDS slot lds_dst + lane*16.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, unsigned char* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_byte*)lds_dst, 16, int(voff), int(soff), 0, 0);
 }
 
 constexpr int kBR = 256;
@@ -122,53 +136,59 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int wr = wave >> 1, wt = wave & 1;
-  const int nsteps = K >> 6;                 // K % 128 == 0 on this path
+  const int nsteps = K >> 6;                 // even: K % 128 == 0 on this path
   const int S = K >> 1;                      // packed values per row
   const int irow_bytes = K >> 3;             // index bytes per row (2 bits per survivor)
 
-  // Per-lane source pointers.  Instruction j of a wave fills slots
+  // Tile bases are uniform; each lane adds a 32-bit byte offset (the launcher
+  // checks that every offset fits).  Instruction j of a wave fills slots
   // [(wave*4 + j)*64, +64); lane l takes slot base + l.
+  const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(act + int64_t(T0) * ldx);
+  const __amdgpu_buffer_rsrc_t asrc = make_rsrc(values + int64_t(R0) * S);
+  const __amdgpu_buffer_rsrc_t isrc = make_rsrc(reinterpret_cast<const unsigned char*>(idx) + int64_t(R0) * irow_bytes);
   // Activations, one step: slot (token, chunk) at token*8 + (c ^ (token & 7)).
-  const unsigned char* bsrc[4];
+  uint32_t boff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (wave * 4 + j) * 64 + lane;
     const int tok = slot >> 3;
     const int c = (slot & 7) ^ (tok & 7);
-    const int t = min(T0 + tok, T - 1);
-    bsrc[j] = reinterpret_cast<const unsigned char*>(act + int64_t(t) * ldx + c * 8);
+    const int t = min(T0 + tok, T - 1) - T0;
+    boff[j] = uint32_t(t) * uint32_t(ldx) * 2u + uint32_t(c) * 16u;
   }
-  // Packed values, one step: slot (row, quarter) at row*4 + (q ^ ((row >> 2) & 3)).
-  const unsigned char* asrc[4];
+  // Packed values, one step: slot (row, quarter) at row*4 + (q ^ ((row >> 1) & 3)).
+  uint32_t aoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (wave * 4 + j) * 64 + lane;
     const int row = slot >> 2;
-    const int q = (slot & 3) ^ ((row >> 2) & 3);
-    const int r = min(R0 + row, R - 1);
-    asrc[j] = reinterpret_cast<const unsigned char*>(values + int64_t(r) * S + q * 8);
+    const int q = (slot & 3) ^ ((row >> 1) & 3);
+    const int r = min(R0 + row, R - 1) - R0;
+    aoff[j] = uint32_t(r) * uint32_t(S) * 2u + uint32_t(q) * 16u;
   }
   // Index bits, 8 steps: slot (row, chunk) at row*4 + (c ^ ((row >> 2) & 3)).
-  const unsigned char* isrc[4];
+  uint32_t ioff[4];
   int ichunk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (wave * 4 + j) * 64 + lane;
     const int row = slot >> 2;
     const int c = (slot & 3) ^ ((row >> 2) & 3);
-    const int r = min(R0 + row, R - 1);
+    const int r = min(R0 + row, R - 1) - R0;
     ichunk[j] = c;
-    isrc[j] = reinterpret_cast<const unsigned char*>(idx) + int64_t(r) * irow_bytes + c * 16;
+    ioff[j] = uint32_t(r) * uint32_t(irow_bytes) + uint32_t(c) * 16u;
   }
 
-  auto issue_step = [&](int s) {
-    const int buf = s & (kNS - 1);
+  // Load j (0..3 activations, 4..7 packed values) of step src into ring slot buf.
+  auto issue_load = [&](int j, int src, int buf) {
+    if (j < 4)
+      dma16(bsrc, boff[j], uint32_t(src) * 128u, bbuf + buf * kStageB + (wave * 4 + j) * 1024);
+    else
+      dma16(asrc, aoff[j - 4], uint32_t(src) * 64u, abuf + buf * kStageA + (wave * 4 + j - 4) * 1024);
+  };
+  auto issue_step = [&](int src, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(bsrc[j] + int64_t(s) * 128, bbuf + buf * kStageB + (wave * 4 + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(asrc[j] + int64_t(s) * 64, abuf + buf * kStageA + (wave * 4 + j) * 1024);
+    for (int j = 0; j < kPerStep; ++j) issue_load(j, src, buf);
   };
   auto issue_index = [&](int q) {
     const int steps_left = nsteps - 8 * q;
@@ -176,8 +196,47 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     for (int j = 0; j < 4; ++j) {
       // chunk c holds steps 2c, 2c+1 of the block (steps_left is even); past
       // the row's end the lane rereads chunk 0 of the block
-      const int back = (2 * ichunk[j] < steps_left) ? 0 : ichunk[j] * 16;
-      dma16(isrc[j] + int64_t(q) * 64 - back, ibuf + (q & 1) * kBlockI + (wave * 4 + j) * 1024);
+      const uint32_t back = (2 * ichunk[j] < steps_left) ? 0u : uint32_t(ichunk[j]) * 16u;
+      dma16(isrc, ioff[j] - back, uint32_t(q) * 64u, ibuf + (q & 1) * kBlockI + (wave * 4 + j) * 1024);
+    }
+  };
+
+  // Fragment reads of one step from LDS into registers: row fragment i (packed
+  // values and index bits) and one half (h: K 8q..8q+7 or 32+8q..) of token
+  // fragment j.
+  // byte selector: bytes 2*lq, 2*lq+1 of {w.y, w.x} into bits 0..15, zeros above
+  const uint32_t ix_sel = uint32_t(2 * lq) | (uint32_t(2 * lq + 1) << 8) | (0x0C0Cu << 16);
+  auto read_a = [&](int s, int i, u32x4& a, uint2& ix) {
+    const unsigned char* sa = abuf + (s & (kNS - 1)) * kStageA;
+    const unsigned char* si = ibuf + ((s >> 3) & 1) * kBlockI;
+    const int u8 = s & 7;
+    const int row = wr * 128 + i * 16 + li;
+    a = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
+    // the row's 8 index bytes of this step (all four lane quarters), then
+    // this lane's 2 bytes picked out by a byte permute
+    const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
+    // (a uint64_t load: read through the uint2 struct, the compiler cannot
+    // tell this from the slots the direct loads are filling and waits for them)
+    const uint64_t w = *reinterpret_cast<const uint64_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8);
+    ix.x = uint32_t(w);
+    ix.y = uint32_t(w >> 32);
+  };
+  auto read_b = [&](int s, int j, int h, u32x8& bf) {
+    const unsigned char* sb = bbuf + (s & (kNS - 1)) * kStageB;
+    const int tok = wt * (kBT / 2) + j * 16 + li;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4 * h) ^ (tok & 7))) * 16);
+    bf[4 * h + 0] = v[0];
+    bf[4 * h + 1] = v[1];
+    bf[4 * h + 2] = v[2];
+    bf[4 * h + 3] = v[3];
+  };
+  auto read_frags = [&](int s, u32x4 (&a)[FR], uint2 (&ix)[FR], u32x8 (&bf)[FT]) {
+#pragma unroll
+    for (int i = 0; i < FR; ++i) read_a(s, i, a[i], ix[i]);
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      read_b(s, j, 0, bf[j]);
+      read_b(s, j, 1, bf[j]);
     }
   };
 
@@ -187,58 +246,58 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
 #pragma unroll
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: index block 0, then steps 0 .. kNS-2
+  // Two register sets: the fragments of step s+1 are read from LDS while the
+  // MFMAs of step s run.  The loop is unrolled by two so the sets alternate
+  // without copies.
+  u32x4 a0[FR], a1[FR];
+  uint2 x0[FR], x1[FR];
+  u32x8 b0[FT], b1[FT];
+
+  // One step: make step s+1 visible, refill the slot step s used, read step
+  // s+1, multiply step s.  Every step issues the same loads: past the last
+  // step a slot is refilled with the last step again, into a slot nothing
+  // reads any more.  So the wait counts are fixed and the loads, the fragment
+  // reads and the MFMAs form one branch-free block the scheduler interleaves
+  // (a burst of loads would hold up the MFMAs behind it).
+  auto body = [&](int s, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT], u32x4 (&na)[FR],
+                  uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
+    // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
+    // index block issued in between only makes the wait stricter)
+    wait_vmcnt<2 * kPerStep>();
+    wait_lgkm0();        // this wave's reads of step s are done
+    barrier_no_fence();  // publishes step s+1; every wave is done reading step s
+    if ((s & 7) == 0 && s + 8 < nsteps) issue_index((s >> 3) + 1);
+    // Eight chunks, each: the 4 MFMAs of row fragment k, one load, and three
+    // fragment reads of step s+1 (the last step reads a stale slot it never
+    // uses).  Scheduling barriers keep the chunks in this order.
+    const int src = min(s + kNS, nsteps - 1), buf = s & (kNS - 1);
+#pragma unroll
+    for (int k = 0; k < FR; ++k) {
+      const uint32_t ik = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
+#pragma unroll
+      for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik);
+      issue_load(k, src, buf);
+      read_a(s + 1, k, na[k], nx[k]);
+      read_b(s + 1, k >> 1, k & 1, nb[k >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  static_assert(FR == kPerStep && FT * 2 == FR, "one load and one token-fragment half per chunk");
+
+  // ---- prologue: index block 0 and steps 0 .. kNS-2, then step 0 into set 0
   issue_index(0);
 #pragma unroll
-  for (int p = 0; p < kNS - 1; ++p)
-    if (p < nsteps) issue_step(p);
+  for (int p = 0; p < kNS - 1; ++p) issue_step(min(p, nsteps - 1), p);
+  wait_vmcnt<2 * kPerStep>();
+  barrier_no_fence();
+  issue_step(min(kNS - 1, nsteps - 1), kNS - 1);  // slot kNS-1 is still unused
+  read_frags(0, a0, x0, b0);
 
-  for (int s = 0; s < nsteps; ++s) {
-    // Step s has landed once at most the loads issued after it remain: those
-    // of steps s+1, s+2 (an index block issued in between only makes the
-    // wait stricter).
-    if (s + 2 < nsteps) wait_vmcnt<2 * kPerStep>();
-    else if (s + 1 < nsteps) wait_vmcnt<kPerStep>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();  // publishes step s, retires step s - 1
-    if (s + kNS - 1 < nsteps) issue_step(s + kNS - 1);
-    if ((s & 7) == 0 && s + 8 < nsteps) issue_index((s >> 3) + 1);
-
-    const unsigned char* sb = bbuf + (s & (kNS - 1)) * kStageB;
-    const unsigned char* sa = abuf + (s & (kNS - 1)) * kStageA;
-    const unsigned char* si = ibuf + ((s >> 3) & 1) * kBlockI;
-    const int u8 = s & 7;
-    u32x4 a[FR];
-    uint32_t ix[FR];
-#pragma unroll
-    for (int i = 0; i < FR; ++i) {
-      const int row = wr * 128 + i * 16 + li;
-      a[i] = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 2) & 3))) * 16);
-      const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
-      ix[i] = *reinterpret_cast<const uint16_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8 + lq * 2);
-    }
-    u32x8 bf[FT];
-#pragma unroll
-    for (int j = 0; j < FT; ++j) {
-      const int tok = wt * (kBT / 2) + j * 16 + li;
-      const int sw = tok & 7;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + (lq ^ sw)) * 16);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4) ^ sw)) * 16);
-      bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-#pragma unroll
-    for (int j = 0; j < FT; ++j)
-#pragma unroll
-      for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
-    // Schedule: the A reads and the first B fragment, then MFMAs with the
-    // remaining B reads spread between them.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FR + 2, 0);
-    for (int k = 0; k < 2 * FT - 2; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FR * FT - 2 * (2 * FT - 2), 0);
+  for (int s = 0; s < nsteps; s += 2) {
+    body(s, a0, x0, b0, a1, x1, b1);
+    body(s + 1, a1, x1, b1, a0, x0, b0);
   }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   // ---- epilogue
   const bool vec_ok = (ldy & 3) == 0;
@@ -299,6 +358,9 @@ bool spmm_lds_applies(const SpmmArgs& a) {
   if (!(a.perm == nullptr && a.n == 2 && a.m == 4 && (a.K % 128) == 0 && a.T >= 128 &&
         a.R >= 256))
     return false;
+  // per-lane byte offsets within a tile are 32-bit
+  const int64_t lim = int64_t(0xFFFFFFFFu);
+  if (int64_t(kBT) * a.ldx * 2 > lim || int64_t(kBR) * a.K > lim) return false;
   // needs a workgroup LDS allocation of kLds bytes
   static int max_lds = -1;
   if (max_lds < 0) {
