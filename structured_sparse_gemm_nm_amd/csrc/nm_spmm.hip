@@ -418,7 +418,7 @@ hipError_t launch_generic(const SpmmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Kernel choice.  variant 0 picks by shape; 1..4 force one kernel family when
+// Kernel choice.  variant 0 picks by shape; 1..5 force one kernel family when
 // the shape allows it (ablations, tests), else fall back to the choice by shape.
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
   switch (a.variant) {
@@ -432,6 +432,9 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
       break;
     case NM_VARIANT_DECODE:
       if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
+      break;
+    case NM_VARIANT_WIDE:
+      if (spmm_wide_applies(a)) return launch_spmm_wide(a, s);
       break;
     default: break;
   }

@@ -145,8 +145,9 @@ def test_decompress_and_misc_errors():
     assert L.nm_check_perm(None, 16, None) == 1
     assert L.nm_check_perm(FAKE, 0, None) == 2
     assert L.nm_set_variant(7) == 3
+    assert L.nm_set_variant(6) == 3
     assert L.nm_set_variant(-1) == 3
-    for v in range(5):
+    for v in range(6):
         assert L.nm_set_variant(v) == 0
     assert L.nm_set_variant(0) == 0
 

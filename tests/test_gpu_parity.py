@@ -313,7 +313,7 @@ def test_kernel_families_agree(n, m):
     A = to_dev(act, "bf16")
     outs = {}
     try:
-        for v in (1, 2, 3):
+        for v in (1, 2, 3, 5):
             nm.nm_set_variant(v)
             outs[v] = nm.nm_spmm(vals, idx, A, K, n, m)
         nm.nm_set_variant(4)
@@ -325,6 +325,7 @@ def test_kernel_families_agree(n, m):
     torch.cuda.synchronize()
     # families that add the K steps in order from zero give identical bits
     assert torch.equal(outs[1], outs[2]) and torch.equal(outs[1], outs[3])
+    assert torch.equal(outs[1], outs[5])
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "bf16")
     assert_close(outs[1], yref, error_bound(ref_vals, ref_idx, K, n, m, act, "bf16"))
