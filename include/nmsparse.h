@@ -124,11 +124,19 @@ nm_status nm_spmm(const void* values, const uint32_t* idx, int64_t R, int64_t K,
                   int out_dtype, void* stream);
 
 /*
- * Permuted sparse GEMM  y = (W Pi) x:  Y[t, r] = sum_k W_nm[r, k] * act[t, perm[k]].
+ * Permuted sparse GEMM  y = (W Pi) x:  Y[t, r] = sum_k W_nm[r, k] * act[t, perm[k]]
+ * (ShuffleSparse, inference with a learned input-channel permutation).
  *   perm  device int32 [K], a permutation of 0..K-1 (precondition, not checked
- *         on the hot path; out-of-range entries are undefined behaviour).
- * All other arguments as nm_spmm.  The permutation is applied while X is read;
- * no permuted copy of X is made.
+ *         on the hot path; an out-of-range entry gives wrong values for its
+ *         column, never an out-of-bounds access).
+ * All other arguments as nm_spmm.  By default (nm_set_variant 0) the
+ * permutation is applied as an index map while X is read by a gather pass
+ * that writes X' = act[:, perm] (T * K * 2 bytes) to scratch memory, followed
+ * by the plain GEMM on X'.  The library keeps one scratch buffer per (device,
+ * stream), grown to the largest T * K * 2 seen on that stream and held until
+ * the process ends; growing it synchronises that stream.  Variants 1 and 3
+ * gather inside the GEMM kernel instead (no scratch).  NM_ERR_HIP if the
+ * scratch cannot be allocated.
  */
 nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                        int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,

@@ -56,6 +56,11 @@ hipError_t launch_spmm_perm_lds(const SpmmArgs& a, hipStream_t s);
 bool spmm_lds_applies(const SpmmArgs& a);
 hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);
 
+// Permuted GEMM as a gather pass into stream-ordered scratch followed by the
+// plain GEMM (nm_permute.hip), and the shapes it takes.
+bool spmm_perm_gather_applies(const SpmmArgs& a);
+hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s);
+
 // 256 x 256-tile 2:4 kernel (nm_spmm_wide.hip) and the shapes it takes.
 bool spmm_wide_applies(const SpmmArgs& a);
 hipError_t launch_spmm_wide(const SpmmArgs& a, hipStream_t s);

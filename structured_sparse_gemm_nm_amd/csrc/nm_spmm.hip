@@ -438,6 +438,7 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
       break;
     default: break;
   }
+  if (spmm_perm_gather_applies(a)) return launch_spmm_perm_gather(a, s);
   if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
   if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
   if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
