@@ -18,7 +18,7 @@
 //   index bits     block = 8 K steps (64 bytes per row); slot (row, chunk) at
 //                  row*4 + (chunk ^ ((row >> 2) & 3)).
 //
-// A workgroup (4 waves) owns a 256 x 128 tile; waves are 2 x 2, each owning
+// A workgroup (4 waves) computes 256 x 128 tiles; waves are 2 x 2, each owning
 // 128 rows x 64 tokens (8 x 4 fragments: the fragment-read volume per MFMA is
 // lowest for this split).  Stages form a 4-deep ring, so three K steps of
 // loads are in flight while one is read.  Fragments go through two register
@@ -26,6 +26,11 @@
 // Each step waits (counted vmcnt) for exactly the loads of the step it is
 // about to read and passes one fence-free barrier, which both publishes that
 // step and retires the slot the new loads reuse.
+//
+// With more tiles than compute units one workgroup per CU walks the tiles,
+// and the ring runs on from one tile into the next: the last steps of a tile
+// already load and read the first steps of the following one, so neither the
+// ring's fill nor the epilogue's stores leave the MFMAs idle between tiles.
 #include "nm_internal.h"
 
 namespace nm {
@@ -109,107 +114,120 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Where a workgroup's tiles are: tile i of the grid-stride sequence
+// (blockIdx.x, + grid, ...) -> (row tile, token tile).  Within a full round of
+// `grid` tiles the XCD-aware remap gives each XCD a contiguous run; tiles are
+// then ordered in groups of group_r row tiles sharing activation columns.
+struct TileMap {
+  int tilesR, tilesT, group_r, ntiles, grid;
+  __device__ void rt(int i, int& R0, int& T0) const {
+    const int round = i / grid, p = i - round * grid;
+    int q = p;
+    if ((grid & 7) == 0 && (round + 1) * grid <= ntiles) q = (p & 7) * (grid >> 3) + (p >> 3);
+    const int b = round * grid + q;
+    const int per_group = group_r * tilesT;
+    const int grp = b / per_group;
+    const int rem = b - grp * per_group;
+    const int rows_in_grp = min(group_r, tilesR - grp * group_r);
+    R0 = (grp * group_r + rem % rows_in_grp) * kBR;
+    T0 = (rem / rows_in_grp) * kBT;
+  }
+};
+
 template <int DT, int OUT>
 __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K,
     const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y, int64_t ldy,
-    int tilesR, int tilesT, int group_r) {
+    TileMap tm) {
   constexpr int FR = 8, FT = kBT / 32;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* bbuf = smem;                              // [kNS][kStageB]
   unsigned char* abuf = smem + kNS * kStageB;              // [kNS][kStageA]
   unsigned char* ibuf = smem + kNS * (kStageB + kStageA);  // [2][kBlockI]
 
-  // ---- tile: XCD-aware remap, then groups of group_r row tiles sharing X
-  const int ntiles = tilesR * tilesT;
-  int b = blockIdx.x;
-  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
-  const int per_group = group_r * tilesT;
-  const int grp = b / per_group;
-  const int rem = b - grp * per_group;
-  const int rows_in_grp = min(group_r, tilesR - grp * group_r);
-  const int tr = grp * group_r + rem % rows_in_grp;
-  const int tt = rem / rows_in_grp;
-  const int R0 = tr * kBR, T0 = tt * kBT;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int wr = wave >> 1, wt = wave & 1;
   const int nsteps = K >> 6;                 // even: K % 128 == 0 on this path
+  const int nblocks = (nsteps + 7) >> 3;     // index blocks of 8 steps per tile
   const int S = K >> 1;                      // packed values per row
   const int irow_bytes = K >> 3;             // index bytes per row (2 bits per survivor)
 
-  // Tile bases are uniform; each lane adds a 32-bit byte offset (the launcher
-  // checks that every offset fits).  Instruction j of a wave fills slots
-  // [(wave*4 + j)*64, +64); lane l takes slot base + l.
-  const __amdgpu_buffer_rsrc_t bsrc = make_rsrc(act + int64_t(T0) * ldx);
-  const __amdgpu_buffer_rsrc_t asrc = make_rsrc(values + int64_t(R0) * S);
-  const __amdgpu_buffer_rsrc_t isrc = make_rsrc(reinterpret_cast<const unsigned char*>(idx) + int64_t(R0) * irow_bytes);
-  // Activations, one step: slot (token, chunk) at token*8 + (c ^ (token & 7)).
-  uint32_t boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int slot = (wave * 4 + j) * 64 + lane;
-    const int tok = slot >> 3;
-    const int c = (slot & 7) ^ (tok & 7);
-    const int t = min(T0 + tok, T - 1) - T0;
-    boff[j] = uint32_t(t) * uint32_t(ldx) * 2u + uint32_t(c) * 16u;
-  }
-  // Packed values, one step: slot (row, quarter) at row*4 + (q ^ ((row >> 1) & 3)).
-  uint32_t aoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int slot = (wave * 4 + j) * 64 + lane;
-    const int row = slot >> 2;
-    const int q = (slot & 3) ^ ((row >> 1) & 3);
-    const int r = min(R0 + row, R - 1) - R0;
-    aoff[j] = uint32_t(r) * uint32_t(S) * 2u + uint32_t(q) * 16u;
-  }
-  // Index bits, 8 steps: slot (row, chunk) at row*4 + (c ^ ((row >> 2) & 3)).
-  uint32_t ioff[4];
+  // Per-lane slot roles (instruction j of a wave fills slots [(wave*4 + j)*64,
+  // +64); lane l takes slot base + l):
+  //   activations, one step: slot (token, chunk) at token*8 + (c ^ (token & 7));
+  //   packed values, one step: slot (row, quarter) at row*4 + (q ^ ((row >> 1) & 3));
+  //   index bits, 8 steps: slot (row, chunk) at row*4 + (c ^ ((row >> 2) & 3)).
   int ichunk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (wave * 4 + j) * 64 + lane;
-    const int row = slot >> 2;
-    const int c = (slot & 3) ^ ((row >> 2) & 3);
-    const int r = min(R0 + row, R - 1) - R0;
-    ichunk[j] = c;
-    ioff[j] = uint32_t(r) * uint32_t(irow_bytes) + uint32_t(c) * 16u;
+    ichunk[j] = (slot & 3) ^ ((slot >> 4) & 3);
   }
 
-  // Load j (0..3 activations, 4..7 packed values) of step src into ring slot buf.
-  auto issue_load = [&](int j, int src, int buf) {
-    if (j < 4)
-      dma16(bsrc, boff[j], uint32_t(src) * 128u, bbuf + buf * kStageB + (wave * 4 + j) * 1024);
-    else
-      dma16(asrc, aoff[j - 4], uint32_t(src) * 64u, abuf + buf * kStageA + (wave * 4 + j - 4) * 1024);
+  // A tile's load sources: uniform buffer resources at the tile's corner and
+  // per-lane 32-bit byte offsets (rows / tokens past the edge reread the last
+  // one; the launcher checks that every offset fits).
+  struct Src {
+    __amdgpu_buffer_rsrc_t a, b, i;
+    uint32_t boff[4], aoff[4], ioff[4];
   };
-  auto issue_step = [&](int src, int buf) {
+  auto make_src = [&](int R0, int T0, Src& o) {
+    o.b = make_rsrc(act + int64_t(T0) * ldx);
+    o.a = make_rsrc(values + int64_t(R0) * S);
+    o.i = make_rsrc(reinterpret_cast<const unsigned char*>(idx) + int64_t(R0) * irow_bytes);
 #pragma unroll
-    for (int j = 0; j < kPerStep; ++j) issue_load(j, src, buf);
+    for (int j = 0; j < 4; ++j) {
+      const int slot = (wave * 4 + j) * 64 + lane;
+      const int tok = slot >> 3;
+      const int c = (slot & 7) ^ (tok & 7);
+      const int t = min(T0 + tok, T - 1) - T0;
+      o.boff[j] = uint32_t(t) * uint32_t(ldx) * 2u + uint32_t(c) * 16u;
+      const int row = slot >> 2;
+      const int q = (slot & 3) ^ ((row >> 1) & 3);
+      const int r = min(R0 + row, R - 1) - R0;
+      o.aoff[j] = uint32_t(r) * uint32_t(S) * 2u + uint32_t(q) * 16u;
+      o.ioff[j] = uint32_t(r) * uint32_t(irow_bytes) + uint32_t(ichunk[j]) * 16u;
+    }
   };
-  auto issue_index = [&](int q) {
+
+  // Load j (0..3 activations, 4..7 packed values) of step src of the current
+  // tile (nt false) or the next one (nt true) into ring slot buf.  Fields are
+  // selected by value (a reference to either source would put both on the
+  // stack).
+  auto issue_load = [&](const Src& c, const Src& n, bool nt, int j, int src, int buf) {
+    if (j < 4)
+      dma16(nt ? n.b : c.b, nt ? n.boff[j] : c.boff[j], uint32_t(src) * 128u,
+            bbuf + buf * kStageB + (wave * 4 + j) * 1024);
+    else
+      dma16(nt ? n.a : c.a, nt ? n.aoff[j - 4] : c.aoff[j - 4], uint32_t(src) * 64u,
+            abuf + buf * kStageA + (wave * 4 + j - 4) * 1024);
+  };
+  auto issue_step = [&](const Src& c, const Src& n, bool nt, int src, int buf) {
+#pragma unroll
+    for (int j = 0; j < kPerStep; ++j) issue_load(c, n, nt, j, src, buf);
+  };
+  // index block q of a tile into buffer ib
+  auto issue_index = [&](const Src& o, int q, int ib) {
     const int steps_left = nsteps - 8 * q;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // chunk c holds steps 2c, 2c+1 of the block (steps_left is even); past
       // the row's end the lane rereads chunk 0 of the block
       const uint32_t back = (2 * ichunk[j] < steps_left) ? 0u : uint32_t(ichunk[j]) * 16u;
-      dma16(isrc, ioff[j] - back, uint32_t(q) * 64u, ibuf + (q & 1) * kBlockI + (wave * 4 + j) * 1024);
+      dma16(o.i, o.ioff[j] - back, uint32_t(q) * 64u, ibuf + ib * kBlockI + (wave * 4 + j) * 1024);
     }
   };
 
-  // Fragment reads of one step from LDS into registers: row fragment i (packed
-  // values and index bits) and one half (h: K 8q..8q+7 or 32+8q..) of token
-  // fragment j.
+  // Fragment reads of a step from LDS into registers (ring slot sl, index
+  // buffer ib, step u8 within its index block): row fragment i (packed values
+  // and index bits) and one half (h: K 8q..8q+7 or 32+8q..) of token fragment j.
   // byte selector: bytes 2*lq, 2*lq+1 of {w.y, w.x} into bits 0..15, zeros above
   const uint32_t ix_sel = uint32_t(2 * lq) | (uint32_t(2 * lq + 1) << 8) | (0x0C0Cu << 16);
-  auto read_a = [&](int s, int i, u32x4& a, uint2& ix) {
-    const unsigned char* sa = abuf + (s & (kNS - 1)) * kStageA;
-    const unsigned char* si = ibuf + ((s >> 3) & 1) * kBlockI;
-    const int u8 = s & 7;
+  auto read_a = [&](int sl, int ib, int u8, int i, u32x4& a, uint2& ix) {
+    const unsigned char* sa = abuf + sl * kStageA;
+    const unsigned char* si = ibuf + ib * kBlockI;
     const int row = wr * 128 + i * 16 + li;
     a = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
     // the row's 8 index bytes of this step (all four lane quarters), then
@@ -221,8 +239,8 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     ix.x = uint32_t(w);
     ix.y = uint32_t(w >> 32);
   };
-  auto read_b = [&](int s, int j, int h, u32x8& bf) {
-    const unsigned char* sb = bbuf + (s & (kNS - 1)) * kStageB;
+  auto read_b = [&](int sl, int j, int h, u32x8& bf) {
+    const unsigned char* sb = bbuf + sl * kStageB;
     const int tok = wt * (kBT / 2) + j * 16 + li;
     const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4 * h) ^ (tok & 7))) * 16);
     bf[4 * h + 0] = v[0];
@@ -230,22 +248,17 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     bf[4 * h + 2] = v[2];
     bf[4 * h + 3] = v[3];
   };
-  auto read_frags = [&](int s, u32x4 (&a)[FR], uint2 (&ix)[FR], u32x8 (&bf)[FT]) {
+  auto read_frags = [&](int sl, int ib, int u8, u32x4 (&a)[FR], uint2 (&ix)[FR], u32x8 (&bf)[FT]) {
 #pragma unroll
-    for (int i = 0; i < FR; ++i) read_a(s, i, a[i], ix[i]);
+    for (int i = 0; i < FR; ++i) read_a(sl, ib, u8, i, a[i], ix[i]);
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      read_b(s, j, 0, bf[j]);
-      read_b(s, j, 1, bf[j]);
+      read_b(sl, j, 0, bf[j]);
+      read_b(sl, j, 1, bf[j]);
     }
   };
 
   f32x4 acc[FR][FT];
-#pragma unroll
-  for (int i = 0; i < FR; ++i)
-#pragma unroll
-    for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // Two register sets: the fragments of step s+1 are read from LDS while the
   // MFMAs of step s run.  The loop is unrolled by two so the sets alternate
   // without copies.
@@ -253,12 +266,31 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   uint2 x0[FR], x1[FR];
   u32x8 b0[FT], b1[FT];
 
+  // The workgroup walks tiles blockIdx.x, + grid, ...  The ring runs on
+  // across tiles: in a tile's last steps the loads, index blocks and fragment
+  // reads of the steps after it belong to the next tile, so a tile starts
+  // with its first steps already in flight.
+  int tile = blockIdx.x;
+  int R0, T0, nR0 = 0, nT0 = 0;
+  tm.rt(tile, R0, T0);
+  Src cur, nxt;
+  make_src(R0, T0, cur);
+  bool has_next = tile + tm.grid < tm.ntiles;
+  if (has_next) {
+    tm.rt(tile + tm.grid, nR0, nT0);
+    make_src(nR0, nT0, nxt);
+  } else {
+    nxt = cur;
+  }
+  int g = 0;    // ring position of the tile's step 0
+  int qb = 0;   // index-buffer parity of the tile's block 0
+
   // One step: make step s+1 visible, refill the slot step s used, read step
   // s+1, multiply step s.  Every step issues the same loads: past the last
-  // step a slot is refilled with the last step again, into a slot nothing
-  // reads any more.  So the wait counts are fixed and the loads, the fragment
-  // reads and the MFMAs form one branch-free block the scheduler interleaves
-  // (a burst of loads would hold up the MFMAs behind it).
+  // step of the last tile a slot is refilled with that step again, into a slot
+  // nothing reads any more.  So the wait counts are fixed and the loads, the
+  // fragment reads and the MFMAs form one branch-free block the scheduler
+  // interleaves (a burst of loads would hold up the MFMAs behind it).
   auto body = [&](int s, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT], u32x4 (&na)[FR],
                   uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
     // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
@@ -266,68 +298,115 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     wait_vmcnt<2 * kPerStep>();
     wait_lgkm0();        // this wave's reads of step s are done
     barrier_no_fence();  // publishes step s+1; every wave is done reading step s
-    if ((s & 7) == 0 && s + 8 < nsteps) issue_index((s >> 3) + 1);
+    // at a block's first step, the block after it: this tile's next, or the
+    // next tile's first
+    if ((s & 7) == 0) {
+      const int ib = (qb + (s >> 3) + 1) & 1;
+      if (s + 8 < nsteps) issue_index(cur, (s >> 3) + 1, ib);
+      else if (has_next) issue_index(nxt, 0, ib);
+    }
+    // loads of the step 4 ahead into step s's slot
+    const int buf = (g + s) & (kNS - 1);
+    const bool in_tile = s + kNS < nsteps;
+    const bool ln = !in_tile && has_next;
+    const int src = in_tile ? s + kNS : (has_next ? s + kNS - nsteps : nsteps - 1);
+    // where step s+1 is read from
+    const int rsl = (g + s + 1) & (kNS - 1);
+    const bool r_in = s + 1 < nsteps;
+    const int rib = (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
+    const int ru8 = r_in ? ((s + 1) & 7) : 0;
     // Eight chunks, each: the 4 MFMAs of row fragment k, one load, and three
-    // fragment reads of step s+1 (the last step reads a stale slot it never
-    // uses).  Scheduling barriers keep the chunks in this order.
-    const int src = min(s + kNS, nsteps - 1), buf = s & (kNS - 1);
+    // fragment reads of step s+1.  Scheduling barriers keep the chunks in
+    // this order.
 #pragma unroll
     for (int k = 0; k < FR; ++k) {
       const uint32_t ik = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik);
-      issue_load(k, src, buf);
-      read_a(s + 1, k, na[k], nx[k]);
-      read_b(s + 1, k >> 1, k & 1, nb[k >> 1]);
+      issue_load(cur, nxt, ln, k, src, buf);
+      read_a(rsl, rib, ru8, k, na[k], nx[k]);
+      read_b(rsl, k >> 1, k & 1, nb[k >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   static_assert(FR == kPerStep && FT * 2 == FR, "one load and one token-fragment half per chunk");
 
-  // ---- prologue: index block 0 and steps 0 .. kNS-2, then step 0 into set 0
-  issue_index(0);
+  // ---- prologue: index block 0 and steps 0 .. kNS-2 of the first tile, then
+  // step 0 into set 0
+  issue_index(cur, 0, 0);
 #pragma unroll
-  for (int p = 0; p < kNS - 1; ++p) issue_step(min(p, nsteps - 1), p);
+  for (int p = 0; p < kNS - 1; ++p) {
+    const bool in_tile = p < nsteps;
+    issue_step(cur, nxt, !in_tile && has_next, in_tile ? p : (has_next ? p - nsteps : nsteps - 1), p);
+  }
   wait_vmcnt<2 * kPerStep>();
   barrier_no_fence();
-  issue_step(min(kNS - 1, nsteps - 1), kNS - 1);  // slot kNS-1 is still unused
-  read_frags(0, a0, x0, b0);
-
-  for (int s = 0; s < nsteps; s += 2) {
-    body(s, a0, x0, b0, a1, x1, b1);
-    body(s + 1, a1, x1, b1, a0, x0, b0);
+  {
+    const bool in_tile = kNS - 1 < nsteps;
+    issue_step(cur, nxt, !in_tile && has_next,
+               in_tile ? kNS - 1 : (has_next ? kNS - 1 - nsteps : nsteps - 1), kNS - 1);  // slot still unused
   }
-  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+  read_frags(0, 0, 0, a0, x0, b0);
 
-  // ---- epilogue
-  const bool vec_ok = (ldy & 3) == 0;
+  while (true) {
 #pragma unroll
-  for (int i = 0; i < FR; ++i) {
-    const int r = R0 + wr * 128 + i * 16 + lq * 4;
+    for (int i = 0; i < FR; ++i)
 #pragma unroll
-    for (int j = 0; j < FT; ++j) {
-      const int t = T0 + wt * (kBT / 2) + j * 16 + li;
-      if (t >= T || r >= R) continue;
-      const f32x4 v = acc[i][j];
-      if constexpr (OUT == NM_F32) {
-        float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
-        if (vec_ok && r + 3 < R) {
-          *reinterpret_cast<f32x4*>(y) = v;
+      for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsteps; s += 2) {
+      body(s, a0, x0, b0, a1, x1, b1);
+      body(s + 1, a1, x1, b1, a0, x0, b0);
+    }
+
+    // ---- epilogue
+    const bool vec_ok = (ldy & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const int r = R0 + wr * 128 + i * 16 + lq * 4;
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int t = T0 + wt * (kBT / 2) + j * 16 + li;
+        if (t >= T || r >= R) continue;
+        const f32x4 v = acc[i][j];
+        if constexpr (OUT == NM_F32) {
+          float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
+          if (vec_ok && r + 3 < R) {
+            *reinterpret_cast<f32x4*>(y) = v;
+          } else {
+            for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
+          }
         } else {
-          for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
-        }
-      } else {
-        uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
-        const uint16_t h0 = to_half_bits<DT>(v[0]), h1 = to_half_bits<DT>(v[1]);
-        const uint16_t h2 = to_half_bits<DT>(v[2]), h3 = to_half_bits<DT>(v[3]);
-        if (vec_ok && r + 3 < R) {
-          *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h0) | (uint32_t(h1) << 16),
-                                                    uint32_t(h2) | (uint32_t(h3) << 16));
-        } else {
-          const uint16_t hh[4] = {h0, h1, h2, h3};
-          for (int e = 0; e < 4 && r + e < R; ++e) y[e] = hh[e];
+          uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
+          const uint16_t h0 = to_half_bits<DT>(v[0]), h1 = to_half_bits<DT>(v[1]);
+          const uint16_t h2 = to_half_bits<DT>(v[2]), h3 = to_half_bits<DT>(v[3]);
+          if (vec_ok && r + 3 < R) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h0) | (uint32_t(h1) << 16),
+                                                      uint32_t(h2) | (uint32_t(h3) << 16));
+          } else {
+            const uint16_t hh[4] = {h0, h1, h2, h3};
+            for (int e = 0; e < 4 && r + e < R; ++e) y[e] = hh[e];
+          }
         }
       }
+    }
+    // Stores share the load counter, so while they are pending a counted
+    // wait only waits longer: the next tile's loads, already in flight, stay
+    // in flight across the epilogue.  The last tile waits for everything, so
+    // no direct load is still writing LDS when the workgroup ends.
+    if (!has_next) {
+      wait_vmcnt<0>();
+      break;
+    }
+    tile += tm.grid;
+    R0 = nR0;
+    T0 = nT0;
+    cur = nxt;
+    g += nsteps;
+    qb += nblocks;
+    has_next = tile + tm.grid < tm.ntiles;
+    if (has_next) {
+      tm.rt(tile + tm.grid, nR0, nT0);
+      make_src(nR0, nT0, nxt);
     }
   }
 }
@@ -338,7 +417,27 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
   const int tilesT = int((a.T + kBT - 1) / kBT);
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int group_r = tilesR < 4 ? tilesR : 4;
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus = v;
+  }
+  // One workgroup per CU walks the tiles (each CU holds one: 160 KB of LDS).
+  // Running the ring on into the next tile needs the next tile's index block
+  // issued at least four steps before its first step is read, i.e. a tile's
+  // last index block at least four steps long (nsteps % 8 != 2) and nsteps >= 4;
+  // otherwise every tile gets its own workgroup.
+  const int64_t nsteps = a.K / 64;
+  const bool walk = nsteps >= 4 && nsteps % 8 != 2;
+  TileMap tm;
+  tm.tilesR = tilesR;
+  tm.tilesT = tilesT;
+  tm.group_r = tilesR < 4 ? tilesR : 4;
+  tm.ntiles = int(ntiles);
+  tm.grid = int(walk && ntiles > cus ? cus : ntiles);
   auto kern = spmm_lds_kernel<DT, OUT>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -347,8 +446,8 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(256), kLds, s, a.values, a.idx, int(a.R),
-                     int(a.K), a.act, int(a.T), a.ldx, a.Y, a.ldy, tilesR, tilesT, group_r);
+  hipLaunchKernelGGL(kern, dim3(unsigned(tm.grid)), dim3(256), kLds, s, a.values, a.idx, int(a.R),
+                     int(a.K), a.act, int(a.T), a.ldx, a.Y, a.ldy, tm);
   return hipGetLastError();
 }
 

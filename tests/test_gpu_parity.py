@@ -332,3 +332,35 @@ def test_kernel_families_agree(n, m):
     # the few-token family splits K: same product within the summation bound
     assert_close(y_few, yref[:, :16], error_bound(ref_vals, ref_idx, K, n, m, act[:16], "bf16"))
     assert_close(y_few_ref, yref[:, :16])
+
+
+# ---------------------------------------------------------------------------
+# prefill kernel with more tiles than compute units: each workgroup walks
+# several tiles and starts a tile's loads during the one before it
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,K,T,out", [(2200, 256, 3900, "f32"), (2200, 384, 3900, "f32"),
+                                       (2200, 640, 3900, "f32"), (2200, 768, 3900, "half"),
+                                       (2200, 1408, 3900, "f32"), (4100, 256, 4000, "f32")])
+def test_lds_tile_walk(R, K, T, out):
+    log(f"lds tile walk R={R} K={K} T={T} out={out}")
+    dt = "bf16"
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 50, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 50, 1, R + K + T)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    od = torch.bfloat16 if out == "half" else torch.float32
+    try:
+        nm.nm_set_variant(3)
+        y = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od)
+        nm.nm_set_variant(1)
+        y_gen = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od)
+    finally:
+        nm.nm_set_variant(0)
+    torch.cuda.synchronize()
+    # both add the K steps in order from zero
+    assert torch.equal(y, y_gen)
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt),
+                 **({"out_half": dt} if out == "half" else {}))
