@@ -51,6 +51,7 @@ def parse():
                     help="copies of the inputs cycled through (defeats the 256 MB last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / matmul peaks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy, the reference a counter "
                          "profile of this command scales HBM byte counters against")
@@ -85,12 +86,16 @@ def cpu_baseline(wl, n, m, T, reps):
     w = wl.weights()
     act = wl.activations(T)
     perm = wl.permutation()
-    times = []
+    times, t_pack, t_gemm = [], [], []
     for _ in range(reps):
         t0 = time.perf_counter()
         vals, idx = O.prune_pack(w, n, m)
+        t1 = time.perf_counter()
         O.spmm_ref(vals, idx, wl.K, n, m, act, wl.dtype, perm=perm)
-        times.append(time.perf_counter() - t0)
+        t2 = time.perf_counter()
+        times.append(t2 - t0)
+        t_pack.append(t1 - t0)
+        t_gemm.append(t2 - t1)
     t = statistics.median(times)
     try:
         cores = len(os.sched_getaffinity(0))
@@ -101,9 +106,43 @@ def cpu_baseline(wl, n, m, T, reps):
             cores = min(cores, int(os.environ[var]))
             break
     flops = 2.0 * wl.R * wl.K * T
+    tg = statistics.median(t_gemm)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"whole workload ({wl.R}x{wl.K}x{T}, {n}:{m}): prune+pack, decompress and "
-                      f"fp64 matmul; median of {reps} runs, {t:.2f} s each"}
+                      f"fp64 matmul; median of {reps} runs, {t:.2f} s each",
+            "prune_pack_s": statistics.median(t_pack), "decompress_gemm_s": tg,
+            "gemm_dense_eq_gflops": flops / tg / 1e9}
+
+
+def measured_peaks(torch):
+    """Peaks measured on this GPU with plain library calls (context for the
+    roofline fractions): a 1 GiB device-to-device copy (read + write bytes)
+    and a dense bf16 8192^3 matmul (hipBLASLt)."""
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    t_mm = timed(lambda: torch.matmul(a, b), 10)
+    out = {"copy_gbps": 2.0 * src.numel() * 2 / t_copy / 1e9,
+           "dense_bf16_matmul_tflops": 2.0 * 8192 ** 3 / t_mm / 1e12,
+           "how": "1 GiB torch copy (read+write bytes / t); torch.matmul bf16 8192^3"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -252,6 +291,35 @@ def main():
                     "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(kernel_key, hsh)}
     roofline["kernel"] = "nm_spmm" if perm is None else "nm_spmm_perm"
     roofline["per_launch"] = {"flop": alg_flop, "bytes": step_bytes, "mean_us": gemm_mean_us}
+    # roofline times: the algorithmic bound (stored weights only) and the bound
+    # at the 2:4 smfmac rate (1:4 / 1:8 widened to the 2:4 operand), each the
+    # larger of the MFMA time and the HBM time of the algorithmic bytes
+    peak_f = PEAK_MFMA_TFLOPS[dt] * 1e12
+    t_hbm = step_bytes / (PEAK_HBM_GBPS * 1e9)
+    t_alg = max(alg_flop / peak_f, t_hbm)
+    t_24 = max(dense_eq_flop / 2.0 / peak_f, t_hbm)
+    roofline["t_roof_us"] = {"algorithmic": t_alg * 1e6, "at_2of4_rate": t_24 * 1e6}
+    roofline["frac_of_t_roof"] = {"algorithmic": t_alg / (gemm_mean_us * 1e-6),
+                                  "at_2of4_rate": t_24 / (gemm_mean_us * 1e-6)}
+
+    extra = {}
+    if perm is not None:
+        y_plain = torch.empty((T, R), dtype=out_dtype, device="cuda")
+        ident = torch.arange(K, dtype=torch.int32, device="cuda")
+
+        def plain(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=y_plain)
+
+        def identity(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm_perm(vals, idx, Ac, ident, K, n, m, out_dtype=out_dtype, out=y_plain)
+
+        plain_us = time_loop(plain, iters)
+        ident_us = time_loop(identity, iters)
+        extra = {"nm_spmm_no_perm_us": plain_us, "nm_spmm_perm_identity_us": ident_us,
+                 "perm_overhead_vs_no_perm": gemm_loop_us / plain_us - 1.0,
+                 "perm_overhead_vs_identity_perm": gemm_loop_us / ident_us - 1.0}
 
     out = {
         "metric": METRIC,
@@ -282,6 +350,7 @@ def main():
             "dense_linear_us": dense_us,
             "speedup_vs_dense_half_out": dense_us / gemm_half_us,
             "speedup_vs_dense_f32_out": dense_us / gemm_loop_us,
+            **extra,
         },
         "wall_s_timed": wall,
         "source_hash": hsh,
@@ -292,6 +361,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = src.numel() * 4
+    if not args.no_peaks:
+        pk = measured_peaks(torch)
+        out["measured_peaks"] = pk
+        if roofline["bound"] == "hbm":
+            roofline["frac_of_measured_copy"] = roofline["achieved"] / pk["copy_gbps"]
+        else:
+            roofline["frac_of_measured_dense_matmul"] = roofline["achieved"] / pk["dense_bf16_matmul_tflops"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, n, m, T, args.cpu_reps)
     print(json.dumps(out), flush=True)

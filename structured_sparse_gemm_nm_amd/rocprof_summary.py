@@ -7,7 +7,9 @@
 `counters`: per-kernel mean of every collected counter (one directory per
 --pmc pass).  With FETCH_SIZE / WRITE_SIZE passes that include the plain
 256 MiB copy of `bench.py --copy-calibration`, it also prints the HBM bytes
-per launch of each kernel scaled by the copy's bytes / counter ratio.
+per launch of each kernel scaled by the copy's bytes / counter ratio.  The
+calibration dispatch is the largest copy-kernel dispatch of each pass (the
+profiled command must copy nothing larger than 256 MiB: bench.py --no-peaks).
 """
 from __future__ import annotations
 
@@ -42,7 +44,10 @@ def trace(path):
 
 
 def counters(paths):
+    """Per-kernel mean of each counter, and each counter's value for the
+    largest copy-kernel dispatch (the calibration copy)."""
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    calib = {}
     for path in paths:
         for db in _dbs(path):
             con = sqlite3.connect(db)
@@ -54,7 +59,10 @@ def counters(paths):
                 names[did] = kname
             for (did, cname), val in per.items():
                 agg[short(names[did])][cname].append(val)
-    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in agg.items()}
+                if "copyBuffer" in names[did]:
+                    calib[cname] = max(calib.get(cname, 0.0), val)
+    means = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in agg.items()}
+    return means, calib
 
 
 def main(argv):
@@ -66,13 +74,11 @@ def main(argv):
         for name, n, us in trace(argv[1]):
             print(f"{name[:70]:70s} {n:6d} {us:10.3f}")
         return 0
-    res = counters(argv[1:])
-    copy = next((v for k, v in res.items() if "copyBuffer" in k or "copy" in k.lower()), None)
+    res, copy = counters(argv[1:])
     scale = {}
-    if copy:
-        for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            if copy.get(c):
-                scale[c] = COPY_BYTES / (copy[c] * 1024.0)
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if copy.get(c):
+            scale[c] = COPY_BYTES / (copy[c] * 1024.0)
     for k, d in sorted(res.items()):
         line = ", ".join(f"{c}={v:.1f}" for c, v in sorted(d.items()))
         print(f"{k[:90]}: {line}")
@@ -81,8 +87,9 @@ def main(argv):
             print(f"    HBM bytes per launch (copy-scaled): read {hbm[0]/1e6:.2f} MB, "
                   f"write {hbm[1]/1e6:.2f} MB, total {sum(hbm)/1e6:.2f} MB")
     if scale:
-        print("copy calibration (bytes per counter byte): " +
-              ", ".join(f"{c} x{v:.3f}" for c, v in scale.items()))
+        print(f"copy calibration ({COPY_BYTES}-byte copy, largest copy dispatch: " +
+              ", ".join(f"{c}={copy[c]:.1f} KiB" for c in scale) + "; bytes per counter byte: " +
+              ", ".join(f"{c} x{v:.3f}" for c, v in scale.items()) + ")")
     return 0
 
 
