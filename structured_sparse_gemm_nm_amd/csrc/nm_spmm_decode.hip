@@ -320,13 +320,19 @@ __global__ __launch_bounds__(kWaves * 64) void spmm_decode_lds_kernel(
   }
 }
 
-// Persistent 2:4 variant: one workgroup per CU walks an equal, contiguous
-// range of rows (ceil(R / grid) of them) in 16-row blocks, so every CU
-// streams the same number of bytes.  Each wave keeps its K slice of the
-// activations in registers for the whole range and double buffers its
-// wave-private LDS staging across blocks: the next block's direct loads are in
-// flight while the current block is multiplied and reduced.
-template <int DT, int OUT, bool PERM, int SPW>
+// Persistent 2:4 variant: one workgroup per CU owns an equal, contiguous
+// range of rows (ceil(R / grid) of them, NBLK blocks of 16; a range with fewer
+// rows, at the end of R, rereads its last row and stores nothing for it), so
+// every CU streams the same number of bytes.  With the block count fixed at
+// compile time every load is issued unconditionally and every wait count is
+// a constant.  Each wave keeps its K slice of the
+// activations in registers and double buffers its wave-private LDS staging
+// across blocks: block b+2's direct loads are issued as soon as block b's
+// fragments are in registers.  No wave waits for another until every block
+// is multiplied: each wave keeps one accumulator tile per block, and the
+// partial tiles of all blocks are summed across waves once, at the end (in
+// LDS reused from the staging area), in a fixed wave order.
+template <int DT, int OUT, bool PERM, int SPW, int NBLK>
 __global__ __launch_bounds__(kWaves * 64, 1) void spmm_decode_stream_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K,
     const uint16_t* __restrict__ act, int T, int64_t ldx, const int32_t* __restrict__ perm,
@@ -337,19 +343,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void spmm_decode_stream_kernel(
   constexpr int IPR = SPW * 8 / 16;
   constexpr int PER_BLOCK = SPW + 1;           // direct loads per wave per block
   static_assert(16 * IPR == 64, "the index load must use every lane");
-  // Staging [2][kWaves][VBYTES + IBYTES] then the partial tiles, in dynamic
-  // LDS.  The explicit counted waits below order the direct loads and the
-  // fragment reads.
+  static_assert(NBLK * kWaves * 64 * 16 <= 2 * kWaves * (VBYTES + IBYTES), "partials fit the staging");
+  // Staging [2][kWaves][VBYTES + IBYTES] in dynamic LDS; after the last block
+  // it holds the partial tiles [kWaves][NBLK][64].  Explicit counted waits
+  // order the direct loads and the fragment reads.
   extern __shared__ __align__(16) unsigned char dyn[];
   auto stage_at = [&](int buf, int w) { return dyn + (buf * kWaves + w) * (VBYTES + IBYTES); };
-  f32x4 (*part)[64] = reinterpret_cast<f32x4 (*)[64]>(dyn + 2 * kWaves * (VBYTES + IBYTES));
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int li = lane & 15, lq = lane >> 4;
   const int row_begin = blockIdx.x * rows_per_wg;
   const int row_end = min(R, row_begin + rows_per_wg);
   if (row_begin >= row_end) return;  // uniform over the workgroup
-  const int nblk = (row_end - row_begin + 15) >> 4;
+  constexpr int nblk = NBLK;
   const int S = K >> 1;
   const int irow_bytes = K >> 3;
   const int s0 = wave * SPW;
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void spmm_decode_stream_kernel(
       __builtin_amdgcn_global_load_lds(values + int64_t(r) * S + off, (lds_byte*)(vst + j * 1024),
                                        16, 0, 0);
     }
-    if (lane < 16 * IPR) {
+    {
       const int row = lane / IPR;
       const int c = lane % IPR;
       int64_t off = int64_t(s0) * 8 + c * 16;
@@ -385,71 +392,157 @@ __global__ __launch_bounds__(kWaves * 64, 1) void spmm_decode_stream_kernel(
     }
   };
 
-  // Blocks 0 and 1 are fetched first, then this wave's K slice of the
-  // activations (kept in registers for every block); one full wait before the
-  // loop leaves no register load outstanding across it, so the compiler's own
-  // wait analysis inside the loop does not fall back to draining the queue.
-  issue_block(0, 0);
-  if (nblk > 1) issue_block(1, 1);
-  u32x8 bf[SPW];
+  f32x4 acc[NBLK];
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) load_bfrag<PERM>(bf[u], act, ldx, perm, li, T, K, s0 + u, lq);
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  for (int b = 0; b < NBLK; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x8 bf[SPW];
+  constexpr int kOne = PER_BLOCK;
+  constexpr int kTwo = 2 * PER_BLOCK;
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1;
-    // block blk's loads are done once at most the next block's remain
-    if (blk + 1 < nblk) __builtin_amdgcn_s_waitcnt((PER_BLOCK & 0xF) | (0x7 << 4) | (0xF << 8) | ((PER_BLOCK >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-    asm volatile("" ::: "memory");
-    const unsigned char* vst = stage_at(buf, wave);
+  // Fragments of block b from its staging slot into registers; once they are
+  // there, the slot takes block b+2.
+  auto take_block = [&](int b, u32x4 (&a)[SPW], uint32_t (&ix)[SPW]) {
+    const unsigned char* vst = stage_at(b & 1, wave);
     const unsigned char* ist = vst + VBYTES;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
-      const int s = s0 + u;
-      u32x4 a = *reinterpret_cast<const u32x4*>(vst + (li * CPR + ((u * 4 + lq) ^ (li & 15 & (CPR - 1)))) * 16);
-      uint32_t ix = *reinterpret_cast<const uint16_t*>(ist + li * (SPW * 8) + u * 8 + lq * 2);
-      if (s >= nsteps) {
-        a = u32x4{0u, 0u, 0u, 0u};
-        ix = 0u;
-      }
-      acc = smfmac<DT>(a, bf[u], acc, ix);
+      a[u] = *reinterpret_cast<const u32x4*>(vst + (li * CPR + ((u * 4 + lq) ^ (li & 15 & (CPR - 1)))) * 16);
+      ix[u] = *reinterpret_cast<const uint16_t*>(ist + li * (SPW * 8) + u * 8 + lq * 2);
     }
-    // This wave's staging slot is consumed (its reads fed the MFMAs above):
-    // refill it with block blk + 2 now, without waiting for the other waves.
-    if (blk + 2 < nblk) issue_block(blk + 2, buf);
-    part[wave][lane] = acc;
-    barrier_lds();
-    if (wave == 0) {
-      f32x4 sum = part[0][lane];
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (b + 2 < nblk) issue_block(b + 2, b & 1);
+  };
+  // steps past K (whole steps: K % 128 == 0 here) are skipped by the wave
+  auto multiply = [&](int b, const u32x4 (&a)[SPW], const uint32_t (&ix)[SPW]) {
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) sum += part[w][lane];
-      const int t = li;
-      const int r = row_begin + blk * 16 + lq * 4;
-      if (t < T && r < row_end) {
-        const bool vec_ok = (ldy & 3) == 0 && r + 3 < row_end;
-        if constexpr (OUT == NM_F32) {
-          float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
-          if (vec_ok) *reinterpret_cast<f32x4*>(y) = sum;
-          else for (int e = 0; e < 4 && r + e < row_end; ++e) y[e] = sum[e];
+    for (int u = 0; u < SPW; ++u)
+      if (s0 + u < nsteps) acc[b] = smfmac<DT>(a[u], bf[u], acc[b], ix[u]);
+  };
+  // block b has landed once at most block b+1's loads remain
+  auto wait_block = [&](int b) {
+    if (b + 1 < nblk) __builtin_amdgcn_s_waitcnt((kOne & 0xF) | (0x7 << 4) | (0xF << 8) | ((kOne >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+  };
+
+  if constexpr (!PERM) {
+    // Blocks 0 and 1 go out first (with a single block, block 1 rereads it
+    // into the unused buffer, so the count is fixed), then this wave's K slice
+    // of the activations: exactly 2*SPW loads, every lane issuing one (lanes
+    // of absent tokens reread token T-1 into output columns that are not
+    // stored; steps past K reread the row's first step and are skipped).
+    // Nothing but the MFMAs reads these registers.  The activations
+    // queue behind the weight streams, and loads complete in order, so block 0
+    // is waited for past them: its slot is refilled before they arrive, and
+    // its MFMAs wait for block 1, by which time they have.
+    issue_block(0, 0);
+    issue_block(nblk > 1 ? 1 : 0, 1);
+    const int t = min(li, T - 1);
+    const uint16_t* arow = act + int64_t(t) * ldx;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = (s0 + u < nsteps ? (s0 + u) * 64 : 0) + h * 32 + lq * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(arow + k);
+        bf[u][4 * h + 0] = v.x;
+        bf[u][4 * h + 1] = v.y;
+        bf[u][4 * h + 2] = v.z;
+        bf[u][4 * h + 3] = v.w;
+      }
+    }
+    constexpr int kFirst = PER_BLOCK + 2 * SPW;
+    __builtin_amdgcn_s_waitcnt((kFirst & 0xF) | (0x7 << 4) | (0xF << 8) | ((kFirst >> 4) << 14));
+    asm volatile("" ::: "memory");
+    u32x4 a0[SPW];
+    uint32_t ix0[SPW];
+    take_block(0, a0, ix0);
+    if constexpr (nblk == 1) {
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // the activations
+      asm volatile("" ::: "memory");
+      multiply(0, a0, ix0);
+    }
+#pragma unroll
+    for (int b = 1; b < NBLK; ++b) {
+      wait_block(b);
+      if (b == 1) multiply(0, a0, ix0);  // the activations have landed
+      u32x4 a[SPW];
+      uint32_t ix[SPW];
+      take_block(b, a, ix);
+      multiply(b, a, ix);
+    }
+  } else {
+    // Through the index map the activation loads depend on loaded indices,
+    // so they go first and are waited for before the blocks' loads are counted.
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) load_bfrag<PERM>(bf[u], act, ldx, perm, li, T, K, s0 + u, lq);
+    issue_block(0, 0);
+    issue_block(nblk > 1 ? 1 : 0, 1);
+    __builtin_amdgcn_s_waitcnt((kTwo & 0xF) | (0x7 << 4) | (0xF << 8) | ((kTwo >> 4) << 14));
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      wait_block(b);
+      u32x4 a[SPW];
+      uint32_t ix[SPW];
+      take_block(b, a, ix);
+      multiply(b, a, ix);
+    }
+  }
+
+  // Partial tiles of every block, summed across waves in wave order.  The
+  // last block's wait left no direct load in flight; the barrier makes every
+  // wave's staging reads complete before the area is rewritten.
+  f32x4 (*part)[NBLK][64] = reinterpret_cast<f32x4 (*)[NBLK][64]>(dyn);
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) part[wave][b][lane] = acc[b];
+  __syncthreads();
+  for (int b = wave; b < nblk; b += kWaves) {
+    f32x4 sum = part[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += part[w][b][lane];
+    const int t = li;
+    const int r = row_begin + b * 16 + lq * 4;
+    if (t < T && r < row_end) {
+      const bool vec_ok = (ldy & 3) == 0 && r + 3 < row_end;
+      if constexpr (OUT == NM_F32) {
+        float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
+        if (vec_ok) *reinterpret_cast<f32x4*>(y) = sum;
+        else for (int e = 0; e < 4 && r + e < row_end; ++e) y[e] = sum[e];
+      } else {
+        uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
+        const uint16_t h[4] = {to_half_bits<DT>(sum[0]), to_half_bits<DT>(sum[1]),
+                               to_half_bits<DT>(sum[2]), to_half_bits<DT>(sum[3])};
+        if (vec_ok) {
+          *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                                    uint32_t(h[2]) | (uint32_t(h[3]) << 16));
         } else {
-          uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
-          const uint16_t h[4] = {to_half_bits<DT>(sum[0]), to_half_bits<DT>(sum[1]),
-                                 to_half_bits<DT>(sum[2]), to_half_bits<DT>(sum[3])};
-          if (vec_ok) {
-            *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16),
-                                                      uint32_t(h[2]) | (uint32_t(h[3]) << 16));
-          } else {
-            for (int e = 0; e < 4 && r + e < row_end; ++e) y[e] = h[e];
-          }
+          for (int e = 0; e < 4 && r + e < row_end; ++e) y[e] = h[e];
         }
       }
     }
-    barrier_lds();  // part is rewritten by the next block
   }
 }
 
+template <int DT, int OUT, bool PERM, int SPW, int NBLK>
+hipError_t launch_dec_stream_n(const SpmmArgs& a, hipStream_t s, int grid, int rows_per_wg) {
+  constexpr int lds = 2 * kWaves * (16 * SPW * 4 * 16 + 16 * SPW * 8);
+  auto kern = spmm_decode_stream_kernel<DT, OUT, PERM, SPW, NBLK>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kWaves * 64), lds, s, a.values, a.idx, int(a.R),
+                     int(a.K), a.act, int(a.T), a.ldx, a.perm, a.Y, a.ldy, rows_per_wg);
+  return hipGetLastError();
+}
+
+// One workgroup per CU while that keeps a workgroup's rows within 8 blocks of
+// 16; more rows than that take more workgroups.
 template <int DT, int OUT, bool PERM, int SPW>
 hipError_t launch_dec_stream(const SpmmArgs& a, hipStream_t s) {
   static int cus = -1;
@@ -461,20 +554,23 @@ hipError_t launch_dec_stream(const SpmmArgs& a, hipStream_t s) {
     cus = v;
   }
   const int64_t blocks16 = (a.R + 15) / 16;
-  const int64_t grid = blocks16 < cus ? blocks16 : cus;
-  const int rows_per_wg = int((a.R + grid - 1) / grid);
-  constexpr int lds = 2 * kWaves * (16 * SPW * 4 * 16 + 16 * SPW * 8) + kWaves * 64 * 16;
-  auto kern = spmm_decode_stream_kernel<DT, OUT, PERM, SPW>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  int64_t grid = blocks16 < cus ? blocks16 : cus;
+  if ((blocks16 + grid - 1) / grid > 8) grid = (blocks16 + 7) / 8;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // rows per workgroup: the even split (a range's last block may be partial)
+  const int64_t even = (a.R + grid - 1) / grid;
+  const int nblk = int((even + 15) / 16);
+  const int rows_per_wg = int(even);
+  switch (nblk) {
+    case 1: return launch_dec_stream_n<DT, OUT, PERM, SPW, 1>(a, s, int(grid), rows_per_wg);
+    case 2: return launch_dec_stream_n<DT, OUT, PERM, SPW, 2>(a, s, int(grid), rows_per_wg);
+    case 3: return launch_dec_stream_n<DT, OUT, PERM, SPW, 3>(a, s, int(grid), rows_per_wg);
+    case 4: return launch_dec_stream_n<DT, OUT, PERM, SPW, 4>(a, s, int(grid), rows_per_wg);
+    case 5: return launch_dec_stream_n<DT, OUT, PERM, SPW, 5>(a, s, int(grid), rows_per_wg);
+    case 6: return launch_dec_stream_n<DT, OUT, PERM, SPW, 6>(a, s, int(grid), rows_per_wg);
+    case 7: return launch_dec_stream_n<DT, OUT, PERM, SPW, 7>(a, s, int(grid), rows_per_wg);
+    default: return launch_dec_stream_n<DT, OUT, PERM, SPW, 8>(a, s, int(grid), rows_per_wg);
   }
-  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kWaves * 64), lds, s, a.values, a.idx, int(a.R), int(a.K), a.act, int(a.T),
-                     a.ldx, a.perm, a.Y, a.ldy, rows_per_wg);
-  return hipGetLastError();
 }
 
 template <int DT, int OUT, bool PERM, int SPW>

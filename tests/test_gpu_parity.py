@@ -364,3 +364,36 @@ def test_lds_tile_walk(R, K, T, out):
     yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt)
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt),
                  **({"out_half": dt} if out == "half" else {}))
+
+
+# ---------------------------------------------------------------------------
+# few-token kernel for tall weights: one workgroup per CU owns 1..8 blocks of
+# 16 rows (the even split, last block partial); K slices past the last step
+# in some waves; the index map read inside the kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,K,T,dt,permuted", [(4096, 4096, 1, "bf16", False),
+                                               (6000, 4096, 16, "bf16", False),
+                                               (20000, 4096, 5, "f16", False),
+                                               (33000, 2176, 16, "bf16", False),
+                                               (5000, 2176, 7, "f16", False),
+                                               (6000, 4096, 9, "f16", True)])
+def test_decode_stream(R, K, T, dt, permuted):
+    log(f"decode stream R={R} K={K} T={T} {dt} perm={permuted}")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 51, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 51, 1, R + K + T)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    perm = nm_inputs.random_permutation(K, 51, R) if permuted else None
+    try:
+        nm.nm_set_variant(4)
+        if perm is None:
+            y = nm.nm_spmm(vals, idx, A, K, 2, 4)
+        else:
+            y = nm.nm_spmm_perm(vals, idx, A, torch.from_numpy(perm).cuda(), K, 2, 4)
+    finally:
+        nm.nm_set_variant(0)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
