@@ -84,17 +84,19 @@ __device__ inline void load_afrag(AFrag& f, const uint16_t* __restrict__ values,
     const uint2 t = *reinterpret_cast<const uint2*>(vrow + s * 16 + lq * 4);
     f.v[0] = t.x; f.v[1] = t.y; f.v[2] = 0u; f.v[3] = 0u;
     f.ib = irow[s * 4 + lq];
-  } else {  // 1:8: 2 values (4 B), 6 index bits at bit 24 s + 6 lq
+  } else {  // 1:8: 2 values (4 B), 6 index bits at bit 24 s + 6 lq of the row
     f.v[0] = *reinterpret_cast<const uint32_t*>(vrow + s * 8 + lq * 2);
-    f.v[1] = f.v[2] = f.v[3] = 0u;
-    // The 6 bits of lane lq sit in byte 3s + (6lq >> 3); lanes lq = 1, 2 also
-    // need the next byte (inside the step's 3 bytes).  Every wave holds all
-    // four lq values, so the second load is issued by every wave.
-    const int bit = 6 * lq;
-    const int byte = s * 3 + (bit >> 3);
-    uint32_t b = irow[byte];
-    if ((bit & 7) + 6 > 8) b |= uint32_t(irow[byte + 1]) << 8;
-    f.ib = b >> (bit & 7);
+    f.v[3] = 0u;
+    // the aligned word holding the first bit and the next one (clamped to the
+    // row's last word, whose bits then suffice): two loads from every lane,
+    // kept as loaded (widen extracts the bits, so nothing here waits for them)
+    const uint32_t* wrow = idx + int64_t(row) * words;
+    const int bit = 24 * s + 6 * lq;
+    const int w0 = bit >> 5;
+    const int w1 = min(w0 + 1, int(words) - 1);
+    f.v[1] = wrow[w0];
+    f.v[2] = wrow[w1];
+    f.ib = uint32_t(bit & 31);
   }
 }
 
@@ -114,7 +116,8 @@ __device__ inline void widen(const AFrag& f, u32x4& a, uint32_t& idx16) {
     idx16 = t | (t << 2);
   } else {
     const uint32_t v0 = f.v[0] & 0xFFFFu, v1 = f.v[0] >> 16;
-    const uint32_t p0 = f.ib & 7u, p1 = (f.ib >> 3) & 7u;
+    const uint32_t ib = uint32_t((uint64_t(f.v[1]) | (uint64_t(f.v[2]) << 32)) >> f.ib);
+    const uint32_t p0 = ib & 7u, p1 = (ib >> 3) & 7u;
     const bool h0 = p0 >= 4, h1 = p1 >= 4;
     a[0] = h0 ? 0u : v0; a[1] = h0 ? v0 : 0u;
     a[2] = h1 ? 0u : v1; a[3] = h1 ? v1 : 0u;
