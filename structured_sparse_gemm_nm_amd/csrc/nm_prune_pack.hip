@@ -9,8 +9,11 @@
 // in-group position stored as a b-bit field of an LSB-first per-row bitstream
 // padded to whole 32-bit words.
 //
-// Thread mapping.  One lane owns one 16-byte chunk (8 consecutive weights) of
-// a row, so a wavefront reads 1 KiB of W contiguously.  A lane produces
+// Thread mapping.  A lane position owns one 16-byte chunk (8 consecutive
+// weights) of a row, so a wavefront reads 1 KiB of W contiguously.  A
+// workgroup covers 256 chunk positions of kRows consecutive rows: each thread
+// issues the loads of its position in all kRows rows before selecting, and
+// row and position come from the workgroup coordinates (no division).  A lane produces
 // 8*N/M survivors and BPL = 8*N/M*b index bits.  The smallest run of lanes
 // whose bits fill whole words (L = 32 / gcd(BPL, 32) lanes -> L*BPL/32 words)
 // assembles its words with an OR-reduction over cross-lane shuffles; rows are
@@ -56,24 +59,16 @@ __device__ inline void select_group(const uint32_t* key, int* pos) {
   }
 }
 
+constexpr int kRows = 4;   // rows per workgroup (chunks per thread)
+
+// Prune and pack chunk c of row r (loaded into w).
 template <int N, int M>
-__global__ __launch_bounds__(256) void prune_pack_kernel(const uint16_t* __restrict__ W, int64_t R,
-                                                         int64_t K, int64_t ldw, int64_t lanes_per_row,
-                                                         uint16_t* __restrict__ values,
-                                                         uint32_t* __restrict__ idx,
-                                                         int64_t idx_row_words) {
+__device__ inline void pack_chunk(const uint32_t (&w)[4], int64_t r, int64_t c, int64_t R, int64_t K,
+                                  uint16_t* __restrict__ values, uint32_t* __restrict__ idx,
+                                  int64_t idx_row_words) {
   using PS = PackShape<N, M>;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t r = gid / lanes_per_row;
-  const int64_t c = gid - r * lanes_per_row;  // chunk index inside the row
   const int64_t chunks = K / 8;
   const bool live = (r < R) && (c < chunks);
-
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (live) {
-    const uint4 v = *reinterpret_cast<const uint4*>(W + r * ldw + c * 8);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
   uint32_t bits[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -137,6 +132,42 @@ __global__ __launch_bounds__(256) void prune_pack_kernel(const uint16_t* __restr
   }
 }
 
+// A row takes 2^shift chunk positions: shift 8 when it has 256 chunks or
+// more (position c = 256 blockIdx.x + threadIdx.x); shorter rows are padded to
+// a power of two (at least L) and 256 >> shift of them share a workgroup, in
+// row slots threadIdx.x >> shift.  The workgroup walks the row groups
+// blockIdx.y, + gridDim.y, ... (kRows row slots each).  Positions past the
+// row's chunks (or rows past R) load nothing but still take part in the
+// cross-lane reductions; a row's positions start on a multiple of L, so every
+// L-lane run stays inside one row.
+template <int N, int M>
+__global__ __launch_bounds__(256) void prune_pack_kernel(const uint16_t* __restrict__ W, int64_t R,
+                                                         int64_t K, int64_t ldw, int shift,
+                                                         uint16_t* __restrict__ values,
+                                                         uint32_t* __restrict__ idx,
+                                                         int64_t idx_row_words) {
+  const int per_wg = 256 >> shift;                      // rows side by side in a workgroup
+  const int64_t c = int64_t(blockIdx.x) * 256 + (threadIdx.x & ((1 << shift) - 1));
+  const int sub = threadIdx.x >> shift;
+  const int64_t chunks = K / 8;
+  for (int64_t g = blockIdx.y; g * kRows * per_wg < R; g += gridDim.y) {
+    const int64_t r0 = g * kRows * per_wg + sub;
+    uint32_t w[kRows][4];
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) {
+      const int64_t r = r0 + int64_t(p) * per_wg;
+      w[p][0] = w[p][1] = w[p][2] = w[p][3] = 0u;
+      if (r < R && c < chunks) {
+        const uint4 v = *reinterpret_cast<const uint4*>(W + r * ldw + c * 8);
+        w[p][0] = v.x; w[p][1] = v.y; w[p][2] = v.z; w[p][3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kRows; ++p)
+      pack_chunk<N, M>(w[p], r0 + int64_t(p) * per_wg, c, R, K, values, idx, idx_row_words);
+  }
+}
+
 // Decompress: one lane writes one 16-byte chunk (8 dense positions).
 template <int N, int M>
 __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restrict__ values,
@@ -178,14 +209,18 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
 template <int N, int M>
 hipError_t prune_pack_t(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, uint16_t* values,
                         uint32_t* idx, int64_t idx_row_words, hipStream_t s) {
-  using PS = PackShape<N, M>;
+  constexpr int L = PackShape<N, M>::L;
+  static_assert(256 % L == 0, "runs inside a segment");
   const int64_t chunks = K / 8;
-  const int64_t lanes_per_row = (chunks + PS::L - 1) / PS::L * PS::L;
-  const int64_t threads = R * lanes_per_row;
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prune_pack_kernel<N, M>), dim3(unsigned(blocks)), dim3(256), 0, s, W, R, K,
-                     ldw, lanes_per_row, values, idx, idx_row_words);
+  const int64_t segs = (chunks + 255) / 256;
+  if (segs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  int shift = 8;  // positions per row: 2^shift, the least power of two >= chunks and >= L, at most 256
+  while (shift > 0 && (int64_t(1) << (shift - 1)) >= chunks && (1 << (shift - 1)) >= L) --shift;
+  const int64_t rows_per_group = int64_t(kRows) * (256 >> shift);
+  const int64_t groups = (R + rows_per_group - 1) / rows_per_group;
+  const unsigned gy = unsigned(groups < 65535 ? groups : 65535);   // grid-stride beyond
+  hipLaunchKernelGGL((prune_pack_kernel<N, M>), dim3(unsigned(segs), gy), dim3(256), 0,
+                     s, W, R, K, ldw, shift, values, idx, idx_row_words);
   return hipGetLastError();
 }
 
