@@ -146,7 +146,9 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   unsigned char* ibuf = smem + kNS * (kStageB + kStageA);  // [2][kBlockI]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // uniform: LDS destinations of the direct loads (M0) are then scalar sums
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const int wr = wave >> 1, wt = wave & 1;
   const int nsteps = K >> 6;                 // even: K % 128 == 0 on this path
@@ -203,6 +205,14 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     else
       dma16(nt ? n.a : c.a, nt ? n.aoff[j - 4] : c.aoff[j - 4], uint32_t(src) * 64u,
             abuf + buf * kStageA + (wave * 4 + j - 4) * 1024);
+  };
+  // Load j of a step whose per-lane offset was selected beforehand.
+  auto issue_load_at = [&](__amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t ra, uint32_t off, int j,
+                           int src, int buf) {
+    if (j < 4)
+      dma16(rb, off, uint32_t(src) * 128u, bbuf + buf * kStageB + (wave * 4 + j) * 1024);
+    else
+      dma16(ra, off, uint32_t(src) * 64u, abuf + buf * kStageA + (wave * 4 + j - 4) * 1024);
   };
   auto issue_step = [&](const Src& c, const Src& n, bool nt, int src, int buf) {
 #pragma unroll
@@ -315,15 +325,27 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     const bool r_in = s + 1 < nsteps;
     const int rib = (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
     const int ru8 = r_in ? ((s + 1) & 7) : 0;
+    // The step's index operands and load offsets are worked out before its
+    // first MFMA: a VALU result that an MFMA (or a load) waits for inside
+    // the chunks would stall the matrix pipe every chunk.
+    uint32_t ik[FR], lo[kPerStep];
+#pragma unroll
+    for (int k = 0; k < FR; ++k) ik[k] = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = ln ? nxt.boff[j] : cur.boff[j];
+      lo[4 + j] = ln ? nxt.aoff[j] : cur.aoff[j];
+    }
+    const __amdgpu_buffer_rsrc_t lrb = ln ? nxt.b : cur.b, lra = ln ? nxt.a : cur.a;
+    __builtin_amdgcn_sched_barrier(0);
     // Eight chunks, each: the 4 MFMAs of row fragment k, one load, and three
     // fragment reads of step s+1.  Scheduling barriers keep the chunks in
     // this order.
 #pragma unroll
     for (int k = 0; k < FR; ++k) {
-      const uint32_t ik = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
 #pragma unroll
-      for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik);
-      issue_load(cur, nxt, ln, k, src, buf);
+      for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik[k]);
+      issue_load_at(lrb, lra, lo[k], k, src, buf);
       read_a(rsl, rib, ru8, k, na[k], nx[k]);
       read_b(rsl, k >> 1, k & 1, nb[k >> 1]);
       __builtin_amdgcn_sched_barrier(0);
