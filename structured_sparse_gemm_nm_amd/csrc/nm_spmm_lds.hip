@@ -33,6 +33,8 @@
 // ring's fill nor the epilogue's stores leave the MFMAs idle between tiles.
 #include "nm_internal.h"
 
+#include <type_traits>
+
 namespace nm {
 namespace {
 
@@ -301,8 +303,12 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // nothing reads any more.  So the wait counts are fixed and the loads, the
   // fragment reads and the MFMAs form one branch-free block the scheduler
   // interleaves (a burst of loads would hold up the MFMAs behind it).
-  auto body = [&](int s, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT], u32x4 (&na)[FR],
+  // IN (compile time): steps s+1 .. s+kNS lie inside the tile (every step
+  // but a tile's last kNS), so the loads come from this tile and nothing on
+  // them is selected at run time.
+  auto body = [&](auto in_c, int s, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT], u32x4 (&na)[FR],
                   uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
+    constexpr bool IN = decltype(in_c)::value;
     // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
     // index block issued in between only makes the wait stricter)
     wait_vmcnt<2 * kPerStep>();
@@ -317,12 +323,12 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     }
     // loads of the step 4 ahead into step s's slot
     const int buf = (g + s) & (kNS - 1);
-    const bool in_tile = s + kNS < nsteps;
+    const bool in_tile = IN || s + kNS < nsteps;
     const bool ln = !in_tile && has_next;
     const int src = in_tile ? s + kNS : (has_next ? s + kNS - nsteps : nsteps - 1);
     // where step s+1 is read from
     const int rsl = (g + s + 1) & (kNS - 1);
-    const bool r_in = s + 1 < nsteps;
+    const bool r_in = IN || s + 1 < nsteps;
     const int rib = (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
     const int ru8 = r_in ? ((s + 1) & 7) : 0;
     // The step's index operands and load offsets are worked out before its
@@ -331,12 +337,21 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     uint32_t ik[FR], lo[kPerStep];
 #pragma unroll
     for (int k = 0; k < FR; ++k) ik[k] = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
+    __amdgpu_buffer_rsrc_t lrb = cur.b, lra = cur.a;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lo[j] = ln ? nxt.boff[j] : cur.boff[j];
-      lo[4 + j] = ln ? nxt.aoff[j] : cur.aoff[j];
+      lo[j] = cur.boff[j];
+      lo[4 + j] = cur.aoff[j];
     }
-    const __amdgpu_buffer_rsrc_t lrb = ln ? nxt.b : cur.b, lra = ln ? nxt.a : cur.a;
+    if constexpr (!IN) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = ln ? nxt.boff[j] : lo[j];
+        lo[4 + j] = ln ? nxt.aoff[j] : lo[4 + j];
+      }
+      lrb = ln ? nxt.b : lrb;
+      lra = ln ? nxt.a : lra;
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Eight chunks, each: the 4 MFMAs of row fragment k, one load, and three
     // fragment reads of step s+1.  Scheduling barriers keep the chunks in
@@ -375,9 +390,15 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     for (int i = 0; i < FR; ++i)
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsteps; s += 2) {
-      body(s, a0, x0, b0, a1, x1, b1);
-      body(s + 1, a1, x1, b1, a0, x0, b0);
+    // nsteps is even, so both loops run whole pairs of steps
+    int s = 0;
+    for (; s + kNS < nsteps; s += 2) {
+      body(std::true_type{}, s, a0, x0, b0, a1, x1, b1);
+      body(std::true_type{}, s + 1, a1, x1, b1, a0, x0, b0);
+    }
+    for (; s < nsteps; s += 2) {
+      body(std::false_type{}, s, a0, x0, b0, a1, x1, b1);
+      body(std::false_type{}, s + 1, a1, x1, b1, a0, x0, b0);
     }
 
     // ---- epilogue
