@@ -303,12 +303,20 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // nothing reads any more.  So the wait counts are fixed and the loads, the
   // fragment reads and the MFMAs form one branch-free block the scheduler
   // interleaves (a burst of loads would hold up the MFMAs behind it).
-  // IN (compile time): steps s+1 .. s+kNS lie inside the tile (every step
-  // but a tile's last kNS), so the loads come from this tile and nothing on
-  // them is selected at run time.
-  auto body = [&](auto in_c, int s, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT], u32x4 (&na)[FR],
-                  uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
-    constexpr bool IN = decltype(in_c)::value;
+  // MODE (compile time):
+  //   -2  any step;
+  //   -1  steps s+1 .. s+kNS lie inside the tile (every step but a tile's last
+  //       kNS), so the loads come from this tile and nothing on them is
+  //       selected at run time;
+  //   0..7  as -1, and moreover s = 8m + MODE with the tile starting at a ring
+  //       position that is a multiple of kNS: ring slots and the index bytes'
+  //       place in their block are constants, and ibc / ibn are the index
+  //       buffers of this step's block and of the next.
+  auto body = [&](auto mode_c, int s, int ibc, int ibn, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT],
+                  u32x4 (&na)[FR], uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool IN = MODE != -2;
+    constexpr bool FAST = MODE >= 0;
     // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
     // index block issued in between only makes the wait stricter)
     wait_vmcnt<2 * kPerStep>();
@@ -316,21 +324,23 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     barrier_no_fence();  // publishes step s+1; every wave is done reading step s
     // at a block's first step, the block after it: this tile's next, or the
     // next tile's first
-    if ((s & 7) == 0) {
+    if constexpr (FAST) {
+      if constexpr (MODE == 0) issue_index(cur, (s >> 3) + 1, ibn);  // s + 8 < nsteps here
+    } else if ((s & 7) == 0) {
       const int ib = (qb + (s >> 3) + 1) & 1;
       if (s + 8 < nsteps) issue_index(cur, (s >> 3) + 1, ib);
       else if (has_next) issue_index(nxt, 0, ib);
     }
     // loads of the step 4 ahead into step s's slot
-    const int buf = (g + s) & (kNS - 1);
+    const int buf = FAST ? (MODE & (kNS - 1)) : (g + s) & (kNS - 1);
     const bool in_tile = IN || s + kNS < nsteps;
     const bool ln = !in_tile && has_next;
     const int src = in_tile ? s + kNS : (has_next ? s + kNS - nsteps : nsteps - 1);
     // where step s+1 is read from
-    const int rsl = (g + s + 1) & (kNS - 1);
+    const int rsl = FAST ? ((MODE + 1) & (kNS - 1)) : (g + s + 1) & (kNS - 1);
     const bool r_in = IN || s + 1 < nsteps;
-    const int rib = (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
-    const int ru8 = r_in ? ((s + 1) & 7) : 0;
+    const int rib = FAST ? (MODE == 7 ? ibn : ibc) : (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
+    const int ru8 = FAST ? ((MODE + 1) & 7) : r_in ? ((s + 1) & 7) : 0;
     // The step's index operands and load offsets are worked out before its
     // first MFMA: a VALU result that an MFMA (or a load) waits for inside
     // the chunks would stall the matrix pipe every chunk.
@@ -390,15 +400,31 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     for (int i = 0; i < FR; ++i)
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // nsteps is even, so both loops run whole pairs of steps
+    // Eight steps at a time while all eight stay in the tile and the tile
+    // starts on a multiple of kNS in the ring; then pairs of in-tile steps;
+    // then the last kNS steps (nsteps is even, so every loop runs whole pairs).
+    using std::integral_constant;
     int s = 0;
+    if ((g & (kNS - 1)) == 0) {
+      for (; s + 8 + kNS - 1 < nsteps; s += 8) {
+        const int ibc = (qb + (s >> 3)) & 1, ibn = ibc ^ 1;
+        body(integral_constant<int, 0>{}, s, ibc, ibn, a0, x0, b0, a1, x1, b1);
+        body(integral_constant<int, 1>{}, s + 1, ibc, ibn, a1, x1, b1, a0, x0, b0);
+        body(integral_constant<int, 2>{}, s + 2, ibc, ibn, a0, x0, b0, a1, x1, b1);
+        body(integral_constant<int, 3>{}, s + 3, ibc, ibn, a1, x1, b1, a0, x0, b0);
+        body(integral_constant<int, 4>{}, s + 4, ibc, ibn, a0, x0, b0, a1, x1, b1);
+        body(integral_constant<int, 5>{}, s + 5, ibc, ibn, a1, x1, b1, a0, x0, b0);
+        body(integral_constant<int, 6>{}, s + 6, ibc, ibn, a0, x0, b0, a1, x1, b1);
+        body(integral_constant<int, 7>{}, s + 7, ibc, ibn, a1, x1, b1, a0, x0, b0);
+      }
+    }
     for (; s + kNS < nsteps; s += 2) {
-      body(std::true_type{}, s, a0, x0, b0, a1, x1, b1);
-      body(std::true_type{}, s + 1, a1, x1, b1, a0, x0, b0);
+      body(integral_constant<int, -1>{}, s, 0, 0, a0, x0, b0, a1, x1, b1);
+      body(integral_constant<int, -1>{}, s + 1, 0, 0, a1, x1, b1, a0, x0, b0);
     }
     for (; s < nsteps; s += 2) {
-      body(std::false_type{}, s, a0, x0, b0, a1, x1, b1);
-      body(std::false_type{}, s + 1, a1, x1, b1, a0, x0, b0);
+      body(integral_constant<int, -2>{}, s, 0, 0, a0, x0, b0, a1, x1, b1);
+      body(integral_constant<int, -2>{}, s + 1, 0, 0, a1, x1, b1, a0, x0, b0);
     }
 
     // ---- epilogue
