@@ -11,10 +11,11 @@
 // the GEMM keeps its full-width, conflict-free loads.
 //
 // The pass: a workgroup stages a block of token rows in LDS with 16-byte
-// loads, then each thread builds 8 consecutive output columns of one row
-// from 8 LDS reads at perm[c..c+7] and writes them as one 16-byte store.
-// Out-of-range perm entries (a broken precondition) are clamped into the row,
-// so they give wrong values, never wrong addresses.
+// loads, then each thread builds 8 consecutive output columns (chunk c) from
+// 8 LDS reads at perm[c..c+7] and writes them as one 16-byte store.  A thread
+// keeps one chunk for every row it handles, so its 8 perm entries are read
+// from memory once.  Out-of-range perm entries (a broken precondition) are
+// clamped into the row, so they give wrong values, never wrong addresses.
 #include "nm_internal.h"
 
 #include <functional>
@@ -25,7 +26,7 @@ namespace nm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 48 * 1024;   // LDS for staged rows per workgroup
+constexpr int kRowBytes = 16 * 1024;   // LDS for staged rows per workgroup (several per CU)
 constexpr int64_t kMaxK = 65536;       // one row must fit the LDS a workgroup can have
 
 __global__ __launch_bounds__(kThreads) void permute_cols_kernel(
@@ -42,19 +43,29 @@ __global__ __launch_bounds__(kThreads) void permute_cols_kernel(
         *reinterpret_cast<const uint4*>(X + int64_t(t0 + r) * ldx + c * 8);
   }
   __syncthreads();
+  // thread -> (chunk c, first row): chunks c, c + kThreads, ... of the rows
+  // r0, r0 + rstep, ... (rstep = kThreads / cpr rows at a time when a row has
+  // fewer chunks than threads)
   const uint32_t kmax = uint32_t(K - 1);
-  for (int i = threadIdx.x; i < total; i += kThreads) {
-    const int r = i / cpr, c = i - r * cpr;
+  const int rstep = cpr >= kThreads ? 1 : kThreads / cpr;
+  const int lanes = cpr >= kThreads ? kThreads : rstep * cpr;
+  if (threadIdx.x >= lanes) return;
+  const int r0 = cpr >= kThreads ? 0 : threadIdx.x / cpr;
+  for (int c = cpr >= kThreads ? threadIdx.x : threadIdx.x - r0 * cpr; c < cpr; c += kThreads) {
     const int4 p0 = *reinterpret_cast<const int4*>(perm + c * 8);
     const int4 p1 = *reinterpret_cast<const int4*>(perm + c * 8 + 4);
-    const uint16_t* row = rowbuf + r * K;
-    auto g = [&](int p) { return uint32_t(row[min(uint32_t(p), kmax)]); };
-    uint4 o;
-    o.x = g(p0.x) | (g(p0.y) << 16);
-    o.y = g(p0.z) | (g(p0.w) << 16);
-    o.z = g(p1.x) | (g(p1.y) << 16);
-    o.w = g(p1.z) | (g(p1.w) << 16);
-    *reinterpret_cast<uint4*>(Xp + int64_t(t0 + r) * K + c * 8) = o;
+    const uint32_t q[8] = {min(uint32_t(p0.x), kmax), min(uint32_t(p0.y), kmax), min(uint32_t(p0.z), kmax),
+                           min(uint32_t(p0.w), kmax), min(uint32_t(p1.x), kmax), min(uint32_t(p1.y), kmax),
+                           min(uint32_t(p1.z), kmax), min(uint32_t(p1.w), kmax)};
+    for (int r = r0; r < nr; r += rstep) {
+      const uint16_t* row = rowbuf + r * K;
+      uint4 o;
+      o.x = uint32_t(row[q[0]]) | (uint32_t(row[q[1]]) << 16);
+      o.y = uint32_t(row[q[2]]) | (uint32_t(row[q[3]]) << 16);
+      o.z = uint32_t(row[q[4]]) | (uint32_t(row[q[5]]) << 16);
+      o.w = uint32_t(row[q[6]]) | (uint32_t(row[q[7]]) << 16);
+      *reinterpret_cast<uint4*>(Xp + int64_t(t0 + r) * K + c * 8) = o;
+    }
   }
 }
 
