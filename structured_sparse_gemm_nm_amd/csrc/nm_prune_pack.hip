@@ -35,27 +35,69 @@ struct PackShape {
   static constexpr int WPR = L * BPL / 32;                       // words per run
 };
 
-// Select the N largest of M keys (ties -> lower position); positions ascending.
+// Composite key of element i (0..7) of a chunk held in w[4]: the magnitude
+// key (the 16-bit pattern with the sign cleared) above the tie-break
+// M-1-(i mod M).  Keys of one group are distinct and a larger composite key
+// wins: larger magnitude first, then the lower position.
+template <int M>
+__device__ inline uint32_t ckey(const uint32_t (&w)[4], int i) {
+  const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : w[i >> 1];
+  return ((h & 0x7FFFu) << 3) | uint32_t(M - 1 - (i % M));
+}
+
+// Position (0..M-1) encoded in a composite key.
+template <int M>
+__device__ inline uint32_t ckey_pos(uint32_t k) { return uint32_t(M - 1) - (k & 7u); }
+
+// Byte selector for v_perm picking element p (0..3) of the dword pair
+// {hi, lo} into the low half and element q into the high half.
+__device__ inline uint32_t pick2(uint32_t p, uint32_t q) {
+  return (p * 0x0202u + 0x0100u) | ((q * 0x0202u + 0x0100u) << 16);
+}
+
+// The chunk's survivors, pushed left (vals: SPL halves, two per dword) and
+// their in-group positions in survivor order (BPL bits).  Selection works on
+// the composite keys with min / max; survivors come out in ascending
+// position order.
 template <int N, int M>
-__device__ inline void select_group(const uint32_t* key, int* pos) {
-  // Composite keys (key << 3 | (M-1-i)) are all distinct and larger means
-  // "wins"; an element is kept when fewer than N others beat it.  The kept
-  // set becomes a bit mask whose set bits, lowest first, are the positions.
-  uint32_t ck[M];
+__device__ inline void select_chunk(const uint32_t (&w)[4], uint32_t (&vals)[2], uint32_t& lane_idx) {
+  if constexpr (N == 2 && M == 4) {
 #pragma unroll
-  for (int i = 0; i < M; ++i) ck[i] = (key[i] << 3) | uint32_t(M - 1 - i);
-  uint32_t mask = 0;
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t a = ckey<4>(w, 4 * g), b = ckey<4>(w, 4 * g + 1);
+      const uint32_t c = ckey<4>(w, 4 * g + 2), d = ckey<4>(w, 4 * g + 3);
+      const uint32_t hi1 = max(a, b), lo1 = min(a, b), hi2 = max(c, d), lo2 = min(c, d);
+      const uint32_t k1 = max(hi1, hi2);                       // largest
+      const uint32_t k2 = max(min(hi1, hi2), max(lo1, lo2));   // second largest
+      const uint32_t p1 = ckey_pos<4>(k1), p2 = ckey_pos<4>(k2);
+      const uint32_t pl = min(p1, p2), ph = max(p1, p2);
+      vals[g] = __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], pick2(pl, ph));
+      lane_idx |= (pl | (ph << 2)) << (4 * g);
+    }
+  } else if constexpr (N == 1 && M == 4) {
+    uint32_t v[2];
 #pragma unroll
-  for (int i = 0; i < M; ++i) {
-    int beaten = 0;
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t k = max(max(ckey<4>(w, 4 * g), ckey<4>(w, 4 * g + 1)),
+                             max(ckey<4>(w, 4 * g + 2), ckey<4>(w, 4 * g + 3)));
+      const uint32_t p = ckey_pos<4>(k);
+      v[g] = __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], pick2(p, p));
+      lane_idx |= p << (2 * g);
+    }
+    vals[0] = (v[0] & 0xFFFFu) | (v[1] << 16);
+    vals[1] = 0u;
+  } else {
+    static_assert(N == 1 && M == 8, "2:4, 1:4 or 1:8");
+    uint32_t k = ckey<8>(w, 0);
 #pragma unroll
-    for (int j = 0; j < M; ++j) beaten += (ck[j] > ck[i]) ? 1 : 0;
-    mask |= (beaten < N) ? (1u << i) : 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    pos[j] = __builtin_ctz(mask);
-    mask &= mask - 1u;
+    for (int i = 1; i < 8; ++i) k = max(k, ckey<8>(w, i));
+    const uint32_t p = ckey_pos<8>(k);
+    const uint32_t q = p & 3u;
+    const uint32_t lo = __builtin_amdgcn_perm(w[1], w[0], pick2(q, q));
+    const uint32_t hi = __builtin_amdgcn_perm(w[3], w[2], pick2(q, q));
+    vals[0] = (p < 4 ? lo : hi) & 0xFFFFu;
+    vals[1] = 0u;
+    lane_idx = p;
   }
 }
 
@@ -69,47 +111,20 @@ __device__ inline void pack_chunk(const uint32_t (&w)[4], int64_t r, int64_t c, 
   using PS = PackShape<N, M>;
   const int64_t chunks = K / 8;
   const bool live = (r < R) && (c < chunks);
-  uint32_t bits[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bits[2 * i] = w[i] & 0xFFFFu;
-    bits[2 * i + 1] = w[i] >> 16;
-  }
-
   uint32_t lane_idx = 0;        // this lane's BPL index bits, survivor order
-  uint16_t kept[PS::SPL];
-#pragma unroll
-  for (int g = 0; g < PS::GPL; ++g) {
-    uint32_t key[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) key[i] = bits[g * M + i] & 0x7FFFu;
-    int pos[N];
-    select_group<N, M>(key, pos);
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      // pos[j] < M; pick the bits with a short unrolled select (no dynamic
-      // register indexing).
-      uint32_t val = 0;
-#pragma unroll
-      for (int i = 0; i < M; ++i) val = (pos[j] == i) ? bits[g * M + i] : val;
-      kept[g * N + j] = uint16_t(val);
-      lane_idx |= uint32_t(pos[j]) << ((g * N + j) * PS::B);
-    }
-  }
+  uint32_t kept[2];
+  select_chunk<N, M>(w, kept, lane_idx);
 
   // Values: SPL consecutive halves at survivor offset c*SPL of the row.
   if (live) {
     const int64_t S = K / M * N;
     uint16_t* dst = values + r * S + c * PS::SPL;
     if constexpr (PS::SPL == 4) {
-      uint2 o;
-      o.x = uint32_t(kept[0]) | (uint32_t(kept[1]) << 16);
-      o.y = uint32_t(kept[2]) | (uint32_t(kept[3]) << 16);
-      *reinterpret_cast<uint2*>(dst) = o;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(kept[0], kept[1]);
     } else if constexpr (PS::SPL == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = uint32_t(kept[0]) | (uint32_t(kept[1]) << 16);
+      *reinterpret_cast<uint32_t*>(dst) = kept[0];
     } else {
-      *dst = kept[0];
+      *dst = uint16_t(kept[0]);
     }
   }
 
