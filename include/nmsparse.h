@@ -158,9 +158,11 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
  *   4  few-token kernel (T <= 16, K <= 4096)
  *   5  all-LDS direct-load kernel with 256 x 256 tiles (2:4; K % 128 == 0,
  *      T >= 256, R >= 256)
+ *   6  all-LDS direct-load kernel with 128 x 64 tiles (1:4 and 1:8;
+ *      K % 256 == 0, T >= 64, R >= 128)
  * A forced family that does not take the shape falls back to the choice by
  * shape.  Every family computes the same product; all but 4 add the K steps
- * in the same order and give the same bits.  NM_ERR_UNSUPPORTED outside 0..5.
+ * in the same order and give the same bits.  NM_ERR_UNSUPPORTED outside 0..6.
  */
 nm_status nm_set_variant(int variant);
 

@@ -10,7 +10,7 @@
 namespace nm {
 
 enum { NM_VARIANT_AUTO = 0, NM_VARIANT_GENERIC = 1, NM_VARIANT_PIPE = 2, NM_VARIANT_LDS = 3,
-       NM_VARIANT_DECODE = 4, NM_VARIANT_WIDE = 5, NM_VARIANT_MAX = 5 };
+       NM_VARIANT_DECODE = 4, NM_VARIANT_WIDE = 5, NM_VARIANT_LDS_NM = 6, NM_VARIANT_MAX = 6 };
 
 // Launchers (defined next to their kernels).  Arguments are already
 // validated; each returns the hipError_t of its launch.
@@ -55,6 +55,11 @@ hipError_t launch_spmm_perm_lds(const SpmmArgs& a, hipStream_t s);
 // All-LDS 2:4 kernel (nm_spmm_lds.hip) and the shapes it takes.
 bool spmm_lds_applies(const SpmmArgs& a);
 hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);
+
+// All-LDS 1:4 / 1:8 kernel with 128 x 64 tiles (nm_spmm_lds_nm.hip) and the
+// shapes it takes.
+bool spmm_lds_nm_applies(const SpmmArgs& a);
+hipError_t launch_spmm_lds_nm(const SpmmArgs& a, hipStream_t s);
 
 // Permuted GEMM as a gather pass into stream-ordered scratch followed by the
 // plain GEMM (nm_permute.hip), and the shapes it takes.

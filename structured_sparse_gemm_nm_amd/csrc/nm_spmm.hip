@@ -436,12 +436,16 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
     case NM_VARIANT_WIDE:
       if (spmm_wide_applies(a)) return launch_spmm_wide(a, s);
       break;
+    case NM_VARIANT_LDS_NM:
+      if (spmm_lds_nm_applies(a)) return launch_spmm_lds_nm(a, s);
+      break;
     default: break;
   }
   if (spmm_perm_gather_applies(a)) return launch_spmm_perm_gather(a, s);
   if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
   if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
   if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
+  if (spmm_lds_nm_applies(a)) return launch_spmm_lds_nm(a, s);
   if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);
   return launch_generic(a, s);
 }

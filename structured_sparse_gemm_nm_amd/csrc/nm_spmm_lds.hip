@@ -237,11 +237,14 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // and index bits) and one half (h: K 8q..8q+7 or 32+8q..) of token fragment j.
   // byte selector: bytes 2*lq, 2*lq+1 of {w.y, w.x} into bits 0..15, zeros above
   const uint32_t ix_sel = uint32_t(2 * lq) | (uint32_t(2 * lq + 1) << 8) | (0x0C0Cu << 16);
-  auto read_a = [&](int sl, int ib, int u8, int i, u32x4& a, uint2& ix) {
+  auto read_av = [&](int sl, int i, u32x4& a) {
     const unsigned char* sa = abuf + sl * kStageA;
-    const unsigned char* si = ibuf + ib * kBlockI;
     const int row = wr * 128 + i * 16 + li;
     a = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
+  };
+  auto read_ix = [&](int ib, int u8, int i, uint2& ix) {
+    const unsigned char* si = ibuf + ib * kBlockI;
+    const int row = wr * 128 + i * 16 + li;
     // the row's 8 index bytes of this step (all four lane quarters), then
     // this lane's 2 bytes picked out by a byte permute
     const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
@@ -262,7 +265,10 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   };
   auto read_frags = [&](int sl, int ib, int u8, u32x4 (&a)[FR], uint2 (&ix)[FR], u32x8 (&bf)[FT]) {
 #pragma unroll
-    for (int i = 0; i < FR; ++i) read_a(sl, ib, u8, i, a[i], ix[i]);
+    for (int i = 0; i < FR; ++i) {
+      read_av(sl, i, a[i]);
+      read_ix(ib, u8, i, ix[i]);
+    }
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
       read_b(sl, j, 0, bf[j]);
@@ -363,20 +369,34 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
       lra = ln ? nxt.a : lra;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Eight chunks, each: the 4 MFMAs of row fragment k, one load, and three
-    // fragment reads of step s+1.  Scheduling barriers keep the chunks in
-    // this order.
+    // Eight chunks, each: fragment reads of step s+1, then the 4 MFMAs of
+    // row fragment k and one load.  The reads come early in the step, the
+    // token fragments and index words (which the next step needs from its
+    // first chunk on) before the row fragments, and the last chunk reads
+    // nothing: when the next step starts its wait for them, they have long
+    // landed.  Scheduling barriers keep the chunks, and the reads ahead of
+    // the MFMAs within a chunk, in this order.
 #pragma unroll
     for (int k = 0; k < FR; ++k) {
+      if (k < FT) {
+        read_b(rsl, k, 0, nb[k]);
+        read_b(rsl, k, 1, nb[k]);
+        read_ix(rib, ru8, 2 * k, nx[2 * k]);
+        read_ix(rib, ru8, 2 * k + 1, nx[2 * k + 1]);
+      } else {
+#pragma unroll
+        for (int i = 3 * (k - FT); i < 3 * (k - FT) + 3; ++i)
+          if (i < FR) read_av(rsl, i, na[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik[k]);
       issue_load_at(lrb, lra, lo[k], k, src, buf);
-      read_a(rsl, rib, ru8, k, na[k], nx[k]);
-      read_b(rsl, k >> 1, k & 1, nb[k >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  static_assert(FR == kPerStep && FT * 2 == FR, "one load and one token-fragment half per chunk");
+  static_assert(FR == kPerStep && FT * 2 == FR && 3 * (FR - FT) >= FR,
+                "one load per chunk; token fragments in the first FT chunks, row fragments after");
 
   // ---- prologue: index block 0 and steps 0 .. kNS-2 of the first tile, then
   // step 0 into set 0

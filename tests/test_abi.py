@@ -144,10 +144,10 @@ def test_decompress_and_misc_errors():
     assert L.nm_decompress(FAKE, FAKE * 2, 4, 64, 2, 4, nm.NM_F16, FAKE, 64, None) == 5
     assert L.nm_check_perm(None, 16, None) == 1
     assert L.nm_check_perm(FAKE, 0, None) == 2
+    assert L.nm_set_variant(8) == 3
     assert L.nm_set_variant(7) == 3
-    assert L.nm_set_variant(6) == 3
     assert L.nm_set_variant(-1) == 3
-    for v in range(6):
+    for v in range(7):
         assert L.nm_set_variant(v) == 0
     assert L.nm_set_variant(0) == 0
 

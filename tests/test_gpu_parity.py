@@ -313,7 +313,7 @@ def test_kernel_families_agree(n, m):
     A = to_dev(act, "bf16")
     outs = {}
     try:
-        for v in (1, 2, 3, 5):
+        for v in (1, 2, 3, 5, 6):
             nm.nm_set_variant(v)
             outs[v] = nm.nm_spmm(vals, idx, A, K, n, m)
         nm.nm_set_variant(4)
@@ -325,7 +325,7 @@ def test_kernel_families_agree(n, m):
     torch.cuda.synchronize()
     # families that add the K steps in order from zero give identical bits
     assert torch.equal(outs[1], outs[2]) and torch.equal(outs[1], outs[3])
-    assert torch.equal(outs[1], outs[5])
+    assert torch.equal(outs[1], outs[5]) and torch.equal(outs[1], outs[6])
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "bf16")
     assert_close(outs[1], yref, error_bound(ref_vals, ref_idx, K, n, m, act, "bf16"))
@@ -363,6 +363,40 @@ def test_lds_tile_walk(R, K, T, out):
     ref_vals, ref_idx = O.prune_pack(w, 2, 4)
     yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt)
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt),
+                 **({"out_half": dt} if out == "half" else {}))
+
+
+# ---------------------------------------------------------------------------
+# 1:4 / 1:8 through LDS: 128 x 64 tiles; index bits in 16-step blocks (a
+# partial last block when K / 64 is not a multiple of 16); ragged rows and
+# tokens; more tiles than two per compute unit (walked)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", [(1, 4), (1, 8)])
+@pytest.mark.parametrize("R,K,T,dt,out", [(4096, 4096, 512, "f16", "f32"), (300, 768, 100, "bf16", "f32"),
+                                          (130, 256, 64, "f16", "half"), (1000, 1280, 1000, "bf16", "half"),
+                                          (2200, 512, 3900, "f16", "f32")])
+def test_lds_nm(R, K, T, dt, out, n, m):
+    log(f"lds 1:4/1:8 {n}:{m} R={R} K={K} T={T} {dt} out={out}")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 52, 0, R + K + T + m)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 52, 1, R + K + T + m)
+    vals, idx = gpu_compress(w, dt, n, m)
+    A = to_dev(act, dt)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    od = tdt if out == "half" else torch.float32
+    try:
+        nm.nm_set_variant(6)
+        y = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od)
+        nm.nm_set_variant(2)
+        y_pipe = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od)
+    finally:
+        nm.nm_set_variant(0)
+    torch.cuda.synchronize()
+    # same widened operands, K steps added in the same order
+    assert torch.equal(y, y_pipe)
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt),
                  **({"out_half": dt} if out == "half" else {}))
 
 
