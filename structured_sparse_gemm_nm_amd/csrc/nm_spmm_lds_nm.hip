@@ -26,8 +26,9 @@
 //                  bytes loaded 4 at a time, rows contiguous (a 48-byte row
 //                  stride puts a fragment's 16 rows on distinct banks).
 //
-// A workgroup (4 waves as 2 x 2, each 64 rows x 32 tokens = 4 x 2 fragments)
-// computes 128 x 64 tiles: a 4096-row layer at 512 tokens then has one tile
+// A workgroup (4 waves stacked along the rows, each 32 rows x 64 tokens = 2 x 4
+// fragments, so every row fragment is widened by one wave only) computes
+// 128 x 64 tiles: a 4096-row layer at 512 tokens then has one tile
 // per compute unit, where 256 x 128 tiles would leave three quarters of the
 // chip idle.  Stages form a 4-deep ring (three K steps of loads in flight),
 // with counted vmcnt waits and one fence-free barrier per step; every step
@@ -47,14 +48,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
-template <int DT>
+// ABID selects the 16-bit half of the index register the instruction reads.
+template <int DT, int ABID>
 __device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
   if constexpr (DT == NM_F16) {
     return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
-                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, 0);
+                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, ABID);
   } else {
     return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
-                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, 0);
+                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, ABID);
   }
 }
 
@@ -143,28 +145,39 @@ struct TileMapNM {
   }
 };
 
-// Widening of one lane's share of a row fragment to the 2:4 operand.
-//   1:4: v = 4 survivors (two per word), ib = their 2-bit positions (8 bits);
-//   1:8: v0 = 2 survivors, bits = their 3-bit positions (6 bits).
-__device__ inline void widen_1of4(uint32_t v0, uint32_t v1, uint32_t ib, u32x4& a, uint32_t& idx16) {
+// Widening of one lane's share of a row fragment to the 2:4 operand (the
+// lane covers four 4-groups of the step).
+//   1:4 values: the 4 survivors (two per word) each with a zero partner.
+//   1:4 index: ib2 holds the lane's index byte of row fragment 0 in bits 0..7
+//     and of fragment 1 in bits 16..23 (four 2-bit positions each); every
+//     position p becomes the 4-bit field p | p << 2 = 5p (both slots of its
+//     4-group), so fragment 0's 16 index bits come out in the low half and
+//     fragment 1's in the high half of one register.
+//   1:8: v = the lane's 2 survivors, bits = their 3-bit positions in their
+//     8-groups; bit 2 (bit 5) tells which 4-group of the pair holds survivor
+//     0 (1); the other 4-group gets zeros at position 0.
+__device__ inline void widen_1of4_values(uint32_t v0, uint32_t v1, u32x4& a) {
   a[0] = v0 & 0xFFFFu;
   a[1] = v0 >> 16;
   a[2] = v1 & 0xFFFFu;
   a[3] = v1 >> 16;
-  const uint32_t t = (ib & 0x3u) | ((ib & 0xCu) << 2) | ((ib & 0x30u) << 4) | ((ib & 0xC0u) << 6);
-  idx16 = t | (t << 2);
+}
+
+__device__ inline uint32_t widen_1of4_index2(uint32_t ib2) {
+  uint32_t x = (ib2 | (ib2 << 4)) & 0x0F0F0F0Fu;  // fields 0,1 | 2,3 into separate bytes
+  x = (x | (x << 2)) & 0x33333333u;               // one field per nibble
+  return x * 5u;                                  // p -> p | p << 2 (no carries: p <= 3)
 }
 
 __device__ inline void widen_1of8(uint32_t v, uint32_t bits, u32x4& a, uint32_t& idx16) {
-  const uint32_t v0 = v & 0xFFFFu, v1 = v >> 16;
-  const uint32_t p0 = bits & 7u, p1 = (bits >> 3) & 7u;
-  const bool h0 = p0 >= 4, h1 = p1 >= 4;
-  a[0] = h0 ? 0u : v0;
-  a[1] = h0 ? v0 : 0u;
-  a[2] = h1 ? 0u : v1;
-  a[3] = h1 ? v1 : 0u;
-  const uint32_t f0 = (p0 & 3u) * 5u, f1 = (p1 & 3u) * 5u;
-  idx16 = (h0 ? (f0 << 4) : f0) | (h1 ? (f1 << 12) : (f1 << 8));
+  const uint64_t a01 = uint64_t(v & 0xFFFFu) << ((bits << 3) & 32u);
+  const uint64_t a23 = uint64_t(v >> 16) << (bits & 32u);
+  a[0] = uint32_t(a01);
+  a[1] = uint32_t(a01 >> 32);
+  a[2] = uint32_t(a23);
+  a[3] = uint32_t(a23 >> 32);
+  const uint32_t f0 = (bits & 3u) * 5u, f1 = ((bits >> 3) & 3u) * 5u;
+  idx16 = (f0 << (bits & 4u)) | (f1 << (((bits >> 3) & 4u) + 8u));
 }
 
 template <int P, int DT, int OUT>
@@ -172,7 +185,8 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K, int irow_bytes,
     const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y, int64_t ldy,
     TileMapNM tm) {
-  constexpr int FR = 4, FT = 2;
+  constexpr int FR = 2, FT = 4;
+  static_assert(FR == 2, "1:4 index registers hold two row fragments");
   constexpr int VB = NmPat<P>::VB, IBLK = NmPat<P>::IBLK;
   constexpr int SA = kBR * VB;      // packed values, one step
   constexpr int SI = kBR * IBLK;    // index bits, one block
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   // uniform: LDS destinations of the direct loads (M0) are then scalar sums
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
-  const int wr = wave >> 1, wt = wave & 1;
+  const int wr = wave;  // rows wr*32 .. wr*32+31 of the tile, all 64 tokens
   const int nsteps = K >> 6;  // a multiple of 4 on this path
   const int S = K / (P == 1 ? 4 : 8);
   const int iwords = irow_bytes >> 2;  // index words per row
@@ -267,10 +281,10 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     }
   };
 
-  // Fragment reads.  Row fragment i of this wave: rows wr*64 + i*16 + li.
+  // Fragment reads.  Row fragment i of this wave: rows wr*32 + i*16 + li.
   auto read_b = [&](int sl, int j, int h, u32x8& bf) {
     const unsigned char* sb = bbuf + sl * kStageB;
-    const int tok = wt * (kBT / 2) + j * 16 + li;
+    const int tok = j * 16 + li;
     const u32x4 v = *reinterpret_cast<const u32x4*>(sb + (tok * 8 + ((lq + 4 * h) ^ (tok & 7))) * 16);
     bf[4 * h + 0] = v[0];
     bf[4 * h + 1] = v[1];
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   };
   auto read_v = [&](int sl, int i, uint32_t (&v)[2]) {
     const unsigned char* sa = abuf + sl * SA;
-    const int row = wr * 64 + i * 16 + li;
+    const int row = wr * 32 + i * 16 + li;
     if constexpr (P == 1) {
       // (a uint64_t load: read through the uint2 struct, the compiler cannot
       // tell this from the slots the direct loads are filling and waits for them)
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   // 1:4 one 16-byte chunk (4 bytes per step), 1:8 three words (24 bits per step)
   auto read_ix = [&](int ib, int g, int i, uint32_t (&w)[4]) {
     const unsigned char* si = ibuf + ib * SI;
-    const int row = wr * 64 + i * 16 + li;
+    const int row = wr * 32 + i * 16 + li;
     if constexpr (P == 1) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(si + row * 64 + (g ^ ((row >> 2) & 3)) * 16);
       w[0] = v[0];
@@ -308,17 +322,30 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       w[3] = 0u;
     }
   };
-  // widen step t (0..3) of the current four-step group
-  auto widen = [&](int t, const uint32_t (&v)[2], const uint32_t (&w)[4], u32x4& a, uint32_t& ik) {
+  // Widen step t (0..3, a constant at every call) of the current four-step
+  // index group into row operands a[] and index registers k[] (1:4: one
+  // register for both fragments, read through the MFMA's abid; 1:8: one each).
+  // byte selector: byte lq of fragment 0's word into bits 0..7, of fragment
+  // 1's into bits 16..23, zeros elsewhere
+  const uint32_t sel14 = uint32_t(lq) | (0x0Cu << 8) | (uint32_t(4 + lq) << 16) | (0x0Cu << 24);
+  const uint32_t off6 = uint32_t(6 * lq);  // the lane's 6 bits in a 1:8 step's 24
+  auto widen = [&](int t, const uint32_t (&v)[FR][2], const uint32_t (&w)[FR][4], u32x4 (&a)[FR],
+                   uint32_t (&k)[FR]) {
     if constexpr (P == 1) {
-      const uint32_t ib = (w[t] >> (8 * lq)) & 0xFFu;
-      widen_1of4(v[0], v[1], ib, a, ik);
+#pragma unroll
+      for (int i = 0; i < FR; ++i) widen_1of4_values(v[i][0], v[i][1], a[i]);
+      k[0] = widen_1of4_index2(__builtin_amdgcn_perm(w[1][t], w[0][t], sel14));
+      k[1] = k[0];
     } else {
-      const int o = 24 * t + 6 * lq;  // bit offset in the group's 96 bits
-      const uint32_t lo = o < 32 ? w[0] : (o < 64 ? w[1] : w[2]);
-      const uint32_t hi = o < 32 ? w[1] : (o < 64 ? w[2] : 0u);
-      const uint32_t bits = __builtin_amdgcn_alignbit(hi, lo, uint32_t(o & 31)) & 63u;
-      widen_1of8(v[0], bits, a, ik);
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        // step t's 24 bits start at bit 24t of the group's three words
+        const uint32_t x = t == 0   ? w[i][0]
+                           : t == 1 ? __builtin_amdgcn_alignbit(w[i][1], w[i][0], 24u)
+                           : t == 2 ? __builtin_amdgcn_alignbit(w[i][2], w[i][1], 16u)
+                                    : w[i][2] >> 8;
+        widen_1of8(v[i][0], (x >> off6) & 63u, a[i], k[i]);
+      }
     }
   };
 
@@ -359,12 +386,12 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < FR; ++i)
-#pragma unroll
-      for (int j = 0; j < FT; ++j) acc[i][j] = smfmac<DT>(ca[i], cb[j], acc[i][j], ck[i]);
+    for (int j = 0; j < FT; ++j) {
+      acc[0][j] = smfmac<DT, 0>(ca[0], cb[j], acc[0][j], ck[0]);
+      acc[1][j] = smfmac<DT, P == 1 ? 1 : 0>(ca[1], cb[j], acc[1][j], ck[1]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < FR; ++i) widen(RS, rv[i], rw[i], na[i], nk[i]);
+    widen(RS, rv, rw, na, nk);
     // keeps the widening here, behind the MFMAs it overlaps, rather than in
     // front of the next step's MFMAs, which need its results
     __builtin_amdgcn_sched_barrier(0);
@@ -398,8 +425,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       read_v(0, i, rv[i]);
       read_ix(0, 0, i, rw[i]);
     }
-#pragma unroll
-    for (int i = 0; i < FR; ++i) widen(0, rv[i], rw[i], a0[i], k0[i]);
+    widen(0, rv, rw, a0, k0);
 
     for (int s = 0; s < nsteps; s += 4) {
       body(integral_constant<int, 0>{}, s, a0, k0, b0, a1, k1, b1);
@@ -421,10 +447,10 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
-      const int r = R0 + wr * 64 + i * 16 + lq * 4;
+      const int r = R0 + wr * 32 + i * 16 + lq * 4;
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
-        const int t = T0 + wt * (kBT / 2) + j * 16 + li;
+        const int t = T0 + j * 16 + li;
         if (t >= T || r >= R) continue;
         const f32x4 v = acc[i][j];
         if constexpr (OUT == NM_F32) {
