@@ -524,7 +524,13 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
   TileMap tm;
   tm.tilesR = tilesR;
   tm.tilesT = tilesT;
+  // Row tiles sharing activation columns are grouped four at a time (per
+  // XCD run, four row tiles x eight token tiles: the fewest unique bytes).
+  // When the packed values fit an XCD's L2 (4 MB) they stay there across
+  // rounds anyway, so all row tiles of a token tile are grouped and each
+  // token tile's activations are fetched about once.
   tm.group_r = tilesR < 4 ? tilesR : 4;
+  if (a.R * a.K <= (int64_t(4) << 20)) tm.group_r = tilesR;
   tm.ntiles = int(ntiles);
   tm.grid = int(walk && ntiles > cus ? cus : ntiles);
   auto kern = spmm_lds_kernel<DT, OUT>;
