@@ -216,9 +216,9 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   }
 
   // A tile's load sources: buffer resources at the tile's corner and per-lane
-  // 32-bit byte offsets (rows / tokens past the edge reread the last one; the
-  // index resource ends with the array, so block loads running past the last
-  // row read zeros).
+  // 32-bit byte offsets (rows / tokens past the edge reread the last one).
+  // Every load is kept inside its row by construction; the index resource
+  // also ends with the array.
   __amdgpu_buffer_rsrc_t rb, ra, ri;
   uint32_t boff[2], aoff, ioff[NmPat<P>::IL];
   auto make_src = [&](int R0, int T0) {
