@@ -278,8 +278,12 @@ def test_spmm_few_tokens(R, K, T, permuted, n, m):
 # permuted 2:4 prefill path (X tile gathered through perm from LDS)
 # ---------------------------------------------------------------------------
 
+# (128, 768, 11000) and (128, 8192, 2100): more row blocks than gather
+# workgroups, so workgroups walk blocks through both LDS buffers;
+# (130, 8448, 70): rows longer than the walking gather takes
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("R,K,T", [(300, 768, 100), (512, 128, 64), (256, 640, 130), (3072, 768, 197)])
+@pytest.mark.parametrize("R,K,T", [(300, 768, 100), (512, 128, 64), (256, 640, 130), (3072, 768, 197),
+                                   (128, 768, 11000), (128, 8192, 2100), (130, 8448, 70)])
 def test_perm_prefill(R, K, T, dt):
     log(f"perm prefill R={R} K={K} T={T} {dt}")
     w = nm_inputs.normal_half((R, K), 0.02, dt, 48, 0, R + K + T)
