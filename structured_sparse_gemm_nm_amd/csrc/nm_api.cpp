@@ -5,7 +5,11 @@
 #include <atomic>
 #include <cstdio>
 #include <cstdarg>
+#include <map>
+#include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "nm_internal.h"
@@ -131,6 +135,49 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
 }
 
 }  // namespace
+
+namespace nm {
+namespace {
+
+std::mutex g_dev_mu;
+
+int cached_attr(std::map<int, int>& cache, hipDeviceAttribute_t attr, int fallback) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fallback;
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+  cache[dev] = v;
+  return v;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static std::map<int, int> cache;
+  return cached_attr(cache, hipDeviceAttributeMultiprocessorCount, 256);
+}
+
+int device_max_lds() {
+  static std::map<int, int> cache;
+  return cached_attr(cache, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
+}
+
+hipError_t ensure_lds_limit(const void* kern, int bytes) {
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  if (done.count({dev, kern})) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({dev, kern});
+  return e;
+}
+
+}  // namespace nm
 
 extern "C" {
 

@@ -70,6 +70,14 @@ hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s);
 bool spmm_wide_applies(const SpmmArgs& a);
 hipError_t launch_spmm_wide(const SpmmArgs& a, hipStream_t s);
 
+// Device properties and per-kernel launch set-up, kept per device and safe to
+// call from several host threads (nm_api.cpp).
+int device_cu_count();                 // CUs of the current device (256 if the query fails)
+int device_max_lds();                  // its largest workgroup LDS allocation (0 if the query fails)
+// Allow kern up to `bytes` of dynamic LDS on the current device (done once per
+// device and kernel).
+hipError_t ensure_lds_limit(const void* kern, int bytes);
+
 inline int index_bits(int m) {
   int b = 0;
   while ((1 << b) < m) ++b;

@@ -236,12 +236,7 @@ hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s) {
   if (rows_blk > 64) rows_blk = 64;
   const int64_t blocks = (a.T + rows_blk - 1) / rows_blk;
   if (K <= kDbMaxK && blocks <= 0x7FFFFFFF && int64_t(a.T) * a.ldx * 2 <= int64_t(0xFFFFFFFFu)) {
-    static int cus = -1;
-    if (cus < 0) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-      cus = v;
-    }
+    const int cus = device_cu_count();
     // four workgroups per CU (32 KB of LDS each; measured: 8.9 us for the
     // 3072 x 768 x 12608 layer's 38.7 MB, against 9.2 with two and 10.0 for
     // one workgroup per block)
@@ -250,13 +245,8 @@ hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s) {
                        a.ldx, a.perm, int(a.T), K, rows_blk, int(blocks), static_cast<uint16_t*>(xp));
   } else {
     const size_t lds = size_t(rows_blk) * size_t(K) * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_cols_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxK * 2));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    if ((e = ensure_lds_limit(reinterpret_cast<const void*>(permute_cols_kernel), int(kMaxK * 2))) != hipSuccess)
+      return e;
     hipLaunchKernelGGL(permute_cols_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, s, a.act, a.ldx,
                        a.perm, int(a.T), K, rows_blk, static_cast<uint16_t*>(xp));
   }

@@ -375,13 +375,7 @@ hipError_t launch_cfg(const SpmmArgs& a, hipStream_t s) {
   const int group_r = tilesR < 4 ? tilesR : 4;
   const size_t lds = 2 * C::BUF_BYTES;
   auto kern = spmm_kernel<P, DT, OUT, PERM, BR, BT, WR, WT>;
-  static bool attr_set = false;  // per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), int(lds)); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(256), lds, s, a.values, a.idx, int(a.R),
                      int(a.K), a.idx_row_words, a.act, int(a.T), a.ldx, a.perm, a.Y, a.ldy, tilesR,
                      tilesT, group_r);

@@ -536,13 +536,7 @@ template <int DT, int OUT, bool PERM, int SPW, int NBLK>
 hipError_t launch_dec_stream_n(const SpmmArgs& a, hipStream_t s, int grid, int rows_per_wg) {
   constexpr int lds = 2 * kWaves * (16 * SPW * 4 * 16 + 16 * SPW * 8);
   auto kern = spmm_decode_stream_kernel<DT, OUT, PERM, SPW, NBLK>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kWaves * 64), lds, s, a.values, a.idx, int(a.R),
                      int(a.K), a.act, int(a.T), a.ldx, a.perm, a.Y, a.ldy, rows_per_wg);
   return hipGetLastError();
@@ -552,14 +546,7 @@ hipError_t launch_dec_stream_n(const SpmmArgs& a, hipStream_t s, int grid, int r
 // 16; more rows than that take more workgroups.
 template <int DT, int OUT, bool PERM, int SPW>
 hipError_t launch_dec_stream(const SpmmArgs& a, hipStream_t s) {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cus = v;
-  }
+  const int cus = device_cu_count();
   const int64_t blocks16 = (a.R + 15) / 16;
   int64_t grid = blocks16 < cus ? blocks16 : cus;
   if ((blocks16 + grid - 1) / grid > 8) grid = (blocks16 + 7) / 8;

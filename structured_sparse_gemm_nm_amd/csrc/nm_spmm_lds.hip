@@ -506,14 +506,7 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
   const int tilesT = int((a.T + kBT - 1) / kBT);
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cus = v;
-  }
+  const int cus = device_cu_count();
   // One workgroup per CU walks the tiles (each CU holds one: 160 KB of LDS).
   // Running the ring on into the next tile needs the next tile's index block
   // issued at least four steps before its first step is read, i.e. a tile's
@@ -534,13 +527,7 @@ hipError_t launch_lds(const SpmmArgs& a, hipStream_t s) {
   tm.ntiles = int(ntiles);
   tm.grid = int(walk && ntiles > cus ? cus : ntiles);
   auto kern = spmm_lds_kernel<DT, OUT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(tm.grid)), dim3(256), kLds, s, a.values, a.idx, int(a.R),
                      int(a.K), a.act, int(a.T), a.ldx, a.Y, a.ldy, tm);
   return hipGetLastError();
@@ -556,15 +543,7 @@ bool spmm_lds_applies(const SpmmArgs& a) {
   const int64_t lim = int64_t(0xFFFFFFFFu);
   if (int64_t(kBT) * a.ldx * 2 > lim || int64_t(kBR) * a.K > lim) return false;
   // needs a workgroup LDS allocation of kLds bytes
-  static int max_lds = -1;
-  if (max_lds < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    max_lds = v;
-  }
-  return max_lds >= kLds;
+  return device_max_lds() >= kLds;
 }
 
 hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s) {

@@ -483,27 +483,14 @@ hipError_t launch_lds_nm(const SpmmArgs& a, hipStream_t s) {
   const int tilesT = int((a.T + kBT - 1) / kBT);
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cus = v;
-  }
+  const int cus = device_cu_count();
   // two workgroups fit a CU (LDS and registers); more tiles than that are walked
   TileMapNM tm;
   tm.tilesT = tilesT;
   tm.ntiles = int(ntiles);
   tm.grid = int(ntiles > 2 * cus ? 2 * cus : ntiles);
   auto kern = spmm_lds_nm_kernel<P, DT, OUT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<P>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds_bytes<P>()); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(tm.grid)), dim3(256), lds_bytes<P>(), s, a.values, a.idx, int(a.R),
                      int(a.K), int(a.idx_row_words * 4), a.act, int(a.T), a.ldx, a.Y, a.ldy, tm);
   return hipGetLastError();

@@ -237,13 +237,7 @@ hipError_t launch_perm(const SpmmArgs& a, hipStream_t s) {
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   auto kern = spmm_perm_kernel<DT, OUT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(256), kLds, s, a.values, a.idx, int(a.R),
                      int(a.K), a.act, int(a.T), a.ldx, a.perm, a.Y, a.ldy, tilesR, tilesT);
   return hipGetLastError();
@@ -255,15 +249,7 @@ bool spmm_perm_lds_applies(const SpmmArgs& a) {
   if (!(a.perm != nullptr && a.n == 2 && a.m == 4 && a.K % 128 == 0 && a.K <= kKMax &&
         a.T >= 64 && a.R >= 256))
     return false;
-  static int max_lds = -1;
-  if (max_lds < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    max_lds = v;
-  }
-  return max_lds >= kLds;
+  return device_max_lds() >= kLds;
 }
 
 hipError_t launch_spmm_perm_lds(const SpmmArgs& a, hipStream_t s) {

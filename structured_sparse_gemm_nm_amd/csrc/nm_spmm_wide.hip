@@ -350,13 +350,7 @@ hipError_t launch_wide(const SpmmArgs& a, hipStream_t s) {
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int group_r = tilesR < 4 ? tilesR : 4;
   auto kern = spmm_wide_kernel<DT, OUT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(256), kLds, s, a.values, a.idx, int(a.R),
                      int(a.K), a.act, int(a.T), a.ldx, a.Y, a.ldy, tilesR, tilesT, group_r);
   return hipGetLastError();
@@ -371,15 +365,7 @@ bool spmm_wide_applies(const SpmmArgs& a) {
   // per-lane byte offsets within a tile are 32-bit
   const int64_t lim = int64_t(0xFFFFFFFFu);
   if (int64_t(kBT) * a.ldx * 2 > lim || int64_t(kBR) * a.K > lim) return false;
-  static int max_lds = -1;
-  if (max_lds < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      v = 0;
-    max_lds = v;
-  }
-  return max_lds >= kLds;
+  return device_max_lds() >= kLds;
 }
 
 hipError_t launch_spmm_wide(const SpmmArgs& a, hipStream_t s) {
