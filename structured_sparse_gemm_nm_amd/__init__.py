@@ -178,6 +178,13 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
         torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty((T, R), dtype=_torch_dtype(od), device=act.device)
+    else:
+        _require_cuda(out)
+        _row_major(out, "out")
+        if out.dtype != _torch_dtype(od):
+            raise TypeError(f"out is {out.dtype}, the output dtype is {_torch_dtype(od)}")
+        if out.shape[0] < T or out.shape[1] < R or out.device != act.device:
+            raise ValueError(f"out must be a [{T}, {R}] tensor on {act.device}")
     stream = _stream_ptr(act.device)
     if perm is None:
         st = lib().nm_spmm(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,

@@ -303,6 +303,22 @@ def test_perm_prefill(R, K, T, dt):
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
 
 
+def test_out_tensor_checked():
+    R, K, T = 64, 128, 16
+    w = nm_inputs.normal_half((R, K), 0.02, "f16", 53, 0, 1)
+    act = nm_inputs.normal_half((T, K), 1.0, "f16", 53, 1, 1)
+    vals, idx = gpu_compress(w, "f16", 2, 4)
+    A = to_dev(act, "f16")
+    with pytest.raises(TypeError):  # fp32 output into an fp16 tensor
+        nm.nm_spmm(vals, idx, A, K, 2, 4, out=torch.empty((T, R), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):  # too few rows
+        nm.nm_spmm(vals, idx, A, K, 2, 4, out=torch.empty((T - 1, R), dtype=torch.float32, device="cuda"))
+    y = torch.full((T, R), 7.0, dtype=torch.float32, device="cuda")
+    assert nm.nm_spmm(vals, idx, A, K, 2, 4, out=y) is y
+    torch.cuda.synchronize()
+    assert torch.equal(y, nm.nm_spmm(vals, idx, A, K, 2, 4))
+
+
 # ---------------------------------------------------------------------------
 # every kernel family on the same inputs
 # ---------------------------------------------------------------------------
