@@ -7,9 +7,10 @@
 // bytes at slot base + l of LDS, so the LDS layout is chosen by which global
 // address each lane reads.  The XOR swizzles below were picked by measuring
 // the LDS bank-conflict counter for the exact fragment reads of this kernel;
-// each layout reads without conflicts.  A lane reads the 8 index bytes of its
-// row's step (8-byte reads cost half of what 2-byte reads do) and keeps its
-// own 2 bytes:
+// each layout reads without conflicts.  A lane reads just its own 2 index
+// bytes of its row's step: they land in the low half of a register, which is
+// the index operand the MFMA takes as it is (reading the row's 8 bytes and
+// picking 2 with a byte permute cost ~8% more time: LDS traffic and VALU):
 //
 //   packed values  one K step per stage; slot (row, quarter q) at
 //                  row*4 + (q ^ ((row >> 1) & 3)): a load covers 16 rows x 64 B;
@@ -235,24 +236,17 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // Fragment reads of a step from LDS into registers (ring slot sl, index
   // buffer ib, step u8 within its index block): row fragment i (packed values
   // and index bits) and one half (h: K 8q..8q+7 or 32+8q..) of token fragment j.
-  // byte selector: bytes 2*lq, 2*lq+1 of {w.y, w.x} into bits 0..15, zeros above
-  const uint32_t ix_sel = uint32_t(2 * lq) | (uint32_t(2 * lq + 1) << 8) | (0x0C0Cu << 16);
   auto read_av = [&](int sl, int i, u32x4& a) {
     const unsigned char* sa = abuf + sl * kStageA;
     const int row = wr * 128 + i * 16 + li;
     a = *reinterpret_cast<const u32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
   };
-  auto read_ix = [&](int ib, int u8, int i, uint2& ix) {
+  auto read_ix = [&](int ib, int u8, int i, uint32_t& ix) {
     const unsigned char* si = ibuf + ib * kBlockI;
     const int row = wr * 128 + i * 16 + li;
-    // the row's 8 index bytes of this step (all four lane quarters), then
-    // this lane's 2 bytes picked out by a byte permute
+    // this lane's 2 index bytes of the step (bytes 2lq, 2lq+1 of the row's 8)
     const int ch = (u8 >> 1) ^ ((row >> 2) & 3);
-    // (a uint64_t load: read through the uint2 struct, the compiler cannot
-    // tell this from the slots the direct loads are filling and waits for them)
-    const uint64_t w = *reinterpret_cast<const uint64_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8);
-    ix.x = uint32_t(w);
-    ix.y = uint32_t(w >> 32);
+    ix = *reinterpret_cast<const uint16_t*>(si + row * 64 + ch * 16 + (u8 & 1) * 8 + lq * 2);
   };
   auto read_b = [&](int sl, int j, int h, u32x8& bf) {
     const unsigned char* sb = bbuf + sl * kStageB;
@@ -263,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     bf[4 * h + 2] = v[2];
     bf[4 * h + 3] = v[3];
   };
-  auto read_frags = [&](int sl, int ib, int u8, u32x4 (&a)[FR], uint2 (&ix)[FR], u32x8 (&bf)[FT]) {
+  auto read_frags = [&](int sl, int ib, int u8, u32x4 (&a)[FR], uint32_t (&ix)[FR], u32x8 (&bf)[FT]) {
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
       read_av(sl, i, a[i]);
@@ -281,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // MFMAs of step s run.  The loop is unrolled by two so the sets alternate
   // without copies.
   u32x4 a0[FR], a1[FR];
-  uint2 x0[FR], x1[FR];
+  uint32_t x0[FR], x1[FR];
   u32x8 b0[FT], b1[FT];
 
   // The workgroup walks tiles blockIdx.x, + grid, ...  The ring runs on
@@ -318,8 +312,8 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   //       position that is a multiple of kNS: ring slots and the index bytes'
   //       place in their block are constants, and ibc / ibn are the index
   //       buffers of this step's block and of the next.
-  auto body = [&](auto mode_c, int s, int ibc, int ibn, u32x4 (&ca)[FR], uint2 (&cx)[FR], u32x8 (&cb)[FT],
-                  u32x4 (&na)[FR], uint2 (&nx)[FR], u32x8 (&nb)[FT]) {
+  auto body = [&](auto mode_c, int s, int ibc, int ibn, u32x4 (&ca)[FR], uint32_t (&cx)[FR],
+                  u32x8 (&cb)[FT], u32x4 (&na)[FR], uint32_t (&nx)[FR], u32x8 (&nb)[FT]) {
     constexpr int MODE = decltype(mode_c)::value;
     constexpr bool IN = MODE != -2;
     constexpr bool FAST = MODE >= 0;
@@ -347,12 +341,10 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     const bool r_in = IN || s + 1 < nsteps;
     const int rib = FAST ? (MODE == 7 ? ibn : ibc) : (qb + (r_in ? ((s + 1) >> 3) : nblocks)) & 1;
     const int ru8 = FAST ? ((MODE + 1) & 7) : r_in ? ((s + 1) & 7) : 0;
-    // The step's index operands and load offsets are worked out before its
-    // first MFMA: a VALU result that an MFMA (or a load) waits for inside
-    // the chunks would stall the matrix pipe every chunk.
-    uint32_t ik[FR], lo[kPerStep];
-#pragma unroll
-    for (int k = 0; k < FR; ++k) ik[k] = __builtin_amdgcn_perm(cx[k].y, cx[k].x, ix_sel);
+    // The step's load offsets are worked out before its first MFMA: a VALU
+    // result that an MFMA (or a load) waits for inside the chunks would stall
+    // the matrix pipe every chunk.
+    uint32_t lo[kPerStep];
     __amdgpu_buffer_rsrc_t lrb = cur.b, lra = cur.a;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -390,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], ik[k]);
+      for (int j = 0; j < FT; ++j) acc[k][j] = smfmac<DT>(ca[k], cb[j], acc[k][j], cx[k]);
       issue_load_at(lrb, lra, lo[k], k, src, buf);
       __builtin_amdgcn_sched_barrier(0);
     }
