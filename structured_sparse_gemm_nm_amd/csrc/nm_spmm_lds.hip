@@ -295,6 +295,14 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     nxt = cur;
   }
   int g = 0;    // ring position of the tile's step 0
+  // The vector-memory counter retires loads and stores in issue order.  A
+  // tile's epilogue issues its stores after the loads of the next tile's
+  // steps 1 .. kNS-1, so the waits for those steps may leave the stores
+  // outstanding: they drain under three steps of MFMAs instead of holding up
+  // the first.  Only after a full tile, whose waves each issued at least
+  // kStores stores (fewer would let such a wait pass early).
+  constexpr int kStores = FR * FT;
+  bool stores_behind = false;
   int qb = 0;   // index-buffer parity of the tile's block 0
 
   // One step: make step s+1 visible, refill the slot step s used, read step
@@ -318,8 +326,12 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     constexpr bool IN = MODE != -2;
     constexpr bool FAST = MODE >= 0;
     // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
-    // index block issued in between only makes the wait stricter)
-    wait_vmcnt<2 * kPerStep>();
+    // index block issued in between only makes the wait stricter), and, in a
+    // tile's first kNS-1 steps, the previous tile's stores issued after them
+    if (s < kNS - 1 && stores_behind)
+      wait_vmcnt<2 * kPerStep + kStores>();
+    else
+      wait_vmcnt<2 * kPerStep>();
     wait_lgkm0();        // this wave's reads of step s are done
     barrier_no_fence();  // publishes step s+1; every wave is done reading step s
     // at a block's first step, the block after it: this tile's next, or the
@@ -441,6 +453,7 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
 
     // ---- epilogue
     const bool vec_ok = (ldy & 3) == 0;
+    stores_behind = R0 + kBR <= R && T0 + kBT <= T;
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
       const int r = R0 + wr * 128 + i * 16 + lq * 4;
@@ -470,10 +483,9 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
         }
       }
     }
-    // Stores share the load counter, so while they are pending a counted
-    // wait only waits longer: the next tile's loads, already in flight, stay
-    // in flight across the epilogue.  The last tile waits for everything, so
-    // no direct load is still writing LDS when the workgroup ends.
+    // The next tile's loads, already in flight, stay in flight across the
+    // epilogue.  The last tile waits for everything, so no direct load is
+    // still writing LDS when the workgroup ends.
     if (!has_next) {
       wait_vmcnt<0>();
       break;
