@@ -395,7 +395,7 @@ def test_lds_tile_walk(R, K, T, out):
 @pytest.mark.parametrize("n,m", [(1, 4), (1, 8)])
 @pytest.mark.parametrize("R,K,T,dt,out", [(4096, 4096, 512, "f16", "f32"), (300, 768, 100, "bf16", "f32"),
                                           (130, 256, 64, "f16", "half"), (1000, 1280, 1000, "bf16", "half"),
-                                          (2200, 512, 3900, "f16", "f32")])
+                                          (2432, 512, 1000, "bf16", "f32"), (2200, 512, 3900, "f16", "f32")])
 def test_lds_nm(R, K, T, dt, out, n, m):
     log(f"lds 1:4/1:8 {n}:{m} R={R} K={K} T={T} {dt} out={out}")
     w = nm_inputs.normal_half((R, K), 0.02, dt, 52, 0, R + K + T + m)
