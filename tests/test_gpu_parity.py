@@ -422,8 +422,9 @@ def test_lds_nm(R, K, T, dt, out, n, m):
 
 # ---------------------------------------------------------------------------
 # few-token kernel for tall weights: one workgroup per CU owns 1..8 blocks of
-# 16 rows (the even split, last block partial); K slices past the last step
-# in some waves; the index map read inside the kernel
+# 16 rows (the even split, last block partial; with 256 CUs the last three
+# shapes have three, as the 11008-row decode layer does); K slices past the
+# last step in some waves; the index map read inside the kernel
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("R,K,T,dt,permuted", [(4096, 4096, 1, "bf16", False),
@@ -431,7 +432,8 @@ def test_lds_nm(R, K, T, dt, out, n, m):
                                                (20000, 4096, 5, "f16", False),
                                                (33000, 2176, 16, "bf16", False),
                                                (5000, 2176, 7, "f16", False),
-                                               (6000, 4096, 9, "f16", True)])
+                                               (6000, 4096, 9, "f16", True), (10000, 4096, 3, "bf16", False),
+                                               (11008, 2176, 16, "f16", False), (11008, 4096, 2, "bf16", True)])
 def test_decode_stream(R, K, T, dt, permuted):
     log(f"decode stream R={R} K={K} T={T} {dt} perm={permuted}")
     w = nm_inputs.normal_half((R, K), 0.02, dt, 51, 0, R + K + T)
