@@ -176,8 +176,13 @@ __device__ inline void widen_1of8(uint32_t v, uint32_t bits, u32x4& a, uint32_t&
   a[1] = uint32_t(a01 >> 32);
   a[2] = uint32_t(a23);
   a[3] = uint32_t(a23 >> 32);
-  const uint32_t f0 = (bits & 3u) * 5u, f1 = ((bits >> 3) & 3u) * 5u;
-  idx16 = (f0 << (bits & 4u)) | (f1 << (((bits >> 3) & 4u) + 8u));
+  // Each survivor's index byte depends only on its 3-bit position p:
+  // 5 (p & 3) in the nibble of its 4-group, 5 (p & 3) << 4 (p >> 2).  The
+  // eight possible bytes form a table that one byte permute reads at p0 and
+  // p1 (selector byte 0x0C gives zero).
+  constexpr uint32_t kTabLo = 0x0F0A0500u, kTabHi = 0xF0A05000u;
+  const uint32_t sel = ((bits >> 3) << 8) | (bits & 7u) | 0x0C0C0000u;
+  idx16 = __builtin_amdgcn_perm(kTabHi, kTabLo, sel);
 }
 
 template <int P, int DT, int OUT>
