@@ -1,0 +1,65 @@
+"""Host-side parts of the benchmark script (no GPU): the one-GPU refusal, the
+oracle baseline leg and the lookup of committed traffic counters."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import nm_inputs  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line for a configuration that was not measured
+
+
+def test_cpu_baseline_fields():
+    wl = nm_inputs.WORKLOADS[1]
+    out = bench.cpu_baseline(wl, 2, 4, wl.Ts[0], reps=1)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert out["prune_pack_s"] > 0 and out["decompress_gemm_s"] > 0
+    assert f"{wl.R}x{wl.K}x{wl.Ts[0]}" in out["sample"]
+
+
+def test_source_hash_is_stable_and_content_based(tmp_path):
+    a, b = tmp_path / "a.hip", tmp_path / "b.hip"
+    a.write_text("x")
+    b.write_text("y")
+    h1 = bench.source_hash([str(a), str(b)])
+    assert h1 == bench.source_hash([str(a), str(b)]) and len(h1) == 16
+    b.write_text("z")
+    assert bench.source_hash([str(a), str(b)]) != h1
+
+
+def test_traffic_lookup_requires_matching_source(monkeypatch, tmp_path):
+    (tmp_path / "profiles").mkdir()
+    entry = {"source_hash": "0123456789abcdef", "hbm_bytes_per_launch": 3000,
+             "read_bytes": 1000, "write_bytes": 2000}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps({"k": entry}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_from_profile("k", "0123456789abcdef") == 3000
+    assert bench.traffic_from_profile("k", "ffffffffffffffff") is None  # stale counters
+    assert bench.traffic_from_profile("other", "0123456789abcdef") is None
+
+
+def test_committed_traffic_entries_are_well_formed():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        d = json.load(f)
+    assert d, "no traffic entries committed"
+    for key, e in d.items():
+        assert len(e["source_hash"]) == 16
+        assert e["read_bytes"] > 0 and e["write_bytes"] > 0, key
+        # each part is rounded to whole bytes on its own
+        assert abs(e["hbm_bytes_per_launch"] - e["read_bytes"] - e["write_bytes"]) <= 1, key
+        assert os.path.exists(os.path.join(ROOT, e["profile"])), key
