@@ -40,7 +40,8 @@ Readings taken where the pages are silent:
 Parity pins: every function here is pinned by tests under tests/ (worked
 row, 36-bit group cost, brute-force top-N, exhaustive ties, worked K = 8
 product, identity and integer GEMMs, dense N = M case, explicit-matrix
-permutation route).  No function is "parity unpinned".
+permutation route; for int8: the 20-bit group cost, brute-force top-N by |w|
+with -128 and ties, big-integer products).  No function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -222,6 +223,75 @@ def spmm_rows_ref(values, idx, K: int, n: int, m: int, act_bits, dtype: str, row
             xt = xt[p]
         out[i] = float(np.dot(wd[where[int(r)]], xt))
     return out
+
+
+# --------------------------------------------------------------------------
+# 8-bit integer weights and activations
+# --------------------------------------------------------------------------
+# The 2:4 pattern is also taken for INT8 weights (COE-592 lecture 04-2, "M:N
+# sparsity on NVIDIA tensor cores", opening section).  The index stays 2 bits
+# per stored value, so a group costs 2 x 8 value bits + 2 x 2 index bits = 20
+# of the dense 32 (25% index overhead, a 37.5% saving; same page, section
+# "Where this sits among the three case studies"), and the reduction length
+# must be a multiple of 32 for INT8 (same section).  Readings:
+#   R8  the magnitude of an int8 weight is |w| as an integer, so -128 ranks
+#       above 127; equal magnitudes go to the lower position (as R2);
+#   R9  the product accumulates in 32-bit integers; with |w|, |x| <= 128 and
+#       K <= 2^16 survivors per row it is exact, so the reference is the exact
+#       integer result.
+
+I8 = "i8"
+
+
+def magnitude_keys_i8(w: np.ndarray) -> np.ndarray:
+    """|w| of int8 weights as int32 (0..128)."""
+    return np.abs(np.asarray(w, dtype=np.int8).astype(np.int32))
+
+
+def select_survivors_i8(w: np.ndarray, n: int, m: int) -> np.ndarray:
+    """As select_survivors, ranking int8 weights by |w| (R8)."""
+    w = np.asarray(w, dtype=np.int8)
+    R, K = w.shape
+    if K % m:
+        raise ValueError("K must be a multiple of m")
+    keys = magnitude_keys_i8(w).reshape(R, K // m, m)
+    ranking = np.argsort(-keys, axis=-1, kind="stable")
+    return np.sort(ranking[..., :n], axis=-1).astype(np.int64)
+
+
+def prune_pack_i8(w: np.ndarray, n: int, m: int):
+    """Magnitude top-n-of-m prune of int8 W, then pack.
+
+    Returns (values int8 [R, S], idx uint32 [R, W]); the index stream is the
+    same as for 16-bit weights (pack_indices).
+    """
+    w = np.asarray(w, dtype=np.int8)
+    positions = select_survivors_i8(w, n, m)
+    R, K = w.shape
+    vals = np.take_along_axis(w.reshape(R, K // m, m), positions, axis=-1).reshape(R, -1).copy()
+    return vals, pack_indices(positions, m)
+
+
+def decompress_i8(values: np.ndarray, idx: np.ndarray, K: int, n: int, m: int) -> np.ndarray:
+    """Dense int8 [R, K]: each stored value back at g*m + position, zeros elsewhere."""
+    values = np.asarray(values, dtype=np.int8)
+    R, S = values.shape
+    if S != survivors_per_row(K, n, m):
+        raise ValueError("values width does not match K*n/m")
+    pos = unpack_indices(idx, S, m)
+    cols = (np.arange(S, dtype=np.int64) // n)[None, :] * m + pos
+    dense = np.zeros((R, K), dtype=np.int8)
+    dense[np.broadcast_to(np.arange(R)[:, None], (R, S)), cols] = values
+    return dense
+
+
+def spmm_ref_i8(values, idx, K: int, n: int, m: int, act, perm=None) -> np.ndarray:
+    """Y = W_nm X exactly, int64 [R, T], for int8 W_nm and act[T, K] (R6, R7, R9)."""
+    wd = decompress_i8(values, idx, K, n, m).astype(np.int64)
+    x = np.asarray(act, dtype=np.int8).astype(np.int64).T  # [K, T]
+    if perm is not None:
+        x = x[np.asarray(perm, dtype=np.int64), :]
+    return wd @ x
 
 
 def relative_error(y: np.ndarray, yref: np.ndarray):

@@ -87,7 +87,42 @@ def inverse_permutation(values, idx, K, n, m, act_bits, dtype, perm=None):
     return _orig_spmm(values, idx, K, n, m, act_bits, dtype, perm=perm)
 
 
+_orig_decompress_i8 = O.decompress_i8
+_orig_spmm_i8 = O.spmm_ref_i8
+
+
+def i8_keys_wrap_at_128(w):
+    # |w| computed in int8 arithmetic: abs(-128) wraps back to -128
+    return np.abs(np.asarray(w, dtype=np.int8)).astype(np.int32)
+
+
+def i8_signed_keys(w):
+    return np.asarray(w, dtype=np.int8).astype(np.int32)
+
+
+def i8_drop_last_group(values, idx, K, n, m):
+    d = _orig_decompress_i8(values, idx, K, n, m)
+    d[:, K - m:] = 0
+    return d
+
+
+def i8_inverse_permutation(values, idx, K, n, m, act, perm=None):
+    if perm is not None:
+        perm = np.argsort(np.asarray(perm))
+    return _orig_spmm_i8(values, idx, K, n, m, act, perm=perm)
+
+
+def i8_product_wraps_int32(values, idx, K, n, m, act, perm=None):
+    # accumulating in int16 by mistake
+    return _orig_spmm_i8(values, idx, K, n, m, act, perm=perm).astype(np.int16).astype(np.int64)
+
+
 MUTATIONS = {
+    "i8_keys_wrap_at_128": ("magnitude_keys_i8", i8_keys_wrap_at_128),
+    "i8_signed_keys": ("magnitude_keys_i8", i8_signed_keys),
+    "i8_drop_last_group": ("decompress_i8", i8_drop_last_group),
+    "i8_inverse_permutation": ("spmm_ref_i8", i8_inverse_permutation),
+    "i8_product_wraps": ("spmm_ref_i8", i8_product_wraps_int32),
     "tie_to_higher_position": ("select_survivors", tie_to_higher_position),
     "keep_smallest": ("select_survivors", keep_smallest),
     "unsorted_positions": ("select_survivors", unsorted_positions),

@@ -277,10 +277,88 @@ def check_permutation(oracle):
     assert np.allclose(pts, y[rows, cols], rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# int8 weights (COE-592 lecture 04-2, "M:N sparsity on NVIDIA tensor cores":
+# INT8 is a 2:4 weight type, opening section; 2 index bits per stored value,
+# 25% overhead and a 37.5% saving, section "Where this sits among the three
+# case studies")
+# ---------------------------------------------------------------------------
+
+def check_i8_worked_row(oracle):
+    # the worked row's pattern "value, zero, zero, value / zero, value, value, zero"
+    w = np.array([[5, 0, 0, -7, 0, 3, -2, 0]], dtype=np.int8)
+    pos = oracle.select_survivors_i8(w, 2, 4)
+    assert pos.tolist() == [[[0, 3], [1, 2]]]
+    vals, idx = oracle.prune_pack_i8(w, 2, 4)
+    assert vals.tolist() == [[5, -7, 3, -2]]
+    assert int(idx[0, 0]) & 0xFF == 0x9C
+
+
+def check_i8_group_cost(oracle):
+    # 2 x 8 value bits + 2 x 2 index bits = 20 of 32 bits per group of four
+    R, K = 64, 4096
+    w = np.random.default_rng(3).integers(-128, 128, (R, K)).astype(np.int8)
+    vals, idx = oracle.prune_pack_i8(w, 2, 4)
+    assert vals.nbytes + idx.nbytes == R * (K // 4) * 20 // 8
+    assert 1 - (vals.nbytes + idx.nbytes) / w.nbytes == 0.375
+    assert idx.nbytes / vals.nbytes == 0.25
+
+
+def check_i8_brute_force(oracle):
+    rng = np.random.default_rng(11)
+    # many ties, both extremes, zeros
+    pool = np.array([-128, -127, -2, -1, 0, 1, 2, 127], dtype=np.int8)
+    for n, m in ((2, 4), (1, 4), (1, 8)):
+        w = rng.choice(pool, size=(40, 8 * m))
+        mask = oracle.select_survivors_i8(w, n, m)
+        got = np.zeros((40, 8, m), dtype=bool)
+        np.put_along_axis(got, mask, True, axis=-1)
+        want = brute_force_kept(w.astype(np.float64).reshape(-1, m), n).reshape(40, 8, m)
+        assert np.array_equal(got, want), (n, m)
+    # -128 has the largest magnitude
+    assert oracle.select_survivors_i8(np.array([[127, -128, 0, 0]], np.int8), 1, 4).tolist() == [[[1]]]
+
+
+def check_i8_round_trip_and_gemm(oracle):
+    rng = np.random.default_rng(12)
+    R, K, T = 6, 64, 5
+    w = rng.integers(-128, 128, (R, K)).astype(np.int8)
+    act = rng.integers(-128, 128, (T, K)).astype(np.int8)
+    vals, idx = oracle.prune_pack_i8(w, 2, 4)
+    dense = oracle.decompress_i8(vals, idx, K, 2, 4)
+    mask = brute_force_kept(w.astype(np.float64).reshape(-1, 4), 2).reshape(R, K)
+    assert np.array_equal(dense, np.where(mask, w, 0).astype(np.int8))
+    y = oracle.spmm_ref_i8(vals, idx, K, 2, 4, act)
+    # Python integers, one product at a time
+    for r in range(R):
+        for t in range(T):
+            ref = sum(int(w[r, k]) * int(act[t, k]) for k in range(K) if mask[r, k])
+            assert int(y[r, t]) == ref
+    # the extreme product: every weight and activation -128, every group full
+    wx = np.full((1, 128), -128, np.int8)
+    v2, i2 = oracle.prune_pack_i8(wx, 2, 4)
+    assert int(oracle.spmm_ref_i8(v2, i2, 128, 2, 4, np.full((1, 128), -128, np.int8))[0, 0]) == 64 * 128 * 128
+
+
+def check_i8_permutation(oracle):
+    rng = np.random.default_rng(13)
+    R, K, T = 5, 32, 4
+    w = rng.integers(-128, 128, (R, K)).astype(np.int8)
+    act = rng.integers(-128, 128, (T, K)).astype(np.int8)
+    perm = rng.permutation(K)
+    vals, idx = oracle.prune_pack_i8(w, 2, 4)
+    wd = oracle.decompress_i8(vals, idx, K, 2, 4).astype(np.int64)
+    Pi = np.zeros((K, K), np.int64)
+    Pi[np.arange(K), perm] = 1
+    y = oracle.spmm_ref_i8(vals, idx, K, 2, 4, act, perm=perm)
+    assert np.array_equal(y, (wd @ Pi) @ act.astype(np.int64).T)
+
+
 ALL_CHECKS = [check_worked_row, check_group_cost, check_exactly_n_ascending, check_brute_force,
               check_exhaustive_ties, check_round_trip, check_bitstream, check_k8_walkthrough,
               check_identity_gemm, check_integer_gemm_brute_force, check_dense_case,
-              check_permutation]
+              check_permutation, check_i8_worked_row, check_i8_group_cost, check_i8_brute_force,
+              check_i8_round_trip_and_gemm, check_i8_permutation]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
