@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "2:4 sparse GEMM dense-equivalent TFLOP/s and HBM GB/s; speedup vs dense"
-PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}  # MI355X dense MFMA (int8: TOP/s), published
 PEAK_HBM_GBPS = 8000.0
 
 
@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=1500.0,
                     help="dense-matmul load before the warmup, so the clock has settled "
                          "(an idle GPU takes about a second of load to reach it)")
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: prefill 4096x4096x2048)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1..6 (default 2: prefill 4096x4096x2048; 6: the same shape in INT8)")
     ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
     ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
@@ -85,18 +86,24 @@ def traffic_from_profile(kernel_key, hsh):
 
 
 def cpu_baseline(wl, n, m, T, reps):
-    """The oracle as it stands, timed on the host: prune+pack, decompress, fp64 GEMM."""
+    """The oracle as it stands, timed on the host: prune+pack, decompress, fp64 GEMM
+    (int8: the exact int64 product, on a sample of rows; NumPy has no BLAS for it)."""
     import numpy as np
     from oracle import nm_oracle as O
     w = wl.weights()
     act = wl.activations(T)
     perm = wl.permutation()
+    i8 = wl.dtype == "i8"
+    rows = 512 if i8 else wl.R  # about 6 s of int64 matmul at 4096 x 2048
     times, t_pack, t_gemm = [], [], []
     for _ in range(reps):
         t0 = time.perf_counter()
-        vals, idx = O.prune_pack(w, n, m)
+        vals, idx = O.prune_pack_i8(w, n, m) if i8 else O.prune_pack(w, n, m)
         t1 = time.perf_counter()
-        O.spmm_ref(vals, idx, wl.K, n, m, act, wl.dtype, perm=perm)
+        if i8:
+            O.spmm_ref_i8(vals[:rows], idx[:rows], wl.K, n, m, act, perm=perm)
+        else:
+            O.spmm_ref(vals, idx, wl.K, n, m, act, wl.dtype, perm=perm)
         t2 = time.perf_counter()
         times.append(t2 - t0)
         t_pack.append(t1 - t0)
@@ -110,13 +117,21 @@ def cpu_baseline(wl, n, m, T, reps):
         if os.environ.get(var, "").isdigit():
             cores = min(cores, int(os.environ[var]))
             break
-    flops = 2.0 * wl.R * wl.K * T
     tg = statistics.median(t_gemm)
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole workload ({wl.R}x{wl.K}x{T}, {n}:{m}): prune+pack, decompress and "
-                      f"fp64 matmul; median of {reps} runs, {t:.2f} s each",
-            "prune_pack_s": statistics.median(t_pack), "decompress_gemm_s": tg,
-            "gemm_dense_eq_gflops": flops / tg / 1e9}
+    tp = statistics.median(t_pack)
+    gemm_flops = 2.0 * rows * wl.K * T
+    if i8:
+        # whole-workload time: the pack as timed, the product scaled from its row sample
+        t = tp + tg * wl.R / rows
+        sample = (f"{wl.R}x{wl.K}x{T} int8 2:4: prune+pack of all of W, decompress and exact int64 "
+                  f"product of its first {rows} rows, scaled to R; median of {reps} runs")
+    else:
+        sample = (f"whole workload ({wl.R}x{wl.K}x{T}, {n}:{m}): prune+pack, decompress and "
+                  f"fp64 matmul; median of {reps} runs, {t:.2f} s each")
+    flops = 2.0 * wl.R * wl.K * T
+    return {"value": flops / t / 1e12, "unit": "TOP/s" if i8 else "TFLOP/s", "cores": cores,
+            "kind": "oracle", "sample": sample, "prune_pack_s": tp, "decompress_gemm_s": tg,
+            "gemm_dense_eq_gflops": gemm_flops / tg / 1e9}
 
 
 def measured_peaks(torch):
@@ -177,20 +192,26 @@ def main():
     R, K = wl.R, wl.K
     S = K // m * n
     dt = wl.dtype
-    tdt = torch.float16 if dt == "f16" else torch.bfloat16
-    out_dtype = torch.float32 if args.out_dtype == "f32" else tdt
+    i8 = dt == "i8"
+    tdt = torch.int8 if i8 else torch.float16 if dt == "f16" else torch.bfloat16
+    # int8 weights give the exact int32 product
+    out_dtype = torch.int32 if i8 else torch.float32 if args.out_dtype == "f32" else tdt
     nm.nm_set_variant(args.variant)
 
     def dev(bits):
+        if i8:
+            return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
 
     W = dev(wl.weights())
     act = dev(wl.activations(T))
     perm_np = wl.permutation()
     perm = torch.from_numpy(perm_np).cuda() if perm_np is not None else None
-    vb, ib, words = nm.nm_packed_sizes(R, K, n, m, nm.NM_F16 if dt == "f16" else nm.NM_BF16)
-    ybytes = T * R * (4 if out_dtype == torch.float32 else 2)
-    step_bytes = vb + ib + T * K * 2 + ybytes  # the GEMM's algorithmic bytes
+    dcode = nm.NM_I8 if i8 else nm.NM_F16 if dt == "f16" else nm.NM_BF16
+    vb, ib, words = nm.nm_packed_sizes(R, K, n, m, dcode)
+    esz = 1 if i8 else 2
+    ybytes = T * R * (4 if out_dtype in (torch.float32, torch.int32) else 2)
+    step_bytes = vb + ib + T * K * esz + ybytes  # the GEMM's algorithmic bytes
 
     # Rotation: enough copies that one pass over them exceeds the 256 MB cache.
     rotate = args.rotate if args.rotate is not None else (1 if args.workload == 2 else
@@ -281,20 +302,33 @@ def main():
     actp = [copies[c][1] if perm is None else copies[c][1][:, perm.long()].contiguous()
             for c in range(rotate)]
 
-    def dense_gemm(c):
-        torch.nn.functional.linear(actp[c], dense[c])
+    if i8:
+        # dense int8 GEMM with an int32 result (hipBLASLt through torch._int_mm)
+        dense_t = [d.t() for d in dense]  # [K, R], column-major view of the row-major W
 
-    dense_us = time_loop(dense_gemm, iters)
-    y_half = torch.empty((T, R), dtype=tdt, device="cuda")
+        def dense_gemm(c):
+            torch._int_mm(actp[c], dense_t[c])
+    else:
+        def dense_gemm(c):
+            torch.nn.functional.linear(actp[c], dense[c])
 
-    def gemm_half(c):
-        _, Ac, vals, idx, _ = copies[c]
-        if perm is None:
-            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=tdt, out=y_half)
-        else:
-            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half)
+    try:
+        dense_us = time_loop(dense_gemm, iters)
+    except RuntimeError as e:  # no dense int8 GEMM for this shape / build
+        print(f"dense reference unavailable: {e}", file=sys.stderr)
+        dense_us = None
+    gemm_half_us = None
+    if not i8:  # a rounded half-precision output (int8 has only the exact int32 one)
+        y_half = torch.empty((T, R), dtype=tdt, device="cuda")
 
-    gemm_half_us = time_loop(gemm_half, iters)
+        def gemm_half(c):
+            _, Ac, vals, idx, _ = copies[c]
+            if perm is None:
+                nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=tdt, out=y_half)
+            else:
+                nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half)
+
+        gemm_half_us = time_loop(gemm_half, iters)
 
     dense_eq_flop = 2.0 * R * K * T
     alg_flop = 2.0 * R * S * T
@@ -303,10 +337,11 @@ def main():
                for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
     hsh = source_hash(lib_src)
     kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{args.out_dtype}"
-    roofline_bound = "mfma" if args.workload in (1, 2, 4) else "hbm"
+    roofline_bound = "mfma" if args.workload in (1, 2, 4, 6) else "hbm"
+    unit = "TOP/s" if i8 else "TFLOP/s"
     if roofline_bound == "mfma":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_MFMA_TFLOPS[dt],
-                    "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_MFMA_TFLOPS[dt],
+                    "unit": unit, "frac": achieved_tflops / PEAK_MFMA_TFLOPS[dt],
                     "traffic": traffic_from_profile(kernel_key, hsh)}
     else:
         gbps = step_bytes / (gemm_mean_us * 1e-6) / 1e9
@@ -347,7 +382,7 @@ def main():
     out = {
         "metric": METRIC,
         "value": dense_eq_flop / (ms_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -357,9 +392,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dt,
-        "data": "synthetic (seeded N(0,sigma) inputs of the workload's shapes)",
+        "data": ("synthetic (seeded N(0,1)*32 rounded to int8, the workload's shapes)" if i8 else
+                 "synthetic (seeded N(0,sigma) inputs of the workload's shapes)"),
         "config": {"workload": wl.name, "R": R, "K": K, "T": T, "pattern": f"{n}:{m}",
-                   "out_dtype": args.out_dtype, "permuted": perm is not None, "rotate": rotate,
+                   "out_dtype": "i32" if i8 else args.out_dtype, "permuted": perm is not None,
+                   "rotate": rotate,
                    "step": "nm_compress + nm_spmm", "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {
@@ -371,10 +408,10 @@ def main():
             "nm_spmm_alg_gbps": step_bytes / (gemm_loop_us * 1e-6) / 1e9,
             "nm_spmm_half_out_us": gemm_half_us,
             "nm_compress_us": compress_us,
-            "nm_compress_gbps": (R * K * 2 + vb + ib) / (compress_us * 1e-6) / 1e9,
+            "nm_compress_gbps": (R * K * esz + vb + ib) / (compress_us * 1e-6) / 1e9,
             "dense_linear_us": dense_us,
-            "speedup_vs_dense_half_out": dense_us / gemm_half_us,
-            "speedup_vs_dense_f32_out": dense_us / gemm_loop_us,
+            "speedup_vs_dense_half_out": dense_us / gemm_half_us if dense_us and gemm_half_us else None,
+            "speedup_vs_dense_f32_out": dense_us / gemm_loop_us if dense_us else None,
             **extra,
         },
         "wall_s_timed": wall,
@@ -391,7 +428,7 @@ def main():
         out["measured_peaks"] = pk
         if roofline["bound"] == "hbm":
             roofline["frac_of_measured_copy"] = roofline["achieved"] / pk["copy_gbps"]
-        else:
+        elif not i8:
             roofline["frac_of_measured_dense_matmul"] = roofline["achieved"] / pk["dense_bf16_matmul_tflops"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, n, m, T, args.cpu_reps)

@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   NM_OK = 0,
   NM_ERR_NULL = 1,         /* a required pointer is NULL                          */
-  NM_ERR_SHAPE = 2,        /* R, K or T out of range; K % 16 or K % M non-zero    */
+  NM_ERR_SHAPE = 2,        /* R, K or T out of range; K % 16 (K % 32 for int8) or K % M non-zero */
   NM_ERR_UNSUPPORTED = 3,  /* (n, m) pair or dtype combination not provided       */
   NM_ERR_STRIDE = 4,       /* leading dimension smaller than the row width        */
   NM_ERR_ALIAS = 5,        /* output overlaps an input                            */
@@ -50,9 +50,24 @@ typedef enum {
   NM_ERR_ALIGN = 7         /* pointer or leading dimension misaligned (see below) */
 } nm_status;
 
-typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2 } nm_dtype;
+typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4 } nm_dtype;
 
-/* Version of this ABI (major * 100 + minor). */
+/*
+ * INT8 weights (NM_I8).  The 2:4 pattern is also offered for 8-bit integer
+ * weights; the index stays 2 bits per stored value, so a group of four costs
+ * 2*8 + 2*2 = 20 bits (37.5% below dense), and the reduction length must be a
+ * multiple of 32 (COE-592 lecture 04-2, "M:N sparsity on NVIDIA tensor cores":
+ * opening section, and section "Where this sits among the three case
+ * studies").  With dtype NM_I8 every entry point below takes only (n, m) =
+ * (2, 4) (else NM_ERR_UNSUPPORTED) and K % 32 == 0 (else NM_ERR_SHAPE); values
+ * are one byte each; magnitude is |w| as an integer (-128 ranks above 127,
+ * equal magnitudes go to the lower position); act is int8 and Y is int32
+ * (out_dtype NM_I32, the only one), the exact integer product; leading
+ * dimensions of int8 matrices (ldw, ldx) must be multiples of 16.
+ * nm_spmm_perm does not take NM_I8 (NM_ERR_UNSUPPORTED).
+ */
+
+/* Version of this ABI (major * 100 + minor): 101 adds NM_I8 / NM_I32. */
 int nm_version(void);
 
 /* Short fixed text for a status code (never NULL). */
@@ -63,7 +78,7 @@ const char* nm_last_error(void);
 
 /*
  * Sizes of the packed format.  Pure host arithmetic, no device access.
- *   values_bytes  = R * S * 2            (values [R, S], same 16-bit type as W)
+ *   values_bytes  = R * S * 2            (values [R, S], same type as W; R * S for NM_I8)
  *   idx_row_words = ceil(S * b / 32)     (uint32 words per row)
  *   idx_bytes     = R * idx_row_words * 4
  * Any output pointer may be NULL.  Same validation as nm_compress.
@@ -76,7 +91,7 @@ const char* nm_last_error(void);
  *                       of survivor s = g*N + j sits in bits [s*b, s*b + b);
  *                       stream bit i is bit (i % 32) of word (i / 32); words
  *                       are little-endian uint32, the tail is zero-padded.
- * With 2:4, one group of four 16-bit weights costs 2*16 + 2*2 = 36 bits
+ * With 2:4, one group of four 16-bit weights costs 2*16 + 2*2 = 36 bits (int8: 20)
  * (+ per-row padding to a whole word when S*b is not a multiple of 32).
  */
 nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype,
@@ -85,7 +100,7 @@ nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype,
 /*
  * Prune + pack (magnitude top-N of every M along the rows of W).
  *   W       device, [R, K] row-major, leading dimension ldw >= K (elements),
- *           dtype NM_F16 or NM_BF16.
+ *           dtype NM_F16, NM_BF16 or NM_I8 (see above).
  *   values  device, [R, S] contiguous, same dtype (written).
  *   idx     device, [R, idx_row_words] uint32 contiguous (written, padding
  *           bits zero).
@@ -108,12 +123,13 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
 
 /*
  * Sparse GEMM  Y = W_nm X,  X = act^T.
- *   values, idx  packed W (see nm_packed_sizes), dtype NM_F16 or NM_BF16.
+ *   values, idx  packed W (see nm_packed_sizes), dtype NM_F16, NM_BF16 or NM_I8.
  *   act          device, [T, K] row-major (each token's K features contiguous),
  *                leading dimension ldx >= K, same dtype as values.
  *   Y            device, [T, R] row-major, leading dimension ldy >= R, i.e. the
  *                transpose of Y = W_nm X (the layout of a linear layer's output);
- *                out_dtype NM_F32 (default) or the input dtype (RNE rounded).
+ *                out_dtype NM_F32 (default) or the input dtype (RNE rounded);
+ *                NM_I32 for NM_I8 (exact).
  *   Y[t, r] = sum_k W_nm[r, k] * act[t, k], products and sums in fp32.
  * Shapes: R >= 1, T >= 0 (T == 0 enqueues nothing), K >= 16, K % 16 == 0,
  * K % m == 0.  Alignment: every pointer 16-byte aligned, ldx % 8 == 0 (ldy

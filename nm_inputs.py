@@ -24,6 +24,7 @@ import numpy as np
 
 F16 = "f16"
 BF16 = "bf16"
+I8 = "i8"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -69,6 +70,15 @@ def integer_half(shape, lo: int, hi: int, dtype: str, workload_id: int, tensor_i
     return to_half_bits(x, dtype)
 
 
+def normal_i8(shape, scale: float, workload_id: int, tensor_id: int, variant: int = 0) -> np.ndarray:
+    """int8 samples of N(0, 1) * scale, rounded to nearest and clipped to [-128, 127]
+    (a symmetric per-tensor quantisation of normal data; many small magnitudes,
+    so many ties)."""
+    rng = rng_for(workload_id, tensor_id, variant)
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(scale)
+    return np.clip(np.rint(x), -128, 127).astype(np.int8)
+
+
 def random_permutation(k: int, workload_id: int, variant: int = 0) -> np.ndarray:
     return rng_for(workload_id, 2, variant).permutation(int(k)).astype(np.int32)
 
@@ -89,10 +99,14 @@ class Workload:
     note: str = ""
 
     def weights(self) -> np.ndarray:
+        if self.dtype == I8:
+            return normal_i8((self.R, self.K), self.sigma_w, self.wid, 0)
         return normal_half((self.R, self.K), self.sigma_w, self.dtype, self.wid, 0)
 
     def activations(self, T: int | None = None) -> np.ndarray:
         T = self.Ts[0] if T is None else T
+        if self.dtype == I8:
+            return normal_i8((T, self.K), self.sigma_x, self.wid, 1, T)
         return normal_half((T, self.K), self.sigma_x, self.dtype, self.wid, 1, T)
 
     def permutation(self) -> np.ndarray | None:
@@ -114,4 +128,8 @@ WORKLOADS = {
                 note="1:4 and 1:8 fp16"),
     5: Workload(5, "vit-b16-fc1-perm-2of4-fp16", 3072, 768, (12608,), ((2, 4),), F16, 0.02,
                 permuted=True, note="2:4 fp16 with column permutation, 197 tokens x 64 images"),
+    # INT8 2:4 (the pages chart INT8 sparse GEMMs against dense ones) at the
+    # prefill projection's shape; weights and activations quantised normal data
+    6: Workload(6, "int8-2of4-prefill", 4096, 4096, (2048,), ((2, 4),), I8, 32.0, 32.0,
+                note="INT8 2:4, int32 output"),
 }

@@ -14,12 +14,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NMError", "lib", "lib_path",
+__all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
            "nm_check_perm", "nm_set_variant", "PATTERNS"]
 
 NM_OK = 0
-NM_F16, NM_BF16, NM_F32 = 0, 1, 2
+NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32 = 0, 1, 2, 3, 4
 PATTERNS = ((2, 4), (1, 4), (1, 8))
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,12 +92,15 @@ def _dtype_code(t) -> int:
         return NM_F16
     if t.dtype == torch.bfloat16:
         return NM_BF16
-    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.int8:
+        return NM_I8
+    raise TypeError(f"expected float16, bfloat16 or int8, got {t.dtype}")
 
 
 def _torch_dtype(code: int):
     torch = _torch()
-    return {NM_F16: torch.float16, NM_BF16: torch.bfloat16, NM_F32: torch.float32}[code]
+    return {NM_F16: torch.float16, NM_BF16: torch.bfloat16, NM_F32: torch.float32,
+            NM_I8: torch.int8, NM_I32: torch.int32}[code]
 
 
 def _stream_ptr(device) -> int:
@@ -125,7 +128,8 @@ def nm_packed_sizes(R: int, K: int, n: int, m: int, dtype: int = NM_F16):
 
 
 def nm_compress(W, n: int = 2, m: int = 4, values=None, idx=None):
-    """Prune W [R, K] (fp16/bf16, device) to n:m and pack.  Returns (values [R, S], idx [R, words])."""
+    """Prune W [R, K] (fp16/bf16, or int8 for 2:4; device) to n:m and pack.
+    Returns (values [R, S], idx [R, words])."""
     torch = _torch()
     _require_cuda(W)
     _row_major(W, "W")
@@ -174,8 +178,13 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
     dt = _dtype_code(values)
     if act.dtype != values.dtype:
         raise TypeError("act and values must share a dtype")
-    od = NM_F32 if (out_dtype is None or out_dtype == torch.float32) else _dtype_code(
-        torch.empty(0, dtype=out_dtype))
+    if dt == NM_I8:  # the exact integer product
+        if out_dtype not in (None, torch.int32):
+            raise TypeError("int8 weights give an int32 output")
+        od = NM_I32
+    else:
+        od = NM_F32 if (out_dtype is None or out_dtype == torch.float32) else _dtype_code(
+            torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty((T, R), dtype=_torch_dtype(od), device=act.device)
     else:

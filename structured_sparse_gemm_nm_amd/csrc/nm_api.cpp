@@ -46,13 +46,17 @@ bool supported_pattern(int n, int m) {
 
 // Checks shared by every entry point that names a packed weight.
 nm_status check_format(int64_t R, int64_t K, int n, int m, int dtype) {
-  if (dtype != NM_F16 && dtype != NM_BF16)
-    return fail(NM_ERR_UNSUPPORTED, "weight dtype %d is not NM_F16 or NM_BF16", dtype);
+  if (dtype != NM_F16 && dtype != NM_BF16 && dtype != NM_I8)
+    return fail(NM_ERR_UNSUPPORTED, "weight dtype %d is not NM_F16, NM_BF16 or NM_I8", dtype);
   if (!supported_pattern(n, m))
     return fail(NM_ERR_UNSUPPORTED, "pattern %d:%d is not one of 2:4, 1:4, 1:8", n, m);
+  if (dtype == NM_I8 && !(n == 2 && m == 4))
+    return fail(NM_ERR_UNSUPPORTED, "int8 weights take the 2:4 pattern only");
   if (R < 0 || R > kMaxRT) return fail(NM_ERR_SHAPE, "R = %lld out of range", (long long)R);
   if (K < 16 || K > kMaxK) return fail(NM_ERR_SHAPE, "K = %lld out of range [16, 2^24]", (long long)K);
   if (K % 16) return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+  if (dtype == NM_I8 && K % 32)
+    return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of 32 (int8)", (long long)K);
   if (K % m) return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of m = %d", (long long)K, m);
   if (R * K > kMaxElems) return fail(NM_ERR_SHAPE, "R*K too large");
   return NM_OK;
@@ -63,11 +67,17 @@ struct Sizes {
   size_t values_bytes, idx_bytes;
 };
 
-Sizes sizes_of(int64_t R, int64_t K, int n, int m) {
+// Bytes per element of a storage type.
+size_t elt_bytes(int dtype) { return dtype == NM_I8 ? 1 : dtype == NM_F32 || dtype == NM_I32 ? 4 : 2; }
+
+// Leading dimensions (elements) keep every row 16-byte aligned.
+int64_t ld_quantum(int dtype) { return dtype == NM_I8 ? 16 : 8; }
+
+Sizes sizes_of(int64_t R, int64_t K, int n, int m, int dtype) {
   Sizes z;
   z.S = K / m * n;
   z.words = (z.S * nm::index_bits(m) + 31) / 32;
-  z.values_bytes = size_t(R) * size_t(z.S) * 2;
+  z.values_bytes = size_t(R) * size_t(z.S) * elt_bytes(dtype);
   z.idx_bytes = size_t(R) * size_t(z.words) * 4;
   return z;
 }
@@ -95,22 +105,28 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
   if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
-  if (out_dtype != NM_F32 && out_dtype != dtype)
+  if (dtype == NM_I8) {
+    if (out_dtype != NM_I32) return fail(NM_ERR_UNSUPPORTED, "int8 weights give an NM_I32 output");
+    if (want_perm) return fail(NM_ERR_UNSUPPORTED, "nm_spmm_perm does not take int8 weights");
+  } else if (out_dtype != NM_F32 && out_dtype != dtype) {
     return fail(NM_ERR_UNSUPPORTED, "out_dtype %d must be NM_F32 or the input dtype", out_dtype);
+  }
   if (ldx < K) return fail(NM_ERR_STRIDE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
   if (ldy < R) return fail(NM_ERR_STRIDE, "ldy = %lld < R = %lld", (long long)ldy, (long long)R);
   if (R == 0 || T == 0) return ok();  // empty product: nothing to enqueue
   if (!values || !idx || !act || !Y || (want_perm && !perm))
     return fail(NM_ERR_NULL, "values, idx, act, Y%s must be non-NULL", want_perm ? ", perm" : "");
-  if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of 8", (long long)ldx);
+  if (ldx % ld_quantum(dtype))
+    return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of %lld", (long long)ldx,
+                (long long)ld_quantum(dtype));
   if (!aligned16(values) || !aligned16(idx) || !aligned16(act) || !aligned16(Y) ||
       (want_perm && !aligned16(perm)))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (T * ldx > kMaxElems || T * ldy > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
-  Sizes z = sizes_of(R, K, n, m);
-  size_t ybytes = extent(T, R, ldy, out_dtype == NM_F32 ? 4 : 2);
+  Sizes z = sizes_of(R, K, n, m, dtype);
+  size_t ybytes = extent(T, R, ldy, elt_bytes(out_dtype));
   if (overlaps(Y, ybytes, values, z.values_bytes) || overlaps(Y, ybytes, idx, z.idx_bytes) ||
-      overlaps(Y, ybytes, act, extent(T, K, ldx, 2)) ||
+      overlaps(Y, ybytes, act, extent(T, K, ldx, elt_bytes(dtype))) ||
       (want_perm && overlaps(Y, ybytes, perm, size_t(K) * 4)))
     return fail(NM_ERR_ALIAS, "Y overlaps an input");
 
@@ -181,7 +197,7 @@ hipError_t ensure_lds_limit(const void* kern, int bytes) {
 
 extern "C" {
 
-int nm_version(void) { return 100; }
+int nm_version(void) { return 101; }
 
 const char* nm_status_string(int status) {
   switch (status) {
@@ -203,7 +219,7 @@ nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype, size_t*
                           size_t* idx_bytes, int64_t* idx_row_words) {
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
-  Sizes z = sizes_of(R, K, n, m);
+  Sizes z = sizes_of(R, K, n, m, dtype);
   if (values_bytes) *values_bytes = z.values_bytes;
   if (idx_bytes) *idx_bytes = z.idx_bytes;
   if (idx_row_words) *idx_row_words = z.words;
@@ -217,15 +233,22 @@ nm_status nm_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtyp
   if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
   if (R == 0) return ok();
   if (!W || !values || !idx) return fail(NM_ERR_NULL, "W, values and idx must be non-NULL");
-  if (ldw % 8) return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of 8", (long long)ldw);
+  if (ldw % ld_quantum(dtype))
+    return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of %lld", (long long)ldw,
+                (long long)ld_quantum(dtype));
   if (!aligned16(W) || !aligned16(values) || !aligned16(idx))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (R * ldw > kMaxElems) return fail(NM_ERR_SHAPE, "R*ldw too large");
-  Sizes z = sizes_of(R, K, n, m);
-  size_t wbytes = extent(R, K, ldw, 2);
+  Sizes z = sizes_of(R, K, n, m, dtype);
+  size_t wbytes = extent(R, K, ldw, elt_bytes(dtype));
   if (overlaps(values, z.values_bytes, W, wbytes) || overlaps(idx, z.idx_bytes, W, wbytes) ||
       overlaps(values, z.values_bytes, idx, z.idx_bytes))
     return fail(NM_ERR_ALIAS, "outputs overlap each other or W");
+  if (dtype == NM_I8)
+    return hip_status(nm::launch_prune_pack_i8(static_cast<const uint8_t*>(W), R, K, ldw,
+                                               static_cast<uint8_t*>(values), idx, z.words,
+                                               static_cast<hipStream_t>(stream)),
+                      "nm_compress launch");
   return hip_status(nm::launch_prune_pack(static_cast<const uint16_t*>(W), R, K, ldw, n, m,
                                           static_cast<uint16_t*>(values), idx, z.words,
                                           static_cast<hipStream_t>(stream)),
@@ -239,14 +262,21 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
   if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
   if (R == 0) return ok();
   if (!W_out || !values || !idx) return fail(NM_ERR_NULL, "values, idx and W_out must be non-NULL");
-  if (ldw % 8) return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of 8", (long long)ldw);
+  if (ldw % ld_quantum(dtype))
+    return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of %lld", (long long)ldw,
+                (long long)ld_quantum(dtype));
   if (!aligned16(W_out) || !aligned16(values) || !aligned16(idx))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (R * ldw > kMaxElems) return fail(NM_ERR_SHAPE, "R*ldw too large");
-  Sizes z = sizes_of(R, K, n, m);
-  size_t wbytes = extent(R, K, ldw, 2);
+  Sizes z = sizes_of(R, K, n, m, dtype);
+  size_t wbytes = extent(R, K, ldw, elt_bytes(dtype));
   if (overlaps(W_out, wbytes, values, z.values_bytes) || overlaps(W_out, wbytes, idx, z.idx_bytes))
     return fail(NM_ERR_ALIAS, "W_out overlaps an input");
+  if (dtype == NM_I8)
+    return hip_status(nm::launch_decompress_i8(static_cast<const uint8_t*>(values), idx, R, K, z.words,
+                                               static_cast<uint8_t*>(W_out), ldw,
+                                               static_cast<hipStream_t>(stream)),
+                      "nm_decompress launch");
   return hip_status(nm::launch_decompress(static_cast<const uint16_t*>(values), idx, R, K, n, m,
                                           z.words, static_cast<uint16_t*>(W_out), ldw,
                                           static_cast<hipStream_t>(stream)),

@@ -22,13 +22,20 @@ hipError_t launch_decompress(const uint16_t* values, const uint32_t* idx, int64_
                              int n, int m, int64_t idx_row_words, uint16_t* W, int64_t ldw,
                              hipStream_t s);
 
+// INT8 2:4 (nm_int8.hip): prune + pack, decompress (leading dimensions in
+// bytes, multiples of 16; K % 32 == 0).
+hipError_t launch_prune_pack_i8(const uint8_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* values,
+                                uint32_t* idx, int64_t idx_row_words, hipStream_t s);
+hipError_t launch_decompress_i8(const uint8_t* values, const uint32_t* idx, int64_t R, int64_t K,
+                                int64_t idx_row_words, uint8_t* W, int64_t ldw, hipStream_t s);
+
 struct SpmmArgs {
   const uint16_t* values;
   const uint32_t* idx;
   int64_t R, K;
   int n, m;
-  int dtype;             // NM_F16 / NM_BF16
-  const uint16_t* act;   // [T, K], ldx
+  int dtype;             // NM_F16 / NM_BF16 / NM_I8 (values and act then hold bytes)
+  const uint16_t* act;   // [T, K], ldx (elements)
   int64_t T, ldx;
   const int32_t* perm;   // nullptr: identity
   void* Y;               // [T, R], ldy
@@ -39,6 +46,8 @@ struct SpmmArgs {
 };
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
+// INT8 2:4 GEMM (nm_int8.hip): Y int32.
+hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s);
 
 // Pipelined large-tile kernel (nm_spmm_pipe.hip) and the shapes it takes.
 bool spmm_pipe_applies(const SpmmArgs& a);

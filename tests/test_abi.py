@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
     assert {"nm_compress", "nm_spmm", "nm_spmm_perm", "nm_decompress", "nm_packed_sizes"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
-    assert L.nm_version() == 100
+    assert L.nm_version() == 101
 
 
 def test_status_codes_match_header():
@@ -135,6 +135,36 @@ def test_spmm_errors():
     assert st_spmm(T=0, values=None, idx=None, act=None, Y=None) == 0
     assert st_spmm(R=0, values=None, idx=None, act=None, Y=None, ldy=0) == 0
     assert nm.lib().nm_last_error().decode() == ""
+
+
+def test_int8_sizes_and_rules():
+    # 20 bits per INT8 2:4 group (one byte per value, 2 index bits each);
+    # the reduction length must be a multiple of 32 (COE-592 lecture 04-2,
+    # "M:N sparsity on NVIDIA tensor cores", section "Where this sits among
+    # the three case studies")
+    vb, ib, words = nm.nm_packed_sizes(4096, 4096, 2, 4, nm.NM_I8)
+    assert (vb + ib) * 8 == 4096 * (4096 // 4) * 20
+    assert vb == 4096 * 2048 and words == 4096 // 32
+    L = nm.lib()
+    st = lambda K, n=2, m=4: L.nm_packed_sizes(8, K, n, m, nm.NM_I8, None, None, None)
+    assert st(64) == 0 and st(32) == 0
+    assert st(48) == 2                             # K % 32 for int8
+    assert st(64, 1, 4) == 3 and st(64, 1, 8) == 3  # int8 takes 2:4 only
+    # compress: int8 rows must be 16-byte aligned (ldw % 16)
+    assert st_compress(dt=nm.NM_I8, ldw=72) == 7
+    assert st_compress(dt=nm.NM_I8, K=48, ldw=48) == 2
+    assert st_compress(dt=nm.NM_I8, n=1, m=8) == 3
+    # spmm: int32 output only, no permuted form, ldx % 16
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_F32) == 3
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I8) == 3
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, perm=FAKE * 5) == 3
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, ldx=72) == 7
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, K=96, ldx=96, values=None) == 1
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, K=80, ldx=80) == 2
+    # NM_I32 is an output type only
+    assert st_spmm(dt=nm.NM_I32, od=nm.NM_I32) == 3
+    # Y (int32) overlapping act (int8)
+    assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, Y=FAKE * 3 + 16) == 5
 
 
 def test_decompress_and_misc_errors():

@@ -453,3 +453,70 @@ def test_decode_stream(R, K, T, dt, permuted):
     ref_vals, ref_idx = O.prune_pack(w, 2, 4)
     yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
+
+
+# ---------------------------------------------------------------------------
+# INT8 2:4: packed values and indices, the decompressed weight and the int32
+# product, all bit for bit (the product is exact); ragged rows, tokens and K
+# tails (K a multiple of 32 but not of the 128-wide step), T = 1, extremes
+# ---------------------------------------------------------------------------
+
+def _i8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("R,K,T", [(1, 32, 1), (7, 96, 5), (130, 160, 129), (300, 4128, 70),
+                                   (256, 256, 256), (1000, 1024, 3), (257, 2048, 300)])
+def test_i8_bit_exact(R, K, T):
+    log(f"int8 2:4 R={R} K={K} T={T}")
+    w = nm_inputs.normal_i8((R, K), 32.0, 61, 0, R + K + T)
+    act = nm_inputs.normal_i8((T, K), 32.0, 61, 1, R + K + T)
+    vals, idx = nm.nm_compress(_i8(w), 2, 4)
+    dense = nm.nm_decompress(vals, idx, K, 2, 4)
+    y = nm.nm_spmm(vals, idx, _i8(act), K, 2, 4)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack_i8(w, 2, 4)
+    assert vals.dtype == torch.int8 and y.dtype == torch.int32
+    assert np.array_equal(vals.cpu().numpy(), ref_vals)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    assert np.array_equal(dense.cpu().numpy(), O.decompress_i8(ref_vals, ref_idx, K, 2, 4))
+    yref = O.spmm_ref_i8(ref_vals, ref_idx, K, 2, 4, act)
+    assert np.array_equal(y.cpu().numpy().T.astype(np.int64), yref)
+
+
+def test_i8_extremes():
+    log("int8 2:4 extremes")
+    R, K, T = 64, 4096, 32
+    # every weight and activation -128: each group keeps positions 0 and 1,
+    # every product is 2^14 and the sums reach K/2 * 2^14 = 2^25
+    w = np.full((R, K), -128, np.int8)
+    act = np.full((T, K), -128, np.int8)
+    vals, idx = nm.nm_compress(_i8(w), 2, 4)
+    y = nm.nm_spmm(vals, idx, _i8(act), K, 2, 4)
+    torch.cuda.synchronize()
+    assert np.all(idx.cpu().numpy().view(np.uint32) == 0x44444444)
+    assert np.all(y.cpu().numpy() == (K // 2) * 128 * 128)
+    # ties of +/-x: the lower position wins; zeros rows give zeros
+    w2 = np.tile(np.array([3, -3, 3, -3, 0, 0, 0, 0, -128, 127, -127, 128 - 1], np.int8), (R, K // 12 + 1))[:, :K]
+    w2 = np.ascontiguousarray(w2[:, :K])
+    vals2, idx2 = nm.nm_compress(_i8(w2), 2, 4)
+    rv, ri = O.prune_pack_i8(w2, 2, 4)
+    assert np.array_equal(vals2.cpu().numpy(), rv)
+    assert np.array_equal(idx2.cpu().numpy().view(np.uint32), ri)
+
+
+def test_i8_workload_sampled():
+    wl = nm_inputs.WORKLOADS[6]
+    T = wl.Ts[0]
+    log(f"int8 workload {wl.R}x{wl.K}x{T}")
+    w = wl.weights()
+    act = wl.activations(T)
+    vals, idx = nm.nm_compress(_i8(w), 2, 4)
+    y = nm.nm_spmm(vals, idx, _i8(act), wl.K, 2, 4)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack_i8(w, 2, 4)
+    assert np.array_equal(vals.cpu().numpy(), ref_vals)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    rows = np.sort(np.random.default_rng(5).choice(wl.R, 48, replace=False))
+    yref = O.spmm_ref_i8(ref_vals[rows], ref_idx[rows], wl.K, 2, 4, act)
+    assert np.array_equal(y.cpu().numpy()[:, rows].T.astype(np.int64), yref)
