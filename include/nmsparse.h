@@ -176,6 +176,9 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
  *      T >= 256, R >= 256)
  *   6  all-LDS direct-load kernel with 128 x 64 tiles (1:4 and 1:8;
  *      K % 256 == 0, T >= 64, R >= 128)
+ * For int8 weights there are two: the LDS-staged kernel (whole 256 x 128 tiles,
+ * K % 128 == 0) and, for variant 1 or any other shape, a kernel that loads
+ * its operands straight into registers.
  * A forced family that does not take the shape falls back to the choice by
  * shape.  Every family computes the same product; all but 4 add the K steps
  * in the same order and give the same bits.  NM_ERR_UNSUPPORTED outside 0..6.

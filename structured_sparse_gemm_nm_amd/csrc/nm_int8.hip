@@ -22,6 +22,8 @@
 // So every operand is a plain 16- or 4-byte load of the stored data.
 #include "nm_internal.h"
 
+#include <type_traits>
+
 namespace nm {
 namespace {
 
@@ -188,6 +190,210 @@ __global__ __launch_bounds__(256) void spmm_i8_kernel(const uint8_t* __restrict_
   }
 }
 
+// The prefill kernel for INT8: 256 x 128 tiles, 4 waves as 2 x 2 (128 rows x
+// 64 tokens each, 8 x 4 fragments), both operands staged in LDS by direct
+// global->LDS loads through a 4-deep ring of 128-wide K steps.  At one byte
+// per element a step's packed values (64 B per row) and activations (128 B
+// per token) have the byte layout of a 64-wide step of the 16-bit kernel, so
+// its XOR-swizzled slots serve here unchanged:
+//   packed values  slot (row, quarter q) at row*4 + (q ^ ((row >> 1) & 3));
+//   activations    slot (token, chunk c) at token*8 + (c ^ (token & 7)).
+// Index bits (16 bytes per row and step) are staged the same way in blocks
+// of four steps (64 bytes per row, two blocks in LDS): slot (row, step c of
+// the block) at row*4 + (c ^ ((row >> 2) & 3)), so a fragment's 16 rows x 4
+// lanes read distinct banks; a lane's index word is one 4-byte LDS read.
+// (Per-lane 4-byte global loads of the words took more than the rest of the
+// step together, and one 16-byte load per row and step used an eighth of each
+// line it fetched.)  Fragments go through two register
+// sets: step s+1 is read while step s multiplies.  Every step issues the same loads (past the last
+// step the last one again, into a slot nothing reads any more), so each wait
+// is one constant count.  Shapes: R % 256 == 0, T % 128 == 0, K % 128 == 0.
+constexpr int kBR8L = 256, kBT8L = 128, kNS8 = 4;
+constexpr int kStage8 = 16384;                    // one operand, one step
+constexpr int kBlockI8 = kBR8L * 64;              // index bits, four steps
+constexpr int kLds8 = kNS8 * 2 * kStage8 + 2 * kBlockI8;  // 160 KB
+constexpr int kPer8 = 8;                          // direct loads per wave per step: 4 + 4
+
+typedef __attribute__((address_space(3))) unsigned char lds_byte8;
+
+template <int N>
+__device__ inline void wait_vmcnt8() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __restrict__ values,
+                                                             const uint32_t* __restrict__ idx, int K,
+                                                             int words, const uint8_t* __restrict__ act,
+                                                             int64_t ldx, int32_t* __restrict__ Y,
+                                                             int64_t ldy, int tilesT) {
+  extern __shared__ __align__(16) unsigned char smem8[];
+  unsigned char* bbuf = smem8;                  // [kNS8][kStage8] activations
+  unsigned char* abuf = smem8 + kNS8 * kStage8;  // [kNS8][kStage8] packed values
+  unsigned char* ibuf = smem8 + 2 * kNS8 * kStage8;  // [2][kBlockI8] index blocks
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  const int wr = wave >> 1, wt = wave & 1;
+  // Tile order: each XCD (workgroup p runs on XCD p % 8) takes a contiguous run
+  // of the tile sequence, which goes through groups of up to four row tiles
+  // sharing activation columns.
+  int R0, T0;
+  {
+    const int grid = int(gridDim.x), p = int(blockIdx.x);
+    const int q = (grid & 7) == 0 ? (p & 7) * (grid >> 3) + (p >> 3) : p;
+    const int tilesR = grid / tilesT;
+    const int gr = tilesR < 4 ? tilesR : 4;
+    const int per_group = gr * tilesT;
+    const int grp = q / per_group, rem = q - grp * per_group;
+    const int rows_in = min(gr, tilesR - grp * gr);
+    R0 = (grp * gr + rem % rows_in) * kBR8L;
+    T0 = (rem / rows_in) * kBT8L;
+  }
+  const int64_t S = K >> 1;
+  const int nsteps = K >> 7;
+
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(act + int64_t(T0) * ldx), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(values + int64_t(R0) * S), (short)0, -1, 0x00020000);
+  // per-lane byte offsets of the direct loads within a step (instruction j)
+  uint32_t boff[4], aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int tok = slot >> 3, c = (slot & 7) ^ (tok & 7);
+    boff[j] = uint32_t(tok) * uint32_t(ldx) + uint32_t(c) * 16u;
+    const int row = slot >> 2, q = (slot & 3) ^ ((row >> 1) & 3);
+    aoff[j] = uint32_t(row) * uint32_t(S) + uint32_t(q) * 16u;
+  }
+  // index blocks: instruction j of wave w fills slots [(w*4 + j)*64, +64),
+  // slot (row, position p) holding step c = p ^ ((row >> 2) & 3) of the block
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(idx + int64_t(R0) * words), (short)0, -1, 0x00020000);
+  uint32_t ioff[4];
+  int istep[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int row = slot >> 2;
+    istep[j] = (slot & 3) ^ ((row >> 2) & 3);
+    ioff[j] = uint32_t(row) * uint32_t(words) * 4u;
+  }
+  // block q into buffer ib; a step past the last rereads the last step, so
+  // no load leaves the row
+  auto issue_block = [&](int q, int ib) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int st = min(4 * q + istep[j], nsteps - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_byte8*)(ibuf + ib * kBlockI8 + (wave * 4 + j) * 1024),
+                                               16, int(ioff[j] + uint32_t(st) * 16u), 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  // A step's loads, fenced so that no load of another step moves in between
+  // (the counted waits rely on whole steps completing in order).
+  auto issue = [&](int src, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte8*)(bbuf + SL * kStage8 + (wave * 4 + j) * 1024),
+                                               16, int(boff[j]), int(src * 128), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_byte8*)(abuf + SL * kStage8 + (wave * 4 + j) * 1024),
+                                               16, int(aoff[j]), int(src * 64), 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  i32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  // fragments of a step from its ring slot into registers
+  // fragments of step t (ring slot SL = t & 3, index block t / 4)
+  auto read_frags = [&](int t, auto slot_c, i32x4 (&a)[8], i32x8 (&b)[4], uint32_t (&x)[8]) {
+    constexpr int SL = decltype(slot_c)::value;
+    const unsigned char* sb = bbuf + SL * kStage8;
+    const unsigned char* sa = abuf + SL * kStage8;
+    const unsigned char* si = ibuf + ((t >> 2) & 1) * kBlockI8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = wt * 64 + j * 16 + li;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(sb + (tok * 8 + (lq ^ (tok & 7))) * 16);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(sb + (tok * 8 + ((lq + 4) ^ (tok & 7))) * 16);
+      b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = wr * 128 + i * 16 + li;
+      a[i] = *reinterpret_cast<const i32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
+      x[i] = *reinterpret_cast<const uint32_t*>(si + (row * 4 + (SL ^ ((row >> 2) & 3))) * 16 + lq * 4);
+    }
+  };
+
+  // One step s: make step s+1 visible, refill step s's slot with step s+4,
+  // read step s+1's fragments, multiply step s (fragments read one step
+  // earlier, so the reads overlap the MFMAs).
+  auto step = [&](int s, auto slot_c, const i32x4 (&ca)[8], const i32x8 (&cb)[4], const uint32_t (&cx)[8],
+                  i32x4 (&na)[8], i32x8 (&nb)[4], uint32_t (&nx)[8]) {
+    constexpr int SL = decltype(slot_c)::value;
+    wait_vmcnt8<2 * kPer8>();  // step s+1 has landed (steps s+2, s+3 may remain)
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // this wave's reads of step s are done
+    __builtin_amdgcn_s_barrier();  // step s+1 visible; every wave is done reading step s
+    asm volatile("" ::: "memory");
+    issue(min(s + 4, nsteps - 1), slot_c);
+    // at a block's first step every wave is done with the block before it:
+    // its buffer takes the next block (first read three steps later)
+    if (SL == 0 && s + 4 < nsteps) issue_block((s >> 2) + 1, ((s >> 2) + 1) & 1);
+    read_frags(s + 1, std::integral_constant<int, (SL + 1) & 3>{}, na, nb, nx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(ca[i], cb[j], acc[i][j], int(cx[i]), 0, 0);
+  };
+
+  using std::integral_constant;
+  i32x4 a0[8], a1[8];
+  i32x8 b0[4], b1[4];
+  uint32_t x0[8], x1[8];
+  issue_block(0, 0);
+  issue(0, integral_constant<int, 0>{});
+  issue(min(1, nsteps - 1), integral_constant<int, 1>{});
+  issue(min(2, nsteps - 1), integral_constant<int, 2>{});
+  wait_vmcnt8<2 * kPer8>();  // index block 0 and step 0 have landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  issue(min(3, nsteps - 1), integral_constant<int, 3>{});
+  read_frags(0, integral_constant<int, 0>{}, a0, b0, x0);
+  int s = 0;
+  for (; s + 4 <= nsteps; s += 4) {
+    step(s, integral_constant<int, 0>{}, a0, b0, x0, a1, b1, x1);
+    step(s + 1, integral_constant<int, 1>{}, a1, b1, x1, a0, b0, x0);
+    step(s + 2, integral_constant<int, 2>{}, a0, b0, x0, a1, b1, x1);
+    step(s + 3, integral_constant<int, 3>{}, a1, b1, x1, a0, b0, x0);
+  }
+  if (s < nsteps) step(s, integral_constant<int, 0>{}, a0, b0, x0, a1, b1, x1);
+  if (s + 1 < nsteps) step(s + 1, integral_constant<int, 1>{}, a1, b1, x1, a0, b0, x0);
+  if (s + 2 < nsteps) step(s + 2, integral_constant<int, 2>{}, a0, b0, x0, a1, b1, x1);
+  wait_vmcnt8<0>();  // no direct load still writing LDS when the workgroup ends
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = R0 + wr * 128 + i * 16 + 4 * lq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = T0 + wt * 64 + j * 16 + li;
+      *reinterpret_cast<i32x4*>(Y + int64_t(t) * ldy + r) = acc[i][j];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prune_pack_i8(const uint8_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* values,
@@ -213,6 +419,22 @@ hipError_t launch_decompress_i8(const uint8_t* values, const uint32_t* idx, int6
 }
 
 hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s) {
+  // whole tiles only, 32-bit per-lane offsets, 16-byte output rows
+  const bool lds = a.R % kBR8L == 0 && a.T % kBT8L == 0 && a.K % 128 == 0 && (a.ldy & 3) == 0 &&
+                   int64_t(kBT8L) * a.ldx < 0x7FFFFFFF && int64_t(kBR8L) * (a.K >> 1) < 0x7FFFFFFF &&
+                   int64_t(kBR8L) * a.idx_row_words * 4 < 0x7FFFFFFF &&
+                   a.variant != NM_VARIANT_GENERIC && device_max_lds() >= kLds8;
+  if (lds) {
+    const int64_t tiles = (a.R / kBR8L) * (a.T / kBT8L);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const void* kern = reinterpret_cast<const void*>(spmm_i8_lds_kernel);
+    if (hipError_t e = ensure_lds_limit(kern, kLds8); e != hipSuccess) return e;
+    hipLaunchKernelGGL(spmm_i8_lds_kernel, dim3(unsigned(tiles)), dim3(256), kLds8, s,
+                       reinterpret_cast<const uint8_t*>(a.values), a.idx, int(a.K), int(a.idx_row_words),
+                       reinterpret_cast<const uint8_t*>(a.act), a.ldx, static_cast<int32_t*>(a.Y), a.ldy,
+                       int(a.T / kBT8L));
+    return hipGetLastError();
+  }
   const int64_t tilesR = (a.R + kBR8 - 1) / kBR8;
   const int64_t tilesT = (a.T + kBT8 - 1) / kBT8;
   if (tilesR * tilesT > 0x7FFFFFFF || a.R > 0x7FFFFFFF || a.T > 0x7FFFFFFF || a.K > 0x7FFFFFFF)

@@ -466,7 +466,11 @@ def _i8(a):
 
 
 @pytest.mark.parametrize("R,K,T", [(1, 32, 1), (7, 96, 5), (130, 160, 129), (300, 4128, 70),
-                                   (256, 256, 256), (1000, 1024, 3), (257, 2048, 300)])
+                                   (1000, 1024, 3), (257, 2048, 300),
+                                   # whole 256 x 128 tiles, K % 128 == 0: the LDS-staged kernel,
+                                   # 1, 2, 3, 4 and 9 K steps (the ring's tail cases)
+                                   (256, 128, 128), (256, 256, 256), (512, 384, 128),
+                                   (256, 512, 384), (768, 1152, 256)])
 def test_i8_bit_exact(R, K, T):
     log(f"int8 2:4 R={R} K={K} T={T}")
     w = nm_inputs.normal_i8((R, K), 32.0, 61, 0, R + K + T)
@@ -482,6 +486,13 @@ def test_i8_bit_exact(R, K, T):
     assert np.array_equal(dense.cpu().numpy(), O.decompress_i8(ref_vals, ref_idx, K, 2, 4))
     yref = O.spmm_ref_i8(ref_vals, ref_idx, K, 2, 4, act)
     assert np.array_equal(y.cpu().numpy().T.astype(np.int64), yref)
+    try:  # the register-operand kernel on the same input
+        nm.nm_set_variant(1)
+        y1 = nm.nm_spmm(vals, idx, _i8(act), K, 2, 4)
+    finally:
+        nm.nm_set_variant(0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y)
 
 
 def test_i8_extremes():
