@@ -336,7 +336,7 @@ def main():
     lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
                for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
     hsh = source_hash(lib_src)
-    kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{args.out_dtype}"
+    kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{'i32' if i8 else args.out_dtype}"
     roofline_bound = "mfma" if args.workload in (1, 2, 4, 6) else "hbm"
     unit = "TOP/s" if i8 else "TFLOP/s"
     if roofline_bound == "mfma":
