@@ -41,7 +41,9 @@ Parity pins: every function here is pinned by tests under tests/ (worked
 row, 36-bit group cost, brute-force top-N, exhaustive ties, worked K = 8
 product, identity and integer GEMMs, dense N = M case, explicit-matrix
 permutation route; for int8: the 20-bit group cost, brute-force top-N by |w|
-with -128 and ties, big-integer products).  No function is "parity unpinned".
+with -128 and ties, big-integer products; for E4M3: the decode against the
+library's float8_e4m3fn and printed field values, brute-force top-N by |w|,
+exact small-integer products).  No function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -289,6 +291,68 @@ def spmm_ref_i8(values, idx, K: int, n: int, m: int, act, perm=None) -> np.ndarr
     """Y = W_nm X exactly, int64 [R, T], for int8 W_nm and act[T, K] (R6, R7, R9)."""
     wd = decompress_i8(values, idx, K, n, m).astype(np.int64)
     x = np.asarray(act, dtype=np.int8).astype(np.int64).T  # [K, T]
+    if perm is not None:
+        x = x[np.asarray(perm, dtype=np.int64), :]
+    return wd @ x
+
+
+# --------------------------------------------------------------------------
+# 8-bit floating-point weights and activations (OCP E4M3)
+# --------------------------------------------------------------------------
+# The pages name 16-bit and INT8 2:4 types; an 8-bit float takes the same
+# one-byte packed layout, group cost and K % 32 rule as INT8 (reading R10).
+# Readings:
+#   R10 the format is OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3
+#       mantissa bits; exponent 0 subnormal; S.1111.111 is NaN; no inf), the
+#       one the 8-bit sparse MFMA of this hardware takes;
+#   R11 magnitude is compared on bits & 0x7F (the sign bit dropped), which
+#       orders finite values by |w| as for 16-bit floats; equal keys go to the
+#       lower position;
+#   R12 the reference product is exact (fp64 of the decoded values).
+
+F8 = "f8e4m3"
+
+
+def fp8_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of OCP E4M3 bit patterns (uint8), from the field definition."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((b & 0x7F) == 0x7F, np.nan, out)
+
+
+def select_survivors_fp8(w_bits: np.ndarray, n: int, m: int) -> np.ndarray:
+    """As select_survivors, with keys bits & 0x7F of the 8-bit patterns (R11)."""
+    w = np.asarray(w_bits, dtype=np.uint8)
+    R, K = w.shape
+    if K % m:
+        raise ValueError("K must be a multiple of m")
+    keys = (w & np.uint8(0x7F)).astype(np.int32).reshape(R, K // m, m)
+    ranking = np.argsort(-keys, axis=-1, kind="stable")
+    return np.sort(ranking[..., :n], axis=-1).astype(np.int64)
+
+
+def prune_pack_fp8(w_bits: np.ndarray, n: int, m: int):
+    """Returns (values uint8 [R, S] bit patterns, idx uint32 [R, W])."""
+    w = np.asarray(w_bits, dtype=np.uint8)
+    positions = select_survivors_fp8(w, n, m)
+    R, K = w.shape
+    vals = np.take_along_axis(w.reshape(R, K // m, m), positions, axis=-1).reshape(R, -1).copy()
+    return vals, pack_indices(positions, m)
+
+
+def decompress_fp8(values: np.ndarray, idx: np.ndarray, K: int, n: int, m: int) -> np.ndarray:
+    """Dense uint8 bit patterns [R, K] (zeros elsewhere)."""
+    return decompress_i8(np.asarray(values, dtype=np.uint8).view(np.int8), idx, K, n, m).view(np.uint8)
+
+
+def spmm_ref_fp8(values, idx, K: int, n: int, m: int, act_bits, perm=None) -> np.ndarray:
+    """Y = W_nm X in float64, [R, T], for E4M3 W_nm and act[T, K] (R6, R7, R12)."""
+    wd = fp8_to_f64(decompress_fp8(values, idx, K, n, m))
+    x = fp8_to_f64(np.asarray(act_bits, dtype=np.uint8)).T  # [K, T]
     if perm is not None:
         x = x[np.asarray(perm, dtype=np.int64), :]
     return wd @ x

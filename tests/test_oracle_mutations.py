@@ -117,7 +117,25 @@ def i8_product_wraps_int32(values, idx, K, n, m, act, perm=None):
     return _orig_spmm_i8(values, idx, K, n, m, act, perm=perm).astype(np.int16).astype(np.int64)
 
 
+_orig_fp8_decode = O.fp8_to_f64
+
+
+def fp8_bias_8(bits):
+    # exponent bias 8 instead of 7
+    return _orig_fp8_decode(bits) / 2.0
+
+
+def fp8_signed_keys(w_bits, n, m):
+    w = np.asarray(w_bits, dtype=np.uint8)
+    R, K = w.shape
+    keys = w.view(np.int8).astype(np.int32).reshape(R, K // m, m)
+    ranking = np.argsort(-keys, axis=-1, kind="stable")
+    return np.sort(ranking[..., :n], axis=-1).astype(np.int64)
+
+
 MUTATIONS = {
+    "fp8_bias_8": ("fp8_to_f64", fp8_bias_8),
+    "fp8_signed_keys": ("select_survivors_fp8", fp8_signed_keys),
     "i8_keys_wrap_at_128": ("magnitude_keys_i8", i8_keys_wrap_at_128),
     "i8_signed_keys": ("magnitude_keys_i8", i8_signed_keys),
     "i8_drop_last_group": ("decompress_i8", i8_drop_last_group),

@@ -354,11 +354,66 @@ def check_i8_permutation(oracle):
     assert np.array_equal(y, (wd @ Pi) @ act.astype(np.int64).T)
 
 
+# ---------------------------------------------------------------------------
+# OCP FP8 E4M3 weights (same packed layout and group cost as INT8)
+# ---------------------------------------------------------------------------
+
+def check_fp8_decode(oracle):
+    import torch
+    b = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_to_f64(b)
+    lib = torch.from_numpy(b).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    assert np.array_equal(ours[~np.isnan(ours)], lib[~np.isnan(lib)])
+    # field values: 1.0, the largest finite 448, the smallest subnormal 2^-9,
+    # the smallest normal 2^-6, and the sign
+    assert oracle.fp8_to_f64(np.array([0x38, 0x7E, 0x01, 0x08, 0xB8], np.uint8)).tolist() == \
+        [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, -1.0]
+
+
+def _fp8_bits(vals):
+    import torch
+    return torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check_fp8_worked_row_and_brute_force(oracle):
+    w = _fp8_bits([[5, 0, 0, -7, 0, 3, -2, 0]])
+    assert oracle.select_survivors_fp8(w, 2, 4).tolist() == [[[0, 3], [1, 2]]]
+    vals, idx = oracle.prune_pack_fp8(w, 2, 4)
+    assert oracle.fp8_to_f64(vals).tolist() == [[5.0, -7.0, 3.0, -2.0]]
+    assert int(idx[0, 0]) & 0xFF == 0x9C
+    rng = np.random.default_rng(21)
+    pool = _fp8_bits([-448, -2, -1, -0.0, 0.0, 1, 2, 448, 2.0 ** -9, -(2.0 ** -9)])
+    w = rng.choice(pool, size=(30, 32))
+    got = np.zeros((30, 8, 4), dtype=bool)
+    np.put_along_axis(got, oracle.select_survivors_fp8(w, 2, 4), True, axis=-1)
+    want = brute_force_kept(oracle.fp8_to_f64(w).reshape(-1, 4), 2).reshape(30, 8, 4)
+    assert np.array_equal(got, want)
+
+
+def check_fp8_integer_gemm(oracle):
+    # small integers are exact in E4M3, so is their product
+    rng = np.random.default_rng(22)
+    R, K, T = 5, 64, 4
+    wi = rng.integers(-8, 9, (R, K)); xi = rng.integers(-8, 9, (T, K))
+    w, x = _fp8_bits(wi.astype(float)), _fp8_bits(xi.astype(float))
+    vals, idx = oracle.prune_pack_fp8(w, 2, 4)
+    mask = brute_force_kept(wi.astype(np.float64).reshape(-1, 4), 2).reshape(R, K)
+    y = oracle.spmm_ref_fp8(vals, idx, K, 2, 4, x)
+    for r in range(R):
+        for t in range(T):
+            assert y[r, t] == sum(int(wi[r, k]) * int(xi[t, k]) for k in range(K) if mask[r, k])
+    perm = rng.permutation(K)
+    yp = oracle.spmm_ref_fp8(vals, idx, K, 2, 4, x, perm=perm)
+    assert np.array_equal(yp, oracle.spmm_ref_fp8(vals, idx, K, 2, 4, x[:, perm]))
+
+
 ALL_CHECKS = [check_worked_row, check_group_cost, check_exactly_n_ascending, check_brute_force,
               check_exhaustive_ties, check_round_trip, check_bitstream, check_k8_walkthrough,
               check_identity_gemm, check_integer_gemm_brute_force, check_dense_case,
               check_permutation, check_i8_worked_row, check_i8_group_cost, check_i8_brute_force,
-              check_i8_round_trip_and_gemm, check_i8_permutation]
+              check_i8_round_trip_and_gemm, check_i8_permutation, check_fp8_decode,
+              check_fp8_worked_row_and_brute_force, check_fp8_integer_gemm]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
