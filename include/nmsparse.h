@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   NM_OK = 0,
   NM_ERR_NULL = 1,         /* a required pointer is NULL                          */
-  NM_ERR_SHAPE = 2,        /* R, K or T out of range; K % 16 (K % 32 for int8) or K % M non-zero */
+  NM_ERR_SHAPE = 2,        /* R, K or T out of range; K % 16 (K % 32 for 8-bit W) or K % M non-zero */
   NM_ERR_UNSUPPORTED = 3,  /* (n, m) pair or dtype combination not provided       */
   NM_ERR_STRIDE = 4,       /* leading dimension smaller than the row width        */
   NM_ERR_ALIAS = 5,        /* output overlaps an input                            */
@@ -50,7 +50,7 @@ typedef enum {
   NM_ERR_ALIGN = 7         /* pointer or leading dimension misaligned (see below) */
 } nm_status;
 
-typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4 } nm_dtype;
+typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP8 = 5 } nm_dtype;
 
 /*
  * INT8 weights (NM_I8).  The 2:4 pattern is also offered for 8-bit integer
@@ -65,9 +65,21 @@ typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4 } nm_d
  * (out_dtype NM_I32, the only one), the exact integer product; leading
  * dimensions of int8 matrices (ldw, ldx) must be multiples of 16.
  * nm_spmm_perm does not take NM_I8 (NM_ERR_UNSUPPORTED).
+ *
+ * FP8 weights (NM_FP8, OCP E4M3: sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, S.1111.111 is NaN).  The pages name 16-bit
+ * and INT8 2:4 types only; an 8-bit float takes the one-byte layout and every
+ * rule of NM_I8 above (2:4 only, K % 32, ldw and ldx multiples of 16, no
+ * nm_spmm_perm), with these differences: magnitude is compared on the stored
+ * pattern with the sign bit cleared (bits & 0x7F, so +x and -x tie, equal keys
+ * going to the lower position), act is E4M3 and Y is fp32 (out_dtype NM_F32,
+ * the only one).  The hardware's fp8 sparse multiply-accumulate sums with
+ * somewhat less than fp32 precision (relative error near 1e-4 of the result
+ * at K = 2048); NaN inputs give NaN outputs.
  */
 
-/* Version of this ABI (major * 100 + minor): 101 adds NM_I8 / NM_I32. */
+/* Version of this ABI (major * 100 + minor): 101 adds NM_I8 / NM_I32,
+ * 102 adds NM_FP8. */
 int nm_version(void);
 
 /* Short fixed text for a status code (never NULL). */
@@ -78,7 +90,7 @@ const char* nm_last_error(void);
 
 /*
  * Sizes of the packed format.  Pure host arithmetic, no device access.
- *   values_bytes  = R * S * 2            (values [R, S], same type as W; R * S for NM_I8)
+ *   values_bytes  = R * S * 2            (values [R, S], same type as W; R * S for 8-bit W)
  *   idx_row_words = ceil(S * b / 32)     (uint32 words per row)
  *   idx_bytes     = R * idx_row_words * 4
  * Any output pointer may be NULL.  Same validation as nm_compress.
@@ -91,7 +103,7 @@ const char* nm_last_error(void);
  *                       of survivor s = g*N + j sits in bits [s*b, s*b + b);
  *                       stream bit i is bit (i % 32) of word (i / 32); words
  *                       are little-endian uint32, the tail is zero-padded.
- * With 2:4, one group of four 16-bit weights costs 2*16 + 2*2 = 36 bits (int8: 20)
+ * With 2:4, one group of four 16-bit weights costs 2*16 + 2*2 = 36 bits (8-bit: 20)
  * (+ per-row padding to a whole word when S*b is not a multiple of 32).
  */
 nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype,
@@ -100,7 +112,7 @@ nm_status nm_packed_sizes(int64_t R, int64_t K, int n, int m, int dtype,
 /*
  * Prune + pack (magnitude top-N of every M along the rows of W).
  *   W       device, [R, K] row-major, leading dimension ldw >= K (elements),
- *           dtype NM_F16, NM_BF16 or NM_I8 (see above).
+ *           dtype NM_F16, NM_BF16, NM_I8 or NM_FP8 (see above).
  *   values  device, [R, S] contiguous, same dtype (written).
  *   idx     device, [R, idx_row_words] uint32 contiguous (written, padding
  *           bits zero).
@@ -123,13 +135,14 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
 
 /*
  * Sparse GEMM  Y = W_nm X,  X = act^T.
- *   values, idx  packed W (see nm_packed_sizes), dtype NM_F16, NM_BF16 or NM_I8.
+ *   values, idx  packed W (see nm_packed_sizes), dtype NM_F16, NM_BF16, NM_I8 or
+ *                NM_FP8.
  *   act          device, [T, K] row-major (each token's K features contiguous),
  *                leading dimension ldx >= K, same dtype as values.
  *   Y            device, [T, R] row-major, leading dimension ldy >= R, i.e. the
  *                transpose of Y = W_nm X (the layout of a linear layer's output);
  *                out_dtype NM_F32 (default) or the input dtype (RNE rounded);
- *                NM_I32 for NM_I8 (exact).
+ *                NM_I32 for NM_I8 (exact); NM_F32 only for NM_FP8.
  *   Y[t, r] = sum_k W_nm[r, k] * act[t, k], products and sums in fp32.
  * Shapes: R >= 1, T >= 0 (T == 0 enqueues nothing), K >= 16, K % 16 == 0,
  * K % m == 0.  Alignment: every pointer 16-byte aligned, ldx % 8 == 0 (ldy
@@ -176,7 +189,7 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
  *      T >= 256, R >= 256)
  *   6  all-LDS direct-load kernel with 128 x 64 tiles (1:4 and 1:8;
  *      K % 256 == 0, T >= 64, R >= 128)
- * For int8 weights there are two: the LDS-staged kernel (whole 256 x 128 tiles,
+ * For 8-bit weights there are two: the LDS-staged kernel (whole 256 x 128 tiles,
  * K % 128 == 0) and, for variant 1 or any other shape, a kernel that loads
  * its operands straight into registers.
  * A forced family that does not take the shape falls back to the choice by

@@ -25,6 +25,7 @@ import numpy as np
 F16 = "f16"
 BF16 = "bf16"
 I8 = "i8"
+F8 = "f8e4m3"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -79,6 +80,15 @@ def normal_i8(shape, scale: float, workload_id: int, tensor_id: int, variant: in
     return np.clip(np.rint(x), -128, 127).astype(np.int8)
 
 
+def normal_fp8(shape, scale: float, workload_id: int, tensor_id: int, variant: int = 0) -> np.ndarray:
+    """uint8 OCP E4M3 bit patterns of N(0, 1) * scale, saturated to +-448 and
+    rounded to nearest even by torch's float8_e4m3fn conversion."""
+    import torch
+    rng = rng_for(workload_id, tensor_id, variant)
+    x = np.clip(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(scale), -448.0, 448.0)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def random_permutation(k: int, workload_id: int, variant: int = 0) -> np.ndarray:
     return rng_for(workload_id, 2, variant).permutation(int(k)).astype(np.int32)
 
@@ -101,12 +111,16 @@ class Workload:
     def weights(self) -> np.ndarray:
         if self.dtype == I8:
             return normal_i8((self.R, self.K), self.sigma_w, self.wid, 0)
+        if self.dtype == F8:
+            return normal_fp8((self.R, self.K), self.sigma_w, self.wid, 0)
         return normal_half((self.R, self.K), self.sigma_w, self.dtype, self.wid, 0)
 
     def activations(self, T: int | None = None) -> np.ndarray:
         T = self.Ts[0] if T is None else T
         if self.dtype == I8:
             return normal_i8((T, self.K), self.sigma_x, self.wid, 1, T)
+        if self.dtype == F8:
+            return normal_fp8((T, self.K), self.sigma_x, self.wid, 1, T)
         return normal_half((T, self.K), self.sigma_x, self.dtype, self.wid, 1, T)
 
     def permutation(self) -> np.ndarray | None:
@@ -132,4 +146,7 @@ WORKLOADS = {
     # prefill projection's shape; weights and activations quantised normal data
     6: Workload(6, "int8-2of4-prefill", 4096, 4096, (2048,), ((2, 4),), I8, 32.0, 32.0,
                 note="INT8 2:4, int32 output"),
+    # the same shape in OCP FP8 E4M3 (an 8-bit float in the one-byte layout)
+    7: Workload(7, "fp8-e4m3-2of4-prefill", 4096, 4096, (2048,), ((2, 4),), F8, 1.0, 1.0,
+                note="FP8 E4M3 2:4, fp32 output"),
 }

@@ -14,12 +14,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NMError", "lib", "lib_path",
+__all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NM_FP8", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
            "nm_check_perm", "nm_set_variant", "PATTERNS"]
 
 NM_OK = 0
-NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32 = 0, 1, 2, 3, 4
+NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
 PATTERNS = ((2, 4), (1, 4), (1, 8))
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,13 +94,15 @@ def _dtype_code(t) -> int:
         return NM_BF16
     if t.dtype == torch.int8:
         return NM_I8
-    raise TypeError(f"expected float16, bfloat16 or int8, got {t.dtype}")
+    if t.dtype == torch.float8_e4m3fn:
+        return NM_FP8
+    raise TypeError(f"expected float16, bfloat16, int8 or float8_e4m3fn, got {t.dtype}")
 
 
 def _torch_dtype(code: int):
     torch = _torch()
     return {NM_F16: torch.float16, NM_BF16: torch.bfloat16, NM_F32: torch.float32,
-            NM_I8: torch.int8, NM_I32: torch.int32}[code]
+            NM_I8: torch.int8, NM_I32: torch.int32, NM_FP8: torch.float8_e4m3fn}[code]
 
 
 def _stream_ptr(device) -> int:
@@ -128,7 +130,7 @@ def nm_packed_sizes(R: int, K: int, n: int, m: int, dtype: int = NM_F16):
 
 
 def nm_compress(W, n: int = 2, m: int = 4, values=None, idx=None):
-    """Prune W [R, K] (fp16/bf16, or int8 for 2:4; device) to n:m and pack.
+    """Prune W [R, K] (fp16/bf16, or int8 / float8_e4m3fn for 2:4; device) to n:m and pack.
     Returns (values [R, S], idx [R, words])."""
     torch = _torch()
     _require_cuda(W)
@@ -182,6 +184,10 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
         if out_dtype not in (None, torch.int32):
             raise TypeError("int8 weights give an int32 output")
         od = NM_I32
+    elif dt == NM_FP8:  # fp32 sums of the E4M3 products
+        if out_dtype not in (None, torch.float32):
+            raise TypeError("float8_e4m3fn weights give a float32 output")
+        od = NM_F32
     else:
         od = NM_F32 if (out_dtype is None or out_dtype == torch.float32) else _dtype_code(
             torch.empty(0, dtype=out_dtype))

@@ -40,23 +40,26 @@ nm_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// One-byte weight types (INT8, FP8 E4M3).
+bool byte_type(int dtype) { return dtype == NM_I8 || dtype == NM_FP8; }
+
 bool supported_pattern(int n, int m) {
   return (n == 2 && m == 4) || (n == 1 && m == 4) || (n == 1 && m == 8);
 }
 
 // Checks shared by every entry point that names a packed weight.
 nm_status check_format(int64_t R, int64_t K, int n, int m, int dtype) {
-  if (dtype != NM_F16 && dtype != NM_BF16 && dtype != NM_I8)
-    return fail(NM_ERR_UNSUPPORTED, "weight dtype %d is not NM_F16, NM_BF16 or NM_I8", dtype);
+  if (dtype != NM_F16 && dtype != NM_BF16 && dtype != NM_I8 && dtype != NM_FP8)
+    return fail(NM_ERR_UNSUPPORTED, "weight dtype %d is not NM_F16, NM_BF16, NM_I8 or NM_FP8", dtype);
   if (!supported_pattern(n, m))
     return fail(NM_ERR_UNSUPPORTED, "pattern %d:%d is not one of 2:4, 1:4, 1:8", n, m);
-  if (dtype == NM_I8 && !(n == 2 && m == 4))
-    return fail(NM_ERR_UNSUPPORTED, "int8 weights take the 2:4 pattern only");
+  if (byte_type(dtype) && !(n == 2 && m == 4))
+    return fail(NM_ERR_UNSUPPORTED, "8-bit weights take the 2:4 pattern only");
   if (R < 0 || R > kMaxRT) return fail(NM_ERR_SHAPE, "R = %lld out of range", (long long)R);
   if (K < 16 || K > kMaxK) return fail(NM_ERR_SHAPE, "K = %lld out of range [16, 2^24]", (long long)K);
   if (K % 16) return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
-  if (dtype == NM_I8 && K % 32)
-    return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of 32 (int8)", (long long)K);
+  if (byte_type(dtype) && K % 32)
+    return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of 32 (8-bit weights)", (long long)K);
   if (K % m) return fail(NM_ERR_SHAPE, "K = %lld is not a multiple of m = %d", (long long)K, m);
   if (R * K > kMaxElems) return fail(NM_ERR_SHAPE, "R*K too large");
   return NM_OK;
@@ -68,10 +71,10 @@ struct Sizes {
 };
 
 // Bytes per element of a storage type.
-size_t elt_bytes(int dtype) { return dtype == NM_I8 ? 1 : dtype == NM_F32 || dtype == NM_I32 ? 4 : 2; }
+size_t elt_bytes(int dtype) { return byte_type(dtype) ? 1 : dtype == NM_F32 || dtype == NM_I32 ? 4 : 2; }
 
 // Leading dimensions (elements) keep every row 16-byte aligned.
-int64_t ld_quantum(int dtype) { return dtype == NM_I8 ? 16 : 8; }
+int64_t ld_quantum(int dtype) { return byte_type(dtype) ? 16 : 8; }
 
 Sizes sizes_of(int64_t R, int64_t K, int n, int m, int dtype) {
   Sizes z;
@@ -105,9 +108,12 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
   if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
-  if (dtype == NM_I8) {
-    if (out_dtype != NM_I32) return fail(NM_ERR_UNSUPPORTED, "int8 weights give an NM_I32 output");
-    if (want_perm) return fail(NM_ERR_UNSUPPORTED, "nm_spmm_perm does not take int8 weights");
+  if (dtype == NM_I8 || dtype == NM_FP8) {
+    const int want = dtype == NM_I8 ? NM_I32 : NM_F32;
+    if (out_dtype != want)
+      return fail(NM_ERR_UNSUPPORTED, "%s weights give an %s output", dtype == NM_I8 ? "int8" : "fp8",
+                  dtype == NM_I8 ? "NM_I32" : "NM_F32");
+    if (want_perm) return fail(NM_ERR_UNSUPPORTED, "nm_spmm_perm does not take 8-bit weights");
   } else if (out_dtype != NM_F32 && out_dtype != dtype) {
     return fail(NM_ERR_UNSUPPORTED, "out_dtype %d must be NM_F32 or the input dtype", out_dtype);
   }
@@ -197,7 +203,7 @@ hipError_t ensure_lds_limit(const void* kern, int bytes) {
 
 extern "C" {
 
-int nm_version(void) { return 101; }
+int nm_version(void) { return 102; }
 
 const char* nm_status_string(int status) {
   switch (status) {
@@ -244,10 +250,10 @@ nm_status nm_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtyp
   if (overlaps(values, z.values_bytes, W, wbytes) || overlaps(idx, z.idx_bytes, W, wbytes) ||
       overlaps(values, z.values_bytes, idx, z.idx_bytes))
     return fail(NM_ERR_ALIAS, "outputs overlap each other or W");
-  if (dtype == NM_I8)
+  if (byte_type(dtype))
     return hip_status(nm::launch_prune_pack_i8(static_cast<const uint8_t*>(W), R, K, ldw,
                                                static_cast<uint8_t*>(values), idx, z.words,
-                                               static_cast<hipStream_t>(stream)),
+                                               dtype == NM_FP8, static_cast<hipStream_t>(stream)),
                       "nm_compress launch");
   return hip_status(nm::launch_prune_pack(static_cast<const uint16_t*>(W), R, K, ldw, n, m,
                                           static_cast<uint16_t*>(values), idx, z.words,
@@ -272,7 +278,7 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
   size_t wbytes = extent(R, K, ldw, elt_bytes(dtype));
   if (overlaps(W_out, wbytes, values, z.values_bytes) || overlaps(W_out, wbytes, idx, z.idx_bytes))
     return fail(NM_ERR_ALIAS, "W_out overlaps an input");
-  if (dtype == NM_I8)
+  if (byte_type(dtype))
     return hip_status(nm::launch_decompress_i8(static_cast<const uint8_t*>(values), idx, R, K, z.words,
                                                static_cast<uint8_t*>(W_out), ldw,
                                                static_cast<hipStream_t>(stream)),

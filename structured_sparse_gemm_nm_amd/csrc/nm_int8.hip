@@ -29,17 +29,37 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One-byte element types: F8 = false int8 (exact int32 product), true OCP FP8
+// E4M3 (v_smfmac_f32_16x16x128_fp8_fp8, fp32 accumulators; the same operand
+// layout, found the same way).  Magnitude key: |w| for int8, bits & 0x7F for
+// E4M3 (the sign bit dropped; finite E4M3 values order by their low 7 bits).
+template <bool F8>
+using acc8_t = std::conditional_t<F8, f32x4, i32x4>;
+
+template <bool F8>
+__device__ inline acc8_t<F8> smfmac8(const i32x4& a, const i32x8& b, const acc8_t<F8>& c, uint32_t idx) {
+  if constexpr (F8) {
+    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c, int(idx), 0, 0);
+  } else {
+    return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c, int(idx), 0, 0);
+  }
+}
 
 // One group of four int8 weights (byte p = position p): the two kept
 // positions, ascending, with their bytes.  Composite keys put |w| above the
 // tie-break (the lower position wins), so they are distinct and a position is
 // kept when fewer than two keys exceed its own.
+template <bool F8>
 __device__ inline void top2_of_4(uint32_t g, uint32_t& p0, uint32_t& p1, uint32_t& v0, uint32_t& v1) {
   uint32_t key[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int w = int(int8_t(uint8_t(g >> (8 * p))));
-    key[p] = (uint32_t(w < 0 ? -w : w) << 2) | uint32_t(3 - p);
+    const uint32_t byte = (g >> (8 * p)) & 0xFFu;
+    const int w = int(int8_t(uint8_t(byte)));
+    const uint32_t mag = F8 ? (byte & 0x7Fu) : uint32_t(w < 0 ? -w : w);
+    key[p] = (mag << 2) | uint32_t(3 - p);
   }
   uint32_t kept = 0;
 #pragma unroll
@@ -57,6 +77,7 @@ __device__ inline void top2_of_4(uint32_t g, uint32_t& p0, uint32_t& p1, uint32_
 
 // One thread per 16-byte chunk of a row (four groups): 8 value bytes and the
 // chunk's 16 index bits, which sit at byte 2c of the row's stream.
+template <bool F8>
 __global__ __launch_bounds__(256) void prune_pack_i8_kernel(const uint8_t* __restrict__ W, int64_t R,
                                                             int64_t K, int64_t ldw,
                                                             uint8_t* __restrict__ values,
@@ -71,7 +92,7 @@ __global__ __launch_bounds__(256) void prune_pack_i8_kernel(const uint8_t* __res
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t p0, p1, v0, v1;
-    top2_of_4(g4[g], p0, p1, v0, v1);
+    top2_of_4<F8>(g4[g], p0, p1, v0, v1);
     v[g >> 1] |= (v0 | (v1 << 8)) << (16 * (g & 1));
     bits |= (p0 | (p1 << 2)) << (4 * g);
   }
@@ -108,11 +129,15 @@ __global__ __launch_bounds__(256) void decompress_i8_kernel(const uint8_t* __res
 // a multiple of 32, so a range is wholly in or out) loads zeros.
 constexpr int kBR8 = 128, kBT8 = 128;
 
+template <bool F8>
 __global__ __launch_bounds__(256) void spmm_i8_kernel(const uint8_t* __restrict__ values,
                                                       const uint32_t* __restrict__ idx, int R, int K,
                                                       int words, const uint8_t* __restrict__ act, int T,
-                                                      int64_t ldx, int32_t* __restrict__ Y, int64_t ldy,
+                                                      int64_t ldx, acc8_t<F8>* __restrict__ Yv, int64_t ldy,
                                                       int tilesT) {
+  using acc_t = acc8_t<F8>;
+  using out_t = std::conditional_t<F8, float, int32_t>;
+  out_t* Y = reinterpret_cast<out_t*>(Yv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lq = lane >> 4;
   const int R0 = (int(blockIdx.x) / tilesT) * kBR8 + (wave >> 1) * 64;
@@ -146,17 +171,17 @@ __global__ __launch_bounds__(256) void spmm_i8_kernel(const uint8_t* __restrict_
     }
   };
 
-  i32x4 acc[4][4];
+  acc_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
   auto mma = [&](const i32x4 (&a)[4], const uint32_t (&x)[4], const i32x8 (&b)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[i], b[j], acc[i][j], int(x[i]), 0, 0);
+        acc[i][j] = smfmac8<F8>(a[i], b[j], acc[i][j], x[i]);
   };
 
   i32x4 a0[4], a1[4];
@@ -180,9 +205,9 @@ __global__ __launch_bounds__(256) void spmm_i8_kernel(const uint8_t* __restrict_
     for (int j = 0; j < 4; ++j) {
       const int t = T0 + j * 16 + li;
       if (t >= T || r >= R) continue;
-      int32_t* y = Y + int64_t(t) * ldy + r;
+      out_t* y = Y + int64_t(t) * ldy + r;
       if (vec_ok && r + 3 < R) {
-        *reinterpret_cast<i32x4*>(y) = acc[i][j];
+        *reinterpret_cast<acc_t*>(y) = acc[i][j];
       } else {
         for (int e = 0; e < 4 && r + e < R; ++e) y[e] = acc[i][j][e];
       }
@@ -222,10 +247,11 @@ __device__ inline void wait_vmcnt8() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+template <bool F8>
 __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __restrict__ values,
                                                              const uint32_t* __restrict__ idx, int K,
                                                              int words, const uint8_t* __restrict__ act,
-                                                             int64_t ldx, int32_t* __restrict__ Y,
+                                                             int64_t ldx, acc8_t<F8>* __restrict__ Y,
                                                              int64_t ldy, int tilesT) {
   extern __shared__ __align__(16) unsigned char smem8[];
   unsigned char* bbuf = smem8;                  // [kNS8][kStage8] activations
@@ -308,13 +334,13 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
     asm volatile("" ::: "memory");
   };
 
-  i32x4 acc[8][4];
+  using acc_t = acc8_t<F8>;
+  acc_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-  // fragments of a step from its ring slot into registers
   // fragments of step t (ring slot SL = t & 3, index block t / 4)
   auto read_frags = [&](int t, auto slot_c, i32x4 (&a)[8], i32x8 (&b)[4], uint32_t (&x)[8]) {
     constexpr int SL = decltype(slot_c)::value;
@@ -355,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(ca[i], cb[j], acc[i][j], int(cx[i]), 0, 0);
+        acc[i][j] = smfmac8<F8>(ca[i], cb[j], acc[i][j], cx[i]);
   };
 
   using std::integral_constant;
@@ -389,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = T0 + wt * 64 + j * 16 + li;
-      *reinterpret_cast<i32x4*>(Y + int64_t(t) * ldy + r) = acc[i][j];
+      Y[(int64_t(t) * ldy + r) >> 2] = acc[i][j];
     }
   }
 }
@@ -397,13 +423,17 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
 }  // namespace
 
 hipError_t launch_prune_pack_i8(const uint8_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* values,
-                                uint32_t* idx, int64_t idx_row_words, hipStream_t s) {
+                                uint32_t* idx, int64_t idx_row_words, bool f8, hipStream_t s) {
   const int64_t chunks = R * (K >> 4);
   if (chunks <= 0) return hipSuccess;
   const int64_t blocks = (chunks + 255) / 256;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prune_pack_i8_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, W, R, K, ldw, values,
-                     idx, idx_row_words);
+  if (f8)
+    hipLaunchKernelGGL(prune_pack_i8_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, W, R, K, ldw,
+                       values, idx, idx_row_words);
+  else
+    hipLaunchKernelGGL(prune_pack_i8_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, W, R, K, ldw,
+                       values, idx, idx_row_words);
   return hipGetLastError();
 }
 
@@ -418,7 +448,8 @@ hipError_t launch_decompress_i8(const uint8_t* values, const uint32_t* idx, int6
   return hipGetLastError();
 }
 
-hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s) {
+template <bool F8>
+hipError_t launch_spmm_b8(const SpmmArgs& a, hipStream_t s) {
   // whole tiles only, 32-bit per-lane offsets, 16-byte output rows
   const bool lds = a.R % kBR8L == 0 && a.T % kBT8L == 0 && a.K % 128 == 0 && (a.ldy & 3) == 0 &&
                    int64_t(kBT8L) * a.ldx < 0x7FFFFFFF && int64_t(kBR8L) * (a.K >> 1) < 0x7FFFFFFF &&
@@ -427,11 +458,12 @@ hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s) {
   if (lds) {
     const int64_t tiles = (a.R / kBR8L) * (a.T / kBT8L);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const void* kern = reinterpret_cast<const void*>(spmm_i8_lds_kernel);
+    auto kfn = spmm_i8_lds_kernel<F8>;
+    const void* kern = reinterpret_cast<const void*>(kfn);
     if (hipError_t e = ensure_lds_limit(kern, kLds8); e != hipSuccess) return e;
-    hipLaunchKernelGGL(spmm_i8_lds_kernel, dim3(unsigned(tiles)), dim3(256), kLds8, s,
+    hipLaunchKernelGGL(kfn, dim3(unsigned(tiles)), dim3(256), kLds8, s,
                        reinterpret_cast<const uint8_t*>(a.values), a.idx, int(a.K), int(a.idx_row_words),
-                       reinterpret_cast<const uint8_t*>(a.act), a.ldx, static_cast<int32_t*>(a.Y), a.ldy,
+                       reinterpret_cast<const uint8_t*>(a.act), a.ldx, static_cast<acc8_t<F8>*>(a.Y), a.ldy,
                        int(a.T / kBT8L));
     return hipGetLastError();
   }
@@ -439,11 +471,15 @@ hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s) {
   const int64_t tilesT = (a.T + kBT8 - 1) / kBT8;
   if (tilesR * tilesT > 0x7FFFFFFF || a.R > 0x7FFFFFFF || a.T > 0x7FFFFFFF || a.K > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(spmm_i8_kernel, dim3(unsigned(tilesR * tilesT)), dim3(256), 0, s,
+  hipLaunchKernelGGL(spmm_i8_kernel<F8>, dim3(unsigned(tilesR * tilesT)), dim3(256), 0, s,
                      reinterpret_cast<const uint8_t*>(a.values), a.idx, int(a.R), int(a.K),
                      int(a.idx_row_words), reinterpret_cast<const uint8_t*>(a.act), int(a.T), a.ldx,
-                     static_cast<int32_t*>(a.Y), a.ldy, int(tilesT));
+                     static_cast<acc8_t<F8>*>(a.Y), a.ldy, int(tilesT));
   return hipGetLastError();
+}
+
+hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s) {
+  return a.dtype == NM_FP8 ? launch_spmm_b8<true>(a, s) : launch_spmm_b8<false>(a, s);
 }
 
 }  // namespace nm

@@ -22,10 +22,11 @@ hipError_t launch_decompress(const uint16_t* values, const uint32_t* idx, int64_
                              int n, int m, int64_t idx_row_words, uint16_t* W, int64_t ldw,
                              hipStream_t s);
 
-// INT8 2:4 (nm_int8.hip): prune + pack, decompress (leading dimensions in
-// bytes, multiples of 16; K % 32 == 0).
+// 8-bit 2:4 (nm_int8.hip): prune + pack, decompress (leading dimensions in
+// bytes, multiples of 16; K % 32 == 0).  f8: FP8 E4M3 keys (bits & 0x7F)
+// instead of int8 |w|; decompress moves bytes and serves both.
 hipError_t launch_prune_pack_i8(const uint8_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* values,
-                                uint32_t* idx, int64_t idx_row_words, hipStream_t s);
+                                uint32_t* idx, int64_t idx_row_words, bool f8, hipStream_t s);
 hipError_t launch_decompress_i8(const uint8_t* values, const uint32_t* idx, int64_t R, int64_t K,
                                 int64_t idx_row_words, uint8_t* W, int64_t ldw, hipStream_t s);
 
@@ -34,7 +35,7 @@ struct SpmmArgs {
   const uint32_t* idx;
   int64_t R, K;
   int n, m;
-  int dtype;             // NM_F16 / NM_BF16 / NM_I8 (values and act then hold bytes)
+  int dtype;             // NM_F16 / NM_BF16 / NM_I8 / NM_FP8 (the last two: bytes)
   const uint16_t* act;   // [T, K], ldx (elements)
   int64_t T, ldx;
   const int32_t* perm;   // nullptr: identity
@@ -46,7 +47,7 @@ struct SpmmArgs {
 };
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
-// INT8 2:4 GEMM (nm_int8.hip): Y int32.
+// 8-bit 2:4 GEMM (nm_int8.hip): Y int32 for NM_I8, fp32 for NM_FP8.
 hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s);
 
 // Pipelined large-tile kernel (nm_spmm_pipe.hip) and the shapes it takes.

@@ -415,7 +415,7 @@ hipError_t launch_generic(const SpmmArgs& a, hipStream_t s) {
 // Kernel choice.  variant 0 picks by shape; 1..5 force one kernel family when
 // the shape allows it (ablations, tests), else fall back to the choice by shape.
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
-  if (a.dtype == NM_I8) return launch_spmm_i8(a, s);  // one INT8 kernel for every shape
+  if (a.dtype == NM_I8 || a.dtype == NM_FP8) return launch_spmm_i8(a, s);  // 8-bit weights
   switch (a.variant) {
     case NM_VARIANT_GENERIC: return launch_generic(a, s);
     case NM_VARIANT_PIPE:

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
     assert {"nm_compress", "nm_spmm", "nm_spmm_perm", "nm_decompress", "nm_packed_sizes"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
-    assert L.nm_version() == 101
+    assert L.nm_version() == 102
 
 
 def test_status_codes_match_header():
@@ -165,6 +165,32 @@ def test_int8_sizes_and_rules():
     assert st_spmm(dt=nm.NM_I32, od=nm.NM_I32) == 3
     # Y (int32) overlapping act (int8)
     assert st_spmm(dt=nm.NM_I8, od=nm.NM_I32, Y=FAKE * 3 + 16) == 5
+
+
+def test_fp8_sizes_and_rules():
+    # E4M3 takes the one-byte layout and every 8-bit rule; its output is fp32
+    assert header_enum("NM_FP8") == nm.NM_FP8 == 5
+    assert nm.nm_packed_sizes(4096, 4096, 2, 4, nm.NM_FP8) == nm.nm_packed_sizes(4096, 4096, 2, 4, nm.NM_I8)
+    L = nm.lib()
+    st = lambda K, n=2, m=4: L.nm_packed_sizes(8, K, n, m, nm.NM_FP8, None, None, None)
+    assert st(64) == 0 and st(48) == 2 and st(64, 1, 4) == 3
+    assert st_compress(dt=nm.NM_FP8, ldw=72) == 7
+    assert st_compress(dt=nm.NM_FP8, K=48, ldw=48) == 2
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_I32) == 3
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_FP8) == 3
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_F32, perm=FAKE * 5) == 3
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_F32, ldx=72) == 7
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_F32, K=96, ldx=96, values=None) == 1
+    assert st_spmm(dt=nm.NM_FP8, od=nm.NM_F32, Y=FAKE * 3 + 16) == 5
+
+
+def test_fp8_inputs_are_e4m3_patterns():
+    import nm_inputs
+    b = nm_inputs.normal_fp8((64, 256), 1.0, 7, 0)
+    assert b.dtype == np.uint8 and b.shape == (64, 256)
+    v = O.fp8_to_f64(b)
+    assert np.all(np.isfinite(v)) and np.abs(v).max() <= 448.0
+    assert np.array_equal(b, nm_inputs.normal_fp8((64, 256), 1.0, 7, 0))  # seeded
 
 
 def test_decompress_and_misc_errors():

@@ -531,3 +531,110 @@ def test_i8_workload_sampled():
     rows = np.sort(np.random.default_rng(5).choice(wl.R, 48, replace=False))
     yref = O.spmm_ref_i8(ref_vals[rows], ref_idx[rows], wl.K, 2, 4, act)
     assert np.array_equal(y.cpu().numpy()[:, rows].T.astype(np.int64), yref)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) 2:4: packed bytes bit-exact, Y against the exact product
+# ---------------------------------------------------------------------------
+
+def _f8(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).cuda().view(torch.float8_e4m3fn)
+
+
+def _abs_sum_bound(y, yref, ref_vals, ref_idx, K, act, frac=2.0 ** -12):
+    wa = np.abs(O.fp8_to_f64(O.decompress_fp8(ref_vals, ref_idx, K, 2, 4)))
+    xa = np.abs(O.fp8_to_f64(act)).T
+    scale = wa @ xa  # [R, T]
+    err = np.abs(y.float().cpu().numpy().astype(np.float64).T - yref)
+    worst = float(np.max(err / np.maximum(scale, 1e-30)))
+    log(f"fp8 worst |error| / sum|products| = {worst:.3e}")
+    assert worst <= frac, f"error {worst:.3e} of sum|products| > {frac:.3e}"
+
+
+def _f8_case(w, act, K, cross_check=True):
+    vals, idx = nm.nm_compress(_f8(w), 2, 4)
+    dense = nm.nm_decompress(vals, idx, K, 2, 4)
+    y = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack_fp8(w, 2, 4)
+    assert vals.dtype == torch.float8_e4m3fn and y.dtype == torch.float32
+    assert np.array_equal(vals.view(torch.uint8).cpu().numpy(), ref_vals)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    assert np.array_equal(dense.view(torch.uint8).cpu().numpy(), O.decompress_fp8(ref_vals, ref_idx, K, 2, 4))
+    yref = O.spmm_ref_fp8(ref_vals, ref_idx, K, 2, 4, act)
+    # the stated 1e-2 bound on the floored relative error, and each element's
+    # error against the sum of |products| (the hardware's fp8 accumulation is
+    # coarser than fp32 where the sum cancels; a wrong index or operand gives
+    # errors of the order of that sum)
+    assert_close(y, yref, tol=1e-2)
+    _abs_sum_bound(y, yref, ref_vals, ref_idx, K, act)
+    if cross_check:
+        try:  # the register-operand kernel: the same MFMA sequence per tile
+            nm.nm_set_variant(1)
+            y1 = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4)
+        finally:
+            nm.nm_set_variant(0)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y)
+    return y, yref
+
+
+@pytest.mark.parametrize("R,K,T", [(1, 32, 1), (7, 96, 5), (130, 160, 129), (300, 4128, 70),
+                                   (257, 2048, 300),
+                                   # the LDS-staged kernel: 1, 2, 3, 4 and 9 K steps
+                                   (256, 128, 128), (256, 256, 256), (512, 384, 128),
+                                   (256, 512, 384), (768, 1152, 256)])
+def test_fp8_pack_and_product(R, K, T):
+    log(f"fp8 2:4 R={R} K={K} T={T}")
+    w = nm_inputs.normal_fp8((R, K), 1.0, 71, 0, R + K + T)
+    act = nm_inputs.normal_fp8((T, K), 1.0, 71, 1, R + K + T)
+    _f8_case(w, act, K)
+
+
+def test_fp8_extremes():
+    log("fp8 2:4 extremes")
+    R, K, T = 64, 4096, 32
+    # every weight -448 and every activation 448: positions 0 and 1 kept, each
+    # product -200704 = -49 * 2^12, sums -49 * 2^12 * K/2, exact in fp32
+    w = np.full((R, K), 0xFE, np.uint8)   # -448
+    act = np.full((T, K), 0x7E, np.uint8)  # 448
+    vals, idx = nm.nm_compress(_f8(w), 2, 4)
+    y = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4)
+    torch.cuda.synchronize()
+    assert np.all(idx.cpu().numpy().view(np.uint32) == 0x44444444)
+    assert np.all(y.cpu().numpy() == -200704.0 * (K // 2))
+    # +x / -x tie (lower position wins), zeros of both signs, the smallest subnormal
+    pat = np.array([0x38, 0xB8, 0x38, 0xB8, 0x00, 0x80, 0x00, 0x80, 0x01, 0x81, 0x00, 0x02], np.uint8)
+    w2 = np.ascontiguousarray(np.tile(pat, (R, K // 12 + 1))[:, :K])
+    vals2, idx2 = nm.nm_compress(_f8(w2), 2, 4)
+    rv, ri = O.prune_pack_fp8(w2, 2, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(vals2.view(torch.uint8).cpu().numpy(), rv)
+    assert np.array_equal(idx2.cpu().numpy().view(np.uint32), ri)
+
+
+def test_fp8_workload_sampled():
+    wl = nm_inputs.WORKLOADS[7]
+    T = wl.Ts[0]
+    log(f"fp8 workload {wl.R}x{wl.K}x{T}")
+    w = wl.weights()
+    act = wl.activations(T)
+    vals, idx = nm.nm_compress(_f8(w), 2, 4)
+    y = nm.nm_spmm(vals, idx, _f8(act), wl.K, 2, 4)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack_fp8(w, 2, 4)
+    assert np.array_equal(vals.view(torch.uint8).cpu().numpy(), ref_vals)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    rows = np.sort(np.random.default_rng(7).choice(wl.R, 48, replace=False))
+    yref = O.spmm_ref_fp8(ref_vals[rows], ref_idx[rows], wl.K, 2, 4, act)
+    assert_close(y[:, rows], yref, tol=1e-2)
+    _abs_sum_bound(y[:, rows], yref, ref_vals[rows], ref_idx[rows], wl.K, act)
+
+
+def test_fp8_small_magnitudes():
+    # scale 2^-7: most inputs are E4M3 subnormals (below 2^-6)
+    log("fp8 2:4 subnormal inputs")
+    R, K, T = 256, 512, 128
+    w = nm_inputs.normal_fp8((R, K), 2.0 ** -7, 72, 0)
+    act = nm_inputs.normal_fp8((T, K), 1.0, 72, 1)
+    _f8_case(w, act, K, cross_check=False)
