@@ -35,7 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "2:4 sparse GEMM dense-equivalent TFLOP/s and HBM GB/s; speedup vs dense"
-PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}  # MI355X dense MFMA (int8: TOP/s), published
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0,
+                    "f8e4m3": 5000.0}  # MI355X dense MFMA (int8: TOP/s), published
 PEAK_HBM_GBPS = 8000.0
 
 
@@ -48,7 +49,7 @@ def parse():
                     help="dense-matmul load before the warmup, so the clock has settled "
                          "(an idle GPU takes about a second of load to reach it)")
     ap.add_argument("--workload", type=int, default=2,
-                    help="1..6 (default 2: prefill 4096x4096x2048; 6: the same shape in INT8)")
+                    help="1..7 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8)")
     ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
     ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
@@ -87,21 +88,26 @@ def traffic_from_profile(kernel_key, hsh):
 
 def cpu_baseline(wl, n, m, T, reps):
     """The oracle as it stands, timed on the host: prune+pack, decompress, fp64 GEMM
-    (int8: the exact int64 product, on a sample of rows; NumPy has no BLAS for it)."""
+    (int8: the exact int64 product, on a sample of rows; NumPy has no BLAS for it;
+    fp8: the decoded values' fp64 product)."""
     import numpy as np
     from oracle import nm_oracle as O
     w = wl.weights()
     act = wl.activations(T)
     perm = wl.permutation()
     i8 = wl.dtype == "i8"
+    f8 = wl.dtype == "f8e4m3"
     rows = 512 if i8 else wl.R  # about 6 s of int64 matmul at 4096 x 2048
     times, t_pack, t_gemm = [], [], []
     for _ in range(reps):
         t0 = time.perf_counter()
-        vals, idx = O.prune_pack_i8(w, n, m) if i8 else O.prune_pack(w, n, m)
+        vals, idx = (O.prune_pack_i8(w, n, m) if i8 else O.prune_pack_fp8(w, n, m) if f8 else
+                     O.prune_pack(w, n, m))
         t1 = time.perf_counter()
         if i8:
             O.spmm_ref_i8(vals[:rows], idx[:rows], wl.K, n, m, act, perm=perm)
+        elif f8:
+            O.spmm_ref_fp8(vals, idx, wl.K, n, m, act, perm=perm)
         else:
             O.spmm_ref(vals, idx, wl.K, n, m, act, wl.dtype, perm=perm)
         t2 = time.perf_counter()
@@ -193,23 +199,27 @@ def main():
     S = K // m * n
     dt = wl.dtype
     i8 = dt == "i8"
-    tdt = torch.int8 if i8 else torch.float16 if dt == "f16" else torch.bfloat16
-    # int8 weights give the exact int32 product
-    out_dtype = torch.int32 if i8 else torch.float32 if args.out_dtype == "f32" else tdt
+    f8 = dt == "f8e4m3"
+    b8 = i8 or f8  # one-byte weights and activations
+    tdt = (torch.int8 if i8 else torch.float8_e4m3fn if f8 else torch.float16 if dt == "f16" else
+           torch.bfloat16)
+    # int8 weights give the exact int32 product, fp8 ones an fp32 product
+    out_dtype = (torch.int32 if i8 else torch.float32 if f8 or args.out_dtype == "f32" else tdt)
+    out_name = "i32" if i8 else "f32" if f8 else args.out_dtype
     nm.nm_set_variant(args.variant)
 
     def dev(bits):
-        if i8:
-            return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+        if b8:
+            return torch.from_numpy(np.ascontiguousarray(bits)).cuda().view(tdt)
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
 
     W = dev(wl.weights())
     act = dev(wl.activations(T))
     perm_np = wl.permutation()
     perm = torch.from_numpy(perm_np).cuda() if perm_np is not None else None
-    dcode = nm.NM_I8 if i8 else nm.NM_F16 if dt == "f16" else nm.NM_BF16
+    dcode = nm.NM_I8 if i8 else nm.NM_FP8 if f8 else nm.NM_F16 if dt == "f16" else nm.NM_BF16
     vb, ib, words = nm.nm_packed_sizes(R, K, n, m, dcode)
-    esz = 1 if i8 else 2
+    esz = 1 if b8 else 2
     ybytes = T * R * (4 if out_dtype in (torch.float32, torch.int32) else 2)
     step_bytes = vb + ib + T * K * esz + ybytes  # the GEMM's algorithmic bytes
 
@@ -308,17 +318,24 @@ def main():
 
         def dense_gemm(c):
             torch._int_mm(actp[c], dense_t[c])
+    elif f8:
+        # dense fp8 GEMM with an fp32 result (hipBLASLt through torch._scaled_mm, unit scales)
+        dense_t = [d.t() for d in dense]
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+
+        def dense_gemm(c):
+            torch._scaled_mm(actp[c], dense_t[c], scale_a=one, scale_b=one, out_dtype=torch.float32)
     else:
         def dense_gemm(c):
             torch.nn.functional.linear(actp[c], dense[c])
 
     try:
         dense_us = time_loop(dense_gemm, iters)
-    except RuntimeError as e:  # no dense int8 GEMM for this shape / build
+    except RuntimeError as e:  # no dense 8-bit GEMM for this shape / build
         print(f"dense reference unavailable: {e}", file=sys.stderr)
         dense_us = None
     gemm_half_us = None
-    if not i8:  # a rounded half-precision output (int8 has only the exact int32 one)
+    if not b8:  # a rounded half-precision output (8-bit weights have a 4-byte one only)
         y_half = torch.empty((T, R), dtype=tdt, device="cuda")
 
         def gemm_half(c):
@@ -336,8 +353,8 @@ def main():
     lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
                for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
     hsh = source_hash(lib_src)
-    kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{'i32' if i8 else args.out_dtype}"
-    roofline_bound = "mfma" if args.workload in (1, 2, 4, 6) else "hbm"
+    kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{out_name}"
+    roofline_bound = "mfma" if args.workload in (1, 2, 4, 6, 7) else "hbm"
     unit = "TOP/s" if i8 else "TFLOP/s"
     if roofline_bound == "mfma":
         roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_MFMA_TFLOPS[dt],
@@ -393,9 +410,10 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": ("synthetic (seeded N(0,1)*32 rounded to int8, the workload's shapes)" if i8 else
+                 "synthetic (seeded N(0,1) rounded to E4M3, the workload's shapes)" if f8 else
                  "synthetic (seeded N(0,sigma) inputs of the workload's shapes)"),
         "config": {"workload": wl.name, "R": R, "K": K, "T": T, "pattern": f"{n}:{m}",
-                   "out_dtype": "i32" if i8 else args.out_dtype, "permuted": perm is not None,
+                   "out_dtype": out_name, "permuted": perm is not None,
                    "rotate": rotate,
                    "step": "nm_compress + nm_spmm", "parallelism": "single GPU"},
         "roofline": roofline,
@@ -428,7 +446,7 @@ def main():
         out["measured_peaks"] = pk
         if roofline["bound"] == "hbm":
             roofline["frac_of_measured_copy"] = roofline["achieved"] / pk["copy_gbps"]
-        elif not i8:
+        elif not b8:
             roofline["frac_of_measured_dense_matmul"] = roofline["achieved"] / pk["dense_bf16_matmul_tflops"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, n, m, T, args.cpu_reps)
