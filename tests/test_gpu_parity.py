@@ -638,3 +638,25 @@ def test_fp8_small_magnitudes():
     w = nm_inputs.normal_fp8((R, K), 2.0 ** -7, 72, 0)
     act = nm_inputs.normal_fp8((T, K), 1.0, 72, 1)
     _f8_case(w, act, K, cross_check=False)
+
+
+def test_fp8_nan_inputs():
+    # S.1111.111 is E4M3's NaN; its key (0x7F) is the largest, so a group
+    # holding one keeps it, and every output of that row is NaN
+    log("fp8 2:4 NaN weights")
+    R, K, T = 256, 256, 128
+    w = nm_inputs.normal_fp8((R, K), 1.0, 73, 0)
+    act = nm_inputs.normal_fp8((T, K), 1.0, 73, 1)
+    nan_rows = np.array([3, 100, 255])
+    w[nan_rows, [5, 130, 255]] = np.array([0x7F, 0xFF, 0x7F], np.uint8)
+    vals, idx = nm.nm_compress(_f8(w), 2, 4)
+    y = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4)
+    torch.cuda.synchronize()
+    ref_vals, ref_idx = O.prune_pack_fp8(w, 2, 4)
+    assert np.array_equal(vals.view(torch.uint8).cpu().numpy(), ref_vals)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    yv = y.cpu().numpy()
+    assert np.all(np.isnan(yv[:, nan_rows]))
+    rest = np.setdiff1d(np.arange(R), nan_rows)
+    yref = O.spmm_ref_fp8(ref_vals[rest], ref_idx[rest], K, 2, 4, act)
+    assert_close(y[:, rest], yref, tol=1e-2)
