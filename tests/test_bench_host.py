@@ -32,6 +32,14 @@ def test_cpu_baseline_fields():
     assert f"{wl.R}x{wl.K}x{wl.Ts[0]}" in out["sample"]
 
 
+def test_cpu_baseline_fp8_and_int8():
+    # the 8-bit legs: fp8 times the whole workload's fp64 product, int8 a row sample
+    f8 = bench.cpu_baseline(nm_inputs.WORKLOADS[7], 2, 4, 256, reps=1)
+    assert f8["unit"] == "TFLOP/s" and f8["value"] > 0 and "4096x4096x256" in f8["sample"]
+    i8 = bench.cpu_baseline(nm_inputs.WORKLOADS[6], 2, 4, 64, reps=1)
+    assert i8["unit"] == "TOP/s" and i8["value"] > 0 and "first 512 rows" in i8["sample"]
+
+
 def test_source_hash_is_stable_and_content_based(tmp_path):
     a, b = tmp_path / "a.hip", tmp_path / "b.hip"
     a.write_text("x")
