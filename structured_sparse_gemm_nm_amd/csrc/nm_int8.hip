@@ -1,5 +1,6 @@
-// INT8 2:4: prune + pack, decompress, and the sparse GEMM on
-// v_smfmac_i32_16x16x128_i8.
+// 8-bit 2:4 weights: prune + pack, decompress, and the sparse GEMM, for INT8
+// (v_smfmac_i32_16x16x128_i8, exact int32 Y) and for OCP FP8 E4M3
+// (v_smfmac_f32_16x16x128_fp8_fp8, fp32 Y) from one template.
 //
 // The 2:4 pattern is also offered for INT8 weights; the index stays 2 bits per
 // stored value (a 20-bit group, 37.5% smaller than dense) and the reduction
@@ -19,7 +20,10 @@
 //      exactly word 4 s + lq of the row's stored stream for step s;
 //   B  token li, K 16 lq .. 16 lq + 15 and 64 + 16 lq .. 64 + 16 lq + 15;
 //   D  element e is the product's row 4 lq + e, token li.
-// So every operand is a plain 16- or 4-byte load of the stored data.
+// So every operand is a plain 16- or 4-byte load of the stored data.  E4M3
+// differs only in the magnitude key (the pattern's low 7 bits, so +x and -x
+// tie) and in the accumulator: the fp8 instruction was checked the same way
+// and takes the same operand layout.
 #include "nm_internal.h"
 
 #include <type_traits>
