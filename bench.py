@@ -206,7 +206,7 @@ def main():
     # int8 weights give the exact int32 product, fp8 ones an fp32 product
     out_dtype = (torch.int32 if i8 else torch.float32 if f8 or args.out_dtype == "f32" else tdt)
     out_name = "i32" if i8 else "f32" if f8 else args.out_dtype
-    nm.nm_set_variant(args.variant)
+    var = args.variant
 
     def dev(bits):
         if b8:
@@ -235,12 +235,17 @@ def main():
         Y = torch.empty((T, R), dtype=out_dtype, device="cuda")
         copies.append((Wc, Ac, vals, idx, Y))
 
+    # the permuted product's workspace (the gather pass writes X' = act[:, perm]
+    # there), allocated once like the outputs
+    ws_need = nm.nm_spmm_perm_workspace_size(R, K, T, n, m, dcode) if perm is not None else 0
+    ws = torch.empty(ws_need, dtype=torch.uint8, device="cuda") if ws_need else None
+
     def gemm(c):
         _, Ac, vals, idx, Y = copies[c]
         if perm is None:
-            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=Y)
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=Y, variant=var)
         else:
-            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=Y)
+            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=Y, variant=var, workspace=ws)
 
     def compress(c):
         Wc, _, vals, idx, _ = copies[c]
@@ -341,9 +346,10 @@ def main():
         def gemm_half(c):
             _, Ac, vals, idx, _ = copies[c]
             if perm is None:
-                nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=tdt, out=y_half)
+                nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=tdt, out=y_half, variant=var)
             else:
-                nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half)
+                nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half, variant=var,
+                                workspace=ws)
 
         gemm_half_us = time_loop(gemm_half, iters)
 
@@ -384,15 +390,23 @@ def main():
 
         def plain(c):
             _, Ac, vals, idx, _ = copies[c]
-            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=y_plain)
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var)
 
         def identity(c):
             _, Ac, vals, idx, _ = copies[c]
-            nm.nm_spmm_perm(vals, idx, Ac, ident, K, n, m, out_dtype=out_dtype, out=y_plain)
+            nm.nm_spmm_perm(vals, idx, Ac, ident, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
+                            workspace=ws)
+
+        def in_kernel(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
+                            workspace=None)
 
         plain_us = time_loop(plain, iters)
         ident_us = time_loop(identity, iters)
+        in_kernel_us = time_loop(in_kernel, iters)
         extra = {"nm_spmm_no_perm_us": plain_us, "nm_spmm_perm_identity_us": ident_us,
+                 "nm_spmm_perm_no_workspace_us": in_kernel_us,
                  "perm_overhead_vs_no_perm": gemm_loop_us / plain_us - 1.0,
                  "perm_overhead_vs_identity_perm": gemm_loop_us / ident_us - 1.0}
 

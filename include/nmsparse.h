@@ -2,9 +2,11 @@
  * nmsparse.h -- N:M structured weight sparsity on AMD Instinct MI355X (gfx950).
  *
  * A C ABI over plain pointers and sizes.  Every device pointer is HIP device
- * memory owned by the caller; the library allocates nothing on these paths
- * and keeps no state between calls.  Streams are passed as `void*` holding a
- * hipStream_t (NULL = the legacy default stream).
+ * memory owned by the caller; no entry point allocates device or host memory,
+ * synchronises the caller's stream (nm_check_perm excepted, a debug aid) or
+ * keeps state between calls beyond read-only caches of device properties
+ * (CU count, LDS limit).  Streams are passed as `void*` holding a hipStream_t
+ * (NULL = the legacy default stream).
  *
  * Notation.  W is R x K (rows = output features, K = the reduction axis).
  * An N:M pattern keeps N of every M consecutive weights along a row of W;
@@ -79,7 +81,9 @@ typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP
  */
 
 /* Version of this ABI (major * 100 + minor): 101 adds NM_I8 / NM_I32,
- * 102 adds NM_FP8. */
+ * 102 adds NM_FP8; 200 replaces the process-wide nm_set_variant by the
+ * per-call nm_spmm_variant and gives nm_spmm_perm a caller-owned workspace in
+ * place of memory the library allocated. */
 int nm_version(void);
 
 /* Short fixed text for a status code (never NULL). */
@@ -154,22 +158,40 @@ nm_status nm_spmm(const void* values, const uint32_t* idx, int64_t R, int64_t K,
 
 /*
  * Permuted sparse GEMM  y = (W Pi) x:  Y[t, r] = sum_k W_nm[r, k] * act[t, perm[k]]
- * (ShuffleSparse, inference with a learned input-channel permutation).
- *   perm  device int32 [K], a permutation of 0..K-1 (precondition, not checked
- *         on the hot path; an out-of-range entry gives wrong values for its
- *         column, never an out-of-bounds access).
- * All other arguments as nm_spmm.  By default (nm_set_variant 0) the
- * permutation is applied as an index map while X is read by a gather pass
- * that writes X' = act[:, perm] (T * K * 2 bytes) to scratch memory, followed
- * by the plain GEMM on X'.  The library keeps one scratch buffer per (device,
- * stream), grown to the largest T * K * 2 seen on that stream and held until
- * the process ends; growing it synchronises that stream.  Variants 1 and 3
- * gather inside the GEMM kernel instead (no scratch).  NM_ERR_HIP if the
- * scratch cannot be allocated.
+ * (SHUFFLESPARSE technical summary, section 2, and the inference-efficiency
+ * item of its technical components: the hardened permutation is a
+ * precomputed index map applied while the GEMM reads its input).
+ *   perm       device int32 [K], a permutation of 0..K-1 (precondition, not
+ *              checked on the hot path; an entry outside [0, K) is clamped into
+ *              the row, so it gives a wrong value for its column, never an
+ *              out-of-bounds access).
+ *   workspace  device memory owned by the caller, or NULL; workspace_bytes its
+ *              size.  With at least nm_spmm_perm_workspace_size() bytes, one
+ *              gather pass writes X' = act[:, perm] there and the fastest
+ *              unpermuted kernel multiplies X' (the workspace is overwritten;
+ *              calls that share a workspace must be ordered on one stream).
+ *              Otherwise the kernel applies the map as it reads act: the few-
+ *              token kernel (T <= 16), the resident-tile kernel (2:4,
+ *              K % 256 == 0, K <= 4096: each tile of tokens is staged through
+ *              the map once, in LDS, and every weight row streams past it) or
+ *              the generic kernel (correct, slower).  Nothing is allocated.
+ *              16-byte aligned; must not overlap any other argument
+ *              (NM_ERR_ALIAS).
+ * All other arguments as nm_spmm.
  */
 nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                        int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
-                       void* Y, int64_t ldy, int out_dtype, void* stream);
+                       void* Y, int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Workspace bytes nm_spmm_perm uses for its gather pass on this shape (T * K *
+ * 2 for 16-bit weights with K % 8 == 0, K <= 65536 and T > 16; 0 when the shape
+ * always applies the map inside the kernel).  Pure host arithmetic; same
+ * format checks as nm_packed_sizes.
+ */
+nm_status nm_spmm_perm_workspace_size(int64_t R, int64_t K, int64_t T, int n, int m, int dtype,
+                                      size_t* bytes);
 
 /*
  * Host-side check that perm is a permutation of 0..K-1 (copies perm to the
@@ -178,25 +200,32 @@ nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64
 nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
 
 /*
- * Kernel family for nm_spmm / nm_spmm_perm, process-wide (ablations, tests).
- *   0  choose by shape (default)
- *   1  generic tiled kernel (LDS-staged operands, any shape)
- *   2  register-prefetch pipelined kernel (K % 64 == 0, T >= 64, R >= 128)
- *   3  all-LDS direct-load kernels (2:4; K % 128 == 0; the permuted one also
- *      K <= 768)
+ * nm_spmm (perm NULL; workspace ignored) or nm_spmm_perm (perm non-NULL) with
+ * the kernel family named by the call (tests and ablations; no state is kept;
+ * with a large enough workspace the named family multiplies the gathered X'):
+ *   0  choose by shape (what nm_spmm / nm_spmm_perm do)
+ *   1  generic tiled kernel (LDS-staged operands, any shape, any map)
+ *   2  register-prefetch pipelined kernel (K % 64 == 0, T >= 64, R >= 128;
+ *      not permuted)
+ *   3  all-LDS direct-load kernel with 256 x 128 tiles (2:4; K % 128 == 0,
+ *      T >= 128, R >= 256; not permuted)
  *   4  few-token kernel (T <= 16, K <= 4096)
- *   5  all-LDS direct-load kernel with 256 x 256 tiles (2:4; K % 128 == 0,
- *      T >= 256, R >= 256)
+ *   5  resident-tile kernel (2:4; K % 256 == 0, K <= 4096)
  *   6  all-LDS direct-load kernel with 128 x 64 tiles (1:4 and 1:8;
- *      K % 256 == 0, T >= 64, R >= 128)
+ *      K % 256 == 0, T >= 64, R >= 128; not permuted)
  * For 8-bit weights there are two: the LDS-staged kernel (whole 256 x 128 tiles,
  * K % 128 == 0) and, for variant 1 or any other shape, a kernel that loads
  * its operands straight into registers.
- * A forced family that does not take the shape falls back to the choice by
- * shape.  Every family computes the same product; all but 4 add the K steps
- * in the same order and give the same bits.  NM_ERR_UNSUPPORTED outside 0..6.
+ * A named family that does not take the shape falls back to the choice by
+ * shape.  Every family computes the same product; all but 4 add the 64-wide
+ * K steps in the same order and give the same bits (4 splits K over waves:
+ * the same result within the fp32 summation bound).
+ * NM_ERR_UNSUPPORTED outside 0..6.
  */
-nm_status nm_set_variant(int variant);
+nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
+                          int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
+                          void* Y, int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
+                          int variant, void* stream);
 
 #ifdef __cplusplus
 }

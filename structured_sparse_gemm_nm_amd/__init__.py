@@ -16,7 +16,7 @@ import os
 
 __all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NM_FP8", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
-           "nm_check_perm", "nm_set_variant", "PATTERNS"]
+           "nm_spmm_perm_workspace_size", "nm_check_perm", "PATTERNS"]
 
 NM_OK = 0
 NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
@@ -63,11 +63,13 @@ def lib() -> ctypes.CDLL:
     L.nm_spmm.restype = i32
     L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, i32, vp]
     L.nm_spmm_perm.restype = i32
-    L.nm_spmm_perm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp]
+    L.nm_spmm_perm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp, sz, vp]
+    L.nm_spmm_perm_workspace_size.restype = i32
+    L.nm_spmm_perm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
     L.nm_check_perm.restype = i32
     L.nm_check_perm.argtypes = [vp, i64, vp]
-    L.nm_set_variant.restype = i32
-    L.nm_set_variant.argtypes = [i32]
+    L.nm_spmm_variant.restype = i32
+    L.nm_spmm_variant.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp, sz, i32, vp]
     _lib = L
     return L
 
@@ -129,20 +131,44 @@ def nm_packed_sizes(R: int, K: int, n: int, m: int, dtype: int = NM_F16):
     return vb.value, ib.value, w.value
 
 
+def _check_packed(values, idx, R, K, n, m, dt, name_v="values", name_i="idx"):
+    """values must be a contiguous [R, K*n/m] tensor of the weight dtype and idx a
+    contiguous int32 [R, idx_row_words] tensor, both on one device: the C ABI
+    takes bare pointers, so a wrong size here would become an out-of-bounds access."""
+    torch = _torch()
+    _, _, words = nm_packed_sizes(R, K, n, m, dt)
+    S = K // m * n
+    if tuple(values.shape) != (R, S) or not values.is_contiguous():
+        raise ValueError(f"{name_v} must be a contiguous [{R}, {S}] tensor, got {tuple(values.shape)}")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (R, words) or not idx.is_contiguous():
+        raise ValueError(f"{name_i} must be a contiguous int32 [{R}, {words}] tensor, got "
+                         f"{idx.dtype} {tuple(idx.shape)}")
+    if idx.device != values.device:
+        raise ValueError(f"{name_v} and {name_i} must be on one device")
+
+
 def nm_compress(W, n: int = 2, m: int = 4, values=None, idx=None):
     """Prune W [R, K] (fp16/bf16, or int8 / float8_e4m3fn for 2:4; device) to n:m and pack.
     Returns (values [R, S], idx [R, words])."""
     torch = _torch()
-    _require_cuda(W)
     _row_major(W, "W")
     R, K = W.shape
     dt = _dtype_code(W)
     _, _, words = nm_packed_sizes(R, K, n, m, dt)
     S = K // m * n
+    if values is not None or idx is not None:  # caller-provided outputs: check before the device
+        _check_packed(values if values is not None else W.new_empty((R, S)),
+                      idx if idx is not None else W.new_empty((R, words), dtype=torch.int32), R, K, n, m, dt)
+    _require_cuda(W)
     if values is None:
         values = torch.empty((R, S), dtype=W.dtype, device=W.device)
+    elif values.dtype != W.dtype:
+        raise TypeError(f"values is {values.dtype}, W is {W.dtype}")
     if idx is None:
         idx = torch.empty((R, words), dtype=torch.int32, device=W.device)
+    _check_packed(values, idx, R, K, n, m, dt)
+    if values.device != W.device:
+        raise ValueError("values, idx and W must be on one device")
     _check(lib().nm_compress(W.data_ptr(), R, K, W.stride(0), dt, n, m, values.data_ptr(),
                              idx.data_ptr(), _stream_ptr(W.device)))
     return values, idx
@@ -151,9 +177,14 @@ def nm_compress(W, n: int = 2, m: int = 4, values=None, idx=None):
 def nm_decompress(values, idx, K: int, n: int = 2, m: int = 4, out=None):
     """Dense W_nm [R, K] from the packed pair."""
     torch = _torch()
-    _require_cuda(values, idx)
     R = values.shape[0]
     dt = _dtype_code(values)
+    _check_packed(values, idx, R, K, n, m, dt)
+    if out is not None:
+        _row_major(out, "out")
+        if out.dtype != values.dtype or tuple(out.shape) != (R, K) or out.device != values.device:
+            raise ValueError(f"out must be a {values.dtype} [{R}, {K}] tensor on {values.device}")
+    _require_cuda(values, idx)
     if out is None:
         out = torch.empty((R, K), dtype=values.dtype, device=values.device)
     _check(lib().nm_decompress(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, out.data_ptr(),
@@ -161,25 +192,39 @@ def nm_decompress(values, idx, K: int, n: int = 2, m: int = 4, out=None):
     return out
 
 
-def nm_spmm(values, idx, act, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None):
-    """Y^T [T, R] = act [T, K] . W_nm^T, i.e. Y = W_nm X with X = act^T."""
-    return _spmm(values, idx, act, K, n, m, None, out_dtype, out)
+def nm_spmm(values, idx, act, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None, variant: int = 0):
+    """Y^T [T, R] = act [T, K] . W_nm^T, i.e. Y = W_nm X with X = act^T.
+    variant != 0 names the kernel family (tests, ablations; see nm_spmm_variant)."""
+    return _spmm(values, idx, act, K, n, m, None, out_dtype, out, variant, None)
 
 
-def nm_spmm_perm(values, idx, act, perm, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None):
-    """Y^T[t, r] = sum_k W_nm[r, k] act[t, perm[k]]  (y = (W Pi) x)."""
-    return _spmm(values, idx, act, K, n, m, perm, out_dtype, out)
+def nm_spmm_perm_workspace_size(R: int, K: int, T: int, n: int = 2, m: int = 4, dtype: int = NM_F16) -> int:
+    """Bytes of caller workspace nm_spmm_perm uses for its gather pass (0: none)."""
+    b = ctypes.c_size_t()
+    _check(lib().nm_spmm_perm_workspace_size(R, K, T, n, m, dtype, ctypes.byref(b)))
+    return b.value
 
 
-def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
+def nm_spmm_perm(values, idx, act, perm, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None,
+                 variant: int = 0, workspace="auto"):
+    """Y^T[t, r] = sum_k W_nm[r, k] act[t, perm[k]]  (y = (W Pi) x).
+    workspace: "auto" (a torch tensor of nm_spmm_perm_workspace_size bytes, when the
+    shape takes the gather pass), None (the kernel applies the map as it reads act),
+    or a caller-owned device tensor."""
+    return _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace)
+
+
+def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):
     torch = _torch()
-    _require_cuda(values, idx, act)
     _row_major(act, "act")
     R = values.shape[0]
     T = act.shape[0]
     dt = _dtype_code(values)
     if act.dtype != values.dtype:
         raise TypeError("act and values must share a dtype")
+    _check_packed(values, idx, R, K, n, m, dt)
+    if act.shape[1] != K or act.device != values.device:
+        raise ValueError(f"act must be a [T, {K}] tensor on {values.device}")
     if dt == NM_I8:  # the exact integer product
         if out_dtype not in (None, torch.int32):
             raise TypeError("int8 weights give an int32 output")
@@ -191,26 +236,45 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
     else:
         od = NM_F32 if (out_dtype is None or out_dtype == torch.float32) else _dtype_code(
             torch.empty(0, dtype=out_dtype))
-    if out is None:
-        out = torch.empty((T, R), dtype=_torch_dtype(od), device=act.device)
-    else:
-        _require_cuda(out)
+    if out is not None:
         _row_major(out, "out")
         if out.dtype != _torch_dtype(od):
             raise TypeError(f"out is {out.dtype}, the output dtype is {_torch_dtype(od)}")
-        if out.shape[0] < T or out.shape[1] < R or out.device != act.device:
+        if tuple(out.shape) != (T, R) or out.device != act.device:
             raise ValueError(f"out must be a [{T}, {R}] tensor on {act.device}")
+    if perm is not None:
+        if perm.dtype != torch.int32 or perm.numel() != K or not perm.is_contiguous():
+            raise TypeError("perm must be a contiguous int32 tensor of K entries")
+        if perm.device != act.device:
+            raise ValueError("perm must be on the device of act")
+    ws = None
+    if perm is not None and isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        need = nm_spmm_perm_workspace_size(R, K, T, n, m, dt)
+        ws = torch.empty(need, dtype=torch.uint8, device=act.device) if need else None
+    elif perm is not None and workspace is not None:
+        ws = workspace
+        if not ws.is_contiguous() or ws.device != act.device:
+            raise ValueError("workspace must be a contiguous tensor on the device of act")
+    _require_cuda(values, idx, act, *(t for t in (out, perm, ws) if t is not None))
+    if out is None:
+        out = torch.empty((T, R), dtype=_torch_dtype(od), device=act.device)
     stream = _stream_ptr(act.device)
-    if perm is None:
-        st = lib().nm_spmm(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,
-                           act.stride(0), out.data_ptr(), out.stride(0), od, stream)
+    L = lib()
+    ws_ptr = None if ws is None else ws.data_ptr()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if variant:
+        st = L.nm_spmm_variant(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,
+                               act.stride(0), None if perm is None else perm.data_ptr(), out.data_ptr(),
+                               out.stride(0), od, ws_ptr, ws_bytes, variant, stream)
+    elif perm is None:
+        st = L.nm_spmm(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,
+                       act.stride(0), out.data_ptr(), out.stride(0), od, stream)
     else:
-        _require_cuda(perm)
-        if perm.dtype != torch.int32 or perm.numel() != K:
-            raise TypeError("perm must be an int32 tensor of K entries")
-        st = lib().nm_spmm_perm(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(),
-                                T, act.stride(0), perm.data_ptr(), out.data_ptr(), out.stride(0),
-                                od, stream)
+        st = L.nm_spmm_perm(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(),
+                            T, act.stride(0), perm.data_ptr(), out.data_ptr(), out.stride(0),
+                            od, ws_ptr, ws_bytes, stream)
     _check(st)
     return out
 
@@ -218,7 +282,3 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out):
 def nm_check_perm(perm) -> None:
     _require_cuda(perm)
     _check(lib().nm_check_perm(perm.data_ptr(), perm.numel(), _stream_ptr(perm.device)))
-
-
-def nm_set_variant(variant: int) -> None:
-    _check(lib().nm_set_variant(variant))

@@ -2,7 +2,6 @@
 //
 // Every check runs on the host before the first HIP call, so argument errors
 // never touch the device and can be tested without a GPU.
-#include <atomic>
 #include <cstdio>
 #include <cstdarg>
 #include <map>
@@ -17,7 +16,6 @@
 namespace {
 
 thread_local std::string g_last_error;
-std::atomic<int> g_variant{0};
 
 constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int64_t kMaxRT = int64_t(1) << 30;
@@ -104,9 +102,12 @@ nm_status hip_status(hipError_t e, const char* what) {
 
 nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                       int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
-                      bool want_perm, void* Y, int64_t ldy, int out_dtype, void* stream) {
+                      bool want_perm, void* Y, int64_t ldy, int out_dtype, void* workspace,
+                      size_t workspace_bytes, int variant, void* stream) {
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
+  if (variant < 0 || variant > nm::NM_VARIANT_MAX)
+    return fail(NM_ERR_UNSUPPORTED, "kernel family %d is not 0..%d", variant, int(nm::NM_VARIANT_MAX));
   if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
   if (dtype == NM_I8 || dtype == NM_FP8) {
     const int want = dtype == NM_I8 ? NM_I32 : NM_F32;
@@ -119,6 +120,9 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   }
   if (ldx < K) return fail(NM_ERR_STRIDE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
   if (ldy < R) return fail(NM_ERR_STRIDE, "ldy = %lld < R = %lld", (long long)ldy, (long long)R);
+  // bounded before any product of sizes below, so no int64 product overflows
+  if (ldx > kMaxElems || ldy > kMaxElems)
+    return fail(NM_ERR_SHAPE, "leading dimension above 2^40 elements");
   if (R == 0 || T == 0) return ok();  // empty product: nothing to enqueue
   if (!values || !idx || !act || !Y || (want_perm && !perm))
     return fail(NM_ERR_NULL, "values, idx, act, Y%s must be non-NULL", want_perm ? ", perm" : "");
@@ -131,10 +135,19 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   if (T * ldx > kMaxElems || T * ldy > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
   Sizes z = sizes_of(R, K, n, m, dtype);
   size_t ybytes = extent(T, R, ldy, elt_bytes(out_dtype));
+  const size_t abytes = extent(T, K, ldx, elt_bytes(dtype));
   if (overlaps(Y, ybytes, values, z.values_bytes) || overlaps(Y, ybytes, idx, z.idx_bytes) ||
-      overlaps(Y, ybytes, act, extent(T, K, ldx, elt_bytes(dtype))) ||
-      (want_perm && overlaps(Y, ybytes, perm, size_t(K) * 4)))
+      overlaps(Y, ybytes, act, abytes) || (want_perm && overlaps(Y, ybytes, perm, size_t(K) * 4)))
     return fail(NM_ERR_ALIAS, "Y overlaps an input");
+  if (workspace_bytes == 0) workspace = nullptr;
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(NM_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (overlaps(workspace, workspace_bytes, Y, ybytes) || overlaps(workspace, workspace_bytes, act, abytes) ||
+        overlaps(workspace, workspace_bytes, values, z.values_bytes) ||
+        overlaps(workspace, workspace_bytes, idx, z.idx_bytes) ||
+        (want_perm && overlaps(workspace, workspace_bytes, perm, size_t(K) * 4)))
+      return fail(NM_ERR_ALIAS, "workspace overlaps an argument");
+  }
 
   nm::SpmmArgs a;
   a.values = static_cast<const uint16_t*>(values);
@@ -152,7 +165,9 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   a.ldy = ldy;
   a.out_dtype = out_dtype;
   a.idx_row_words = z.words;
-  a.variant = g_variant.load(std::memory_order_relaxed);
+  a.variant = variant;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   return hip_status(nm::launch_spmm(a, static_cast<hipStream_t>(stream)), "nm_spmm launch");
 }
 
@@ -203,7 +218,7 @@ hipError_t ensure_lds_limit(const void* kern, int bytes) {
 
 extern "C" {
 
-int nm_version(void) { return 102; }
+int nm_version(void) { return 200; }
 
 const char* nm_status_string(int status) {
   switch (status) {
@@ -237,6 +252,7 @@ nm_status nm_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtyp
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
   if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw > kMaxElems) return fail(NM_ERR_SHAPE, "ldw above 2^40 elements");
   if (R == 0) return ok();
   if (!W || !values || !idx) return fail(NM_ERR_NULL, "W, values and idx must be non-NULL");
   if (ldw % ld_quantum(dtype))
@@ -266,6 +282,7 @@ nm_status nm_decompress(const void* values, const uint32_t* idx, int64_t R, int6
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
   if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw > kMaxElems) return fail(NM_ERR_SHAPE, "ldw above 2^40 elements");
   if (R == 0) return ok();
   if (!W_out || !values || !idx) return fail(NM_ERR_NULL, "values, idx and W_out must be non-NULL");
   if (ldw % ld_quantum(dtype))
@@ -293,14 +310,33 @@ nm_status nm_spmm(const void* values, const uint32_t* idx, int64_t R, int64_t K,
                   int dtype, const void* act, int64_t T, int64_t ldx, void* Y, int64_t ldy,
                   int out_dtype, void* stream) {
   return spmm_common(values, idx, R, K, n, m, dtype, act, T, ldx, nullptr, false, Y, ldy,
-                     out_dtype, stream);
+                     out_dtype, nullptr, 0, 0, stream);
+}
+
+nm_status nm_spmm_perm_workspace_size(int64_t R, int64_t K, int64_t T, int n, int m, int dtype,
+                                      size_t* bytes) {
+  nm_status st = check_format(R, K, n, m, dtype);
+  if (st != NM_OK) return st;
+  if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (!bytes) return fail(NM_ERR_NULL, "bytes must be non-NULL");
+  *bytes = R == 0 ? 0 : nm::spmm_perm_gather_bytes(T, K, dtype);
+  return ok();
 }
 
 nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                        int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
-                       void* Y, int64_t ldy, int out_dtype, void* stream) {
+                       void* Y, int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   return spmm_common(values, idx, R, K, n, m, dtype, act, T, ldx, perm, true, Y, ldy, out_dtype,
-                     stream);
+                     workspace, workspace_bytes, 0, stream);
+}
+
+nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
+                          int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
+                          void* Y, int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
+                          int variant, void* stream) {
+  return spmm_common(values, idx, R, K, n, m, dtype, act, T, ldx, perm, perm != nullptr, Y, ldy,
+                     out_dtype, workspace, workspace_bytes, variant, stream);
 }
 
 nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream) {
@@ -318,13 +354,6 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream) {
       return fail(NM_ERR_SHAPE, "perm[%lld] = %d breaks the permutation", (long long)k, p);
     seen[size_t(p)] = 1;
   }
-  return ok();
-}
-
-nm_status nm_set_variant(int variant) {
-  if (variant < 0 || variant > nm::NM_VARIANT_MAX)
-    return fail(NM_ERR_UNSUPPORTED, "variant %d", variant);
-  g_variant.store(variant, std::memory_order_relaxed);
   return ok();
 }
 

@@ -24,6 +24,7 @@
 // differs only in the magnitude key (the pattern's low 7 bits, so +x and -x
 // tie) and in the accumulator: the fp8 instruction was checked the same way
 // and takes the same operand layout.
+#include "nm_device.h"
 #include "nm_internal.h"
 
 #include <type_traits>
@@ -33,7 +34,6 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One-byte element types: F8 = false int8 (exact int32 product), true OCP FP8
 // E4M3 (v_smfmac_f32_16x16x128_fp8_fp8, fp32 accumulators; the same operand
@@ -243,14 +243,6 @@ constexpr int kBlockI8 = kBR8L * 64;              // index bits, four steps
 constexpr int kLds8 = kNS8 * 2 * kStage8 + 2 * kBlockI8;  // 160 KB
 constexpr int kPer8 = 8;                          // direct loads per wave per step: 4 + 4
 
-typedef __attribute__((address_space(3))) unsigned char lds_byte8;
-
-template <int N>
-__device__ inline void wait_vmcnt8() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
 template <bool F8>
 __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __restrict__ values,
                                                              const uint32_t* __restrict__ idx, int K,
@@ -317,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int st = min(4 * q + istep[j], nsteps - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_byte8*)(ibuf + ib * kBlockI8 + (wave * 4 + j) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_byte*)(ibuf + ib * kBlockI8 + (wave * 4 + j) * 1024),
                                                16, int(ioff[j] + uint32_t(st) * 16u), 0, 0, 0);
     }
     asm volatile("" ::: "memory");
@@ -330,9 +322,9 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte8*)(bbuf + SL * kStage8 + (wave * 4 + j) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte*)(bbuf + SL * kStage8 + (wave * 4 + j) * 1024),
                                                16, int(boff[j]), int(src * 128), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_byte8*)(abuf + SL * kStage8 + (wave * 4 + j) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_byte*)(abuf + SL * kStage8 + (wave * 4 + j) * 1024),
                                                16, int(aoff[j]), int(src * 64), 0, 0);
     }
     asm volatile("" ::: "memory");
@@ -372,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
   auto step = [&](int s, auto slot_c, const i32x4 (&ca)[8], const i32x8 (&cb)[4], const uint32_t (&cx)[8],
                   i32x4 (&na)[8], i32x8 (&nb)[4], uint32_t (&nx)[8]) {
     constexpr int SL = decltype(slot_c)::value;
-    wait_vmcnt8<2 * kPer8>();  // step s+1 has landed (steps s+2, s+3 may remain)
+    wait_vmcnt<2 * kPer8>();  // step s+1 has landed (steps s+2, s+3 may remain)
     __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // this wave's reads of step s are done
     __builtin_amdgcn_s_barrier();  // step s+1 visible; every wave is done reading step s
     asm volatile("" ::: "memory");
@@ -396,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
   issue(0, integral_constant<int, 0>{});
   issue(min(1, nsteps - 1), integral_constant<int, 1>{});
   issue(min(2, nsteps - 1), integral_constant<int, 2>{});
-  wait_vmcnt8<2 * kPer8>();  // index block 0 and step 0 have landed
+  wait_vmcnt<2 * kPer8>();  // index block 0 and step 0 have landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   issue(min(3, nsteps - 1), integral_constant<int, 3>{});
@@ -411,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
   if (s < nsteps) step(s, integral_constant<int, 0>{}, a0, b0, x0, a1, b1, x1);
   if (s + 1 < nsteps) step(s + 1, integral_constant<int, 1>{}, a1, b1, x1, a0, b0, x0);
   if (s + 2 < nsteps) step(s + 2, integral_constant<int, 2>{}, a0, b0, x0, a1, b1, x1);
-  wait_vmcnt8<0>();  // no direct load still writing LDS when the workgroup ends
+  wait_vmcnt<0>();  // no direct load still writing LDS when the workgroup ends
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -10,7 +10,7 @@
 namespace nm {
 
 enum { NM_VARIANT_AUTO = 0, NM_VARIANT_GENERIC = 1, NM_VARIANT_PIPE = 2, NM_VARIANT_LDS = 3,
-       NM_VARIANT_DECODE = 4, NM_VARIANT_WIDE = 5, NM_VARIANT_LDS_NM = 6, NM_VARIANT_MAX = 6 };
+       NM_VARIANT_DECODE = 4, NM_VARIANT_RESIDENT = 5, NM_VARIANT_LDS_NM = 6, NM_VARIANT_MAX = 6 };
 
 // Launchers (defined next to their kernels).  Arguments are already
 // validated; each returns the hipError_t of its launch.
@@ -44,6 +44,8 @@ struct SpmmArgs {
   int out_dtype;         // NM_F32 or dtype
   int64_t idx_row_words;
   int variant;           // NM_VARIANT_* (0 = choose by shape)
+  void* workspace;       // permuted product: caller memory for X' = act[:, perm], or null
+  size_t workspace_bytes;
 };
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
@@ -58,9 +60,16 @@ hipError_t launch_spmm_pipe(const SpmmArgs& a, hipStream_t s);
 bool spmm_decode_applies(const SpmmArgs& a);
 hipError_t launch_spmm_decode(const SpmmArgs& a, hipStream_t s);
 
-// Permuted 2:4 kernel gathering from LDS (nm_spmm_perm.hip) and its shapes.
-bool spmm_perm_lds_applies(const SpmmArgs& a);
-hipError_t launch_spmm_perm_lds(const SpmmArgs& a, hipStream_t s);
+// Permuted product as a gather pass X' = act[:, perm] into the caller's
+// workspace followed by the plain GEMM on X' (nm_permute.hip): the bytes it
+// needs (0 when the shape does not take it), and the launch.
+size_t spmm_perm_gather_bytes(int64_t T, int64_t K, int dtype);
+hipError_t launch_spmm_perm_gather(const SpmmArgs& a, void* workspace, hipStream_t s);
+
+// 2:4 kernel with the token tile resident in LDS, plain or through the index
+// map (nm_spmm_resident.hip), and the shapes it takes.
+bool spmm_resident_applies(const SpmmArgs& a);
+hipError_t launch_spmm_resident(const SpmmArgs& a, hipStream_t s);
 
 // All-LDS 2:4 kernel (nm_spmm_lds.hip) and the shapes it takes.
 bool spmm_lds_applies(const SpmmArgs& a);
@@ -70,15 +79,6 @@ hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);
 // shapes it takes.
 bool spmm_lds_nm_applies(const SpmmArgs& a);
 hipError_t launch_spmm_lds_nm(const SpmmArgs& a, hipStream_t s);
-
-// Permuted GEMM as a gather pass into stream-ordered scratch followed by the
-// plain GEMM (nm_permute.hip), and the shapes it takes.
-bool spmm_perm_gather_applies(const SpmmArgs& a);
-hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s);
-
-// 256 x 256-tile 2:4 kernel (nm_spmm_wide.hip) and the shapes it takes.
-bool spmm_wide_applies(const SpmmArgs& a);
-hipError_t launch_spmm_wide(const SpmmArgs& a, hipStream_t s);
 
 // Device properties and per-kernel launch set-up, kept per device and safe to
 // call from several host threads (nm_api.cpp).

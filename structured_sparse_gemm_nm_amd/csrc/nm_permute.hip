@@ -1,6 +1,5 @@
 // Permuted sparse GEMM through a gather pass: X' = act[:, perm] is written to
-// scratch memory owned by the calling stream, then the plain sparse GEMM
-// runs on X'.
+// a workspace the caller provides, then the plain sparse GEMM runs on X'.
 //
 // ShuffleSparse (permutation-aware N:M pruning, inference section) applies the
 // learned column permutation to the layer input, so the product is
@@ -21,11 +20,8 @@
 // its next block land while it gathers and stores the current one, so the
 // pass reads and writes HBM at the same time (a workgroup per block would put
 // every workgroup in the same phase: all loading, then all storing).
+#include "nm_device.h"
 #include "nm_internal.h"
-
-#include <functional>
-#include <map>
-#include <mutex>
 
 namespace nm {
 namespace {
@@ -59,9 +55,9 @@ __global__ __launch_bounds__(kThreads) void permute_cols_kernel(
   for (int c = cpr >= kThreads ? threadIdx.x : threadIdx.x - r0 * cpr; c < cpr; c += kThreads) {
     const int4 p0 = *reinterpret_cast<const int4*>(perm + c * 8);
     const int4 p1 = *reinterpret_cast<const int4*>(perm + c * 8 + 4);
-    const uint32_t q[8] = {min(uint32_t(p0.x), kmax), min(uint32_t(p0.y), kmax), min(uint32_t(p0.z), kmax),
-                           min(uint32_t(p0.w), kmax), min(uint32_t(p1.x), kmax), min(uint32_t(p1.y), kmax),
-                           min(uint32_t(p1.z), kmax), min(uint32_t(p1.w), kmax)};
+    const uint32_t q[8] = {umin(uint32_t(p0.x), kmax), umin(uint32_t(p0.y), kmax), umin(uint32_t(p0.z), kmax),
+                           umin(uint32_t(p0.w), kmax), umin(uint32_t(p1.x), kmax), umin(uint32_t(p1.y), kmax),
+                           umin(uint32_t(p1.z), kmax), umin(uint32_t(p1.w), kmax)};
     for (int r = r0; r < nr; r += rstep) {
       const uint16_t* row = rowbuf + r * K;
       uint4 o;
@@ -74,20 +70,7 @@ __global__ __launch_bounds__(kThreads) void permute_cols_kernel(
   }
 }
 
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
 constexpr int kDbMaxK = 8192;  // the persistent variant: a row fits a 16 KB buffer
-
-__device__ inline void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
 
 // Blocks of rows_blk token rows (rows_blk * K * 2 <= kRowBytes); workgroup w
 // takes blocks w, w + grid, ...  Each thread issues 4 direct loads per block
@@ -138,10 +121,10 @@ __global__ __launch_bounds__(kThreads) void permute_cols_db_kernel(
   auto load_perm = [&](int c) {
     const int4 p0 = *reinterpret_cast<const int4*>(perm + c * 8);
     const int4 p1 = *reinterpret_cast<const int4*>(perm + c * 8 + 4);
-    q[0] = min(uint32_t(p0.x), kmax); q[1] = min(uint32_t(p0.y), kmax);
-    q[2] = min(uint32_t(p0.z), kmax); q[3] = min(uint32_t(p0.w), kmax);
-    q[4] = min(uint32_t(p1.x), kmax); q[5] = min(uint32_t(p1.y), kmax);
-    q[6] = min(uint32_t(p1.z), kmax); q[7] = min(uint32_t(p1.w), kmax);
+    q[0] = umin(uint32_t(p0.x), kmax); q[1] = umin(uint32_t(p0.y), kmax);
+    q[2] = umin(uint32_t(p0.z), kmax); q[3] = umin(uint32_t(p0.w), kmax);
+    q[4] = umin(uint32_t(p1.x), kmax); q[5] = umin(uint32_t(p1.y), kmax);
+    q[6] = umin(uint32_t(p1.z), kmax); q[7] = umin(uint32_t(p1.w), kmax);
   };
   if (gathers && cpr < kThreads) load_perm(c0);
 
@@ -176,66 +159,24 @@ __global__ __launch_bounds__(kThreads) void permute_cols_db_kernel(
   }
 }
 
-// Scratch for X': one buffer per (device, stream), grown to the largest size
-// seen and kept until the process ends.  Work on one stream runs in order, so
-// a buffer is never used by two calls at once; calls on different streams
-// use different buffers.
-struct ScratchKey {
-  int dev;
-  hipStream_t stream;
-  bool operator<(const ScratchKey& o) const {
-    return dev != o.dev ? dev < o.dev : std::less<hipStream_t>()(stream, o.stream);
-  }
-};
-struct Scratch {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-
-hipError_t stream_scratch(int dev, hipStream_t s, size_t bytes, void** out) {
-  static std::mutex mu;
-  static std::map<ScratchKey, Scratch> cache;
-  std::lock_guard<std::mutex> g(mu);
-  Scratch& sc = cache[ScratchKey{dev, s}];
-  if (sc.bytes < bytes) {
-    // a smaller buffer may still be read by queued work on this stream
-    if (sc.ptr) {
-      hipError_t e = hipStreamSynchronize(s);
-      if (e == hipSuccess) e = hipFree(sc.ptr);
-      sc.ptr = nullptr;
-      sc.bytes = 0;
-      if (e != hipSuccess) return e;
-    }
-    hipError_t e = hipMalloc(&sc.ptr, bytes);
-    if (e != hipSuccess) {
-      sc.ptr = nullptr;
-      return e;
-    }
-    sc.bytes = bytes;
-  }
-  *out = sc.ptr;
-  return hipSuccess;
-}
-
 }  // namespace
 
-bool spmm_perm_gather_applies(const SpmmArgs& a) {
-  return a.perm != nullptr && (a.K % 8) == 0 && a.K <= kMaxK && a.T > 0;
+// The gather pass takes 16-bit activations with K % 8 == 0 (16-byte chunks)
+// and K <= 65536; few tokens (T <= 16) gather inside the few-token kernel.
+size_t spmm_perm_gather_bytes(int64_t T, int64_t K, int dtype) {
+  const bool applies = (K % 8) == 0 && K <= kMaxK && T > 16 && (dtype == NM_F16 || dtype == NM_BF16);
+  return applies ? size_t(T) * size_t(K) * 2 : 0;
 }
 
-hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  void* xp = nullptr;
-  if ((e = stream_scratch(dev, s, size_t(a.T) * size_t(a.K) * 2, &xp)) != hipSuccess) return e;
-
+hipError_t launch_spmm_perm_gather(const SpmmArgs& a, void* xp, hipStream_t s) {
+  hipError_t e = hipSuccess;
   const int K = int(a.K);
   int rows_blk = kRowBytes / (K * 2);
   if (rows_blk < 1) rows_blk = 1;
   if (rows_blk > 64) rows_blk = 64;
   const int64_t blocks = (a.T + rows_blk - 1) / rows_blk;
-  if (K <= kDbMaxK && blocks <= 0x7FFFFFFF && int64_t(a.T) * a.ldx * 2 <= int64_t(0xFFFFFFFFu)) {
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (K <= kDbMaxK && int64_t(a.T) * a.ldx * 2 <= int64_t(0xFFFFFFFFu)) {
     const int cus = device_cu_count();
     // four workgroups per CU (32 KB of LDS each; measured: 8.9 us for the
     // 3072 x 768 x 12608 layer's 38.7 MB, against 9.2 with two and 10.0 for
@@ -256,6 +197,8 @@ hipError_t launch_spmm_perm_gather(const SpmmArgs& a, hipStream_t s) {
     b.act = static_cast<const uint16_t*>(xp);
     b.ldx = a.K;
     b.perm = nullptr;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
     e = launch_spmm(b, s);
   }
   return e;

@@ -29,29 +29,11 @@
 // gathered through perm when permuted) are staged into LDS, double buffered
 // with register prefetch of the next step; each wave then issues
 // (BR/WR/16) x (BT/WT/16) smfmac per step.  Accumulation is fp32.
+#include "nm_device.h"
 #include "nm_internal.h"
 
 namespace nm {
 namespace {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-
-template <int DT>
-__device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
-                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, 0);
-  } else {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
-                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, 0);
-  }
-}
 
 // Per-pattern constants for one 64-wide K step of one row.
 //   VPS  packed values per step; VB bytes of values a lane takes per step
@@ -70,22 +52,6 @@ template <>
 struct Pat<2> {  // 1:8
   static constexpr int N = 1, M = 8, B = 3, VPS = 8, IBS = 24, VEC = 2;
 };
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-template <int DT>
-__device__ inline uint16_t to_half_bits(float f) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-  } else {
-    return f32_to_bf16_rne(f);
-  }
-}
 
 // Widen one lane's slice of a step to the 2:4 smfmac operand.
 //   raw: the lane's packed values (VEC halves, low bits first)
@@ -233,12 +199,19 @@ __global__ __launch_bounds__(256) void spmm_kernel(const uint16_t* __restrict__ 
       if (ch < C::B_CHUNKS && t < T && kk < K) {
         const uint16_t* arow = act + int64_t(t) * ldx;
         if constexpr (PERM) {
+          // entries outside [0, K) (a broken precondition) are clamped into
+          // the row: a wrong value, never a wrong address
+          const uint32_t kmax = uint32_t(K - 1);
           const int4 p0 = *reinterpret_cast<const int4*>(perm + kk);
           const int4 p1 = *reinterpret_cast<const int4*>(perm + kk + 4);
-          v[0] = uint32_t(arow[p0.x]) | (uint32_t(arow[p0.y]) << 16);
-          v[1] = uint32_t(arow[p0.z]) | (uint32_t(arow[p0.w]) << 16);
-          v[2] = uint32_t(arow[p1.x]) | (uint32_t(arow[p1.y]) << 16);
-          v[3] = uint32_t(arow[p1.z]) | (uint32_t(arow[p1.w]) << 16);
+          const uint32_t q[8] = {umin(uint32_t(p0.x), kmax), umin(uint32_t(p0.y), kmax),
+                                 umin(uint32_t(p0.z), kmax), umin(uint32_t(p0.w), kmax),
+                                 umin(uint32_t(p1.x), kmax), umin(uint32_t(p1.y), kmax),
+                                 umin(uint32_t(p1.z), kmax), umin(uint32_t(p1.w), kmax)};
+          v[0] = uint32_t(arow[q[0]]) | (uint32_t(arow[q[1]]) << 16);
+          v[1] = uint32_t(arow[q[2]]) | (uint32_t(arow[q[3]]) << 16);
+          v[2] = uint32_t(arow[q[4]]) | (uint32_t(arow[q[5]]) << 16);
+          v[3] = uint32_t(arow[q[6]]) | (uint32_t(arow[q[7]]) << 16);
         } else {
           const uint4 t4 = *reinterpret_cast<const uint4*>(arow + kk);
           v[0] = t4.x; v[1] = t4.y; v[2] = t4.z; v[3] = t4.w;
@@ -412,10 +385,19 @@ hipError_t launch_generic(const SpmmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Kernel choice.  variant 0 picks by shape; 1..5 force one kernel family when
-// the shape allows it (ablations, tests), else fall back to the choice by shape.
+// Kernel choice.  variant 0 picks by shape; 1..6 force one kernel family when
+// the shape allows it (ablations, tests), else fall back to the choice by
+// shape.  The permuted product with a large enough workspace gathers
+// X' = act[:, perm] into it once and multiplies X'; without one, the map is
+// applied while the kernel reads its input: in the few-token kernel
+// (T <= 16), the resident-tile kernel (2:4, K % 256 == 0, K <= 4096) or the
+// generic one.
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
   if (a.dtype == NM_I8 || a.dtype == NM_FP8) return launch_spmm_i8(a, s);  // 8-bit weights
+  if (a.perm != nullptr && a.workspace != nullptr) {
+    const size_t need = spmm_perm_gather_bytes(a.T, a.K, a.dtype);
+    if (need > 0 && a.workspace_bytes >= need) return launch_spmm_perm_gather(a, a.workspace, s);
+  }
   switch (a.variant) {
     case NM_VARIANT_GENERIC: return launch_generic(a, s);
     case NM_VARIANT_PIPE:
@@ -423,22 +405,23 @@ hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s) {
       break;
     case NM_VARIANT_LDS:
       if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
-      if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
       break;
     case NM_VARIANT_DECODE:
       if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
       break;
-    case NM_VARIANT_WIDE:
-      if (spmm_wide_applies(a)) return launch_spmm_wide(a, s);
+    case NM_VARIANT_RESIDENT:
+      if (spmm_resident_applies(a)) return launch_spmm_resident(a, s);
       break;
     case NM_VARIANT_LDS_NM:
       if (spmm_lds_nm_applies(a)) return launch_spmm_lds_nm(a, s);
       break;
     default: break;
   }
-  if (spmm_perm_gather_applies(a)) return launch_spmm_perm_gather(a, s);
   if (spmm_decode_applies(a)) return launch_spmm_decode(a, s);
-  if (spmm_perm_lds_applies(a)) return launch_spmm_perm_lds(a, s);
+  if (a.perm != nullptr) {
+    if (spmm_resident_applies(a)) return launch_spmm_resident(a, s);
+    return launch_generic(a, s);
+  }
   if (spmm_lds_applies(a)) return launch_spmm_lds(a, s);
   if (spmm_lds_nm_applies(a)) return launch_spmm_lds_nm(a, s);
   if (spmm_pipe_applies(a)) return launch_spmm_pipe(a, s);

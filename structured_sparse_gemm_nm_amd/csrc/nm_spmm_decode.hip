@@ -14,49 +14,14 @@
 //     first MFMA;
 //   * the 8 partial tiles are summed in LDS in a fixed order (deterministic).
 // Operand layouts and the 1:4 / 1:8 widening are those of nm_spmm.hip.
+#include "nm_device.h"
 #include "nm_internal.h"
 
 namespace nm {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
-
 constexpr int pat_n(int P) { return P == 0 ? 2 : 1; }
 constexpr int pat_m(int P) { return P == 2 ? 8 : 4; }
-
-template <int DT>
-__device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
-                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, 0);
-  } else {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
-                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, 0);
-  }
-}
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-template <int DT>
-__device__ inline uint16_t to_half_bits(float f) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-  } else {
-    return f32_to_bf16_rne(f);
-  }
-}
 
 struct AFrag {
   uint32_t v[4];
@@ -134,12 +99,19 @@ __device__ inline void load_bfrag(u32x8& b, const uint16_t* __restrict__ act, in
     const int k = s * 64 + h * 32 + lq * 8;
     if (k >= K) continue;
     if constexpr (PERM) {
+      // entries outside [0, K) (a broken precondition) are clamped into the
+      // row: a wrong value, never a wrong address
+      const uint32_t kmax = uint32_t(K - 1);
       const int4 p0 = *reinterpret_cast<const int4*>(perm + k);
       const int4 p1 = *reinterpret_cast<const int4*>(perm + k + 4);
-      b[4 * h + 0] = uint32_t(arow[p0.x]) | (uint32_t(arow[p0.y]) << 16);
-      b[4 * h + 1] = uint32_t(arow[p0.z]) | (uint32_t(arow[p0.w]) << 16);
-      b[4 * h + 2] = uint32_t(arow[p1.x]) | (uint32_t(arow[p1.y]) << 16);
-      b[4 * h + 3] = uint32_t(arow[p1.z]) | (uint32_t(arow[p1.w]) << 16);
+      const uint32_t q[8] = {umin(uint32_t(p0.x), kmax), umin(uint32_t(p0.y), kmax),
+                             umin(uint32_t(p0.z), kmax), umin(uint32_t(p0.w), kmax),
+                             umin(uint32_t(p1.x), kmax), umin(uint32_t(p1.y), kmax),
+                             umin(uint32_t(p1.z), kmax), umin(uint32_t(p1.w), kmax)};
+      b[4 * h + 0] = uint32_t(arow[q[0]]) | (uint32_t(arow[q[1]]) << 16);
+      b[4 * h + 1] = uint32_t(arow[q[2]]) | (uint32_t(arow[q[3]]) << 16);
+      b[4 * h + 2] = uint32_t(arow[q[4]]) | (uint32_t(arow[q[5]]) << 16);
+      b[4 * h + 3] = uint32_t(arow[q[6]]) | (uint32_t(arow[q[7]]) << 16);
     } else {
       const uint4 v = *reinterpret_cast<const uint4*>(arow + k);
       b[4 * h + 0] = v.x; b[4 * h + 1] = v.y; b[4 * h + 2] = v.z; b[4 * h + 3] = v.w;

@@ -34,75 +34,11 @@
 // with counted vmcnt waits and one fence-free barrier per step; every step
 // issues the same loads (past the last step a slot is refilled with that step
 // again), so the wait counts are constants.  Each tile fills its own ring.
+#include "nm_device.h"
 #include "nm_internal.h"
 
 namespace nm {
 namespace {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
-
-// ABID selects the 16-bit half of the index register the instruction reads.
-template <int DT, int ABID>
-__device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
-                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, ABID);
-  } else {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
-                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, ABID);
-  }
-}
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-template <int DT>
-__device__ inline uint16_t to_half_bits(float f) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-  } else {
-    return f32_to_bf16_rne(f);
-  }
-}
-
-__device__ inline void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ inline void wait_lgkm0() {
-  // lgkmcnt(0), vmcnt/expcnt untouched (gfx9 encoding)
-  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Buffer resource over [base, base + bytes): raw 32-bit data.  A lane whose
-// offset lies past `bytes` reads zeros and touches no memory.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
-}
-
-// 16 bytes per lane from base + voff + soff into LDS slot lds_dst + lane*16.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, unsigned char* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_byte*)lds_dst, 16, int(voff), int(soff), 0, 0);
-}
 
 constexpr int kBR = 128;
 constexpr int kBT = 64;

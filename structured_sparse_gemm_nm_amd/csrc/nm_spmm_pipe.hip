@@ -16,49 +16,14 @@
 //     whose slot the step's new loads then reuse.
 // The permuted product is not handled here (it gathers X through the index
 // map); shapes with K % 64 != 0 fall back as well.
+#include "nm_device.h"
 #include "nm_internal.h"
 
 namespace nm {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
-
 constexpr int pat_n(int P) { return P == 0 ? 2 : 1; }
 constexpr int pat_m(int P) { return P == 2 ? 8 : 4; }
-
-template <int DT>
-__device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, uint32_t idx) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(half8_t, a),
-                                                    __builtin_bit_cast(half16_t, b), c, int(idx), 0, 0);
-  } else {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
-                                                     __builtin_bit_cast(bf16_t, b), c, int(idx), 0, 0);
-  }
-}
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-template <int DT>
-__device__ inline uint16_t to_half_bits(float f) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-  } else {
-    return f32_to_bf16_rne(f);
-  }
-}
 
 // One lane's share of one 16-row A fragment for one K step.
 struct AFrag {
@@ -124,23 +89,6 @@ __device__ inline void widen(const AFrag& f, u32x4& a, uint32_t& idx16) {
     const uint32_t f0 = (p0 & 3u) * 5u, f1 = (p1 & 3u) * 5u;
     idx16 = (h0 ? (f0 << 4) : f0) | (h1 ? (f1 << 12) : (f1 << 8));
   }
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier without the memory fence __syncthreads() adds: the fence
-// would wait for every outstanding global load (vmcnt(0)) and drain the
-// prefetch pipeline.  Callers wait for exactly the loads they need first; the
-// empty asm statements keep the compiler from moving LDS accesses across.
-__device__ inline void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int P, int DT, int OUT, int BR, int BT, int NS>

@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol():
     assert {"nm_compress", "nm_spmm", "nm_spmm_perm", "nm_decompress", "nm_packed_sizes"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
-    assert L.nm_version() == 102
+    assert L.nm_version() == 200
+    assert not hasattr(L, "nm_set_variant")  # no process-wide kernel state
 
 
 def test_status_codes_match_header():
@@ -79,11 +80,11 @@ def st_compress(W=FAKE, R=4, K=64, ldw=64, dt=nm.NM_F16, n=2, m=4, v=FAKE * 2, i
 
 
 def st_spmm(values=FAKE, idx=FAKE * 2, R=32, K=64, n=2, m=4, dt=nm.NM_F16, act=FAKE * 3, T=8,
-            ldx=64, Y=FAKE * 4, ldy=32, od=nm.NM_F32, perm=None):
+            ldx=64, Y=FAKE * 4, ldy=32, od=nm.NM_F32, perm=None, ws=None, ws_bytes=0):
     L = nm.lib()
     if perm is None:
         return L.nm_spmm(values, idx, R, K, n, m, dt, act, T, ldx, Y, ldy, od, None)
-    return L.nm_spmm_perm(values, idx, R, K, n, m, dt, act, T, ldx, perm, Y, ldy, od, None)
+    return L.nm_spmm_perm(values, idx, R, K, n, m, dt, act, T, ldx, perm, Y, ldy, od, ws, ws_bytes, None)
 
 
 def test_compress_errors():
@@ -131,6 +132,10 @@ def test_spmm_errors():
     assert st_spmm(Y=FAKE + 32) == 5
     assert st_spmm(Y=FAKE * 2) == 5
     assert st_spmm(perm=FAKE * 4 + 64) == 5
+    # leading dimensions are bounded before any size product is formed
+    assert st_spmm(ldx=(1 << 62)) == 2
+    assert st_spmm(ldy=(1 << 62)) == 2
+    assert st_compress(ldw=(1 << 62)) == 2
     # empty products are no-ops
     assert st_spmm(T=0, values=None, idx=None, act=None, Y=None) == 0
     assert st_spmm(R=0, values=None, idx=None, act=None, Y=None, ldy=0) == 0
@@ -200,12 +205,18 @@ def test_decompress_and_misc_errors():
     assert L.nm_decompress(FAKE, FAKE * 2, 4, 64, 2, 4, nm.NM_F16, FAKE, 64, None) == 5
     assert L.nm_check_perm(None, 16, None) == 1
     assert L.nm_check_perm(FAKE, 0, None) == 2
-    assert L.nm_set_variant(8) == 3
-    assert L.nm_set_variant(7) == 3
-    assert L.nm_set_variant(-1) == 3
+
+    # the kernel family is an argument of the call: out-of-range families are
+    # refused; in-range ones with an empty product enqueue nothing
+    def st_var(v, perm=None, T=8):
+        return L.nm_spmm_variant(FAKE, FAKE * 2, 32, 64, 2, 4, nm.NM_F16, FAKE * 3, T, 64, perm,
+                                 FAKE * 4, 32, nm.NM_F32, None, 0, v, None)
+    assert st_var(7) == 3 and st_var(-1) == 3 and st_var(100) == 3
     for v in range(7):
-        assert L.nm_set_variant(v) == 0
-    assert L.nm_set_variant(0) == 0
+        assert st_var(v, T=0) == 0
+        assert st_var(v, perm=FAKE * 5, T=0) == 0
+    assert st_var(3, perm=FAKE * 5 + 4) == 7       # misaligned map
+    assert st_var(3, perm=FAKE * 4 + 64) == 5      # Y overlapping the map
 
 
 def test_binding_refuses_cpu_tensors():
@@ -213,3 +224,61 @@ def test_binding_refuses_cpu_tensors():
     W = torch.zeros((4, 64), dtype=torch.float16)
     with pytest.raises(ValueError):
         nm.nm_compress(W, 2, 4)
+
+
+def test_binding_checks_packed_shapes_before_the_device():
+    # The C ABI sees bare pointers, so the binding checks every tensor's shape,
+    # dtype, layout and device; these checks come before the device check and
+    # run here on CPU tensors.
+    torch = pytest.importorskip("torch")
+    R, K, T = 8, 64, 4
+    vals = torch.zeros((R, K // 2), dtype=torch.float16)
+    idx = torch.zeros((R, K // 32), dtype=torch.int32)
+    act = torch.zeros((T, K), dtype=torch.float16)
+
+    def err(fn):
+        with pytest.raises((ValueError, TypeError)) as e:
+            fn()
+        return str(e.value)
+
+    assert "contiguous [8, 32]" in err(lambda: nm.nm_spmm(vals[:, :16], idx, act, K))
+    assert "int32 [4, 2]" in err(lambda: nm.nm_spmm(vals[:4], idx, act, K))   # R is values' row count
+    assert "int32 [8, 2]" in err(lambda: nm.nm_spmm(vals, idx[:, :1], act, K))
+    assert "int32 [8, 2]" in err(lambda: nm.nm_spmm(vals, idx.to(torch.int64), act, K))
+    assert "int32 [8, 2]" in err(lambda: nm.nm_spmm(vals, idx.t().contiguous().t(), act, K))
+    assert "[T, 64]" in err(lambda: nm.nm_spmm(vals, idx, act[:, :32], K))
+    assert "out must be" in err(lambda: nm.nm_spmm(vals, idx, act, K, out=torch.zeros((T, R + 1))))
+    assert "perm must be" in err(lambda: nm.nm_spmm_perm(vals, idx, act, torch.arange(K - 8, dtype=torch.int32), K))
+    assert "perm must be" in err(lambda: nm.nm_spmm_perm(vals, idx, act, torch.arange(K), K))
+    assert "out must be" in err(lambda: nm.nm_decompress(vals, idx, K, out=torch.zeros((R, K - 16), dtype=torch.float16)))
+    assert "contiguous [8, 32]" in err(lambda: nm.nm_decompress(vals[:, :8], idx, K))
+    assert "int32 [8, 2]" in err(lambda: nm.nm_compress(torch.zeros((R, K), dtype=torch.float16), 2, 4,
+                                                         idx=torch.zeros((R, 1), dtype=torch.int32)))
+    # right shapes: only the device is wrong
+    assert "HIP device" in err(lambda: nm.nm_spmm(vals, idx, act, K))
+    assert "HIP device" in err(lambda: nm.nm_spmm_perm(vals, idx, act, torch.arange(K, dtype=torch.int32), K))
+    assert "HIP device" in err(lambda: nm.nm_decompress(vals, idx, K))
+
+
+def test_perm_workspace_size_and_checks():
+    # the gather pass takes T * K * 2 bytes of caller memory for 16-bit weights
+    # with K % 8 == 0, K <= 65536 and more than 16 tokens; otherwise the map is
+    # applied inside the kernel and no workspace is used
+    ws = nm.nm_spmm_perm_workspace_size
+    assert ws(3072, 768, 12608, 2, 4, nm.NM_F16) == 12608 * 768 * 2
+    assert ws(3072, 768, 12608, 1, 8, nm.NM_BF16) == 12608 * 768 * 2
+    assert ws(3072, 768, 16, 2, 4, nm.NM_F16) == 0            # few tokens: in the kernel
+    assert ws(4096, 65536 + 16, 64, 2, 4, nm.NM_F16) == 0     # rows too long for the gather
+    assert ws(0, 768, 64, 2, 4, nm.NM_F16) == 0
+    assert ws(64, 768, 64, 2, 4, nm.NM_I8) == 0
+    L = nm.lib()
+    assert L.nm_spmm_perm_workspace_size(8, 60, 64, 2, 4, nm.NM_F16, None) == 2   # K % 16
+    assert L.nm_spmm_perm_workspace_size(8, 64, 64, 2, 4, nm.NM_F16, None) == 1   # NULL out
+    # a workspace must be aligned and must not overlap any argument
+    P = FAKE * 5
+    assert st_spmm(perm=P, ws=FAKE * 6 + 8, ws_bytes=4096) == 7
+    assert st_spmm(perm=P, ws=FAKE * 3 + 256, ws_bytes=4096) == 5   # overlaps act
+    assert st_spmm(perm=P, ws=FAKE * 4 - 64, ws_bytes=4096) == 5    # overlaps Y
+    assert st_spmm(perm=P, ws=FAKE * 5 - 16, ws_bytes=64) == 5      # overlaps perm
+    # a zero-size workspace is no workspace (only the shape is checked here)
+    assert st_spmm(perm=P, ws=FAKE * 6 + 8, ws_bytes=0, T=0) == 0

@@ -10,7 +10,8 @@ import pytest
 import nm_inputs
 import structured_sparse_gemm_nm_amd as nm
 from oracle import nm_oracle as O
-from gpu_util import (assert_close, bits_of, error_bound, log, oracle_pack, to_dev, words_of)
+from gpu_util import (assert_close, bits_of, error_bound, log, oracle_pack, to_dev, torch_dtype,
+                      words_of)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -158,10 +159,13 @@ def test_integer_gemm_exact(R, K, T, n, m):
     act = nm_inputs.integer_half((T, K), -2, 2, "f16", 44, 1, K)
     vals, idx = gpu_compress(w, "f16", n, m)
     y = nm.nm_spmm(vals, idx, to_dev(act, "f16"), K, n, m)
+    # the resident-tile family (2:4, K % 256 == 0) on the same input
+    y5 = nm.nm_spmm(vals, idx, to_dev(act, "f16"), K, n, m, variant=5)
     torch.cuda.synchronize()
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "f16")
     assert np.array_equal(y.cpu().numpy().astype(np.float64).T, yref)
+    assert np.array_equal(y5.cpu().numpy().astype(np.float64).T, yref)
 
 
 # ---------------------------------------------------------------------------
@@ -179,18 +183,132 @@ def test_perm_properties(n, m):
     A = to_dev(act, "f16")
     P = torch.from_numpy(perm).cuda()
     nm.nm_check_perm(P)
-    y_perm = nm.nm_spmm_perm(vals, idx, A, P, K, n, m)
     ident = torch.arange(K, dtype=torch.int32, device="cuda")
-    y_id = nm.nm_spmm_perm(vals, idx, A, ident, K, n, m)
-    y_plain = nm.nm_spmm(vals, idx, A, K, n, m)
     A_perm = A[:, P.long()].contiguous()
-    y_gathered = nm.nm_spmm(vals, idx, A_perm, K, n, m)
-    torch.cuda.synchronize()
-    assert torch.equal(y_id, y_plain)                 # identity map = plain product
-    assert torch.equal(y_perm, y_gathered)            # index map = reading a permuted copy
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "f16", perm=perm)
-    assert_close(y_perm, yref, error_bound(ref_vals, ref_idx, K, n, m, act, "f16", perm=perm))
+    bound = error_bound(ref_vals, ref_idx, K, n, m, act, "f16", perm=perm)
+    yref_id = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "f16")
+    bound_id = error_bound(ref_vals, ref_idx, K, n, m, act, "f16")
+    # the gather pass into a workspace, then the kernel the plain product takes
+    y_perm = nm.nm_spmm_perm(vals, idx, A, P, K, n, m)
+    y_id = nm.nm_spmm_perm(vals, idx, A, ident, K, n, m)
+    y_copy = nm.nm_spmm(vals, idx, A_perm, K, n, m)
+    y_plain = nm.nm_spmm(vals, idx, A, K, n, m)
+    # the map applied inside the kernel (no workspace): compared with the
+    # family it takes, named, on the explicitly permuted copy
+    fam = 5 if (n, m) == (2, 4) else 1
+    z_perm = nm.nm_spmm_perm(vals, idx, A, P, K, n, m, workspace=None)
+    z_id = nm.nm_spmm_perm(vals, idx, A, ident, K, n, m, workspace=None)
+    z_copy = nm.nm_spmm(vals, idx, A_perm, K, n, m, variant=fam)
+    z_plain = nm.nm_spmm(vals, idx, A, K, n, m, variant=fam)
+    torch.cuda.synchronize()
+    assert torch.equal(y_perm, y_copy) and torch.equal(z_perm, z_copy)   # map = permuted copy
+    assert torch.equal(y_id, y_plain) and torch.equal(z_id, z_plain)     # identity map = plain
+    for y in (y_perm, z_perm):
+        assert_close(y, yref, bound)
+    for y in (y_id, z_id):
+        assert_close(y, yref_id, bound_id)
+
+
+# Every kernel family that reads activations through the map, on shapes that
+# span several tiles and ragged tails: the resident-tile kernel (5: 64, 32 and
+# 16 tokens per tile; row passes split across units when tokens are few; a
+# partial last pass and token tile; fp32 and half outputs), the generic kernel
+# (1) and the few-token kernel (4), each against the oracle and bit for bit
+# against the same family on an explicitly permuted copy of the activations.
+PERM_CASES = [
+    # (R, K, T, dtype, family, out)
+    (3072, 768, 12608, "f16", 5, "f32"),    # the permuted ViT-B/16 fc1 workload at full size
+    (3072, 768, 197, "f16", 5, "f32"),      # one ViT image's tokens: a partial token tile
+    (300, 768, 100, "bf16", 5, "f32"),      # ragged rows: a partial pass of 512
+    (300, 768, 100, "f16", 5, "half"),
+    (1000, 512, 700, "bf16", 5, "half"),    # R % 8 == 0 (unconditional half stores)
+    (520, 1024, 130, "f16", 5, "f32"),      # K = 1024: 64-token tiles at the LDS limit
+    (700, 2048, 70, "bf16", 5, "f32"),      # 32-token tiles
+    (256, 4096, 40, "f16", 5, "half"),      # 16-token tiles
+    (130, 256, 1500, "bf16", 5, "f32"),     # one block pair per pass, many units per CU
+    (300, 768, 100, "f16", 1, "f32"),       # generic, element gather
+    (258, 640, 65, "bf16", 1, "half"),      # generic, K % 128 != 0
+    (77, 336, 7, "f16", 4, "f32"),          # few tokens
+    (1030, 1024, 16, "bf16", 4, "half"),
+]
+
+
+@pytest.mark.parametrize("R,K,T,dt,fam,out", PERM_CASES)
+def test_perm_families(R, K, T, dt, fam, out):
+    log(f"perm family {fam} R={R} K={K} T={T} {dt} out={out}")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 48, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 48, 1, R + K + T)
+    perm = nm_inputs.random_permutation(K, 48, R + T)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    P = torch.from_numpy(perm).cuda()
+    od = torch_dtype(dt) if out == "half" else torch.float32
+    y = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4, out_dtype=od, variant=fam, workspace=None)
+    y_copy = nm.nm_spmm(vals, idx, A[:, P.long()].contiguous(), K, 2, 4, out_dtype=od, variant=fam)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_copy)
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm),
+                 **({"out_half": dt} if out == "half" else {}))
+
+
+# The default choice for the permuted product, with a workspace (the gather
+# pass, walking more row blocks than workgroups for (128, 768, 11000) and
+# (128, 8192, 2100); rows longer than the walking variant takes for
+# (130, 8448, 70)) and without one (the map inside the kernel), on shapes of
+# every family; with a workspace the result equals the plain product of the
+# explicitly permuted copy bit for bit.
+@pytest.mark.parametrize("ws", ["auto", None])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("R,K,T", [(300, 768, 100), (512, 128, 64), (256, 640, 130), (3072, 768, 197),
+                                   (128, 768, 11000), (128, 8192, 2100), (130, 8448, 70)])
+def test_perm_prefill(R, K, T, dt, ws):
+    log(f"perm prefill R={R} K={K} T={T} {dt} workspace={ws}")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 48, 0, R + K + T)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 48, 1, R + K + T)
+    perm = nm_inputs.random_permutation(K, 48, R + T)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    P = torch.from_numpy(perm).cuda()
+    y = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4, workspace=ws)
+    if ws is not None:
+        y_copy = nm.nm_spmm(vals, idx, A[:, P.long()].contiguous(), K, 2, 4)
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert torch.equal(y, y_copy)
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
+
+
+def test_perm_workspace_caller_tensor():
+    # a caller-owned workspace with room to spare is used and left to the caller;
+    # one too small makes the kernel apply the map itself
+    R, K, T, dt = 256, 512, 300, "bf16"
+    log("perm caller workspace")
+    w = nm_inputs.normal_half((R, K), 0.02, dt, 49, 0, 1)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 49, 1, 1)
+    perm = nm_inputs.random_permutation(K, 49, 1)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    P = torch.from_numpy(perm).cuda()
+    need = nm.nm_spmm_perm_workspace_size(R, K, T, 2, 4, nm.NM_BF16)
+    assert need == T * K * 2
+    big = torch.full((need + 4096,), 7, dtype=torch.uint8, device="cuda")
+    small = torch.full((need - 16,), 7, dtype=torch.uint8, device="cuda")
+    y_big = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4, workspace=big)
+    y_small = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.all(big[need:] == 7)          # nothing written past T * K * 2
+    assert torch.all(small == 7)               # too small: not touched
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    bound = error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
+    assert_close(y_big, yref, bound)
+    assert_close(y_small, yref, bound)
 
 
 def test_check_perm_rejects_non_permutation():
@@ -274,35 +392,6 @@ def test_spmm_few_tokens(R, K, T, permuted, n, m):
     assert_close(y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt, perm=perm))
 
 
-# ---------------------------------------------------------------------------
-# permuted 2:4 prefill path (X tile gathered through perm from LDS)
-# ---------------------------------------------------------------------------
-
-# (128, 768, 11000) and (128, 8192, 2100): more row blocks than gather
-# workgroups, so workgroups walk blocks through both LDS buffers;
-# (130, 8448, 70): rows longer than the walking gather takes
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("R,K,T", [(300, 768, 100), (512, 128, 64), (256, 640, 130), (3072, 768, 197),
-                                   (128, 768, 11000), (128, 8192, 2100), (130, 8448, 70)])
-def test_perm_prefill(R, K, T, dt):
-    log(f"perm prefill R={R} K={K} T={T} {dt}")
-    w = nm_inputs.normal_half((R, K), 0.02, dt, 48, 0, R + K + T)
-    act = nm_inputs.normal_half((T, K), 1.0, dt, 48, 1, R + K + T)
-    perm = nm_inputs.random_permutation(K, 48, R + T)
-    vals, idx = gpu_compress(w, dt, 2, 4)
-    A = to_dev(act, dt)
-    P = torch.from_numpy(perm).cuda()
-    y = nm.nm_spmm_perm(vals, idx, A, P, K, 2, 4)
-    # every prefill kernel adds the K steps in order from zero, so reading a
-    # permuted copy must give the same bits
-    y_copy = nm.nm_spmm(vals, idx, A[:, P.long()].contiguous(), K, 2, 4)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y_copy)
-    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
-    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
-    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm))
-
-
 def test_out_tensor_checked():
     R, K, T = 64, 128, 16
     w = nm_inputs.normal_half((R, K), 0.02, "f16", 53, 0, 1)
@@ -331,19 +420,12 @@ def test_kernel_families_agree(n, m):
     act = nm_inputs.normal_half((T, K), 1.0, "bf16", 49, 1, m)
     vals, idx = gpu_compress(w, "bf16", n, m)
     A = to_dev(act, "bf16")
-    outs = {}
-    try:
-        for v in (1, 2, 3, 5, 6):
-            nm.nm_set_variant(v)
-            outs[v] = nm.nm_spmm(vals, idx, A, K, n, m)
-        nm.nm_set_variant(4)
-        y_few = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m)
-        nm.nm_set_variant(1)
-        y_few_ref = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m)
-    finally:
-        nm.nm_set_variant(0)
+    outs = {v: nm.nm_spmm(vals, idx, A, K, n, m, variant=v) for v in (1, 2, 3, 5, 6)}
+    y_few = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m, variant=4)
+    y_few_ref = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m, variant=1)
     torch.cuda.synchronize()
     # families that add the K steps in order from zero give identical bits
+    # (a family that does not take the shape falls back to the choice by shape)
     assert torch.equal(outs[1], outs[2]) and torch.equal(outs[1], outs[3])
     assert torch.equal(outs[1], outs[5]) and torch.equal(outs[1], outs[6])
     ref_vals, ref_idx = O.prune_pack(w, n, m)
@@ -370,13 +452,8 @@ def test_lds_tile_walk(R, K, T, out):
     vals, idx = gpu_compress(w, dt, 2, 4)
     A = to_dev(act, dt)
     od = torch.bfloat16 if out == "half" else torch.float32
-    try:
-        nm.nm_set_variant(3)
-        y = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od)
-        nm.nm_set_variant(1)
-        y_gen = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od)
-    finally:
-        nm.nm_set_variant(0)
+    y = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od, variant=3)
+    y_gen = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=od, variant=1)
     torch.cuda.synchronize()
     # both add the K steps in order from zero
     assert torch.equal(y, y_gen)
@@ -404,13 +481,8 @@ def test_lds_nm(R, K, T, dt, out, n, m):
     A = to_dev(act, dt)
     tdt = torch.float16 if dt == "f16" else torch.bfloat16
     od = tdt if out == "half" else torch.float32
-    try:
-        nm.nm_set_variant(6)
-        y = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od)
-        nm.nm_set_variant(2)
-        y_pipe = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od)
-    finally:
-        nm.nm_set_variant(0)
+    y = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od, variant=6)
+    y_pipe = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od, variant=2)
     torch.cuda.synchronize()
     # same widened operands, K steps added in the same order
     assert torch.equal(y, y_pipe)
@@ -441,14 +513,10 @@ def test_decode_stream(R, K, T, dt, permuted):
     vals, idx = gpu_compress(w, dt, 2, 4)
     A = to_dev(act, dt)
     perm = nm_inputs.random_permutation(K, 51, R) if permuted else None
-    try:
-        nm.nm_set_variant(4)
-        if perm is None:
-            y = nm.nm_spmm(vals, idx, A, K, 2, 4)
-        else:
-            y = nm.nm_spmm_perm(vals, idx, A, torch.from_numpy(perm).cuda(), K, 2, 4)
-    finally:
-        nm.nm_set_variant(0)
+    if perm is None:
+        y = nm.nm_spmm(vals, idx, A, K, 2, 4, variant=4)
+    else:
+        y = nm.nm_spmm_perm(vals, idx, A, torch.from_numpy(perm).cuda(), K, 2, 4, variant=4, workspace=None)
     torch.cuda.synchronize()
     ref_vals, ref_idx = O.prune_pack(w, 2, 4)
     yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt, perm=perm)
@@ -486,11 +554,7 @@ def test_i8_bit_exact(R, K, T):
     assert np.array_equal(dense.cpu().numpy(), O.decompress_i8(ref_vals, ref_idx, K, 2, 4))
     yref = O.spmm_ref_i8(ref_vals, ref_idx, K, 2, 4, act)
     assert np.array_equal(y.cpu().numpy().T.astype(np.int64), yref)
-    try:  # the register-operand kernel on the same input
-        nm.nm_set_variant(1)
-        y1 = nm.nm_spmm(vals, idx, _i8(act), K, 2, 4)
-    finally:
-        nm.nm_set_variant(0)
+    y1 = nm.nm_spmm(vals, idx, _i8(act), K, 2, 4, variant=1)  # the register-operand kernel
     torch.cuda.synchronize()
     assert torch.equal(y1, y)
 
@@ -569,11 +633,8 @@ def _f8_case(w, act, K, cross_check=True):
     assert_close(y, yref, tol=1e-2)
     _abs_sum_bound(y, yref, ref_vals, ref_idx, K, act)
     if cross_check:
-        try:  # the register-operand kernel: the same MFMA sequence per tile
-            nm.nm_set_variant(1)
-            y1 = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4)
-        finally:
-            nm.nm_set_variant(0)
+        # the register-operand kernel: the same MFMA sequence per tile
+        y1 = nm.nm_spmm(vals, idx, _f8(act), K, 2, 4, variant=1)
         torch.cuda.synchronize()
         assert torch.equal(y1, y)
     return y, yref
