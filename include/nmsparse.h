@@ -194,6 +194,23 @@ nm_status nm_spmm_perm_workspace_size(int64_t R, int64_t K, int64_t T, int n, in
                                       size_t* bytes);
 
 /*
+ * nm_spmm_perm for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * product, with the gather pass's workspace taken from a device array the
+ * library holds on each GPU it runs on, 32 MiB (33554432 bytes), from first
+ * use until the process ends.  Shapes whose workspace (nm_spmm_perm_workspace_size)
+ * exceeds 32 MiB are refused with NM_ERR_SHAPE before anything is enqueued;
+ * shapes with no gather pass (T <= 16, ...) use no workspace.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give wrong results;
+ * calls ordered on one stream are safe.  Allocates nothing and synchronises
+ * nothing; arguments and errors as nm_spmm_perm.
+ */
+nm_status nm_spmm_perm_static(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n,
+                              int m, int dtype, const void* act, int64_t T, int64_t ldx,
+                              const int32_t* perm, void* Y, int64_t ldy, int out_dtype, void* stream);
+
+/*
  * Host-side check that perm is a permutation of 0..K-1 (copies perm to the
  * host and synchronises `stream`).  NM_ERR_SHAPE if it is not.  Debug aid.
  */

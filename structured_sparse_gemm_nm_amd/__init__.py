@@ -16,7 +16,7 @@ import os
 
 __all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NM_FP8", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
-           "nm_spmm_perm_workspace_size", "nm_check_perm", "PATTERNS"]
+           "nm_spmm_perm_workspace_size", "nm_spmm_perm_static", "nm_check_perm", "PATTERNS"]
 
 NM_OK = 0
 NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, i32, vp]
     L.nm_spmm_perm.restype = i32
     L.nm_spmm_perm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp, sz, vp]
+    L.nm_spmm_perm_static.restype = i32
+    L.nm_spmm_perm_static.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp]
     L.nm_spmm_perm_workspace_size.restype = i32
     L.nm_spmm_perm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
     L.nm_check_perm.restype = i32
@@ -214,6 +216,12 @@ def nm_spmm_perm(values, idx, act, perm, K: int, n: int = 2, m: int = 4, out_dty
     return _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace)
 
 
+def nm_spmm_perm_static(values, idx, act, perm, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None):
+    """nm_spmm_perm with the library's static per-GPU workspace (no allocation in
+    the library; calls that overlap in time on one GPU race)."""
+    return _spmm(values, idx, act, K, n, m, perm, out_dtype, out, 0, "static")
+
+
 def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):
     torch = _torch()
     _row_major(act, "act")
@@ -249,10 +257,11 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):
             raise ValueError("perm must be on the device of act")
     ws = None
     if perm is not None and isinstance(workspace, str):
-        if workspace != "auto":
+        if workspace not in ("auto", "static"):
             raise ValueError('workspace must be "auto", None or a device tensor')
-        need = nm_spmm_perm_workspace_size(R, K, T, n, m, dt)
-        ws = torch.empty(need, dtype=torch.uint8, device=act.device) if need else None
+        if workspace == "auto":
+            need = nm_spmm_perm_workspace_size(R, K, T, n, m, dt)
+            ws = torch.empty(need, dtype=torch.uint8, device=act.device) if need else None
     elif perm is not None and workspace is not None:
         ws = workspace
         if not ws.is_contiguous() or ws.device != act.device:
@@ -264,7 +273,10 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):
     L = lib()
     ws_ptr = None if ws is None else ws.data_ptr()
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    if variant:
+    if perm is not None and workspace == "static":
+        st = L.nm_spmm_perm_static(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,
+                                   act.stride(0), perm.data_ptr(), out.data_ptr(), out.stride(0), od, stream)
+    elif variant:
         st = L.nm_spmm_variant(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, act.data_ptr(), T,
                                act.stride(0), None if perm is None else perm.data_ptr(), out.data_ptr(),
                                out.stride(0), od, ws_ptr, ws_bytes, variant, stream)

@@ -103,7 +103,7 @@ nm_status hip_status(hipError_t e, const char* what) {
 nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                       int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
                       bool want_perm, void* Y, int64_t ldy, int out_dtype, void* workspace,
-                      size_t workspace_bytes, int variant, void* stream) {
+                      size_t workspace_bytes, int variant, void* stream, bool static_ws = false) {
   nm_status st = check_format(R, K, n, m, dtype);
   if (st != NM_OK) return st;
   if (variant < 0 || variant > nm::NM_VARIANT_MAX)
@@ -139,8 +139,24 @@ nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_
   if (overlaps(Y, ybytes, values, z.values_bytes) || overlaps(Y, ybytes, idx, z.idx_bytes) ||
       overlaps(Y, ybytes, act, abytes) || (want_perm && overlaps(Y, ybytes, perm, size_t(K) * 4)))
     return fail(NM_ERR_ALIAS, "Y overlaps an input");
-  if (workspace_bytes == 0) workspace = nullptr;
-  if (workspace) {
+  if (static_ws) {
+    // the library's own array: a size it cannot hold is refused (before any
+    // HIP call); its address is looked up only once validation has passed
+    const size_t need = nm::spmm_perm_gather_bytes(T, K, dtype);
+    if (need > nm::kStaticWorkspaceBytes)
+      return fail(NM_ERR_SHAPE, "T*K*2 = %zu bytes exceeds the static workspace (%zu bytes)", need,
+                  nm::kStaticWorkspaceBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const hipError_t e = nm::static_workspace(&workspace);
+      if (e != hipSuccess) return hip_status(e, "static workspace address");
+      workspace_bytes = nm::kStaticWorkspaceBytes;
+    }
+  } else if (workspace_bytes == 0) {
+    workspace = nullptr;
+  }
+  if (workspace && !static_ws) {
     if (!aligned16(workspace)) return fail(NM_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (overlaps(workspace, workspace_bytes, Y, ybytes) || overlaps(workspace, workspace_bytes, act, abytes) ||
         overlaps(workspace, workspace_bytes, values, z.values_bytes) ||
@@ -329,6 +345,13 @@ nm_status nm_spmm_perm(const void* values, const uint32_t* idx, int64_t R, int64
                        void* stream) {
   return spmm_common(values, idx, R, K, n, m, dtype, act, T, ldx, perm, true, Y, ldy, out_dtype,
                      workspace, workspace_bytes, 0, stream);
+}
+
+nm_status nm_spmm_perm_static(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n,
+                              int m, int dtype, const void* act, int64_t T, int64_t ldx,
+                              const int32_t* perm, void* Y, int64_t ldy, int out_dtype, void* stream) {
+  return spmm_common(values, idx, R, K, n, m, dtype, act, T, ldx, perm, true, Y, ldy, out_dtype,
+                     nullptr, 0, 0, stream, true);
 }
 
 nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,

@@ -66,6 +66,11 @@ hipError_t launch_spmm_decode(const SpmmArgs& a, hipStream_t s);
 size_t spmm_perm_gather_bytes(int64_t T, int64_t K, int dtype);
 hipError_t launch_spmm_perm_gather(const SpmmArgs& a, void* workspace, hipStream_t s);
 
+// The file-scope device array nm_spmm_perm_static uses as its workspace
+// (nm_permute.hip): its size, and its address on the current device.
+constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
+hipError_t static_workspace(void** ptr);
+
 // 2:4 kernel with the token tile resident in LDS, plain or through the index
 // map (nm_spmm_resident.hip), and the shapes it takes.
 bool spmm_resident_applies(const SpmmArgs& a);

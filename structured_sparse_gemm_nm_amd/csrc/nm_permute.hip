@@ -23,6 +23,9 @@
 #include "nm_device.h"
 #include "nm_internal.h"
 
+#include <map>
+#include <mutex>
+
 namespace nm {
 namespace {
 
@@ -160,6 +163,30 @@ __global__ __launch_bounds__(kThreads) void permute_cols_db_kernel(
 }
 
 }  // namespace
+
+// The allocation-free entry point's workspace: one array per GPU, held until
+// the process ends.  Host code never uses the array's name as an address (on
+// the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
 
 // The gather pass takes 16-bit activations with K % 8 == 0 (16-byte chunks)
 // and K <= 65536; few tokens (T <= 16) gather inside the few-token kernel.

@@ -282,3 +282,16 @@ def test_perm_workspace_size_and_checks():
     assert st_spmm(perm=P, ws=FAKE * 5 - 16, ws_bytes=64) == 5      # overlaps perm
     # a zero-size workspace is no workspace (only the shape is checked here)
     assert st_spmm(perm=P, ws=FAKE * 6 + 8, ws_bytes=0, T=0) == 0
+
+
+def test_static_workspace_refuses_oversize_on_host():
+    # nm_spmm_perm_static holds a 32 MiB array per GPU: a gather needing more is
+    # refused during validation, before any HIP call (fake pointers)
+    L = nm.lib()
+    G = 1 << 36   # fake buffers far apart, so the large extents do not overlap
+    def st(K, T):
+        return L.nm_spmm_perm_static(G, 2 * G, 32, K, 2, 4, nm.NM_F16, 3 * G, T, K, 5 * G,
+                                     4 * G, 32, nm.NM_F32, None)
+    assert st(4096, 4097) == 2                     # 4096 * 4097 * 2 > 32 MiB
+    assert "static workspace" in L.nm_last_error().decode()
+    assert st(4096, 0) == 0                        # empty product
