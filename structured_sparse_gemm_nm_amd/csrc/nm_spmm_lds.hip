@@ -232,8 +232,9 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
   // steps 1 .. kNS-1, so the waits for those steps may leave the stores
   // outstanding: they drain under three steps of MFMAs instead of holding up
   // the first.  Only after a full tile, whose waves each issued at least
-  // kStores stores (fewer would let such a wait pass early).
-  constexpr int kStores = FR * FT;
+  // kStores stores (fewer would let such a wait pass early; half outputs
+  // store 8 rows per lane, so half as many).
+  constexpr int kStores = OUT == NM_F32 ? FR * FT : (FR / 2) * FT;
   bool stores_behind = false;
   int qb = 0;   // index-buffer parity of the tile's block 0
 
@@ -384,33 +385,54 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     }
 
     // ---- epilogue
-    const bool vec_ok = (ldy & 3) == 0;
     stores_behind = R0 + kBR <= R && T0 + kBT <= T;
+    if constexpr (OUT == NM_F32) {
+      const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < FR; ++i) {
-      const int r = R0 + wr * 128 + i * 16 + lq * 4;
+      for (int i = 0; i < FR; ++i) {
+        const int r = R0 + wr * 128 + i * 16 + lq * 4;
 #pragma unroll
-      for (int j = 0; j < FT; ++j) {
-        const int t = T0 + wt * (kBT / 2) + j * 16 + li;
-        if (t >= T || r >= R) continue;
-        const f32x4 v = acc[i][j];
-        if constexpr (OUT == NM_F32) {
+        for (int j = 0; j < FT; ++j) {
+          const int t = T0 + wt * (kBT / 2) + j * 16 + li;
+          if (t >= T || r >= R) continue;
+          const f32x4 v = acc[i][j];
           float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
           if (vec_ok && r + 3 < R) {
             *reinterpret_cast<f32x4*>(y) = v;
           } else {
             for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
           }
-        } else {
+        }
+      }
+    } else {
+      // Half outputs: fragments i and i+1 (32 rows) are exchanged across lane
+      // quarters so that quarter q holds rows 8q .. 8q+7 of the pair, and a
+      // lane stores 16 contiguous bytes: a token row gets 64-byte runs, not
+      // the 32-byte runs of 4 rows per lane.
+      const bool vec_ok = (ldy & 7) == 0;
+#pragma unroll
+      for (int i = 0; i < FR; i += 2) {
+        const int r = R0 + wr * 128 + i * 16 + lq * 8;
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
+          const uint32_t x0 = pack_half2<DT>(acc[i][j][0], acc[i][j][1]);
+          const uint32_t x1 = pack_half2<DT>(acc[i][j][2], acc[i][j][3]);
+          const uint32_t y0 = pack_half2<DT>(acc[i + 1][j][0], acc[i + 1][j][1]);
+          const uint32_t y1 = pack_half2<DT>(acc[i + 1][j][2], acc[i + 1][j][3]);
+          // lanes 32..63 of x <-> lanes 0..31 of y, then odd 16-lane rows of
+          // x <-> even rows of y
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+          const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+          const int t = T0 + wt * (kBT / 2) + j * 16 + li;
+          if (t >= T || r >= R) continue;
+          const u32x4 v = {t0[0], t1[0], t0[1], t1[1]};   // rows r .. r+7
           uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
-          const uint16_t h0 = to_half_bits<DT>(v[0]), h1 = to_half_bits<DT>(v[1]);
-          const uint16_t h2 = to_half_bits<DT>(v[2]), h3 = to_half_bits<DT>(v[3]);
-          if (vec_ok && r + 3 < R) {
-            *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(h0) | (uint32_t(h1) << 16),
-                                                      uint32_t(h2) | (uint32_t(h3) << 16));
+          if (vec_ok && r + 7 < R) {
+            *reinterpret_cast<u32x4*>(y) = v;
           } else {
-            const uint16_t hh[4] = {h0, h1, h2, h3};
-            for (int e = 0; e < 4 && r + e < R; ++e) y[e] = hh[e];
+            for (int e = 0; e < 8 && r + e < R; ++e) y[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
           }
         }
       }

@@ -349,6 +349,31 @@ def test_spmm_ragged(R, K, T, n, m):
     assert_close(Y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt))
 
 
+# half outputs of the tile kernels store 8 rows per lane (fragment pairs
+# exchanged across lane quarters): ragged rows, a leading dimension that is or
+# is not a multiple of 8, and canary columns past R
+@pytest.mark.parametrize("fam", [3, 5])
+@pytest.mark.parametrize("R,ldy_pad", [(300, 4), (300, 8), (301, 7), (512, 0)])
+def test_half_output_edges(R, ldy_pad, fam):
+    K, T, dt = 512, 200, "bf16"
+    log(f"half edges R={R} pad={ldy_pad} family={fam}")
+    w = nm_inputs.normal_half((R, K), 0.5, dt, 54, 0, R + ldy_pad)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 54, 1, R + ldy_pad)
+    vals, idx = gpu_compress(w, dt, 2, 4)
+    A = to_dev(act, dt)
+    ldy = R + ldy_pad
+    Yfull = torch.full((T, ldy), 77.0, dtype=torch.bfloat16, device="cuda")
+    Y = Yfull[:, :R]
+    nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=torch.bfloat16, out=Y, variant=fam)
+    y1 = nm.nm_spmm(vals, idx, A, K, 2, 4, out_dtype=torch.bfloat16, variant=1)
+    torch.cuda.synchronize()
+    assert torch.all(Yfull[:, R:] == 77.0), "write outside the output"
+    assert torch.equal(Y, y1)     # same sums, same rounding as the generic family
+    ref_vals, ref_idx = O.prune_pack(w, 2, 4)
+    yref = O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt)
+    assert_close(Y, yref, error_bound(ref_vals, ref_idx, K, 2, 4, act, dt), out_half=dt)
+
+
 def test_spmm_deterministic_and_empty():
     log("determinism")
     wl = nm_inputs.WORKLOADS[1]
@@ -443,6 +468,7 @@ def test_kernel_families_agree(n, m):
 
 @pytest.mark.parametrize("R,K,T,out", [(2200, 256, 3900, "f32"), (2200, 384, 3900, "f32"),
                                        (2200, 640, 3900, "f32"), (2200, 768, 3900, "half"),
+                                       (2205, 256, 3900, "half"),
                                        (2200, 1408, 3900, "f32"), (4100, 256, 4000, "f32")])
 def test_lds_tile_walk(R, K, T, out):
     log(f"lds tile walk R={R} K={K} T={T} out={out}")
