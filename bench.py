@@ -18,8 +18,10 @@ Prints one JSON line (rank 0, N = 1):
                compressions first, then their products)
   cpu_baseline the CPU oracle (NumPy, fp64) timed on this host over the same
                workload
-  kernels      per-kernel means (sparse GEMM, compress, dense hipBLASLt GEMM
-               of the same shape) and the speedup over the dense GEMM
+  kernels      per-kernel means (sparse GEMM with fp32 and with half output,
+               compress, dense hipBLASLt GEMMs of the same shape with the same
+               output dtypes), timed in alternating blocks, and the speedup
+               over the dense GEMM at equal output dtype
 """
 from __future__ import annotations
 
@@ -295,52 +297,29 @@ def main():
     compress_mean_us = start.elapsed_time(mid) * 1e3 / args.steps
     gemm_mean_us = mid.elapsed_time(end) * 1e3 / args.steps
 
-    # ---- per-kernel breakdown (back-to-back launches of one kernel)
-    def time_loop(fn, iters):
-        for i in range(5):
-            fn(i % rotate)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(iters):
-            fn(i % rotate)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / iters
-
-    iters = max(20, args.steps)
-    gemm_loop_us = time_loop(gemm, iters)
-    compress_us = time_loop(compress, iters)
+    # ---- per-kernel breakdown.  Each kernel is timed over blocks of `iters`
+    # back-to-back launches, and the blocks of all kernels alternate round
+    # robin (five rounds, median per kernel): a kernel timed right after a long
+    # run of another one (a dense GEMM heats the chip and lowers its clock)
+    # would otherwise carry that other kernel's after-effects.
     dense = []
     for c in range(rotate):
         dense.append(nm.nm_decompress(copies[c][2], copies[c][3], K, n, m))
     actp = [copies[c][1] if perm is None else copies[c][1][:, perm.long()].contiguous()
             for c in range(rotate)]
+    # W^T as its own row-major [K, R] tensor (no transposed views in the dense calls)
+    dense_t = [d.t().contiguous() for d in dense]
 
+    loops = {"gemm": gemm, "compress": compress}
     if i8:
         # dense int8 GEMM with an int32 result (hipBLASLt through torch._int_mm)
-        dense_t = [d.t() for d in dense]  # [K, R], column-major view of the row-major W
-
-        def dense_gemm(c):
-            torch._int_mm(actp[c], dense_t[c])
+        loops["dense_same_out"] = lambda c: torch._int_mm(actp[c], dense_t[c])
     elif f8:
         # dense fp8 GEMM with an fp32 result (hipBLASLt through torch._scaled_mm, unit scales)
-        dense_t = [d.t() for d in dense]
         one = torch.ones((), dtype=torch.float32, device="cuda")
-
-        def dense_gemm(c):
-            torch._scaled_mm(actp[c], dense_t[c], scale_a=one, scale_b=one, out_dtype=torch.float32)
+        loops["dense_same_out"] = lambda c: torch._scaled_mm(actp[c], dense_t[c], scale_a=one, scale_b=one,
+                                                             out_dtype=torch.float32)
     else:
-        def dense_gemm(c):
-            torch.nn.functional.linear(actp[c], dense[c])
-
-    try:
-        dense_us = time_loop(dense_gemm, iters)
-    except RuntimeError as e:  # no dense 8-bit GEMM for this shape / build
-        print(f"dense reference unavailable: {e}", file=sys.stderr)
-        dense_us = None
-    gemm_half_us = None
-    if not b8:  # a rounded half-precision output (8-bit weights have a 4-byte one only)
         y_half = torch.empty((T, R), dtype=tdt, device="cuda")
 
         def gemm_half(c):
@@ -351,7 +330,68 @@ def main():
                 nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=tdt, out=y_half, variant=var,
                                 workspace=ws)
 
-        gemm_half_us = time_loop(gemm_half, iters)
+        loops["gemm_half"] = gemm_half
+        # dense GEMMs (hipBLASLt through torch) with the same output dtypes:
+        # a half-precision result, and an fp32 one
+        loops["dense_half"] = lambda c: torch.mm(actp[c], dense_t[c])
+        loops["dense_f32"] = lambda c: torch.mm(actp[c], dense_t[c], out_dtype=torch.float32)
+    if perm is not None:
+        y_plain = torch.empty((T, R), dtype=out_dtype, device="cuda")
+        ident = torch.arange(K, dtype=torch.int32, device="cuda")
+
+        def plain(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var)
+
+        def identity(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm_perm(vals, idx, Ac, ident, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
+                            workspace=ws)
+
+        def in_kernel(c):
+            _, Ac, vals, idx, _ = copies[c]
+            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
+                            workspace=None)
+
+        loops.update({"no_perm": plain, "identity_perm": identity, "perm_no_workspace": in_kernel})
+
+    iters = max(20, args.steps)
+    for name in list(loops):  # drop what this build of torch cannot run for the shape
+        try:
+            for i in range(3):
+                loops[name](i % rotate)
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"{name} unavailable: {e}", file=sys.stderr)
+            del loops[name]
+    samples = {name: [] for name in loops}
+    for _ in range(5):
+        for name, fn in loops.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(iters):
+                fn(i % rotate)
+            b.record()
+            torch.cuda.synchronize()
+            samples[name].append(a.elapsed_time(b) * 1e3 / iters)
+    loop_us = {name: float(np.median(v)) for name, v in samples.items()}
+    gemm_loop_us = loop_us["gemm"]
+    compress_us = loop_us["compress"]
+    gemm_half_us = loop_us.get("gemm_half")
+
+    def ratio(a, b):
+        return loop_us[a] / loop_us[b] if a in loop_us and b in loop_us else None
+
+    if b8:
+        speedup = {out_name: ratio("dense_same_out", "gemm")}
+        dense_keys = {f"dense_{out_name}_out_us": loop_us.get("dense_same_out")}
+    else:
+        speedup = {out_name: ratio("dense_half" if out_name != "f32" else "dense_f32", "gemm"),
+                   "half": ratio("dense_half", "gemm_half"),
+                   "f32": ratio("dense_f32", "gemm") if out_name == "f32" else None}
+        speedup = {k: v for k, v in speedup.items() if v is not None}
+        dense_keys = {"dense_half_out_us": loop_us.get("dense_half"),
+                      "dense_f32_out_us": loop_us.get("dense_f32")}
 
     dense_eq_flop = 2.0 * R * K * T
     alg_flop = 2.0 * R * S * T
@@ -385,30 +425,11 @@ def main():
 
     extra = {}
     if perm is not None:
-        y_plain = torch.empty((T, R), dtype=out_dtype, device="cuda")
-        ident = torch.arange(K, dtype=torch.int32, device="cuda")
-
-        def plain(c):
-            _, Ac, vals, idx, _ = copies[c]
-            nm.nm_spmm(vals, idx, Ac, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var)
-
-        def identity(c):
-            _, Ac, vals, idx, _ = copies[c]
-            nm.nm_spmm_perm(vals, idx, Ac, ident, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
-                            workspace=ws)
-
-        def in_kernel(c):
-            _, Ac, vals, idx, _ = copies[c]
-            nm.nm_spmm_perm(vals, idx, Ac, perm, K, n, m, out_dtype=out_dtype, out=y_plain, variant=var,
-                            workspace=None)
-
-        plain_us = time_loop(plain, iters)
-        ident_us = time_loop(identity, iters)
-        in_kernel_us = time_loop(in_kernel, iters)
-        extra = {"nm_spmm_no_perm_us": plain_us, "nm_spmm_perm_identity_us": ident_us,
-                 "nm_spmm_perm_no_workspace_us": in_kernel_us,
-                 "perm_overhead_vs_no_perm": gemm_loop_us / plain_us - 1.0,
-                 "perm_overhead_vs_identity_perm": gemm_loop_us / ident_us - 1.0}
+        extra = {"nm_spmm_no_perm_us": loop_us.get("no_perm"),
+                 "nm_spmm_perm_identity_us": loop_us.get("identity_perm"),
+                 "nm_spmm_perm_no_workspace_us": loop_us.get("perm_no_workspace"),
+                 "perm_overhead_vs_no_perm": ratio("gemm", "no_perm") - 1.0,
+                 "perm_overhead_vs_identity_perm": ratio("gemm", "identity_perm") - 1.0}
 
     out = {
         "metric": METRIC,
@@ -441,9 +462,9 @@ def main():
             "nm_spmm_half_out_us": gemm_half_us,
             "nm_compress_us": compress_us,
             "nm_compress_gbps": (R * K * esz + vb + ib) / (compress_us * 1e-6) / 1e9,
-            "dense_linear_us": dense_us,
-            "speedup_vs_dense_half_out": dense_us / gemm_half_us if dense_us and gemm_half_us else None,
-            "speedup_vs_dense_f32_out": dense_us / gemm_loop_us if dense_us else None,
+            **dense_keys,
+            # dense time / sparse time, both sides writing the same output dtype
+            "speedup_vs_dense_same_out_dtype": speedup,
             **extra,
         },
         "wall_s_timed": wall,

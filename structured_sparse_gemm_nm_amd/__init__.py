@@ -23,7 +23,9 @@ NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
 PATTERNS = ((2, 4), (1, 4), (1, 8))
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libnmsparse.so")
+# NMSPARSE_LIB selects another build of the same library (the host-sanitized
+# one that `build --sanitize` writes, for instance)
+_LIB_PATH = os.environ.get("NMSPARSE_LIB") or os.path.join(_HERE, "libnmsparse.so")
 _lib = None
 
 

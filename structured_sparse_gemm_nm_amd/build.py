@@ -1,9 +1,15 @@
 """Build libnmsparse.so in-tree with hipcc for gfx950.
 
-    python -m structured_sparse_gemm_nm_amd.build
+    python -m structured_sparse_gemm_nm_amd.build [--sanitize]
 
 Compiles every source under csrc/ to an object in parallel, then links the
 shared library next to this file.  Always rebuilds.
+
+--sanitize also links _build/libnmsparse_san.so: the same device objects with
+the host-side C ABI (nm_api.cpp) built under AddressSanitizer and
+UndefinedBehaviorSanitizer (host code only; the GPU code is not
+instrumented).  Load it with NMSPARSE_LIB pointing at it and the clang ASan
+runtime (SANITIZER_RUNTIME) preloaded.
 """
 from __future__ import annotations
 
@@ -81,5 +87,42 @@ def build(verbose: bool = True) -> str:
     return LIB_PATH
 
 
+SAN_LIB_PATH = os.path.join(BUILD_DIR, "libnmsparse_san.so")
+SANITIZER_RUNTIME = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+# each sanitizer flag applies to the host compilation only
+SAN_HOST_FLAGS = ["-O1", "-g",
+                  "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """Link SAN_LIB_PATH: nm_api.cpp host-sanitized, every other object as built."""
+    srcs = sources()
+    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    api = os.path.join(CSRC, "nm_api.cpp")
+    san_obj = os.path.join(BUILD_DIR, "nm_api.cpp.san.o")
+    flags = [f for f in COMMON_FLAGS if f != "-O3"]
+    cmd = [hipcc(), *flags, *SAN_HOST_FLAGS, "-x", "hip", *DEVICE_FLAGS, "-c", api, "-o", san_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    link = [o for o in objs if not o.endswith("nm_api.cpp.o")] + [san_obj]
+    # the sanitizer runtime is not linked in: it is preloaded into the process
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SAN_LIB_PATH, *link]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB_PATH} (host ASan + UBSan)")
+    return SAN_LIB_PATH
+
+
 if __name__ == "__main__":
-    build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()
+    else:
+        build()

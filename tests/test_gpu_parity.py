@@ -77,6 +77,62 @@ def test_compress_worked_row():
     assert np.array_equal(words_of(idx), O.prune_pack(w, 2, 4)[1])
 
 
+# fp16 / bf16 bit patterns of +inf, -inf, a quiet NaN, a NaN with the lowest
+# payload, a negative NaN, and the largest finite value
+SPECIALS = {"f16": (0x7C00, 0xFC00, 0x7E00, 0x7C01, 0xFE00, 0x7BFF),
+            "bf16": (0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFC0, 0x7F7F)}
+
+
+@pytest.mark.parametrize("n,m", nm.PATTERNS)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_compress_nan_inf_weights(dt, n, m):
+    # Magnitude is the stored pattern without its sign bit, so NaN (exponent
+    # all ones, payload > 0) outranks inf, which outranks every finite value;
+    # +inf and -inf tie and the lower position wins.  Pack bit-exact; in the
+    # product a kept NaN makes the whole output row NaN and a kept inf makes it
+    # +-inf (activations here are never zero), exactly as the fp64 oracle says.
+    log(f"compress NaN/inf weights {dt} {n}:{m}")
+    R, K, T = 256, 256, 128
+    pinf, ninf, qnan, lnan, nnan, big = SPECIALS[dt]
+    w = nm_inputs.normal_half((R, K), 1.0, dt, 74, 0)
+    act = nm_inputs.normal_half((T, K), 1.0, dt, 74, 1)
+    act[act & 0x7FFF == 0] = 0x3C00 if dt == "f16" else 0x3F80   # no zero activations
+    plant = [(3, 5, qnan), (100, 130, nnan),                    # one NaN in a group
+             (200, 8, qnan), (200, 9, lnan),                    # two NaNs with different payloads
+             (10, 17, pinf), (50, 64, ninf),                    # one inf
+             (150, 40, pinf), (150, 41, ninf),                  # +inf and -inf tie
+             (60, 72, big), (60, 73, pinf),                     # inf beats the largest finite
+             (70, 96, pinf), (70, 97, qnan)]                    # NaN beats inf
+    for r, c, b in plant:
+        w[r, c] = b
+    vals, idx = gpu_compress(w, dt, n, m)
+    ref_vals, ref_idx = O.prune_pack(w, n, m)
+    assert np.array_equal(bits_of(vals), ref_vals)
+    assert np.array_equal(words_of(idx), ref_idx)
+    y = nm.nm_spmm(vals, idx, to_dev(act, dt), K, n, m)
+    torch.cuda.synchronize()
+    yv = y.cpu().numpy().astype(np.float64).T   # [R, T]
+    with np.errstate(invalid="ignore", over="ignore"):
+        yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt)
+    special = ~np.all(np.isfinite(yref), axis=1)
+    assert special.any()
+    # A finite bf16 weight near its largest value times |x| > 1 overflows the
+    # fp32 accumulator although the fp64 oracle does not: on such rows the
+    # output only has to be non-finite wherever the oracle's is.
+    wd = O.half_bits_to_f64(O.decompress(ref_vals, ref_idx, K, n, m), dt)
+    xa = np.abs(O.half_bits_to_f64(act, dt))
+    wmax = np.max(np.where(np.isfinite(wd), np.abs(wd), 0.0), axis=1)
+    ovf = wmax * xa.max() >= 2.0 ** 128
+    assert np.all(~np.isfinite(yv[ovf]) >= ~np.isfinite(yref[ovf]))
+    for name, f in (("nan", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        bad = np.argwhere((f(yv) != f(yref)) & ~ovf[:, None])
+        assert bad.size == 0, (f"{name} mask differs at {len(bad)} outputs, e.g. (row, token) "
+                               f"{bad[:6].tolist()}: gpu {[yv[r, t] for r, t in bad[:6]]} "
+                               f"oracle {[yref[r, t] for r, t in bad[:6]]}")
+    rest = np.flatnonzero(~special & ~ovf)
+    assert_close(y[:, rest], yref[rest], tol=1e-2)
+
+
 @pytest.mark.parametrize("n,m", nm.PATTERNS)
 def test_decompress_round_trip(n, m):
     log(f"decompress {n}:{m}")
