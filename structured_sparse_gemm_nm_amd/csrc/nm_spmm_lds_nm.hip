@@ -10,17 +10,23 @@
 // nm_spmm_pipe.hip step for step, so the results are bit-identical to it.
 //
 // Packed rows of these patterns are short: per 64-wide K step a row holds 32
-// (1:4) or 16 (1:8) bytes of values and 4 or 3 bytes of index bits.  A lane
-// takes its share with one small LDS read, and the widening (a few VALU
-// operations per fragment) is done for the next step after the MFMAs of the
-// current one, where nothing waits on it.
+// (1:4) or 16 (1:8) bytes of values and 4 or 3 bytes of index bits.  Loaded
+// step by step they would arrive as 32- or 16-byte pieces, and the number of
+// outstanding requests a compute unit can keep, not their bytes, would set the
+// pace; so the values come in groups of steps whose rows are whole 128-byte
+// runs (4 steps for 1:4, 8 for 1:8), double-buffered.  A lane takes its share
+// of a step with one small LDS read, and the widening (a few VALU operations
+// per fragment) is done for the next step after the MFMAs of the current one,
+// where nothing waits on it.
 //
 // LDS layout (a direct load puts lane l's 16 bytes at slot base + l, so the
 // layout is chosen by the global address each lane reads):
 //   activations    one K step per stage; slot (token, chunk c) at
 //                  token*8 + (c ^ (token & 7)), as in the 2:4 kernel;
-//   packed values  one K step per stage; rows contiguous (32 or 16 B each),
-//                  so a fragment's 16 rows are one conflict-free run;
+//   packed values  one group of steps per buffer (128 B per row): 16-byte
+//                  chunk c of row r at slot r*8 + (c ^ ((r >> 1) & 7)), so
+//                  a fragment's 16 rows read the same chunk from 16 distinct
+//                  bank quads;
 //   index bits     block = 16 K steps of a row.  1:4: 64 bytes, slot (row,
 //                  chunk) at row*4 + (chunk ^ ((row >> 2) & 3)); 1:8: 48
 //                  bytes loaded 4 at a time, rows contiguous (a 48-byte row
@@ -30,10 +36,12 @@
 // fragments, so every row fragment is widened by one wave only) computes
 // 128 x 64 tiles: a 4096-row layer at 512 tokens then has one tile
 // per compute unit, where 256 x 128 tiles would leave three quarters of the
-// chip idle.  Stages form a 4-deep ring (three K steps of loads in flight),
+// chip idle.  Activation stages form a 4-deep ring (three K steps of loads in
+// flight), a value group is loaded at the first step of the group before it,
 // with counted vmcnt waits and one fence-free barrier per step; every step
 // issues the same loads (past the last step a slot is refilled with that step
-// again), so the wait counts are constants.  Each tile fills its own ring.
+// again, and past the last group the last group is loaded again), so the wait
+// counts are fixed.  Each tile fills its own ring.
 #include "nm_device.h"
 #include "nm_internal.h"
 
@@ -44,25 +52,27 @@ constexpr int kBR = 128;
 constexpr int kBT = 64;
 constexpr int kNS = 4;               // one-K-step stages in the ring
 constexpr int kStageB = kBT * 128;   // activations, one step
-constexpr int kPerStep = 3;          // direct loads per wave per step: 2 activation + 1 packed-value
+constexpr int kPerStep = 2;          // activation loads per wave per step
+constexpr int kGroupLoads = 4;       // packed-value loads per wave per group
+constexpr int kSAG = kBR * 128;      // packed values, one group (128 B per row)
 
-// P = 1: 1:4, P = 2: 1:8.  VB: packed-value bytes per row per step; IBLK:
-// index bytes per row per 16-step block (2 or 3 bits per survivor); IL:
-// index loads per wave per block.
+// P = 1: 1:4, P = 2: 1:8.  VB: packed-value bytes per row per step; GS: steps
+// per 128-byte value group; IBLK: index bytes per row per 16-step block (2 or
+// 3 bits per survivor); IL: index loads per wave per block.
 template <int P>
 struct NmPat;
 template <>
 struct NmPat<1> {
-  static constexpr int VB = 32, IBLK = 64, IL = 2;
+  static constexpr int VB = 32, GS = 4, IBLK = 64, IL = 2;
 };
 template <>
 struct NmPat<2> {
-  static constexpr int VB = 16, IBLK = 48, IL = 6;
+  static constexpr int VB = 16, GS = 8, IBLK = 48, IL = 6;
 };
 
 template <int P>
 constexpr int lds_bytes() {
-  return kNS * (kStageB + kBR * NmPat<P>::VB) + 2 * kBR * NmPat<P>::IBLK;
+  return kNS * kStageB + 2 * kSAG + 2 * kBR * NmPat<P>::IBLK;
 }
 
 // Tile i of the grid-stride sequence -> (row tile, token tile), token tiles
@@ -128,13 +138,12 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     TileMapNM tm) {
   constexpr int FR = 2, FT = 4;
   static_assert(FR == 2, "1:4 index registers hold two row fragments");
-  constexpr int VB = NmPat<P>::VB, IBLK = NmPat<P>::IBLK;
-  constexpr int SA = kBR * VB;      // packed values, one step
+  constexpr int VB = NmPat<P>::VB, GS = NmPat<P>::GS, IBLK = NmPat<P>::IBLK;
   constexpr int SI = kBR * IBLK;    // index bits, one block
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* bbuf = smem;                        // [kNS][kStageB]
-  unsigned char* abuf = smem + kNS * kStageB;        // [kNS][SA]
-  unsigned char* ibuf = smem + kNS * (kStageB + SA);  // [2][SI]
+  unsigned char* bbuf = smem;                         // [kNS][kStageB]
+  unsigned char* abuf = smem + kNS * kStageB;         // [2][kSAG]
+  unsigned char* ibuf = smem + kNS * kStageB + 2 * kSAG;  // [2][SI]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,6 +154,9 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   const int nsteps = K >> 6;  // a multiple of 4 on this path
   const int S = K / (P == 1 ? 4 : 8);
   const int iwords = irow_bytes >> 2;  // index words per row
+  const int ngroups = (nsteps + GS - 1) / GS;
+  // 1:8 with nsteps % 8 == 4: the last group holds four steps (64 B per row)
+  const bool half_last = P == 2 && (nsteps % GS) != 0;
 
   // Per-lane index-block slots, instruction j of a wave.  1:4: 16-byte slots
   // [(wave*2 + j)*64, +64), slot (row, chunk) at row*4 + (chunk ^ ((row >> 2) & 3));
@@ -156,12 +168,21 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     ipart[j] = P == 1 ? (slot & 3) ^ ((slot >> 4) & 3) : slot % 12;
   }
 
+  // Packed-value loads: bit j of ahi is set when load j puts this lane's
+  // chunk in the second half of its row's 128-byte run.
+  int ahi = 0;
+#pragma unroll
+  for (int j = 0; j < kGroupLoads; ++j) {
+    const int slot = (wave * kGroupLoads + j) * 64 + lane;
+    ahi |= (((slot & 7) ^ ((slot >> 4) & 7)) >= 4 ? 1 : 0) << j;
+  }
+
   // A tile's load sources: buffer resources at the tile's corner and per-lane
   // 32-bit byte offsets (rows / tokens past the edge reread the last one).
   // Every load is kept inside its row by construction; the index resource
   // also ends with the array.
   __amdgpu_buffer_rsrc_t rb, ra, ri;
-  uint32_t boff[2], aoff, ioff[NmPat<P>::IL];
+  uint32_t boff[2], aoff[kGroupLoads], ioff[NmPat<P>::IL];
   auto make_src = [&](int R0, int T0) {
     rb = make_rsrc(act + int64_t(T0) * ldx, 0xFFFFFFFFu);
     ra = make_rsrc(values + int64_t(R0) * S, 0xFFFFFFFFu);
@@ -184,23 +205,35 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       const int r = min(R0 + row, R - 1) - R0;
       ioff[j] = uint32_t(r) * uint32_t(irow_bytes);
     }
-    // packed values: 1:4 slot (row, half) = wave*64 + lane; 1:8 slot row =
-    // wave*32 + lane, lanes 0..31 only
-    const int arow = P == 1 ? (wave * 64 + lane) >> 1 : wave * 32 + (lane & 31);
-    const int ac = P == 1 ? (lane & 1) : 0;
-    const int r = min(R0 + arow, R - 1) - R0;
-    aoff = uint32_t(r) * uint32_t(S) * 2u + uint32_t(ac) * 16u;
+    // packed values: load j of a wave fills slots [(wave*4 + j)*64, +64) of a
+    // group buffer, 8 whole rows; slot (row, chunk c) at row*8 + (c ^ ((row >> 1) & 7))
+#pragma unroll
+    for (int j = 0; j < kGroupLoads; ++j) {
+      const int slot = (wave * kGroupLoads + j) * 64 + lane;
+      const int row = slot >> 3;
+      const int c = (slot & 7) ^ ((row >> 1) & 7);
+      const int r = min(R0 + row, R - 1) - R0;
+      aoff[j] = uint32_t(r) * uint32_t(S) * 2u + uint32_t(c) * 16u;
+    }
   };
 
-  // the loads of step src into ring slot buf
+  // the activation loads of step src into ring slot buf
   auto issue_step = [&](int src, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kPerStep; ++j)
       dma16(rb, boff[j], uint32_t(src) * 128u, bbuf + buf * kStageB + (wave * 2 + j) * 1024);
-    if constexpr (P == 1) {
-      dma16(ra, aoff, uint32_t(src) * uint32_t(VB), abuf + buf * SA + wave * 1024);
-    } else {
-      if (lane < 32) dma16(ra, aoff, uint32_t(src) * uint32_t(VB), abuf + buf * SA + wave * 512);
+  };
+  // the packed values of group g (clamped to the last group) into buffer gb.
+  // Every load stays inside its row: a row is nsteps * VB bytes, whole groups
+  // of 128 bytes except a four-step last 1:8 group, whose missing half
+  // (chunks 4..7) rereads chunks 0..3; those slots are never read.
+  auto issue_group = [&](int g, int gb) {
+    g = min(g, ngroups - 1);
+    const bool part = half_last && g == ngroups - 1;
+#pragma unroll
+    for (int j = 0; j < kGroupLoads; ++j) {
+      const uint32_t back = (part && ((ahi >> j) & 1)) ? 64u : 0u;
+      dma16(ra, aoff[j] - back, uint32_t(g) * 128u, abuf + gb * kSAG + (wave * kGroupLoads + j) * 1024);
     }
   };
   // index block q into buffer ib.  Every load stays inside the row: 1:4
@@ -232,17 +265,21 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     bf[4 * h + 2] = v[2];
     bf[4 * h + 3] = v[3];
   };
-  auto read_v = [&](int sl, int i, uint32_t (&v)[2]) {
-    const unsigned char* sa = abuf + sl * SA;
+  // packed values of step u (t = u % GS) of row fragment i: the lane's 8
+  // (1:4) or 4 (1:8) bytes, at byte t*VB + lq*(VB/4) of the row's 128-byte run
+  auto read_v = [&](int u, int t, int i, uint32_t (&v)[2]) {
+    const unsigned char* sa = abuf + ((u / GS) & 1) * kSAG;
     const int row = wr * 32 + i * 16 + li;
+    const int f = (row >> 1) & 7;
     if constexpr (P == 1) {
+      const int c = 2 * t + (lq >> 1);
       // (a uint64_t load: read through the uint2 struct, the compiler cannot
       // tell this from the slots the direct loads are filling and waits for them)
-      const uint64_t w = *reinterpret_cast<const uint64_t*>(sa + row * 32 + lq * 8);
+      const uint64_t w = *reinterpret_cast<const uint64_t*>(sa + (row * 8 + (c ^ f)) * 16 + (lq & 1) * 8);
       v[0] = uint32_t(w);
       v[1] = uint32_t(w >> 32);
     } else {
-      v[0] = *reinterpret_cast<const uint32_t*>(sa + row * 16 + lq * 4);
+      v[0] = *reinterpret_cast<const uint32_t*>(sa + (row * 8 + (t ^ f)) * 16 + lq * 4);
       v[1] = 0u;
     }
   };
@@ -303,13 +340,25 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   auto body = [&](auto c_, int s, u32x4 (&ca)[FR], uint32_t (&ck)[FR], u32x8 (&cb)[FT],
                   u32x4 (&na)[FR], uint32_t (&nk)[FR], u32x8 (&nb)[FT]) {
     constexpr int C = decltype(c_)::value;
-    // step s+1 has landed once at most the loads of steps s+2, s+3 remain (an
-    // index block issued in between only makes the wait stricter)
-    wait_vmcnt<2 * kPerStep>();
+    // Step s+1 has landed once at most the loads issued after its activations
+    // remain: the activations of steps s+2, s+3, and a value group if one of
+    // those two steps began a group (groups begin at steps with C == 0, 1:8
+    // every other one; a group issued at step s' precedes that step's
+    // activation loads and is read from step s'+GS on).  An index block
+    // issued in between only makes the wait stricter.
+    bool grp_behind = false;
+    if constexpr (C == 1 || C == 2) grp_behind = P == 1 || ((s >> 2) & 1) == 0;
+    if (grp_behind)
+      wait_vmcnt<2 * kPerStep + kGroupLoads>();
+    else
+      wait_vmcnt<2 * kPerStep>();
     wait_lgkm0();        // this wave's reads of step s are done
     barrier_no_fence();  // publishes step s+1; every wave is done reading step s
     if constexpr (C == 0) {
       if ((s & 15) == 0 && s + 16 < nsteps) issue_index((s >> 4) + 1, ((s >> 4) + 1) & 1);
+      // the next group's buffer held the previous group, whose last step was
+      // read before this step's barrier
+      if (P == 1 || ((s >> 2) & 1) == 0) issue_group(s / GS + 1, (s / GS + 1) & 1);
     }
     issue_step(min(s + kNS, nsteps - 1), C);
     constexpr int RS = (C + 1) & 3;  // slot and group position of step s+1
@@ -319,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       read_b(RS, j, 1, nb[j]);
     }
 #pragma unroll
-    for (int i = 0; i < FR; ++i) read_v(RS, i, rv[i]);
+    for (int i = 0; i < FR; ++i) read_v(s + 1, P == 1 ? RS : (s + 1) & 7, i, rv[i]);
     if constexpr (RS == 0) {
       const int s1 = s + 1;
 #pragma unroll
@@ -348,12 +397,13 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- prologue: index block 0 and steps 0 .. kNS-2, then step kNS-1 into
-    // the last slot and step 0 into register set 0
+    // ---- prologue: index block 0, value group 0 and steps 0 .. kNS-2, then
+    // step kNS-1 into the last slot and step 0 into register set 0
     issue_index(0, 0);
+    issue_group(0, 0);
 #pragma unroll
     for (int p = 0; p < kNS - 1; ++p) issue_step(min(p, nsteps - 1), p);
-    wait_vmcnt<2 * kPerStep>();  // index block 0 and step 0
+    wait_vmcnt<2 * kPerStep>();  // index block 0, value group 0 and step 0
     barrier_no_fence();
     issue_step(min(kNS - 1, nsteps - 1), kNS - 1);
 #pragma unroll
@@ -363,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
-      read_v(0, i, rv[i]);
+      read_v(0, 0, i, rv[i]);
       read_ix(0, 0, i, rw[i]);
     }
     widen(0, rv, rw, a0, k0);
