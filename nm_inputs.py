@@ -89,6 +89,12 @@ def normal_fp8(shape, scale: float, workload_id: int, tensor_id: int, variant: i
     return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def tile_flags(tile_grid_shape, dense_fraction: float, workload_id: int, variant: int = 0) -> np.ndarray:
+    """uint8 flags over a grid of weight tiles: 1 (dense) with probability dense_fraction."""
+    rng = rng_for(workload_id, 3, variant)
+    return (rng.random(tile_grid_shape) < dense_fraction).astype(np.uint8)
+
+
 def random_permutation(k: int, workload_id: int, variant: int = 0) -> np.ndarray:
     return rng_for(workload_id, 2, variant).permutation(int(k)).astype(np.int32)
 
