@@ -244,6 +244,64 @@ nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, in
                           void* Y, int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
                           int variant, void* stream);
 
+/*
+ * Hybrid dense / 2:4 weight tiles.  Source: thelatestinai.com "Structured
+ * Sparsity" topic cards, the PATCH abstract: the weight matrix is cut into
+ * tiles and each tile is either kept dense or made 2:4 sparse (the choice is
+ * a learned mask, an input here), so the zero fraction can be set anywhere
+ * between 0 and 50%; a 2:4 tile is pruned with the nm_compress rule.
+ *
+ * Tiles are tile_rows x tile_cols blocks on a regular grid (both positive
+ * multiples of 64; tile_cols divides K; at most 8192 tile-columns; the last
+ * tile-row may be shorter when tile_rows does not divide R).  RB = ceil(R /
+ * tile_rows) tile-rows, KB = K / tile_cols tile-columns.
+ *   flags[b*KB + j]  host uint8: 1 keeps tile (b, j) dense, 0 makes it 2:4.
+ * Packed layout: a row stores its tiles in column order, a dense tile as its
+ * tile_cols values (bits unchanged), a 2:4 tile as its tile_cols/2 survivors
+ * (the nm_compress format on the tile's columns); the row's index bytes are
+ * the 2:4 tiles' LSB-first 2-bit streams, tile_cols/8 bytes each, in the
+ * same order.  The rows of tile-row b share one length, Lv[b] values and
+ * Li[b] index bytes; rows follow each other and tile-rows follow each other,
+ * in `values` (dtype of W) and in `idx` (bytes).
+ *
+ * nm_hybrid_layout (host only, no device access) writes the layout tables:
+ *   tile_meta  [RB*KB*2] int64: per tile, the offset of its first value in
+ *              the first row of its tile-row (elements into values) and of its
+ *              first index byte (bytes into idx), or -1 for a dense tile;
+ *   row_meta   [RB*4] int64: per tile-row, Lv, Li and the offsets of its
+ *              first value and first index byte;
+ *   values_count, idx_bytes  the packed sizes (elements, bytes); the index
+ *              array is zero-padded to a multiple of 16 bytes.
+ * Any output may be NULL (a size query).  NM_ERR_SHAPE for a bad grid, a flag
+ * other than 0 or 1, or packed values or index bytes of 2 GiB or more.
+ *
+ * nm_hybrid_compress packs W (device, [R, K] row-major, ldw >= K, ldw % 8 ==
+ * 0; NM_F16 or NM_BF16) into values / idx (device, caller-allocated with the
+ * sizes above); tile_meta / row_meta are the tables of nm_hybrid_layout for
+ * the same flags, copied to the device by the caller (8-byte aligned).  idx
+ * may be NULL when idx_bytes is 0 (every tile dense).
+ *
+ * nm_hybrid_spmm computes Y[t, r] = sum_k W_hat[r, k] act[t, k] (fp32
+ * accumulation) where W_hat is W with every 2:4 tile pruned: act [T, K]
+ * (K <= ldx <= 2^22, ldx % 8 == 0), Y [T, R] (ldy >= R), out_dtype NM_F32 or the
+ * input dtype.  On a dense tile each K step runs dense MFMAs, on a 2:4 tile
+ * the sparse MFMA.  Layout tables that do not match the packed arrays give
+ * wrong values, but every weight access stays inside values_count /
+ * idx_bytes.  Same pointer, alignment and alias rules as nm_spmm; nothing is
+ * allocated and the stream is not synchronised.
+ */
+nm_status nm_hybrid_layout(int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, const uint8_t* flags,
+                           int64_t* tile_meta, int64_t* row_meta, int64_t* values_count, int64_t* idx_bytes);
+
+nm_status nm_hybrid_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, int64_t tile_rows,
+                             int64_t tile_cols, const int64_t* tile_meta, const int64_t* row_meta,
+                             int64_t values_count, int64_t idx_bytes, void* values, uint8_t* idx, void* stream);
+
+nm_status nm_hybrid_spmm(const void* values, const uint8_t* idx, const int64_t* tile_meta, const int64_t* row_meta,
+                         int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, int64_t values_count,
+                         int64_t idx_bytes, int dtype, const void* act, int64_t T, int64_t ldx, void* Y,
+                         int64_t ldy, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

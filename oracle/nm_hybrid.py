@@ -27,7 +27,9 @@ Readings taken where the page is silent (H1-H5):
       another with those strides, and the tile-rows one after another;
   H5  tile_meta[b, j] = (offset of the tile's first value in its tile-row's
       first row, offset of its first index byte there or -1 for a dense tile),
-      row_meta[b] = (Lv[b], Li[b]).
+      row_meta[b] = (Lv[b], Li[b], offset of the tile-row's first value, offset
+      of its first index byte); the index array is zero-padded to a whole
+      number of 16-byte blocks (a block read never leaves it).
 
 The mask learning itself is training and is not reproduced: flags are inputs.
 """
@@ -51,11 +53,11 @@ def rows_of(b: int, R: int, tile_rows: int) -> int:
 
 
 def hybrid_layout(R: int, K: int, tile_rows: int, tile_cols: int, flags):
-    """H3-H5: (tile_meta [RB, KB, 2], row_meta [RB, 2], total values, total index bytes)."""
+    """H3-H5: (tile_meta [RB, KB, 2], row_meta [RB, 4], total values, total index bytes)."""
     RB, KB = tile_grid(R, K, tile_rows, tile_cols)
     flags = np.asarray(flags).reshape(RB, KB)
     tile_meta = np.zeros((RB, KB, 2), dtype=np.int64)
-    row_meta = np.zeros((RB, 2), dtype=np.int64)
+    row_meta = np.zeros((RB, 4), dtype=np.int64)
     vbase = ibase = 0
     for b in range(RB):
         v = i = 0  # position along the first row of tile-row b
@@ -68,10 +70,10 @@ def hybrid_layout(R: int, K: int, tile_rows: int, tile_cols: int, flags):
                 tile_meta[b, j, 1] = ibase + i
                 v += tile_cols // 2
                 i += tile_cols // 8
-        row_meta[b] = (v, i)
+        row_meta[b] = (v, i, vbase, ibase)
         vbase += rows_of(b, R, tile_rows) * v
         ibase += rows_of(b, R, tile_rows) * i
-    return tile_meta, row_meta, vbase, ibase
+    return tile_meta, row_meta, vbase, -(-ibase // 16) * 16
 
 
 def hybrid_pack(w_bits: np.ndarray, tile_rows: int, tile_cols: int, flags):
@@ -85,7 +87,7 @@ def hybrid_pack(w_bits: np.ndarray, tile_rows: int, tile_cols: int, flags):
     idx = np.zeros(ni, dtype=np.uint8)
     for b in range(RB):
         r0, nr = b * tile_rows, rows_of(b, R, tile_rows)
-        Lv, Li = row_meta[b]
+        Lv, Li = row_meta[b, :2]
         for j in range(KB):
             block = w_bits[r0:r0 + nr, j * tile_cols:(j + 1) * tile_cols]
             v0, i0 = tile_meta[b, j]
@@ -111,7 +113,7 @@ def hybrid_decompress(values, idx, R: int, K: int, tile_rows: int, tile_cols: in
     w = np.zeros((R, K), dtype=np.uint16)
     for b in range(RB):
         r0, nr = b * tile_rows, rows_of(b, R, tile_rows)
-        Lv, Li = row_meta[b]
+        Lv, Li = row_meta[b, :2]
         for j in range(KB):
             v0, i0 = tile_meta[b, j]
             c0 = j * tile_cols

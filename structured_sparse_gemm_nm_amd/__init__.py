@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.nm_check_perm.argtypes = [vp, i64, vp]
     L.nm_spmm_variant.restype = i32
     L.nm_spmm_variant.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp, sz, i32, vp]
+    L.nm_hybrid_layout.restype = i32
+    L.nm_hybrid_layout.argtypes = [i64, i64, i64, i64, vp, vp, vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.nm_hybrid_compress.restype = i32
+    L.nm_hybrid_compress.argtypes = [vp, i64, i64, i64, i32, i64, i64, vp, vp, i64, i64, vp, vp, vp]
+    L.nm_hybrid_spmm.restype = i32
+    L.nm_hybrid_spmm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, i64, vp, i64, i32, vp]
     _lib = L
     return L
 
@@ -296,3 +302,93 @@ def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):
 def nm_check_perm(perm) -> None:
     _require_cuda(perm)
     _check(lib().nm_check_perm(perm.data_ptr(), perm.numel(), _stream_ptr(perm.device)))
+
+
+# --------------------------------------------------------------------------
+# hybrid dense / 2:4 tiles
+# --------------------------------------------------------------------------
+
+class HybridLayout:
+    """Layout of a weight cut into tile_rows x tile_cols tiles, each dense (flag 1)
+    or 2:4 (flag 0), as nm_hybrid_layout computes it (host tables, plus their
+    device copies made on first use per device)."""
+
+    def __init__(self, R, K, tile_rows, tile_cols, flags, tile_meta, row_meta, values_count, idx_bytes):
+        self.R, self.K, self.tile_rows, self.tile_cols = R, K, tile_rows, tile_cols
+        self.flags, self.tile_meta, self.row_meta = flags, tile_meta, row_meta
+        self.values_count, self.idx_bytes = values_count, idx_bytes
+        self._dev = {}
+
+    def device_tables(self, device):
+        torch = _torch()
+        key = str(device)
+        if key not in self._dev:
+            self._dev[key] = (torch.from_numpy(self.tile_meta).to(device),
+                              torch.from_numpy(self.row_meta).to(device))
+        return self._dev[key]
+
+
+def nm_hybrid_layout(R: int, K: int, tile_rows: int, tile_cols: int, flags) -> HybridLayout:
+    """Layout tables for the tile flags (uint8 [ceil(R/tile_rows), K/tile_cols]: 1 dense, 0 2:4)."""
+    import numpy as np
+    RB, KB = -(-R // tile_rows) if tile_rows > 0 else 0, K // tile_cols if tile_cols > 0 else 0
+    f = np.ascontiguousarray(np.asarray(flags, dtype=np.uint8))
+    if f.shape != (RB, KB):
+        raise ValueError(f"flags must have shape ({RB}, {KB})")
+    tm = np.zeros((RB, KB, 2), dtype=np.int64)
+    rm = np.zeros((RB, 4), dtype=np.int64)
+    nv, ni = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().nm_hybrid_layout(R, K, tile_rows, tile_cols, f.ctypes.data, tm.ctypes.data, rm.ctypes.data,
+                                  ctypes.byref(nv), ctypes.byref(ni)))
+    return HybridLayout(R, K, tile_rows, tile_cols, f, tm, rm, nv.value, ni.value)
+
+
+def nm_hybrid_compress(W, layout: HybridLayout, values=None, idx=None):
+    """Pack W [R, K] (fp16/bf16, device) by the layout: (values [values_count], idx uint8 [idx_bytes])."""
+    torch = _torch()
+    _row_major(W, "W")
+    R, K = W.shape
+    if (R, K) != (layout.R, layout.K):
+        raise ValueError(f"W is [{R}, {K}], the layout is for [{layout.R}, {layout.K}]")
+    dt = _dtype_code(W)
+    if values is None:
+        values = torch.empty(layout.values_count, dtype=W.dtype, device=W.device)
+    if idx is None:
+        idx = torch.zeros(max(layout.idx_bytes, 16), dtype=torch.uint8, device=W.device)
+    if values.dtype != W.dtype or values.numel() < layout.values_count or not values.is_contiguous():
+        raise ValueError(f"values must be a contiguous {W.dtype} tensor of {layout.values_count} elements")
+    if idx.dtype != torch.uint8 or idx.numel() < layout.idx_bytes or not idx.is_contiguous():
+        raise ValueError(f"idx must be a contiguous uint8 tensor of {layout.idx_bytes} bytes")
+    _require_cuda(W, values, idx)
+    tm, rm = layout.device_tables(W.device)
+    _check(lib().nm_hybrid_compress(W.data_ptr(), R, K, W.stride(0), dt, layout.tile_rows, layout.tile_cols,
+                                    tm.data_ptr(), rm.data_ptr(), layout.values_count, layout.idx_bytes,
+                                    values.data_ptr(), idx.data_ptr(), _stream_ptr(W.device)))
+    return values, idx
+
+
+def nm_hybrid_spmm(values, idx, layout: HybridLayout, act, out_dtype=None, out=None):
+    """Y^T [T, R] = act [T, K] . W_hat^T for a hybrid-tile packed weight."""
+    torch = _torch()
+    _row_major(act, "act")
+    T, K = act.shape
+    R = layout.R
+    dt = _dtype_code(values)
+    if act.dtype != values.dtype or K != layout.K:
+        raise ValueError(f"act must be [T, {layout.K}] of the dtype of values")
+    if values.numel() < layout.values_count or idx.numel() < layout.idx_bytes:
+        raise ValueError("values / idx smaller than the layout's packed sizes")
+    od = NM_F32 if (out_dtype is None or out_dtype == torch.float32) else dt
+    if out is not None:
+        _row_major(out, "out")
+        if out.dtype != _torch_dtype(od) or tuple(out.shape) != (T, R):
+            raise ValueError(f"out must be a {_torch_dtype(od)} [{T}, {R}] tensor")
+    _require_cuda(values, idx, act, *(t for t in (out,) if t is not None))
+    if out is None:
+        out = torch.empty((T, R), dtype=_torch_dtype(od), device=act.device)
+    tm, rm = layout.device_tables(act.device)
+    _check(lib().nm_hybrid_spmm(values.data_ptr(), idx.data_ptr(), tm.data_ptr(), rm.data_ptr(), R, K,
+                                layout.tile_rows, layout.tile_cols, layout.values_count, layout.idx_bytes, dt,
+                                act.data_ptr(), T, act.stride(0), out.data_ptr(), out.stride(0), od,
+                                _stream_ptr(act.device)))
+    return out

@@ -100,6 +100,35 @@ nm_status hip_status(hipError_t e, const char* what) {
   return fail(NM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Tile grid of the hybrid layout: tiles of tile_rows x tile_cols, both
+// positive multiples of 64, tile_cols dividing K, at most kHybridMaxTileCols
+// tile-columns; R up to 2^30, K up to 2^24.
+nm_status check_hybrid_grid(int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols) {
+  if (R < 0 || R > kMaxRT) return fail(NM_ERR_SHAPE, "R = %lld out of range", (long long)R);
+  if (K < 64 || K > kMaxK) return fail(NM_ERR_SHAPE, "K = %lld out of range [64, 2^24]", (long long)K);
+  if (tile_rows < 64 || tile_rows % 64 || tile_rows > kMaxRT)
+    return fail(NM_ERR_SHAPE, "tile_rows = %lld is not a positive multiple of 64", (long long)tile_rows);
+  if (tile_cols < 64 || tile_cols % 64 || K % tile_cols)
+    return fail(NM_ERR_SHAPE, "tile_cols = %lld is not a multiple of 64 dividing K = %lld",
+                (long long)tile_cols, (long long)K);
+  if (K / tile_cols > nm::kHybridMaxTileCols)
+    return fail(NM_ERR_SHAPE, "K / tile_cols = %lld tile-columns exceeds %lld", (long long)(K / tile_cols),
+                (long long)nm::kHybridMaxTileCols);
+  return NM_OK;
+}
+
+// Sizes of the packed hybrid arrays: the kernels address them with 32-bit
+// byte offsets and use offsets from 2^31 up as "outside".
+nm_status check_hybrid_totals(int64_t values_count, int64_t idx_bytes) {
+  if (values_count < 0 || idx_bytes < 0) return fail(NM_ERR_SHAPE, "negative packed size");
+  if (values_count * 2 >= (int64_t(1) << 31) || idx_bytes >= (int64_t(1) << 31))
+    return fail(NM_ERR_SHAPE, "packed hybrid weight of %lld values / %lld index bytes reaches 2 GiB",
+                (long long)values_count, (long long)idx_bytes);
+  return NM_OK;
+}
+
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
 nm_status spmm_common(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
                       int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
                       bool want_perm, void* Y, int64_t ldy, int out_dtype, void* workspace,
@@ -378,6 +407,142 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream) {
     seen[size_t(p)] = 1;
   }
   return ok();
+}
+
+
+nm_status nm_hybrid_layout(int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, const uint8_t* flags,
+                           int64_t* tile_meta, int64_t* row_meta, int64_t* values_count, int64_t* idx_bytes) {
+  nm_status st = check_hybrid_grid(R, K, tile_rows, tile_cols);
+  if (st != NM_OK) return st;
+  const int64_t RB = (R + tile_rows - 1) / tile_rows, KB = K / tile_cols;
+  if (R > 0 && !flags) return fail(NM_ERR_NULL, "flags must be non-NULL");
+  for (int64_t t = 0; t < RB * KB; ++t)
+    if (flags[t] > 1)
+      return fail(NM_ERR_SHAPE, "flag %lld is %d: flags are 0 (2:4) or 1 (dense)", (long long)t, int(flags[t]));
+  int64_t vbase = 0, ibase = 0;
+  for (int64_t b = 0; b < RB; ++b) {
+    int64_t v = 0, i = 0;  // position along the first row of tile-row b
+    for (int64_t j = 0; j < KB; ++j) {
+      const bool dense = flags[b * KB + j] != 0;
+      if (tile_meta) {
+        tile_meta[(b * KB + j) * 2] = vbase + v;
+        tile_meta[(b * KB + j) * 2 + 1] = dense ? -1 : ibase + i;
+      }
+      v += dense ? tile_cols : tile_cols / 2;
+      i += dense ? 0 : tile_cols / 8;
+    }
+    if (row_meta) {
+      row_meta[b * 4] = v;
+      row_meta[b * 4 + 1] = i;
+      row_meta[b * 4 + 2] = vbase;
+      row_meta[b * 4 + 3] = ibase;
+    }
+    const int64_t rows = (b + 1) * tile_rows <= R ? tile_rows : R - b * tile_rows;
+    vbase += rows * v;
+    ibase += rows * i;
+  }
+  ibase = (ibase + 15) / 16 * 16;  // whole 16-byte blocks (zero padding)
+  st = check_hybrid_totals(vbase, ibase);
+  if (st != NM_OK) return st;
+  if (values_count) *values_count = vbase;
+  if (idx_bytes) *idx_bytes = ibase;
+  return ok();
+}
+
+nm_status nm_hybrid_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, int64_t tile_rows,
+                             int64_t tile_cols, const int64_t* tile_meta, const int64_t* row_meta,
+                             int64_t values_count, int64_t idx_bytes, void* values, uint8_t* idx, void* stream) {
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "hybrid tiles take NM_F16 or NM_BF16 weights, not dtype %d", dtype);
+  nm_status st = check_hybrid_grid(R, K, tile_rows, tile_cols);
+  if (st != NM_OK) return st;
+  st = check_hybrid_totals(values_count, idx_bytes);
+  if (st != NM_OK) return st;
+  if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw > kMaxElems) return fail(NM_ERR_SHAPE, "ldw above 2^40 elements");
+  if (R == 0) return ok();
+  if (!W || !values || !tile_meta || !row_meta || (idx_bytes > 0 && !idx))
+    return fail(NM_ERR_NULL, "W, values, tile_meta, row_meta (and idx with 2:4 tiles) must be non-NULL");
+  if (ldw % 8) return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of 8", (long long)ldw);
+  if (!aligned16(W) || !aligned16(values) || (idx && !aligned16(idx)) || !aligned8(tile_meta) ||
+      !aligned8(row_meta))
+    return fail(NM_ERR_ALIGN, "W, values and idx must be 16-byte aligned, the layout tables 8-byte aligned");
+  if (R * ldw > kMaxElems) return fail(NM_ERR_SHAPE, "R*ldw too large");
+  const int64_t RB = (R + tile_rows - 1) / tile_rows, KB = K / tile_cols;
+  const size_t wbytes = extent(R, K, ldw, 2), vbytes = size_t(values_count) * 2, ib = size_t(idx_bytes);
+  const size_t tmb = size_t(RB * KB) * 16, rmb = size_t(RB) * 32;
+  if (overlaps(values, vbytes, W, wbytes) || overlaps(idx, ib, W, wbytes) || overlaps(values, vbytes, idx, ib) ||
+      overlaps(values, vbytes, tile_meta, tmb) || overlaps(values, vbytes, row_meta, rmb) ||
+      overlaps(idx, ib, tile_meta, tmb) || overlaps(idx, ib, row_meta, rmb))
+    return fail(NM_ERR_ALIAS, "outputs overlap each other, W or the layout tables");
+  nm::HybridArgs a;
+  a.W = static_cast<const uint16_t*>(W);
+  a.ldw = ldw;
+  a.R = R;
+  a.K = K;
+  a.tile_rows = tile_rows;
+  a.tile_cols = tile_cols;
+  a.dtype = dtype;
+  a.tile_meta = tile_meta;
+  a.row_meta = row_meta;
+  a.values_out = static_cast<uint16_t*>(values);
+  a.idx_out = idx;
+  a.values_bytes = vbytes;
+  a.idx_bytes = ib;
+  return hip_status(nm::launch_hybrid_pack(a, static_cast<hipStream_t>(stream)), "nm_hybrid_compress launch");
+}
+
+nm_status nm_hybrid_spmm(const void* values, const uint8_t* idx, const int64_t* tile_meta, const int64_t* row_meta,
+                         int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, int64_t values_count,
+                         int64_t idx_bytes, int dtype, const void* act, int64_t T, int64_t ldx, void* Y,
+                         int64_t ldy, int out_dtype, void* stream) {
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "hybrid tiles take NM_F16 or NM_BF16 weights, not dtype %d", dtype);
+  if (out_dtype != NM_F32 && out_dtype != dtype)
+    return fail(NM_ERR_UNSUPPORTED, "out_dtype %d must be NM_F32 or the input dtype", out_dtype);
+  nm_status st = check_hybrid_grid(R, K, tile_rows, tile_cols);
+  if (st != NM_OK) return st;
+  st = check_hybrid_totals(values_count, idx_bytes);
+  if (st != NM_OK) return st;
+  if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (ldx < K) return fail(NM_ERR_STRIDE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldy < R) return fail(NM_ERR_STRIDE, "ldy = %lld < R = %lld", (long long)ldy, (long long)R);
+  if (ldx > kMaxElems || ldy > kMaxElems) return fail(NM_ERR_SHAPE, "leading dimension above 2^40 elements");
+  if (ldx > (int64_t(1) << 22))
+    return fail(NM_ERR_SHAPE, "ldx = %lld above 2^22 (a token tile's offsets are 31-bit)", (long long)ldx);
+  if (R == 0 || T == 0) return ok();
+  if (!values || !tile_meta || !row_meta || !act || !Y || (idx_bytes > 0 && !idx))
+    return fail(NM_ERR_NULL, "values, tile_meta, row_meta, act, Y (and idx with 2:4 tiles) must be non-NULL");
+  if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of 8", (long long)ldx);
+  if (!aligned16(values) || (idx && !aligned16(idx)) || !aligned16(act) || !aligned16(Y) ||
+      !aligned8(tile_meta) || !aligned8(row_meta))
+    return fail(NM_ERR_ALIGN, "values, idx, act and Y must be 16-byte aligned, the layout tables 8-byte aligned");
+  if (T * ldx > kMaxElems || T * ldy > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
+  const int64_t RB = (R + tile_rows - 1) / tile_rows, KB = K / tile_cols;
+  const size_t ybytes = extent(T, R, ldy, elt_bytes(out_dtype)), abytes = extent(T, K, ldx, 2);
+  const size_t vbytes = size_t(values_count) * 2, ib = size_t(idx_bytes);
+  if (overlaps(Y, ybytes, values, vbytes) || overlaps(Y, ybytes, idx, ib) || overlaps(Y, ybytes, act, abytes) ||
+      overlaps(Y, ybytes, tile_meta, size_t(RB * KB) * 16) || overlaps(Y, ybytes, row_meta, size_t(RB) * 32))
+    return fail(NM_ERR_ALIAS, "Y overlaps an input");
+  nm::HybridArgs a;
+  a.values = static_cast<const uint16_t*>(values);
+  a.idx = idx;
+  a.tile_meta = tile_meta;
+  a.row_meta = row_meta;
+  a.R = R;
+  a.K = K;
+  a.tile_rows = tile_rows;
+  a.tile_cols = tile_cols;
+  a.dtype = dtype;
+  a.values_bytes = vbytes;
+  a.idx_bytes = ib;
+  a.act = static_cast<const uint16_t*>(act);
+  a.T = T;
+  a.ldx = ldx;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.out_dtype = out_dtype;
+  return hip_status(nm::launch_hybrid_spmm(a, static_cast<hipStream_t>(stream)), "nm_hybrid_spmm launch");
 }
 
 }  // extern "C"

@@ -85,6 +85,31 @@ hipError_t launch_spmm_lds(const SpmmArgs& a, hipStream_t s);
 bool spmm_lds_nm_applies(const SpmmArgs& a);
 hipError_t launch_spmm_lds_nm(const SpmmArgs& a, hipStream_t s);
 
+// Hybrid dense / 2:4 weight tiles (nm_hybrid.hip): pack and product.  The
+// layout tables are device arrays as nm_hybrid_layout writes them; values_bytes
+// and idx_bytes bound every weight access (both below 2^32).
+struct HybridArgs {
+  const uint16_t* values = nullptr;   // product: packed weights
+  const uint8_t* idx = nullptr;
+  const int64_t* tile_meta = nullptr;
+  const int64_t* row_meta = nullptr;
+  int64_t R = 0, K = 0, tile_rows = 0, tile_cols = 0;
+  int dtype = 0;
+  uint64_t values_bytes = 0, idx_bytes = 0;
+  const uint16_t* act = nullptr;      // product: activations and output
+  int64_t T = 0, ldx = 0;
+  void* Y = nullptr;
+  int64_t ldy = 0;
+  int out_dtype = 0;
+  const uint16_t* W = nullptr;        // pack: dense weights and packed outputs
+  int64_t ldw = 0;
+  uint16_t* values_out = nullptr;
+  uint8_t* idx_out = nullptr;
+};
+constexpr int64_t kHybridMaxTileCols = 8192;  // tile-columns per row the product takes
+hipError_t launch_hybrid_pack(const HybridArgs& a, hipStream_t s);
+hipError_t launch_hybrid_spmm(const HybridArgs& a, hipStream_t s);
+
 // Device properties and per-kernel launch set-up, kept per device and safe to
 // call from several host threads (nm_api.cpp).
 int device_cu_count();                 // CUs of the current device (256 if the query fails)

@@ -56,18 +56,18 @@ constexpr int kPerStep = 2;          // activation loads per wave per step
 constexpr int kGroupLoads = 4;       // packed-value loads per wave per group
 constexpr int kSAG = kBR * 128;      // packed values, one group (128 B per row)
 
-// P = 1: 1:4, P = 2: 1:8.  VB: packed-value bytes per row per step; GS: steps
+// P = 1: 1:4, P = 2: 1:8 (32 or 16 value bytes per row per K step).  GS: steps
 // per 128-byte value group; IBLK: index bytes per row per 16-step block (2 or
 // 3 bits per survivor); IL: index loads per wave per block.
 template <int P>
 struct NmPat;
 template <>
 struct NmPat<1> {
-  static constexpr int VB = 32, GS = 4, IBLK = 64, IL = 2;
+  static constexpr int GS = 4, IBLK = 64, IL = 2;
 };
 template <>
 struct NmPat<2> {
-  static constexpr int VB = 16, GS = 8, IBLK = 48, IL = 6;
+  static constexpr int GS = 8, IBLK = 48, IL = 6;
 };
 
 template <int P>
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     TileMapNM tm) {
   constexpr int FR = 2, FT = 4;
   static_assert(FR == 2, "1:4 index registers hold two row fragments");
-  constexpr int VB = NmPat<P>::VB, GS = NmPat<P>::GS, IBLK = NmPat<P>::IBLK;
+  constexpr int GS = NmPat<P>::GS, IBLK = NmPat<P>::IBLK;
   constexpr int SI = kBR * IBLK;    // index bits, one block
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* bbuf = smem;                         // [kNS][kStageB]

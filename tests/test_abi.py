@@ -295,3 +295,73 @@ def test_static_workspace_refuses_oversize_on_host():
     assert st(4096, 4097) == 2                     # 4096 * 4097 * 2 > 32 MiB
     assert "static workspace" in L.nm_last_error().decode()
     assert st(4096, 0) == 0                        # empty product
+
+
+# ---------------------------------------------------------------------------
+# hybrid dense / 2:4 tiles: layout (host), argument checks (fake pointers)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,K,tr,tc,frac", [(300, 1024, 64, 128, 0.5), (4096, 4096, 128, 128, 0.5),
+                                            (64, 64, 64, 64, 1.0), (130, 512, 64, 64, 0.0),
+                                            (1000, 768, 128, 64, 0.6)])
+def test_hybrid_layout_matches_oracle(R, K, tr, tc, frac):
+    import nm_inputs
+    from oracle import nm_hybrid as H
+    flags = nm_inputs.tile_flags(H.tile_grid(R, K, tr, tc), frac, 90, R)
+    L = nm.nm_hybrid_layout(R, K, tr, tc, flags)
+    tm, rm, nv, ni = H.hybrid_layout(R, K, tr, tc, flags)
+    assert np.array_equal(L.tile_meta, tm) and np.array_equal(L.row_meta, rm)
+    assert (L.values_count, L.idx_bytes) == (nv, ni)
+
+
+def test_hybrid_layout_errors():
+    L = nm.lib()
+    f = np.zeros((4, 4), dtype=np.uint8)
+    nv, ni = ctypes.c_int64(), ctypes.c_int64()
+
+    def lay(R, K, tr, tc, flags=f):
+        p = None if flags is None else flags.ctypes.data
+        return L.nm_hybrid_layout(R, K, tr, tc, p, None, None, ctypes.byref(nv), ctypes.byref(ni))
+    assert lay(256, 256, 64, 64) == 0 and (nv.value, ni.value) == (256 * 128, 256 * 32)
+    assert lay(256, 256, 32, 64) == 2          # tile_rows not a multiple of 64
+    assert lay(256, 256, 64, 96) == 2          # tile_cols not a multiple of 64
+    assert lay(256, 320, 64, 128) == 2         # tile_cols does not divide K
+    assert lay(256, 32, 64, 64) == 2           # K < 64
+    assert lay(256, 256, 64, 64, None) == 1    # flags NULL
+    bad = f.copy()
+    bad[2, 3] = 2
+    assert lay(256, 256, 64, 64, bad) == 2 and "flag" in L.nm_last_error().decode()
+    assert lay(0, 256, 64, 64, None) == 0 and (nv.value, ni.value) == (0, 0)
+    assert lay(64, 64 * 8193, 64, 64, np.zeros((1, 8193), np.uint8)) == 2   # too many tile-columns
+
+
+def test_hybrid_compress_and_spmm_errors():
+    L = nm.lib()
+    F = FAKE
+    # a valid 256 x 256 layout (all 2:4, 64 x 64 tiles): 32768 values, 8192 index bytes
+    def comp(W=F, R=256, K=256, ldw=256, dt=nm.NM_F16, tr=64, tc=64, tm=5 * F, rm=6 * F, nv=32768, ni=8192,
+             v=2 * F, i=3 * F):
+        return L.nm_hybrid_compress(W, R, K, ldw, dt, tr, tc, tm, rm, nv, ni, v, i, None)
+    assert comp(dt=nm.NM_I8) == 3
+    assert comp(tr=48) == 2
+    assert comp(ldw=200) == 4
+    assert comp(W=None) == 1
+    assert comp(i=None) == 1
+    assert comp(i=None, ni=0, v=F + 64) == 5   # every tile dense: idx may be NULL (then the alias check)
+    assert comp(v=2 * F + 8) == 7
+    assert comp(tm=5 * F + 4) == 7             # layout tables 8-byte aligned
+    assert comp(v=F + 64) == 5                 # values overlap W
+    assert comp(nv=1 << 30) == 2               # 2 GiB of values
+    assert comp(R=0) == 0
+
+    def mm(v=2 * F, i=3 * F, tm=5 * F, rm=6 * F, R=256, K=256, tr=64, tc=64, nv=32768, ni=8192,
+           dt=nm.NM_F16, act=F, T=64, ldx=256, Y=4 * F, ldy=256, od=nm.NM_F32):
+        return L.nm_hybrid_spmm(v, i, tm, rm, R, K, tr, tc, nv, ni, dt, act, T, ldx, Y, ldy, od, None)
+    assert mm(od=nm.NM_BF16) == 3
+    assert mm(ldx=128) == 4
+    assert mm(ldy=100) == 4
+    assert mm(ldx=(1 << 22) + 8) == 2
+    assert mm(act=None) == 1
+    assert mm(Y=F + 256) == 5                  # Y overlaps act
+    assert mm(Y=5 * F - 64) == 5               # Y overlaps the tile table
+    assert mm(T=0) == 0

@@ -37,8 +37,8 @@ def test_layout_worked_example():
     # row 1: a 2:4 tile then a dense one
     tm, rm, nv, ni = H.hybrid_layout(2, 16, 1, 8, np.array([[1, 0], [0, 1]]))
     assert tm.tolist() == [[[0, -1], [8, 0]], [[12, 1], [16, -1]]]
-    assert rm.tolist() == [[12, 1], [12, 1]]
-    assert (nv, ni) == (24, 2)
+    assert rm.tolist() == [[12, 1, 0, 0], [12, 1, 12, 1]]
+    assert (nv, ni) == (24, 16)   # 2 index bytes, zero-padded to one 16-byte block
     w = np.arange(1, 33, dtype=np.float32).reshape(2, 16)
     w[0, 8:16] = [5, -7, 1, 2, 0, 3, -3, 1]       # 2:4 tile of row 0
     w[1, 0:8] = [1, 1, 1, 1, -4, 0, 2, 9]         # 2:4 tile of row 1
@@ -52,6 +52,7 @@ def test_layout_worked_example():
     # groups (1,1,1,1) -> 0,1 (ties go low); (-4,0,2,9) -> 0,3
     assert f[12:16].tolist() == [1, 1, -4, 9]
     assert idx[1] == (0 | 1 << 2 | 0 << 4 | 3 << 6)
+    assert not idx[2:].any()
     assert f[16:24].tolist() == list(range(25, 33))
 
 
@@ -78,7 +79,8 @@ def test_all_sparse_is_row_wise_2of4(R, K, tr, tc, dt):
     ref_vals, ref_idx = O.prune_pack(w, 2, 4)
     assert np.array_equal(vals.reshape(R, K // 2), ref_vals)
     ref_bytes = ref_idx.astype("<u4").view(np.uint8).reshape(R, -1)[:, :K // 8]
-    assert np.array_equal(idx.reshape(R, K // 8), ref_bytes)
+    assert np.array_equal(idx[:R * K // 8].reshape(R, K // 8), ref_bytes)
+    assert idx.size == -(-R * K // 8 // 16) * 16 and not idx[R * K // 8:].any()
     y = H.hybrid_spmm_ref(vals, idx, R, K, tr, tc, flags, act, dt)
     assert np.array_equal(y, O.spmm_ref(ref_vals, ref_idx, K, 2, 4, act, dt))
 
@@ -134,7 +136,7 @@ def test_sizes_and_zero_fraction(R, K, tr, tc, frac):
     nd = flags.sum(axis=1)
     ns = grid[1] - nd
     assert nv == int(np.sum(rows * (nd * tc + ns * tc // 2)))
-    assert ni == int(np.sum(rows * ns * tc // 8))
+    assert ni == -(-int(np.sum(rows * ns * tc // 8)) // 16) * 16
     w = int_bits((R, K), -4, 4, 9, nonzero=True)
     vals, idx = H.hybrid_pack(w, tr, tc, flags)
     dec = H.hybrid_decompress(vals, idx, R, K, tr, tc, flags)
