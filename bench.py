@@ -51,7 +51,8 @@ def parse():
                     help="dense-matmul load before the warmup, so the clock has settled "
                          "(an idle GPU takes about a second of load to reach it)")
     ap.add_argument("--workload", type=int, default=2,
-                    help="1..7 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8)")
+                    help="1..8 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8; "
+                         "8: the same shape in hybrid dense / 2:4 tiles)")
     ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
     ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
@@ -142,6 +143,189 @@ def cpu_baseline(wl, n, m, T, reps):
             "gemm_dense_eq_gflops": gemm_flops / tg / 1e9}
 
 
+def cpu_baseline_hybrid(wl, T, reps):
+    """The hybrid-tile oracle as it stands (pack, decompress, fp64 GEMM) on the first
+    eight tile-rows of W, scaled to all of them."""
+    from oracle import nm_hybrid as H
+    tr, tc, _ = wl.hybrid
+    flags = wl.tile_flags()
+    rb = 8
+    w = wl.weights()[:rb * tr]
+    act = wl.activations(T)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        v, i = H.hybrid_pack(w, tr, tc, flags[:rb])
+        H.hybrid_spmm_ref(v, i, rb * tr, wl.K, tr, tc, flags[:rb], act, wl.dtype)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times) * flags.shape[0] / rb
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"value": 2.0 * wl.R * wl.K * T / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{wl.R}x{wl.K}x{T} hybrid {tr}x{tc} tiles: pack, decompress and fp64 matmul of "
+                       f"the first {rb} of {flags.shape[0]} tile-rows, scaled; median of {reps} runs")}
+
+
+def bench_hybrid(args, wl):
+    """Hybrid dense / 2:4 tiles: one step = nm_hybrid_compress + nm_hybrid_spmm."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_nm_amd as nm
+
+    R, K = wl.R, wl.K
+    T = args.T if args.T is not None else wl.Ts[0]
+    tr, tc, frac = wl.hybrid
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+    out_dtype = torch.float32 if args.out_dtype == "f32" else tdt
+    flags = wl.tile_flags()
+    L = nm.nm_hybrid_layout(R, K, tr, tc, flags)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+    W = dev(wl.weights())
+    act = dev(wl.activations(T))
+    vals = torch.empty(L.values_count, dtype=tdt, device="cuda")
+    idx = torch.zeros(max(L.idx_bytes, 16), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((T, R), dtype=out_dtype, device="cuda")
+    y_half = torch.empty((T, R), dtype=tdt, device="cuda")
+
+    def compress(_c=0):
+        nm.nm_hybrid_compress(W, L, values=vals, idx=idx)
+
+    def gemm(_c=0):
+        nm.nm_hybrid_spmm(vals, idx, L, act, out_dtype=out_dtype, out=Y)
+
+    settle = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    tw = time.perf_counter()
+    while (time.perf_counter() - tw) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            torch.matmul(settle, settle)
+        torch.cuda.synchronize()
+    del settle
+    for _ in range(args.warmup):
+        compress()
+    for _ in range(args.warmup):
+        gemm()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    start.record()
+    for _ in range(args.steps):
+        compress()
+    mid.record()
+    for _ in range(args.steps):
+        gemm()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    compress_mean_us = start.elapsed_time(mid) * 1e3 / args.steps
+    gemm_mean_us = mid.elapsed_time(end) * 1e3 / args.steps
+
+    # per-kernel blocks, alternating (see main): the hybrid product with both
+    # output dtypes, the dense GEMMs with the same ones, and the all-2:4 product
+    v24, i24 = nm.nm_compress(W, 2, 4)
+    # dense operand: the weight as the hybrid pruning leaves it (W_hat^T, row-major)
+    W_hat_t = _hybrid_dense_operand(nm, torch, vals, idx, L, tdt)
+    loops = {"gemm": gemm, "compress": compress,
+             "gemm_half": lambda c: nm.nm_hybrid_spmm(vals, idx, L, act, out_dtype=tdt, out=y_half),
+             "dense_half": lambda c: torch.mm(act, W_hat_t),
+             "dense_f32": lambda c: torch.mm(act, W_hat_t, out_dtype=torch.float32),
+             "all_2of4": lambda c: nm.nm_spmm(v24, i24, act, K, 2, 4, out_dtype=out_dtype)}
+    iters = max(20, args.steps)
+    for name in list(loops):
+        try:
+            for _ in range(3):
+                loops[name](0)
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"{name} unavailable: {e}", file=sys.stderr)
+            del loops[name]
+    samples = {name: [] for name in loops}
+    for _ in range(5):
+        for name, fn in loops.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                fn(0)
+            b.record()
+            torch.cuda.synchronize()
+            samples[name].append(a.elapsed_time(b) * 1e3 / iters)
+    loop_us = {name: float(np.median(v)) for name, v in samples.items()}
+
+    def ratio(x, y):
+        return loop_us[x] / loop_us[y] if x in loop_us and y in loop_us else None
+
+    alg_flop = 2.0 * T * L.values_count           # one MAC per stored weight and token
+    dense_eq_flop = 2.0 * R * K * T
+    achieved = alg_flop / (gemm_mean_us * 1e-6) / 1e12
+    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
+               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
+    hsh = source_hash(lib_src)
+    out_name = args.out_dtype
+    kernel_key = f"hybrid_w{wl.wid}_{tr}x{tc}_T{T}_{out_name}"
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS[wl.dtype], "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS[wl.dtype], "traffic": traffic_from_profile(kernel_key, hsh),
+                "kernel": "nm_hybrid_spmm",
+                "per_launch": {"flop": alg_flop, "mean_us": gemm_mean_us,
+                               "bytes": L.values_count * 2 + L.idx_bytes + T * K * 2 +
+                               T * R * (4 if out_name == "f32" else 2)}}
+    dense_tiles = float(flags.mean())
+    out = {
+        "metric": METRIC, "value": dense_eq_flop / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,sigma) inputs of the workload's shapes; seeded tile flags)",
+        "config": {"workload": wl.name, "R": R, "K": K, "T": T, "tiles": f"{tr}x{tc}",
+                   "dense_tile_fraction": dense_tiles, "zero_fraction": 0.5 * (1.0 - dense_tiles),
+                   "out_dtype": out_name, "step": "nm_hybrid_compress + nm_hybrid_spmm",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {
+            "nm_hybrid_spmm_us_in_step": gemm_mean_us, "nm_hybrid_compress_us_in_step": compress_mean_us,
+            "nm_hybrid_spmm_us_loop": loop_us.get("gemm"), "nm_hybrid_spmm_half_out_us": loop_us.get("gemm_half"),
+            "nm_hybrid_compress_us": loop_us.get("compress"),
+            "dense_half_out_us": loop_us.get("dense_half"), "dense_f32_out_us": loop_us.get("dense_f32"),
+            "all_2of4_nm_spmm_us": loop_us.get("all_2of4"),
+            "speedup_vs_dense_same_out_dtype": {k: v for k, v in {
+                "f32": ratio("dense_f32", "gemm") if out_name == "f32" else None,
+                "half": ratio("dense_half", "gemm_half")}.items() if v is not None},
+        },
+        "wall_s_timed": wall, "source_hash": hsh,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_hybrid(wl, T, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+def _hybrid_dense_operand(nm, torch, vals, idx, L, tdt):
+    """W_hat^T [K, R] row-major for the dense reference GEMM: the hybrid-pruned weight
+    rebuilt on the GPU (dense tiles copied, 2:4 tiles decompressed tile by tile)."""
+    R, K, tr, tc = L.R, L.K, L.tile_rows, L.tile_cols
+    W_hat = torch.zeros((R, K), dtype=tdt, device=vals.device)
+    vb = vals.view(-1)
+    ib = idx.view(-1)
+    for b in range(L.row_meta.shape[0]):
+        r0, nr = b * tr, min(R, (b + 1) * tr) - b * tr
+        Lv, Li = int(L.row_meta[b, 0]), int(L.row_meta[b, 1])
+        for j in range(L.tile_meta.shape[1]):
+            v0, i0 = int(L.tile_meta[b, j, 0]), int(L.tile_meta[b, j, 1])
+            rows = torch.arange(nr, device=vals.device)
+            if i0 < 0:
+                src = vb[v0 + rows[:, None] * Lv + torch.arange(tc, device=vals.device)[None, :]]
+                W_hat[r0:r0 + nr, j * tc:(j + 1) * tc] = src
+            else:
+                sv = vb[v0 + rows[:, None] * Lv + torch.arange(tc // 2, device=vals.device)[None, :]].contiguous()
+                si = ib[i0 + rows[:, None] * Li + torch.arange(tc // 8, device=vals.device)[None, :]]
+                words = si.contiguous().view(torch.int32)
+                W_hat[r0:r0 + nr, j * tc:(j + 1) * tc] = nm.nm_decompress(sv, words, tc, 2, 4)
+    return W_hat.t().contiguous()
+
+
 def measured_peaks(torch):
     """Peaks measured on this GPU with plain library calls (context for the
     roofline fractions): a 1 GiB device-to-device copy (read + write bytes)
@@ -192,6 +376,9 @@ def main():
     nm.lib()  # fails loudly if the library is not built
 
     wl = nm_inputs.WORKLOADS[args.workload]
+    if wl.hybrid:
+        bench_hybrid(args, wl)
+        return
     T = args.T if args.T is not None else wl.Ts[-1] if args.workload == 3 else wl.Ts[0]
     if args.pattern:
         n, m = (int(v) for v in args.pattern.split(":"))

@@ -113,6 +113,7 @@ class Workload:
     sigma_x: float = 1.0
     permuted: bool = False
     note: str = ""
+    hybrid: tuple = ()  # (tile_rows, tile_cols, dense fraction) for hybrid dense / 2:4 tiles
 
     def weights(self) -> np.ndarray:
         if self.dtype == I8:
@@ -131,6 +132,10 @@ class Workload:
 
     def permutation(self) -> np.ndarray | None:
         return random_permutation(self.K, self.wid) if self.permuted else None
+
+    def tile_flags(self) -> np.ndarray:
+        tr, tc, frac = self.hybrid
+        return tile_flags((-(-self.R // tr), self.K // tc), frac, self.wid)
 
 
 # The five workloads (sizes R x K x T).  Shapes follow the layers the pages
@@ -155,4 +160,8 @@ WORKLOADS = {
     # the same shape in OCP FP8 E4M3 (an 8-bit float in the one-byte layout)
     7: Workload(7, "fp8-e4m3-2of4-prefill", 4096, 4096, (2048,), ((2, 4),), F8, 1.0, 1.0,
                 note="FP8 E4M3 2:4, fp32 output"),
+    # hybrid dense / 2:4 tiles (PATCH) at the prefill projection's shape: 128 x
+    # 128 tiles, half of them (seeded at random) dense, so 25% of W is zero
+    8: Workload(8, "llama2-7b-proj-prefill-hybrid-tiles-bf16", 4096, 4096, (2048,), ((2, 4),), BF16, 0.02,
+                note="hybrid dense / 2:4 128x128 tiles, half dense", hybrid=(128, 128, 0.5)),
 }

@@ -13,44 +13,25 @@
 // chunk is copied, a 2:4 tile's chunk gives its four survivors and its index
 // byte with the selection nm_compress uses (same largest-magnitude rule).
 //
-// Product: the register-pipelined layout of the N:M kernel (nm_spmm_pipe.hip):
-// a workgroup owns 256 x 64 (or 128 x 64) of Y^T, each wave 64 (32) rows and
-// all tokens; activations go through an LDS ring of direct global->LDS loads,
-// each wave's weight fragments straight from global memory into registers
-// several K steps ahead.  A 64-wide K step of a dense tile is two
+// Product: a workgroup of 8 waves owns 256 x 128 (or 128 x 64) of Y^T;
+// activations and weights go through an LDS ring of direct global->LDS loads,
+// each wave multiplying one of four 64- (32-) row weight slices by half of the
+// workgroup's tokens.  A 64-wide K step of a dense tile is two
 // v_mfma_f32_16x16x32 per fragment pair, of a 2:4 tile one
 // v_smfmac_f32_16x16x64: the activation operand the sparse instruction takes
 // (K 8q..8q+7 and 32+8q..32+8q+7 of token i in lane 16q + i) is the two dense
 // instructions' operands side by side, so both read the same LDS fragments.
 // Tile-rows are multiples of 64 rows, so a wave's rows share one flag per
-// step and the choice is one uniform branch per step.  Every fragment issues
-// two loads per step either way (dense: two 16-byte runs of the row; 2:4: 16
-// bytes of survivors and the 16-byte index block holding the lane's 16 index
-// bits), and without a branch: the second load's buffer and offset are
-// selected, so the counted waits hold on either kind of tile.  Weight reads go through buffer descriptors bounded by
-// the arrays' sizes: offsets from a wrong layout table read zeros instead of
-// memory outside the arrays, and the pack's stores are bounded the same way.
+// step and the choice is one uniform branch per step.  Weight reads go
+// through buffer descriptors bounded by the arrays' sizes: offsets from a
+// wrong layout table read zeros instead of memory outside the arrays, and the
+// pack's stores are bounded the same way.
 #include "nm_device.h"
 #include "nm_internal.h"
 #include "nm_select.h"
 
-#include <type_traits>
-#include <utility>
-
 namespace nm {
 namespace {
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): stage
-// indices stay compile-time constants, so per-stage registers never need an
-// indexed (memory) array.
-template <typename F, int... I>
-__device__ inline void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void unroll(F&& f) {
-  unroll_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // A byte offset into a buffer of `bytes` bytes, or one the buffer refuses.
 __device__ inline uint32_t bounded(int64_t off, uint32_t bytes) {
@@ -98,30 +79,46 @@ __device__ inline f32x4 mfma_dense(const u32x4& a, const u32x4& b, const f32x4& 
   }
 }
 
-// One lane's weight operand of one 16-row fragment for one K step: dense,
-// the row's K 8q..8q+7 (lo) and 32+8q..32+8q+7 (hi); 2:4, the 8 survivors
-// (lo) and the aligned 16 index bytes holding the lane's two (hi).
-struct HFrag {
-  u32x4 lo, hi;
-};
-
 constexpr int kMaxFlagWords = 256;  // tile-columns per row up to 32 * 256
 
+// Product.  A workgroup (8 waves, two per SIMD) owns BR x BT of Y^T in four
+// row slices of WROWS = BR/4 rows; wave w multiplies slice w % 4 by token half
+// w / 4.  The tile-rows are multiples of 64 rows, so a slice's rows share one
+// flag per K step.  Stages form an NS-deep ring; stage = the BT tokens'
+// activations (slot (token, chunk c) at token*8 + (c ^ (token & 7))) plus one
+// weight slice per row slice of WROWS x 128 bytes:
+//   dense step  the rows' 128 bytes of values, slot (row, chunk c) at
+//               row*8 + (c ^ ((row >> 1) & 7));
+//   2:4 step    the rows' 64 bytes of survivors, slot (row, chunk c) at
+//               row*4 + (c ^ ((row >> 1) & 3)), and from the slice's middle
+//               each row's aligned 16-byte index block holding its 8 index
+//               bytes of the step (16 bytes per row).
+// A slice's AL direct loads are split between its two waves, AL/2 each, for
+// both kinds of step (a 2:4 step gives the survivors to the first wave, the
+// index blocks and loads the descriptor refuses, which write zeros into slots
+// nothing reads, to the second), so the counted waits are fixed; the barrier
+// of each step publishes every wave's loads to the others.
 template <int DT, int OUT, int BR, int BT, int NS>
-__global__ __launch_bounds__(256) void hybrid_gemm_kernel(
+__global__ __launch_bounds__(512) void hybrid_gemm_kernel(
     const uint16_t* __restrict__ values, uint32_t values_bytes, const uint8_t* __restrict__ idx,
     uint32_t idx_bytes, const int64_t* __restrict__ tile_meta, const int64_t* __restrict__ row_meta, int R,
     int K, int tile_rows, int tile_cols, int KB, const uint16_t* __restrict__ act, int T, int64_t ldx,
     void* __restrict__ Y, int64_t ldy, int tilesR, int tilesT, int group_r) {
-  constexpr int WROWS = BR / 4;    // rows per wave
-  constexpr int FR = WROWS / 16;   // 16-row fragments per wave
-  constexpr int FT = BT / 16;      // 16-token fragments
-  constexpr int STAGE = BT * 128;  // bytes of one activation stage (BT x 64 halves)
-  constexpr int BLOADS = BT / 32;  // 16-byte direct loads per thread per stage
-  constexpr int PER_STEP = BLOADS + 2 * FR;
+  constexpr int WROWS = BR / 4;          // rows per slice
+  constexpr int TW = BT / 2;             // tokens per wave
+  constexpr int FR = WROWS / 16;         // 16-row fragments per wave
+  constexpr int FT = TW / 16;            // 16-token fragments per wave
+  constexpr int SB = WROWS * 128;        // bytes of one weight slice
+  constexpr int STAGE_B = BT * 128;      // activations of one stage
+  constexpr int STAGE = STAGE_B + 4 * SB;
+  constexpr int BL = BT / 64;            // activation loads per wave per step
+  constexpr int AL = SB / 1024;          // weight loads per slice per step
+  constexpr int AH = AL / 2;             // ... per wave
+  constexpr int PER_STEP = BL + AH;
   static_assert((NS - 2) * PER_STEP < 64, "vmcnt range");
-  extern __shared__ __align__(16) unsigned char smem[];     // [NS][STAGE], then the flag words
-  uint32_t* flag_words = reinterpret_cast<uint32_t*>(smem + NS * STAGE);  // [4][kMaxFlagWords]
+  static_assert(WROWS <= 64 && AL >= 2, "a 2:4 step's index blocks take one load");
+  extern __shared__ __align__(16) unsigned char smem[];  // [NS][STAGE], then the flag words
+  uint32_t* flag_words = reinterpret_cast<uint32_t*>(smem + NS * STAGE);  // [8][kMaxFlagWords]
 
   // ---- tile: XCD-aware remap, then groups of group_r row tiles
   const int ntiles = tilesR * tilesT;
@@ -137,17 +134,16 @@ __global__ __launch_bounds__(256) void hybrid_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rs = wave & 3, th = wave >> 2;  // row slice, token half
   const int li = lane & 15, lq = lane >> 4;
   const int nsteps = K >> 6;
   const int spt = tile_cols >> 6;  // K steps per tile-column
 
-  // ---- this wave's tile-row (its rows lie in one: tile_rows % WROWS == 0;
-  // rows past R read row R - 1, whose tile-row is the last)
-  const int wrow0 = R0 + wave * WROWS;
-  const int b = __builtin_amdgcn_readfirstlane(min(wrow0, R - 1) / tile_rows);
+  // ---- the slice's tile-row (rows past R read row R - 1, in the last one)
+  const int srow0 = R0 + rs * WROWS;
+  const int b = __builtin_amdgcn_readfirstlane(min(srow0, R - 1) / tile_rows);
   const int64_t Lv = row_meta[b * 4], Li = row_meta[b * 4 + 1];
   const int64_t VB = row_meta[b * 4 + 2], IB = row_meta[b * 4 + 3];
-  // dense flags of the tile-row's tiles, one bit each, into this wave's words
   uint32_t* wflags = flag_words + wave * kMaxFlagWords;
   for (int j0 = 0; j0 < KB; j0 += 64) {
     const int j = j0 + lane;
@@ -158,78 +154,78 @@ __global__ __launch_bounds__(256) void hybrid_gemm_kernel(
       if (j0 + 32 < KB) wflags[(j0 >> 5) + 1] = uint32_t(m >> 32);
     }
   }
-
-  // per-fragment row parts of the weight offsets (elements / bytes)
-  uint32_t vrow[FR], irow[FR];
+  // Byte offsets of slice row q's values and index bytes (rows past R lie past
+  // the end of the arrays: the descriptors return zeros for them, and their
+  // outputs are dropped).
+  const int64_t rq0 = int64_t(srow0) - int64_t(b) * tile_rows;  // first slice row in its tile-row
+  auto vrow_bytes = [&](int q) { return uint32_t((VB + (rq0 + q) * Lv) * 2); };
+  auto irow_bytes = [&](int q) { return uint32_t(IB + (rq0 + q) * Li); };
+  // per-lane parts of this wave's weight loads (loads j = th*AH .. th*AH+AH-1
+  // of the slice): dense load j covers slice rows [8j, 8j+8) (lane: row
+  // 8j + l/8, position l%8), 2:4 survivor load j rows [16j, 16j+16) (row
+  // 16j + l/4, position l%4), the index load row l % WROWS
+  uint32_t doff[AH], soff[AH];
 #pragma unroll
-  for (int i = 0; i < FR; ++i) {
-    const int r = min(wrow0 + i * 16 + li, R - 1);
-    const int64_t rr = r - int64_t(b) * tile_rows;
-    vrow[i] = uint32_t(VB + rr * Lv) + uint32_t(lq) * 8u;
-    irow[i] = uint32_t(IB + rr * Li) + uint32_t(lq) * 2u;  // IB, Li: multiples of 8
+  for (int jj = 0; jj < AH; ++jj) {
+    const int j = th * AH + jj;
+    const int q = j * 8 + (lane >> 3);
+    doff[jj] = vrow_bytes(q) + uint32_t((lane & 7) ^ ((q >> 1) & 7)) * 16u;
+    const int q2 = jj * 16 + (lane >> 2);
+    soff[jj] = vrow_bytes(q2) + uint32_t((lane & 3) ^ ((q2 >> 1) & 3)) * 16u;
   }
+  const uint32_t ioff = irow_bytes(lane % WROWS);
+  // for the fragment reads: bit 3 of each fragment row's index-row start
+  uint32_t ihalf = 0;
+#pragma unroll
+  for (int i = 0; i < FR; ++i) ihalf |= ((irow_bytes(i * 16 + li) >> 3) & 1u) << i;
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(values, values_bytes);
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(idx, idx_bytes);
 
-  // activation slots this thread fills each stage: instruction j covers slots
-  // [(wave*BLOADS + j)*64, +64), lane l takes slot base + l; byte offsets from
-  // the tile's first token row (rows past T reread row T - 1, whose outputs
-  // are dropped), through a descriptor ending with the tile's last row
+  // activations: descriptor over the tile's token rows (rows past T reread
+  // row T - 1, whose outputs are dropped)
   const int tlast = min(T0 + BT, T) - 1;
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(act + int64_t(T0) * ldx, uint32_t((int64_t(tlast - T0) * ldx + K) * 2));
-  uint32_t boff[BLOADS];
+  uint32_t boff[BL];
 #pragma unroll
-  for (int j = 0; j < BLOADS; ++j) {
-    const int slot = (wave * BLOADS + j) * 64 + lane;
+  for (int j = 0; j < BL; ++j) {
+    const int slot = (wave * BL + j) * 64 + lane;
     const int tok = slot >> 3;
     const int chunk = (slot & 7) ^ (tok & 7);
     const int t = min(T0 + tok, T - 1) - T0;
     boff[j] = uint32_t(t) * uint32_t(ldx) * 2u + uint32_t(chunk) * 16u;
   }
-  // the activations of step s (past the last step: zeros, from an offset the
-  // descriptor refuses)
-  auto issue_b = [&](int s, int stage) {
-    const uint32_t so = s < nsteps ? uint32_t(s) * 128u : 0x80000000u;
-#pragma unroll
-    for (int j = 0; j < BLOADS; ++j) dma16(rb, boff[j], so, smem + stage * STAGE + (wave * BLOADS + j) * 1024);
-  };
 
-  // The weight stream walks the row's tiles in order: lv / li are the next
+  // The weight stream walks the row's tiles in order: lv / lio are the next
   // step's value / index-byte positions along a row of the tile-row, jt and
-  // kt its tile-column and step within it.
+  // kt its tile-column and step within it.  Past the last step every load
+  // reads zeros (offsets the descriptors refuse), so those steps add zero.
   uint32_t lv = 0, lio = 0;
   int jt = 0, kt = 0;
-  HFrag ar[NS][FR];
-  uint32_t sdense = 0;  // bit u: the step held by register stage u is dense
-  // Per step and fragment: the row's next 16 bytes of values, then either
-  // its following 16 value bytes (dense) or the aligned index block holding
-  // this lane's two index bytes (2:4): same instructions and counts for both.
-  // The lane's index bytes sit at byte irow[i] + lio; the block starts at that
-  // offset rounded down to 16 and (irow[i] + lio) & 15 locates them in it, so
-  // each register stage keeps the lio it was loaded with.
-  uint32_t sio[NS];
-  // Past the last step the loads read zeros (offsets the descriptors refuse),
-  // so those steps' MFMAs add exactly zero.
-  auto issue_a = [&](auto stage_c, int step) {
-    constexpr int stage_u = decltype(stage_c)::value;
+  uint32_t sdense = 0, shalf = 0;  // bit u: stage u's step is dense / reads its index block at +8
+  auto issue = [&](int u, int step) {
+    unsigned char* st = smem + u * STAGE;
+    const uint32_t so = step < nsteps ? uint32_t(step) * 128u : 0x80000000u;
+#pragma unroll
+    for (int j = 0; j < BL; ++j) dma16(rb, boff[j], so, st + (wave * BL + j) * 1024);
     const int jc = min(jt, KB - 1);
     const uint32_t dense = (__builtin_amdgcn_readfirstlane(wflags[jc >> 5]) >> (jc & 31)) & 1u;
     const bool live = step < nsteps;
-    const uint32_t v = lv, io = lio;
-    const __amdgpu_buffer_rsrc_t r1 = dense ? rv : ri;
+    const uint32_t v2 = lv * 2u, io = lio;
+    unsigned char* sl = st + STAGE_B + rs * SB;
 #pragma unroll
-    for (int i = 0; i < FR; ++i) {
-      const uint32_t e = vrow[i] + v;
-      const uint32_t o0 = live ? e * 2u : 0xFFFFFFF0u;
-      const uint32_t o1 = !live ? 0xFFFFFFF0u : dense ? (e + 32u) * 2u : (irow[i] + io) & ~15u;
-      ar[stage_u][i].lo = __builtin_amdgcn_raw_buffer_load_b128(rv, o0, 0, 0);
-      ar[stage_u][i].hi = __builtin_amdgcn_raw_buffer_load_b128(r1, o1, 0, 0);
+    for (int jj = 0; jj < AH; ++jj) {
+      // 2:4: the first wave loads the survivors (AH loads), the second the
+      // index blocks (its load 0) and zeros
+      uint32_t o2 = th == 0 ? soff[jj] + v2 : (jj == 0 ? (ioff + io) & ~15u : 0xFFFFFFF0u);
+      const __amdgpu_buffer_rsrc_t r = (dense || th == 0 || jj != 0) ? rv : ri;
+      const uint32_t o = dense ? doff[jj] + v2 : o2;
+      dma16(r, live ? o : 0xFFFFFFF0u, 0u, sl + (th * AH + jj) * 1024);
     }
-    sdense = (sdense & ~(1u << stage_u)) | (dense << stage_u);
-    sio[stage_u] = io;
-    lv = v + (dense ? 64u : 32u);
-    lio = io + (dense ? 0u : 8u);
+    sdense = (sdense & ~(1u << u)) | (dense << u);
+    shalf = (shalf & ~(1u << u)) | (((io >> 3) & 1u) << u);
+    lv += dense ? 64u : 32u;
+    lio += dense ? 0u : 8u;
     const int nk = kt + 1;
     jt += nk == spt ? 1 : 0;
     kt = nk == spt ? 0 : nk;
@@ -241,77 +237,86 @@ __global__ __launch_bounds__(256) void hybrid_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: steps 0 .. NS-2 in flight.  Every step issues the same
-  // loads (zeros past the last step) and runs its MFMAs, so the waits are
-  // fixed counts and the loop holds no data-dependent branch but the uniform
-  // dense / 2:4 choice.
-  unroll<NS - 1>([&](auto pc) {
-    constexpr int p = decltype(pc)::value;
-    issue_b(p, p);
-    issue_a(pc, p);
-  });
+  // ---- prologue: steps 0 .. NS-2 in flight.  Every step then issues the
+  // same loads (past the last step, zeros nothing reads), so the waits are
+  // fixed counts; the stage index is a run-time value, so one copy of the
+  // step's code (and of its per-lane offsets) serves every stage, and the
+  // loop's only branch is the uniform dense / 2:4 choice.
+  for (int p = 0; p < NS - 1; ++p) issue(p, p);
 
-  for (int s0 = 0; s0 < nsteps; s0 += NS) {
-    unroll<NS>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      const int s = s0 + u;
-      {
-        // step s's loads are done once at most the later steps' loads remain
-        wait_vmcnt<(NS - 2) * PER_STEP>();
-        barrier_no_fence();
-        issue_b(s + NS - 1, (u + NS - 1) % NS);
-        issue_a(std::integral_constant<int, (u + NS - 1) % NS>{}, s + NS - 1);
-        const unsigned char* st = smem + u * STAGE;
-        u32x8 bf[FT];
+  int u = 0, un = NS - 1;  // stages of step s and of step s + NS - 1
+  for (int s = 0; s < nsteps; ++s) {
+    {
+      // step s has landed once at most the later steps' loads remain; the
+      // barrier publishes every wave's loads and retires the slot the new
+      // loads reuse
+      wait_vmcnt<(NS - 2) * PER_STEP>();
+      barrier_no_fence();
+      issue(un, s + NS - 1);
+      const unsigned char* st = smem + u * STAGE;
+      const unsigned char* sl = st + STAGE_B + rs * SB;
+      u32x8 bf[FT];
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const int tok = th * TW + j * 16 + li;
+        const int sw = tok & 7;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(st + (tok * 8 + (lq ^ sw)) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(st + (tok * 8 + ((lq + 4) ^ sw)) * 16);
+        bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      if ((sdense >> u) & 1u) {
+        u32x4 alo[FR], ahi[FR];
+#pragma unroll
+        for (int i = 0; i < FR; ++i) {
+          const int q = i * 16 + li;
+          const int f = (q >> 1) & 7;
+          alo[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + (lq ^ f)) * 16);
+          ahi[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + ((lq + 4) ^ f)) * 16);
+        }
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-          const int tok = j * 16 + li;
-          const int sw = tok & 7;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(st + (tok * 8 + (lq ^ sw)) * 16);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(st + (tok * 8 + ((lq + 4) ^ sw)) * 16);
-          bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        if ((sdense >> u) & 1u) {
-#pragma unroll
-          for (int j = 0; j < FT; ++j) {
-            const u32x4 blo = {bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
-            const u32x4 bhi = {bf[j][4], bf[j][5], bf[j][6], bf[j][7]};
-#pragma unroll
-            for (int i = 0; i < FR; ++i) {
-              acc[i][j] = mfma_dense<DT>(ar[u][i].lo, blo, acc[i][j]);
-              acc[i][j] = mfma_dense<DT>(ar[u][i].hi, bhi, acc[i][j]);
-            }
-          }
-        } else {
-          // this lane's 16 index bits: bytes pos, pos + 1 of its fragment's block
-          uint32_t ix[FR];
+          const u32x4 blo = {bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
+          const u32x4 bhi = {bf[j][4], bf[j][5], bf[j][6], bf[j][7]};
 #pragma unroll
           for (int i = 0; i < FR; ++i) {
-            const uint32_t pos = (irow[i] + sio[u]) & 15u;
-            const u32x4& h = ar[u][i].hi;
-            const uint32_t d = (pos & 8u) ? ((pos & 4u) ? h[3] : h[2]) : ((pos & 4u) ? h[1] : h[0]);
-            ix[i] = (d >> ((pos & 2u) * 8u)) & 0xFFFFu;
+            acc[i][j] = mfma_dense<DT>(alo[i], blo, acc[i][j]);
+            acc[i][j] = mfma_dense<DT>(ahi[i], bhi, acc[i][j]);
           }
-#pragma unroll
-          for (int j = 0; j < FT; ++j)
-#pragma unroll
-            for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(ar[u][i].lo, bf[j], acc[i][j], ix[i]);
         }
+      } else {
+        u32x4 a[FR];
+        uint32_t ix[FR];
+        const uint32_t sh = (shalf >> u) & 1u;
+#pragma unroll
+        for (int i = 0; i < FR; ++i) {
+          const int q = i * 16 + li;
+          a[i] = *reinterpret_cast<const u32x4*>(sl + (q * 4 + (lq ^ ((q >> 1) & 3))) * 16);
+          // this lane's two index bytes: the row's start and the step's
+          // position put them at byte 8*((row bit + step bit) & 1) + 2*lq
+          const uint32_t pos = ((((ihalf >> i) & 1u) ^ sh) << 3) + uint32_t(lq) * 2u;
+          ix[i] = *reinterpret_cast<const uint16_t*>(sl + SB / 2 + q * 16 + pos);
+        }
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+#pragma unroll
+          for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
       }
-    });
+    }
+    u = u + 1 == NS ? 0 : u + 1;
+    un = un + 1 == NS ? 0 : un + 1;
   }
-  // the loads past the last step are still landing: LDS and registers are
-  // done with only once they have
+  // the loads past the last step are still landing: the workgroup ends only
+  // once no direct load is writing LDS
   wait_vmcnt<0>();
 
   // ---- epilogue
   const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FR; ++i) {
-    const int r = R0 + wave * WROWS + i * 16 + lq * 4;
+    const int r = srow0 + i * 16 + lq * 4;
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      const int t = T0 + j * 16 + li;
+      const int t = T0 + th * TW + j * 16 + li;
       if (t >= T || r >= R) continue;
       const f32x4 v = acc[i][j];
       if constexpr (OUT == NM_F32) {
@@ -342,10 +347,10 @@ hipError_t launch_hybrid_cfg(const HybridArgs& a, hipStream_t s) {
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int group_r = tilesR < 4 ? tilesR : 4;
-  constexpr int lds = NS * BT * 128 + 4 * kMaxFlagWords * 4;
+  constexpr int lds = NS * (BT * 128 + BR * 128) + 8 * kMaxFlagWords * 4;
   auto kern = hybrid_gemm_kernel<DT, OUT, BR, BT, NS>;
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(256), lds, s, a.values, uint32_t(a.values_bytes), a.idx,
+  hipLaunchKernelGGL(kern, dim3(unsigned(ntiles)), dim3(512), lds, s, a.values, uint32_t(a.values_bytes), a.idx,
                      uint32_t(a.idx_bytes), a.tile_meta, a.row_meta, int(a.R), int(a.K), int(a.tile_rows),
                      int(a.tile_cols), int(a.K / a.tile_cols), a.act, int(a.T), a.ldx, a.Y, a.ldy, tilesR,
                      tilesT, group_r);
@@ -354,11 +359,9 @@ hipError_t launch_hybrid_cfg(const HybridArgs& a, hipStream_t s) {
 
 template <int DT, int OUT>
 hipError_t hybrid_tile(const HybridArgs& a, hipStream_t s) {
-  // 256 x 64 tiles when they cover the chip's 256 CUs, else 128 x 64 (a
-  // 256 x 128 tile's eight-register weight fragments four steps deep do not
-  // fit beside its accumulators without spilling)
-  const int64_t big = ((a.R + 255) / 256) * ((a.T + 63) / 64);
-  if (big >= 256) return launch_hybrid_cfg<DT, OUT, 256, 64, 4>(a, s);
+  // 256 x 128 tiles when they cover the chip's 256 CUs, else 128 x 64
+  const int64_t big = ((a.R + 255) / 256) * ((a.T + 127) / 128);
+  if (big >= 256) return launch_hybrid_cfg<DT, OUT, 256, 128, 3>(a, s);
   return launch_hybrid_cfg<DT, OUT, 128, 64, 6>(a, s);
 }
 
