@@ -502,9 +502,10 @@ def main():
         # dense int8 GEMM with an int32 result (hipBLASLt through torch._int_mm)
         loops["dense_same_out"] = lambda c: torch._int_mm(actp[c], dense_t[c])
     elif f8:
-        # dense fp8 GEMM with an fp32 result (hipBLASLt through torch._scaled_mm, unit scales)
+        # dense fp8 GEMM with an fp32 result (hipBLASLt through torch._scaled_mm, unit scales;
+        # its second operand must be column-major: the [K, R] view of the row-major W)
         one = torch.ones((), dtype=torch.float32, device="cuda")
-        loops["dense_same_out"] = lambda c: torch._scaled_mm(actp[c], dense_t[c], scale_a=one, scale_b=one,
+        loops["dense_same_out"] = lambda c: torch._scaled_mm(actp[c], dense[c].t(), scale_a=one, scale_b=one,
                                                              out_dtype=torch.float32)
     else:
         y_half = torch.empty((T, R), dtype=tdt, device="cuda")

@@ -7,11 +7,14 @@ draw their inputs from here.
 
 Recipe (the same everywhere):
   * generator: numpy PCG64 seeded with the sequence [workload_id, tensor_id,
-    variant]; tensor_id 0 = weight W, 1 = activations, 2 = permutation;
+    variant]; tensor_id 0 = weight W, 1 = activations, 2 = permutation,
+    3 = hybrid tile flags;
   * W and activations: float32 standard normal times sigma, then rounded to
     the storage type with round-to-nearest-even (fp16 through numpy's cast,
     bf16 through the bit routine below);
-  * permutation: a uniform random permutation of 0..K-1 (int32).
+  * permutation: a uniform random permutation of 0..K-1 (int32);
+  * tile flags: each tile dense (1) when a uniform draw is below the given
+    fraction, else 2:4 (0).
 
 Half-precision arrays are returned as their raw uint16 bit patterns, the form
 every consumer (oracle, C ABI) takes.
@@ -138,10 +141,11 @@ class Workload:
         return tile_flags((-(-self.R // tr), self.K // tc), frac, self.wid)
 
 
-# The five workloads (sizes R x K x T).  Shapes follow the layers the pages
+# The workloads (sizes R x K x T).  Shapes follow the layers the pages
 # measure: a small 2:4 example, a LLaMA-2-7B projection at prefill and at
-# decode, the general 1:4 / 1:8 forms, and a ViT-B/16 MLP fc1 over 64 images
-# of 197 tokens with a learned column permutation.
+# decode, the general 1:4 / 1:8 forms, a ViT-B/16 MLP fc1 over 64 images of
+# 197 tokens with a learned column permutation, the prefill shape in INT8 and
+# in FP8 E4M3, and the prefill shape with hybrid dense / 2:4 tiles.
 WORKLOADS = {
     1: Workload(1, "small-2of4-fp16", 256, 256, (64,), ((2, 4),), F16, 1.0,
                 note="2:4 fp16 small case"),
