@@ -230,7 +230,7 @@ def bench_hybrid(args, wl):
     # output dtypes, the dense GEMMs with the same ones, and the all-2:4 product
     v24, i24 = nm.nm_compress(W, 2, 4)
     # dense operand: the weight as the hybrid pruning leaves it (W_hat^T, row-major)
-    W_hat_t = _hybrid_dense_operand(nm, torch, vals, idx, L, tdt)
+    W_hat_t = _hybrid_dense_operand(nm, torch, W, L, flags, tdt)
     loops = {"gemm": gemm, "compress": compress,
              "gemm_half": lambda c: nm.nm_hybrid_spmm(vals, idx, L, act, out_dtype=tdt, out=y_half),
              "dense_half": lambda c: torch.mm(act, W_hat_t),
@@ -302,28 +302,19 @@ def bench_hybrid(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def _hybrid_dense_operand(nm, torch, vals, idx, L, tdt):
-    """W_hat^T [K, R] row-major for the dense reference GEMM: the hybrid-pruned weight
-    rebuilt on the GPU (dense tiles copied, 2:4 tiles decompressed tile by tile)."""
+def _hybrid_dense_operand(nm, torch, W, L, flags, tdt):
+    """W_hat^T [K, R] row-major for the dense reference GEMM: the weight as the
+    hybrid pruning leaves it.  Dense tiles are W itself; a 2:4 tile keeps what
+    the row-wise 2:4 pruning of W keeps on its columns (the same selection, as
+    the GPU tests check bit for bit), so W_hat = where(dense tile, W,
+    decompress(compress(W))).  Three launches, on the GPU."""
+    import numpy as np
     R, K, tr, tc = L.R, L.K, L.tile_rows, L.tile_cols
-    W_hat = torch.zeros((R, K), dtype=tdt, device=vals.device)
-    vb = vals.view(-1)
-    ib = idx.view(-1)
-    for b in range(L.row_meta.shape[0]):
-        r0, nr = b * tr, min(R, (b + 1) * tr) - b * tr
-        Lv, Li = int(L.row_meta[b, 0]), int(L.row_meta[b, 1])
-        for j in range(L.tile_meta.shape[1]):
-            v0, i0 = int(L.tile_meta[b, j, 0]), int(L.tile_meta[b, j, 1])
-            rows = torch.arange(nr, device=vals.device)
-            if i0 < 0:
-                src = vb[v0 + rows[:, None] * Lv + torch.arange(tc, device=vals.device)[None, :]]
-                W_hat[r0:r0 + nr, j * tc:(j + 1) * tc] = src
-            else:
-                sv = vb[v0 + rows[:, None] * Lv + torch.arange(tc // 2, device=vals.device)[None, :]].contiguous()
-                si = ib[i0 + rows[:, None] * Li + torch.arange(tc // 8, device=vals.device)[None, :]]
-                words = si.contiguous().view(torch.int32)
-                W_hat[r0:r0 + nr, j * tc:(j + 1) * tc] = nm.nm_decompress(sv, words, tc, 2, 4)
-    return W_hat.t().contiguous()
+    v24, i24 = nm.nm_compress(W, 2, 4)
+    pruned = nm.nm_decompress(v24, i24, K, 2, 4)
+    f = torch.from_numpy(np.ascontiguousarray(flags, dtype=np.bool_)).to(W.device)
+    mask = f.repeat_interleave(tr, dim=0)[:R].repeat_interleave(tc, dim=1)
+    return torch.where(mask, W, pruned).t().contiguous()
 
 
 def measured_peaks(torch):

@@ -258,7 +258,11 @@ nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, in
  *   flags[b*KB + j]  host uint8: 1 keeps tile (b, j) dense, 0 makes it 2:4.
  * Packed layout: a row stores its tiles in column order, a dense tile as its
  * tile_cols values (bits unchanged), a 2:4 tile as its tile_cols/2 survivors
- * (the nm_compress format on the tile's columns); the row's index bytes are
+ * (the nm_compress format on the tile's columns).  Within every block of 16
+ * columns a dense tile stores the values at positions 0 and 1 of the block's
+ * four groups of four, then those at positions 2 and 3 (block columns 0 1 4 5
+ * 8 9 12 13, then 2 3 6 7 10 11 14 15), the operand order of the two fixed-
+ * position 2:4 products a dense step takes.  The row's index bytes are
  * the 2:4 tiles' LSB-first 2-bit streams, tile_cols/8 bytes each, in the
  * same order.  The rows of tile-row b share one length, Lv[b] values and
  * Li[b] index bytes; rows follow each other and tile-rows follow each other,

@@ -15,13 +15,18 @@ Readings taken where the page is silent (H1-H5):
   H1  tiles are tile_rows x tile_cols blocks on a regular grid: tile-row b
       holds rows [b*tile_rows, min(R, (b+1)*tile_rows)) (the last one may be
       shorter), tile-column j holds columns [j*tile_cols, (j+1)*tile_cols);
-      K is a multiple of tile_cols and tile_cols of 8;
+      K is a multiple of tile_cols and tile_cols of 16;
   H2  flags[b, j] = 1 keeps tile (b, j) dense, 0 makes it 2:4;
   H3  a row stores its tiles in column order: a dense tile contributes its
-      tile_cols values as they are, a 2:4 tile its tile_cols/2 survivors
-      (pushed left, positions ascending), and the row's index bits are the
-      2:4 tiles' bit streams (2 bits per survivor, LSB first) concatenated in
-      the same order, tile_cols/8 bytes per 2:4 tile (whole bytes);
+      tile_cols values, a 2:4 tile its tile_cols/2 survivors (pushed left,
+      positions ascending), and the row's index bits are the 2:4 tiles' bit
+      streams (2 bits per survivor, LSB first) concatenated in the same order,
+      tile_cols/8 bytes per 2:4 tile (whole bytes).  A dense tile's values
+      keep their bits; within each block of 16 along K they are stored as the
+      values at positions 0 and 1 of the block's four groups of four, then
+      those at positions 2 and 3 (columns 0 1 4 5 8 9 12 13, then 2 3 6 7 10
+      11 14 15): the block as two 2:4 halves with fixed positions, the form a
+      2:4 instruction takes;
   H4  the rows of a tile-row share one length (their tiles have the same
       flags), Lv[b] values and Li[b] index bytes; rows are stored one after
       another with those strides, and the tile-rows one after another;
@@ -42,14 +47,33 @@ from . import nm_oracle as O
 
 def tile_grid(R: int, K: int, tile_rows: int, tile_cols: int):
     """(number of tile-rows, number of tile-columns) under H1."""
-    if tile_rows <= 0 or tile_cols <= 0 or tile_cols % 8 or K % tile_cols:
-        raise ValueError("tile_cols must divide K and be a multiple of 8; tile_rows > 0")
+    if tile_rows <= 0 or tile_cols <= 0 or tile_cols % 16 or K % tile_cols:
+        raise ValueError("tile_cols must divide K and be a multiple of 16; tile_rows > 0")
     return -(-R // tile_rows), K // tile_cols
 
 
 def rows_of(b: int, R: int, tile_rows: int) -> int:
     """Rows in tile-row b (H1)."""
     return min(R, (b + 1) * tile_rows) - b * tile_rows
+
+
+# H3: storage order of a dense block of 16 columns (entry p is the column
+# stored at position p): positions 0 and 1 of the four groups, then 2 and 3
+DENSE_BLOCK_ORDER = np.array([0, 1, 4, 5, 8, 9, 12, 13, 2, 3, 6, 7, 10, 11, 14, 15])
+
+
+def dense_store(cols: np.ndarray) -> np.ndarray:
+    """H3: a dense tile row's values in storage order (blocks of 16 reordered)."""
+    blocks = np.asarray(cols).reshape(-1, 16)
+    return blocks[:, DENSE_BLOCK_ORDER].reshape(-1)
+
+
+def dense_load(stored: np.ndarray) -> np.ndarray:
+    """Inverse of dense_store: the tile row's values in column order."""
+    blocks = np.asarray(stored).reshape(-1, 16)
+    out = np.empty_like(blocks)
+    out[:, DENSE_BLOCK_ORDER] = blocks
+    return out.reshape(-1)
 
 
 def hybrid_layout(R: int, K: int, tile_rows: int, tile_cols: int, flags):
@@ -93,7 +117,7 @@ def hybrid_pack(w_bits: np.ndarray, tile_rows: int, tile_cols: int, flags):
             v0, i0 = tile_meta[b, j]
             for q in range(nr):
                 if flags[b, j]:
-                    values[v0 + q * Lv: v0 + q * Lv + tile_cols] = block[q]
+                    values[v0 + q * Lv: v0 + q * Lv + tile_cols] = dense_store(block[q])
                 else:
                     pv, pw = O.prune_pack(block[q:q + 1], 2, 4)
                     values[v0 + q * Lv: v0 + q * Lv + tile_cols // 2] = pv[0]
@@ -119,7 +143,7 @@ def hybrid_decompress(values, idx, R: int, K: int, tile_rows: int, tile_cols: in
             c0 = j * tile_cols
             for q in range(nr):
                 if flags[b, j]:
-                    w[r0 + q, c0:c0 + tile_cols] = values[v0 + q * Lv: v0 + q * Lv + tile_cols]
+                    w[r0 + q, c0:c0 + tile_cols] = dense_load(values[v0 + q * Lv: v0 + q * Lv + tile_cols])
                 else:
                     pv = values[v0 + q * Lv: v0 + q * Lv + tile_cols // 2]
                     pb = idx[i0 + q * Li: i0 + q * Li + tile_cols // 8]

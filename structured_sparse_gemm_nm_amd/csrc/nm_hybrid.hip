@@ -4,23 +4,25 @@
 // abstract: the weight matrix is cut into tiles, each kept dense or made 2:4
 // sparse, which puts the fraction of zeros anywhere from 0 to 50%.  Tiles are
 // tile_rows x tile_cols blocks (both multiples of 64 here); a row stores its
-// tiles in column order, a dense tile as its tile_cols values, a 2:4 tile as
-// its tile_cols/2 survivors plus tile_cols/8 index bytes (2 bits per
-// survivor, LSB first), and the layout tables give each tile-row's row lengths
-// and starting offsets (nmsparse.h, nm_hybrid_layout).
+// tiles in column order, a dense tile as its tile_cols values (each block of
+// 16 as the values at positions 0 and 1 of its four groups, then those at 2
+// and 3), a 2:4 tile as its tile_cols/2 survivors plus tile_cols/8 index
+// bytes (2 bits per survivor, LSB first), and the layout tables give each
+// tile-row's row lengths and starting offsets (nmsparse.h, nm_hybrid_layout).
 //
 // Pack: one thread per 16-byte chunk (eight weights) of a row: a dense tile's
-// chunk is copied, a 2:4 tile's chunk gives its four survivors and its index
-// byte with the selection nm_compress uses (same largest-magnitude rule).
+// chunk takes its half of its block's reordered values, a 2:4 tile's chunk
+// gives its four survivors and its index byte with the selection nm_compress
+// uses (same largest-magnitude rule).
 //
 // Product: a workgroup of 8 waves owns 256 x 128 (or 128 x 64) of Y^T;
 // activations and weights go through an LDS ring of direct global->LDS loads,
 // each wave multiplying one of four 64- (32-) row weight slices by half of the
-// workgroup's tokens.  A 64-wide K step of a dense tile is two
-// v_mfma_f32_16x16x32 per fragment pair, of a 2:4 tile one
-// v_smfmac_f32_16x16x64: the activation operand the sparse instruction takes
-// (K 8q..8q+7 and 32+8q..32+8q+7 of token i in lane 16q + i) is the two dense
-// instructions' operands side by side, so both read the same LDS fragments.
+// workgroup's tokens.  A 64-wide K step of a 2:4 tile is one
+// v_smfmac_f32_16x16x64 per fragment pair, of a dense tile two: one with the
+// values at positions 0 and 1 of every group and one with those at 2 and 3,
+// each with fixed index bits.  Both kinds read the same activation fragments
+// and accumulate in place.
 // Tile-rows are multiples of 64 rows, so a wave's rows share one flag per
 // step and the choice is one uniform branch per step.  Weight reads go
 // through buffer descriptors bounded by the arrays' sizes: offsets from a
@@ -53,8 +55,16 @@ __global__ __launch_bounds__(256) void hybrid_pack_kernel(
   const int64_t Lv = row_meta[b * 4], Li = row_meta[b * 4 + 1];
   const u32x4 w = *reinterpret_cast<const u32x4*>(W + r * ldw + k0);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(values, values_bytes);
-  if (i0 < 0) {  // dense tile: the chunk as it is
-    __builtin_amdgcn_raw_buffer_store_b128(w, rv, bounded((v0 + rr * Lv + kin) * 2, values_bytes), 0, 0);
+  if (i0 < 0) {
+    // dense tile: a block of 16 values is stored as its values at positions 0
+    // and 1 of each group of four (dwords 0 and 2 of both its chunks), then
+    // those at positions 2 and 3 (dwords 1 and 3); this thread writes half
+    // kin / 8 & 1 of its block, from its own chunk and its partner's
+    const u32x4 p = *reinterpret_cast<const u32x4*>(W + r * ldw + (k0 ^ 8));
+    const bool second = (kin >> 3) & 1;
+    const u32x4 lo = second ? p : w, hi = second ? w : p;  // chunks 0 and 1 of the block
+    const u32x4 o = second ? u32x4{lo[1], lo[3], hi[1], hi[3]} : u32x4{lo[0], lo[2], hi[0], hi[2]};
+    __builtin_amdgcn_raw_buffer_store_b128(o, rv, bounded((v0 + rr * Lv + kin) * 2, values_bytes), 0, 0);
   } else {       // 2:4 tile: four survivors and their index byte
     const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
     uint32_t kept[2];
@@ -68,18 +78,12 @@ __global__ __launch_bounds__(256) void hybrid_pack_kernel(
   }
 }
 
-template <int DT>
-__device__ inline f32x4 mfma_dense(const u32x4& a, const u32x4& b, const f32x4& c) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
-                                                  c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c,
-                                                   0, 0, 0);
-  }
-}
-
 constexpr int kMaxFlagWords = 256;  // tile-columns per row up to 32 * 256
+
+// Positions of a dense step's two 2:4 products: 0 and 1 in every group of
+// four (low half, 0x4444), 2 and 3 (high half, 0xEEEE); two bits per value,
+// the value's position in its group.
+constexpr uint32_t kDensePositions = 0xEEEE4444u;
 
 // Product.  A workgroup (8 waves, two per SIMD) owns BR x BT of Y^T in four
 // row slices of WROWS = BR/4 rows; wave w multiplies slice w % 4 by token half
@@ -87,8 +91,8 @@ constexpr int kMaxFlagWords = 256;  // tile-columns per row up to 32 * 256
 // flag per K step.  Stages form an NS-deep ring; stage = the BT tokens'
 // activations (slot (token, chunk c) at token*8 + (c ^ (token & 7))) plus one
 // weight slice per row slice of WROWS x 128 bytes:
-//   dense step  the rows' 128 bytes of values, slot (row, chunk c) at
-//               row*8 + (c ^ ((row >> 1) & 7));
+//   dense step  the rows' 128 bytes of (reordered) values, slot (row,
+//               chunk c) at row*8 + (c ^ ((row >> 1) & 7));
 //   2:4 step    the rows' 64 bytes of survivors, slot (row, chunk c) at
 //               row*4 + (c ^ ((row >> 1) & 3)), and from the slice's middle
 //               each row's aligned 16-byte index block holding its 8 index
@@ -264,42 +268,57 @@ __global__ __launch_bounds__(512) void hybrid_gemm_kernel(
         const u32x4 hi = *reinterpret_cast<const u32x4*>(st + (tok * 8 + ((lq + 4) ^ sw)) * 16);
         bf[j] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      if ((sdense >> u) & 1u) {
-        u32x4 alo[FR], ahi[FR];
+      // A dense step is two 2:4 products with fixed positions: the values at
+      // positions 0 and 1 of every group of four (index 0x4444), then those at
+      // 2 and 3 (0xEEEE).  A lane's 16 dense values of row q are chunks 2 lq
+      // and 2 lq + 1 of the row; the first product takes dwords 0 and 2 of
+      // each chunk, the second dwords 1 and 3.  A 2:4 step is one product with
+      // the stored values and positions.  Both kinds accumulate in place, so
+      // the accumulators stay in the same registers whichever kind a step is.
+      // A dense step is two 2:4 products with fixed positions: a block of 16
+      // values is stored as those at positions 0 and 1 of its groups of four
+      // (for this lane, chunk 2 lq of the row), then 2 and 3 (chunk 2 lq + 1),
+      // so each chunk is one product's A operand as it stands.  The first
+      // product (a 2:4 step's only one) is shared by both kinds of step and
+      // the dense step's second one follows under a uniform branch: every
+      // product accumulates in place and no operand outlives its branch, so
+      // the accumulators stay in the same registers whatever the step.
+      const bool dense_step = (sdense >> u) & 1u;
+      u32x4 x[FR];
+      uint32_t ix[FR];
+      if (dense_step) {
 #pragma unroll
         for (int i = 0; i < FR; ++i) {
           const int q = i * 16 + li;
-          const int f = (q >> 1) & 7;
-          alo[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + (lq ^ f)) * 16);
-          ahi[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + ((lq + 4) ^ f)) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < FT; ++j) {
-          const u32x4 blo = {bf[j][0], bf[j][1], bf[j][2], bf[j][3]};
-          const u32x4 bhi = {bf[j][4], bf[j][5], bf[j][6], bf[j][7]};
-#pragma unroll
-          for (int i = 0; i < FR; ++i) {
-            acc[i][j] = mfma_dense<DT>(alo[i], blo, acc[i][j]);
-            acc[i][j] = mfma_dense<DT>(ahi[i], bhi, acc[i][j]);
-          }
+          x[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + ((2 * lq) ^ ((q >> 1) & 7))) * 16);
+          ix[i] = kDensePositions;
         }
       } else {
-        u32x4 a[FR];
-        uint32_t ix[FR];
         const uint32_t sh = (shalf >> u) & 1u;
 #pragma unroll
         for (int i = 0; i < FR; ++i) {
           const int q = i * 16 + li;
-          a[i] = *reinterpret_cast<const u32x4*>(sl + (q * 4 + (lq ^ ((q >> 1) & 3))) * 16);
+          x[i] = *reinterpret_cast<const u32x4*>(sl + (q * 4 + (lq ^ ((q >> 1) & 3))) * 16);
           // this lane's two index bytes: the row's start and the step's
           // position put them at byte 8*((row bit + step bit) & 1) + 2*lq
           const uint32_t pos = ((((ihalf >> i) & 1u) ^ sh) << 3) + uint32_t(lq) * 2u;
           ix[i] = *reinterpret_cast<const uint16_t*>(sl + SB / 2 + q * 16 + pos);
         }
+      }
+#pragma unroll
+      for (int j = 0; j < FT; ++j)
+#pragma unroll
+        for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT, 0>(x[i], bf[j], acc[i][j], ix[i]);
+      if (dense_step) {
+#pragma unroll
+        for (int i = 0; i < FR; ++i) {
+          const int q = i * 16 + li;
+          x[i] = *reinterpret_cast<const u32x4*>(sl + (q * 8 + ((2 * lq + 1) ^ ((q >> 1) & 7))) * 16);
+        }
 #pragma unroll
         for (int j = 0; j < FT; ++j)
 #pragma unroll
-          for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT>(a[i], bf[j], acc[i][j], ix[i]);
+          for (int i = 0; i < FR; ++i) acc[i][j] = smfmac<DT, 1>(x[i], bf[j], acc[i][j], kDensePositions);
       }
     }
     u = u + 1 == NS ? 0 : u + 1;

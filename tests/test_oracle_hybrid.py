@@ -1,9 +1,11 @@
 """Pins of the hybrid dense / 2:4 tile oracle (oracle/nm_hybrid.py), on the CPU.
 
 Each check ties the oracle to something other than itself:
-  * a layout worked out by hand for a 2 x 16 matrix;
-  * all tiles dense: the packed values are the matrix itself and the product
-    is the exact integer matrix product;
+  * a layout worked out by hand for a 2 x 32 matrix (tables, the stored
+    order of a dense block, survivors and index bytes, and back);
+  * all tiles dense: the packed values hold the matrix's values block by
+    block, decompress to the matrix itself, and the product is the exact
+    integer matrix product;
   * all tiles 2:4: the packing and the product are the row-wise 2:4 ones of
     nm_oracle (pinned by its own tests);
   * a random mix, ragged tile-rows included: the weight matrix it stands for
@@ -33,36 +35,51 @@ def int_bits(shape, lo, hi, seed, dt="f16", nonzero=False):
 
 
 def test_layout_worked_example():
-    # row 0: dense tile (8 values) then a 2:4 tile (4 values, 1 index byte);
-    # row 1: a 2:4 tile then a dense one
-    tm, rm, nv, ni = H.hybrid_layout(2, 16, 1, 8, np.array([[1, 0], [0, 1]]))
-    assert tm.tolist() == [[[0, -1], [8, 0]], [[12, 1], [16, -1]]]
-    assert rm.tolist() == [[12, 1, 0, 0], [12, 1, 12, 1]]
-    assert (nv, ni) == (24, 16)   # 2 index bytes, zero-padded to one 16-byte block
-    w = np.arange(1, 33, dtype=np.float32).reshape(2, 16)
-    w[0, 8:16] = [5, -7, 1, 2, 0, 3, -3, 1]       # 2:4 tile of row 0
-    w[1, 0:8] = [1, 1, 1, 1, -4, 0, 2, 9]         # 2:4 tile of row 1
+    # 2 x 32 weights, 16-wide tiles, one row per tile-row.  Row 0: a dense tile
+    # (16 values) then a 2:4 tile (8 survivors, 2 index bytes); row 1: a 2:4
+    # tile then a dense one.
+    flags = np.array([[1, 0], [0, 1]])
+    tm, rm, nv, ni = H.hybrid_layout(2, 32, 1, 16, flags)
+    assert tm.tolist() == [[[0, -1], [16, 0]], [[24, 2], [32, -1]]]
+    assert rm.tolist() == [[24, 2, 0, 0], [24, 2, 24, 2]]
+    assert (nv, ni) == (48, 16)   # 4 index bytes, zero-padded to one 16-byte block
+    w = np.arange(1, 65, dtype=np.float32).reshape(2, 32)
+    w[0, 16:32] = [5, -7, 1, 2, 0, 3, -3, 1, 4, 4, -9, 2, -1, 0, 0, 6]   # 2:4 tile of row 0
+    w[1, 0:16] = [1, 1, 1, 1, -4, 0, 2, 9, 7, -7, 0, 0, 0, 0, 0, -2]     # 2:4 tile of row 1
     bits = nm_inputs.to_half_bits(w, "f16")
-    vals, idx = H.hybrid_pack(bits, 1, 8, np.array([[1, 0], [0, 1]]))
+    vals, idx = H.hybrid_pack(bits, 1, 16, flags)
     f = vals.view(np.float16).astype(np.float32)
-    assert f[:8].tolist() == list(range(1, 9))
-    # groups (5,-7,1,2) -> positions 0,1; (0,3,-3,1) -> positions 1,2
-    assert f[8:12].tolist() == [5, -7, 3, -3]
-    assert idx[0] == (0 | 1 << 2 | 1 << 4 | 2 << 6)
-    # groups (1,1,1,1) -> 0,1 (ties go low); (-4,0,2,9) -> 0,3
-    assert f[12:16].tolist() == [1, 1, -4, 9]
-    assert idx[1] == (0 | 1 << 2 | 0 << 4 | 3 << 6)
-    assert not idx[2:].any()
-    assert f[16:24].tolist() == list(range(25, 33))
+    # dense block of 16: positions 0, 1 of each group of four, then 2, 3
+    assert f[0:16].tolist() == [1, 2, 5, 6, 9, 10, 13, 14, 3, 4, 7, 8, 11, 12, 15, 16]
+    # groups (5,-7,1,2) -> positions 0,1; (0,3,-3,1) -> 1,2 (tie kept whole);
+    # (4,4,-9,2) -> 0,2 (tie to the lower position); (-1,0,0,6) -> 0,3
+    assert f[16:24].tolist() == [5, -7, 3, -3, 4, -9, -1, 6]
+    assert idx[0] == (0 | 1 << 2 | 1 << 4 | 2 << 6) == 0x94
+    assert idx[1] == (0 | 2 << 2 | 0 << 4 | 3 << 6) == 0xC8
+    # (1,1,1,1) -> 0,1; (-4,0,2,9) -> 0,3; (7,-7,0,0) -> 0,1; (0,0,0,-2) -> 0,3
+    assert f[24:32].tolist() == [1, 1, -4, 9, 7, -7, 0, -2]
+    assert idx[2] == idx[3] == (0 | 1 << 2 | 0 << 4 | 3 << 6) == 0xC4
+    assert not idx[4:].any()
+    assert f[32:48].tolist() == [49, 50, 53, 54, 57, 58, 61, 62, 51, 52, 55, 56, 59, 60, 63, 64]
+    # and back: the weight matrix the packed form stands for
+    dec = H.hybrid_decompress(vals, idx, 2, 32, 1, 16, flags).view(np.float16).astype(np.float32)
+    expect = w.copy()
+    expect[0, 16:32] = [5, -7, 0, 0, 0, 3, -3, 0, 4, 0, -9, 0, -1, 0, 0, 6]
+    expect[1, 0:16] = [1, 1, 0, 0, -4, 0, 0, 9, 7, -7, 0, 0, 0, 0, 0, -2]
+    assert np.array_equal(dec, expect)
 
 
-@pytest.mark.parametrize("R,K,tr,tc", [(48, 128, 16, 64), (37, 192, 16, 64), (8, 64, 3, 8)])
+@pytest.mark.parametrize("R,K,tr,tc", [(48, 128, 16, 64), (37, 192, 16, 64), (8, 64, 3, 16)])
 def test_all_dense_is_the_matrix(R, K, tr, tc):
     flags = np.ones(H.tile_grid(R, K, tr, tc), dtype=np.uint8)
     w = int_bits((R, K), -8, 8, 1)
     act = int_bits((24, K), -8, 8, 2)
     vals, idx = H.hybrid_pack(w, tr, tc, flags)
-    assert np.array_equal(vals, w.ravel()) and idx.size == 0
+    assert vals.size == R * K and idx.size == 0
+    # every block of 16 holds the same values as the matrix's (storage order
+    # aside), and the packed form stands for the matrix itself
+    assert np.array_equal(np.sort(vals.reshape(-1, 16), axis=1), np.sort(w.reshape(-1, 16), axis=1))
+    assert np.array_equal(H.hybrid_decompress(vals, idx, R, K, tr, tc, flags), w)
     y = H.hybrid_spmm_ref(vals, idx, R, K, tr, tc, flags, act, "f16")
     wi = w.view(np.float16).astype(np.int64)
     ai = act.view(np.float16).astype(np.int64)
