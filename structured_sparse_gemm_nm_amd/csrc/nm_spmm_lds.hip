@@ -53,6 +53,9 @@ constexpr int kPerStep = 8;                // direct loads per wave per step (4 
 // (blockIdx.x, + grid, ...) -> (row tile, token tile).  Within a full round of
 // `grid` tiles the XCD-aware remap gives each XCD a contiguous run; tiles are
 // then ordered in groups of group_r row tiles sharing activation columns.
+// DPP control: each lane reads the lane 8 places further round its row of 16.
+constexpr int kRowRotate8 = 0x128;
+
 struct TileMap {
   int tilesR, tilesT, group_r, ntiles, grid;
   __device__ void rt(int i, int& R0, int& T0) const {
@@ -387,52 +390,96 @@ __global__ __launch_bounds__(256, 1) void spmm_lds_kernel(
     // ---- epilogue
     stores_behind = R0 + kBR <= R && T0 + kBT <= T;
     if constexpr (OUT == NM_F32) {
+      // fp32 Y is written in whole 128-byte lines with non-temporal stores.
+      // Fragments i and i+1 hold rows 0..31 of a token as 8 runs of 16 bytes
+      // (quarter q of fragment i: rows 4q..4q+3; of fragment i+1: 16+4q..).
+      // The upper 8 lanes of each 16-lane row swap their fragment-i values for
+      // the lower 8 lanes' fragment-(i+1) values (a rotate by 8 within the
+      // row), so one store writes tokens 0..7 of the fragment pair and the
+      // next tokens 8..15, each token's 32 rows by 8 lanes: whole lines.
+      // Written past the caches, Y no longer evicts the packed weights and
+      // activations the later tiles re-read from L2 (on a 3072 x 768 layer
+      // over 12608 tokens, HBM reads 126 -> ~70 MB), and whole lines leave no
+      // partial-line writes for the memory to merge.
       const bool vec_ok = (ldy & 3) == 0;
+      const bool upper = li >= 8;
 #pragma unroll
-      for (int i = 0; i < FR; ++i) {
-        const int r = R0 + wr * 128 + i * 16 + lq * 4;
+      for (int i = 0; i < FR; i += 2) {
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-          const int t = T0 + wt * (kBT / 2) + j * 16 + li;
-          if (t >= T || r >= R) continue;
-          const f32x4 v = acc[i][j];
-          float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
-          if (vec_ok && r + 3 < R) {
-            *reinterpret_cast<f32x4*>(y) = v;
-          } else {
-            for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
+          f32x4 va, vb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[i][j][e], y = acc[i + 1][j][e];
+            const float got = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                0, __builtin_bit_cast(int, upper ? x : y), kRowRotate8, 0xF, 0xF, false));
+            va[e] = upper ? got : x;
+            vb[e] = upper ? y : got;
+          }
+          const int r = R0 + wr * 128 + i * 16 + (upper ? 16 : 0) + lq * 4;
+          const int tb = T0 + wt * (kBT / 2) + j * 16 + (li & 7);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = tb + 8 * h;
+            const f32x4 v = h ? vb : va;
+            if (t >= T || r >= R) continue;
+            float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
+            if (vec_ok && r + 3 < R) {
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(y));
+            } else {
+              for (int e = 0; e < 4 && r + e < R; ++e) y[e] = v[e];
+            }
           }
         }
       }
     } else {
-      // Half outputs: fragments i and i+1 (32 rows) are exchanged across lane
-      // quarters so that quarter q holds rows 8q .. 8q+7 of the pair, and a
-      // lane stores 16 contiguous bytes: a token row gets 64-byte runs, not
-      // the 32-byte runs of 4 rows per lane.
+      // Half outputs, also whole 128-byte lines (64 rows) with non-temporal
+      // stores.  First fragments i and i+1 (32 rows) are exchanged across lane
+      // quarters so that quarter q holds rows 8q .. 8q+7 of the pair (16
+      // contiguous bytes); then, as for fp32, the upper 8 lanes of each row of
+      // 16 swap their first pair (rows 0..31) for the lower 8 lanes' second
+      // pair (rows 32..63), so each store writes 8 tokens x 64 rows.
       const bool vec_ok = (ldy & 7) == 0;
+      const bool upper = li >= 8;
+      auto pair_rows = [&](int i, int j) {
+        const uint32_t x0 = pack_half2<DT>(acc[i][j][0], acc[i][j][1]);
+        const uint32_t x1 = pack_half2<DT>(acc[i][j][2], acc[i][j][3]);
+        const uint32_t y0 = pack_half2<DT>(acc[i + 1][j][0], acc[i + 1][j][1]);
+        const uint32_t y1 = pack_half2<DT>(acc[i + 1][j][2], acc[i + 1][j][3]);
+        // lanes 32..63 of x <-> lanes 0..31 of y, then odd 16-lane rows of
+        // x <-> even rows of y
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+        const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+        return u32x4{t0[0], t1[0], t0[1], t1[1]};  // rows 8 lq .. 8 lq + 7 of the pair
+      };
 #pragma unroll
-      for (int i = 0; i < FR; i += 2) {
-        const int r = R0 + wr * 128 + i * 16 + lq * 8;
+      for (int i = 0; i < FR; i += 4) {
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-          const uint32_t x0 = pack_half2<DT>(acc[i][j][0], acc[i][j][1]);
-          const uint32_t x1 = pack_half2<DT>(acc[i][j][2], acc[i][j][3]);
-          const uint32_t y0 = pack_half2<DT>(acc[i + 1][j][0], acc[i + 1][j][1]);
-          const uint32_t y1 = pack_half2<DT>(acc[i + 1][j][2], acc[i + 1][j][3]);
-          // lanes 32..63 of x <-> lanes 0..31 of y, then odd 16-lane rows of
-          // x <-> even rows of y
-          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-          const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
-          const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
-          const int t = T0 + wt * (kBT / 2) + j * 16 + li;
-          if (t >= T || r >= R) continue;
-          const u32x4 v = {t0[0], t1[0], t0[1], t1[1]};   // rows r .. r+7
-          uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
-          if (vec_ok && r + 7 < R) {
-            *reinterpret_cast<u32x4*>(y) = v;
-          } else {
-            for (int e = 0; e < 8 && r + e < R; ++e) y[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+          const u32x4 p0 = pair_rows(i, j), p1 = pair_rows(i + 2, j);
+          u32x4 va, vb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t got = uint32_t(__builtin_amdgcn_update_dpp(
+                0, int(upper ? p0[e] : p1[e]), kRowRotate8, 0xF, 0xF, false));
+            va[e] = upper ? got : p0[e];
+            vb[e] = upper ? p1[e] : got;
+          }
+          const int r = R0 + wr * 128 + i * 16 + (upper ? 32 : 0) + lq * 8;
+          const int tb = T0 + wt * (kBT / 2) + j * 16 + (li & 7);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = tb + 8 * h;
+            const u32x4 v = h ? vb : va;
+            if (t >= T || r >= R) continue;
+            uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
+            if (vec_ok && r + 7 < R) {
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y));
+            } else {
+              for (int e = 0; e < 8 && r + e < R; ++e) y[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
