@@ -245,6 +245,48 @@ nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, in
                           int variant, void* stream);
 
 /*
+ * Training-side products of an N:M layer.  Source: COE-592 lecture 04-2,
+ * "M:N sparsity on NVIDIA tensor cores", section "The recipe", step 3 (the
+ * pruned network is retrained with the zeros held fixed, so the pattern
+ * survives), and the RNM-TD3 abstract of thelatestinai.com's "Structured
+ * Sparsity" cards (row-wise N:M sparsity kept throughout training).  With the
+ * forward product Yt[t, r] = sum_k W_nm[r, k] act[t, k] (nm_spmm) and
+ * G = dL/dYt, the gradient of the output in Yt's layout:
+ *
+ * nm_spmm_dx: dX[t, k] = sum_r G[t, r] W_nm[r, k]  (dX = G W_nm, the gradient
+ *   of act).
+ *   values, idx  packed W (nm_compress), NM_F16 or NM_BF16, patterns as nm_spmm.
+ *   G            device [T, R] row-major, ldg >= R, ldg % 8 == 0, dtype of W.
+ *   dX           device [T, K] row-major, lddx >= K; out_dtype NM_F32 or the
+ *                input dtype (RNE rounded).  Overwritten; with R == 0 it is
+ *                filled with zeros.
+ *   The reduction runs over R, across W's rows, so the N:M groups give the
+ *   matrix cores nothing to skip: the product runs at the dense rate and reads
+ *   the packed weights.  Sums in fp32.
+ *
+ * nm_spmm_dw: dW[r, s] = sum_t G[t, r] act[t, k(r, s)], the gradient of every
+ *   stored survivor s of row r (k(r, s) the column it came from), in the
+ *   packed values' layout [R, S] (S = K*n/m), contiguous.  Dropped weights are
+ *   held at zero and get no gradient; a stored slot that holds a zero is a
+ *   weight like any other and gets its gradient.
+ *   idx          the packed W's index words (the values are not read).
+ *   G            [T, R], ldg as above;  act  [T, K], ldx >= K, ldx % 8 == 0.
+ *   dW           device [R, S], out_dtype NM_F32 or the input dtype.
+ *                Overwritten; with T == 0 it is filled with zeros.
+ *
+ * Both: R % 8 == 0 and K % 32 == 0 besides nm_spmm's format rules
+ * (NM_ERR_SHAPE); every pointer 16-byte aligned; the output must not overlap
+ * an input (NM_ERR_ALIAS); stream-ordered, nothing allocated or synchronised.
+ * NM_ERR_UNSUPPORTED for 8-bit weights; NM_ERR_SHAPE for a packed W or index
+ * array of 4 GiB or more, a 128-token block of G of 4 GiB or more (dX), or G
+ * or act of 4 GiB or more (dW).
+ */
+nm_status nm_spmm_dx(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m, int dtype,
+                     const void* G, int64_t T, int64_t ldg, void* dX, int64_t lddx, int out_dtype, void* stream);
+nm_status nm_spmm_dw(const uint32_t* idx, int64_t R, int64_t K, int n, int m, int dtype, const void* G, int64_t T,
+                     int64_t ldg, const void* act, int64_t ldx, void* dW, int out_dtype, void* stream);
+
+/*
  * Hybrid dense / 2:4 weight tiles.  Source: thelatestinai.com "Structured
  * Sparsity" topic cards, the PATCH abstract: the weight matrix is cut into
  * tiles and each tile is either kept dense or made 2:4 sparse (the choice is

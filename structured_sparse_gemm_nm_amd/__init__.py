@@ -16,7 +16,8 @@ import os
 
 __all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NM_FP8", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
-           "nm_spmm_perm_workspace_size", "nm_spmm_perm_static", "nm_check_perm", "PATTERNS"]
+           "nm_spmm_perm_workspace_size", "nm_spmm_perm_static", "nm_check_perm", "nm_spmm_dx", "nm_spmm_dw",
+           "PATTERNS"]
 
 NM_OK = 0
 NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.nm_check_perm.argtypes = [vp, i64, vp]
     L.nm_spmm_variant.restype = i32
     L.nm_spmm_variant.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, vp, i64, i32, vp, sz, i32, vp]
+    L.nm_spmm_dx.restype = i32
+    L.nm_spmm_dx.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, i32, vp]
+    L.nm_spmm_dw.restype = i32
+    L.nm_spmm_dw.argtypes = [vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, vp, i32, vp]
     L.nm_hybrid_layout.restype = i32
     L.nm_hybrid_layout.argtypes = [i64, i64, i64, i64, vp, vp, vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.nm_hybrid_compress.restype = i32
@@ -228,6 +233,66 @@ def nm_spmm_perm_static(values, idx, act, perm, K: int, n: int = 2, m: int = 4, 
     """nm_spmm_perm with the library's static per-GPU workspace (no allocation in
     the library; calls that overlap in time on one GPU race)."""
     return _spmm(values, idx, act, K, n, m, perm, out_dtype, out, 0, "static")
+
+
+def _train_out_dtype(torch, dt, out_dtype):
+    if dt not in (NM_F16, NM_BF16):
+        raise TypeError("the training products take float16 or bfloat16 weights")
+    if out_dtype is None or out_dtype == torch.float32:
+        return NM_F32
+    od = _dtype_code(torch.empty(0, dtype=out_dtype))
+    if od != dt:
+        raise TypeError("out_dtype must be float32 or the weights' dtype")
+    return od
+
+
+def nm_spmm_dx(values, idx, G, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None):
+    """dX [T, K] = G [T, R] @ W_nm: the gradient of the activations of Yt = act @ W_nm^T."""
+    torch = _torch()
+    _row_major(G, "G")
+    R = values.shape[0]
+    T = G.shape[0]
+    dt = _dtype_code(values)
+    od = _train_out_dtype(torch, dt, out_dtype)
+    _check_packed(values, idx, R, K, n, m, dt)
+    if G.dtype != values.dtype or G.shape[1] != R or G.device != values.device:
+        raise ValueError(f"G must be a [T, {R}] {values.dtype} tensor on {values.device}")
+    if out is not None:
+        _row_major(out, "out")
+        if out.dtype != _torch_dtype(od) or tuple(out.shape) != (T, K) or out.device != G.device:
+            raise ValueError(f"out must be a [{T}, {K}] {_torch_dtype(od)} tensor on {G.device}")
+    _require_cuda(values, idx, G, *(t for t in (out,) if t is not None))
+    if out is None:
+        out = torch.empty((T, K), dtype=_torch_dtype(od), device=G.device)
+    _check(lib().nm_spmm_dx(values.data_ptr(), idx.data_ptr(), R, K, n, m, dt, G.data_ptr(), T, G.stride(0),
+                            out.data_ptr(), out.stride(0), od, _stream_ptr(G.device)))
+    return out
+
+
+def nm_spmm_dw(idx, G, act, K: int, n: int = 2, m: int = 4, out_dtype=None, out=None):
+    """dW [R, S]: the gradient of each stored survivor, sum_t G[t, r] act[t, k(r, s)]."""
+    torch = _torch()
+    _row_major(G, "G")
+    _row_major(act, "act")
+    R = idx.shape[0]
+    T = G.shape[0]
+    dt = _dtype_code(act)
+    od = _train_out_dtype(torch, dt, out_dtype)
+    S = K * n // m
+    if G.dtype != act.dtype or G.shape[1] != R or act.shape != (T, K) or G.device != act.device:
+        raise ValueError(f"G must be [T, {R}] and act [T, {K}], one dtype, on one device")
+    _, _, words = nm_packed_sizes(R, K, n, m, dt)
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (R, words) or not idx.is_contiguous():
+        raise ValueError(f"idx must be a contiguous int32 [{R}, {words}] tensor")
+    if out is not None:
+        if out.dtype != _torch_dtype(od) or tuple(out.shape) != (R, S) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous [{R}, {S}] {_torch_dtype(od)} tensor")
+    _require_cuda(idx, G, act, *(t for t in (out,) if t is not None))
+    if out is None:
+        out = torch.empty((R, S), dtype=_torch_dtype(od), device=G.device)
+    _check(lib().nm_spmm_dw(idx.data_ptr(), R, K, n, m, dt, G.data_ptr(), T, G.stride(0), act.data_ptr(),
+                            act.stride(0), out.data_ptr(), od, _stream_ptr(G.device)))
+    return out
 
 
 def _spmm(values, idx, act, K, n, m, perm, out_dtype, out, variant, workspace):

@@ -410,6 +410,110 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream) {
 }
 
 
+// Shared checks of the training-side products: format, 16-bit types, output
+// dtype, T and the G operand [T, R] (ldg).
+static nm_status check_train(int64_t R, int64_t K, int n, int m, int dtype, int64_t T, int64_t ldg,
+                             int out_dtype) {
+  nm_status st = check_format(R, K, n, m, dtype);
+  if (st != NM_OK) return st;
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "training products take fp16 or bf16 weights");
+  // whole 16-byte pieces of G's rows and whole 32-column segments of W's rows
+  if (R % 8 || K % 32)
+    return fail(NM_ERR_SHAPE, "training products need R %% 8 == 0 and K %% 32 == 0 (R = %lld, K = %lld)",
+                (long long)R, (long long)K);
+  if (out_dtype != NM_F32 && out_dtype != dtype)
+    return fail(NM_ERR_UNSUPPORTED, "out_dtype %d must be NM_F32 or the input dtype", out_dtype);
+  if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (ldg < R) return fail(NM_ERR_STRIDE, "ldg = %lld < R = %lld", (long long)ldg, (long long)R);
+  if (ldg > kMaxElems) return fail(NM_ERR_SHAPE, "ldg above 2^40 elements");
+  return NM_OK;
+}
+
+nm_status nm_spmm_dx(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m, int dtype,
+                     const void* G, int64_t T, int64_t ldg, void* dX, int64_t lddx, int out_dtype, void* stream) {
+  nm_status st = check_train(R, K, n, m, dtype, T, ldg, out_dtype);
+  if (st != NM_OK) return st;
+  if (lddx < K) return fail(NM_ERR_STRIDE, "lddx = %lld < K = %lld", (long long)lddx, (long long)K);
+  if (lddx > kMaxElems) return fail(NM_ERR_SHAPE, "lddx above 2^40 elements");
+  if (T == 0) return ok();  // empty dX: nothing to enqueue (R == 0 writes zeros)
+  if (!dX || (R > 0 && (!values || !idx || !G)))
+    return fail(NM_ERR_NULL, "values, idx, G and dX must be non-NULL");
+  if (ldg % 8) return fail(NM_ERR_ALIGN, "ldg = %lld is not a multiple of 8", (long long)ldg);
+  if (!aligned16(values) || !aligned16(idx) || !aligned16(G) || !aligned16(dX))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (T * ldg > kMaxElems || T * lddx > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
+  Sizes z = sizes_of(R, K, n, m, dtype);
+  // the kernel's per-lane byte offsets are 32-bit: the packed arrays and a
+  // 128-token block of G
+  if (z.values_bytes >= (size_t(1) << 32) || z.idx_bytes >= (size_t(1) << 32) || 128 * ldg * 2 >= (int64_t(1) << 32))
+    return fail(NM_ERR_SHAPE, "packed W of 4 GiB or more, or ldg of 2^24 or more");
+  const size_t xbytes = extent(T, K, lddx, elt_bytes(out_dtype));
+  const size_t gbytes = extent(T, R, ldg, 2);
+  if (overlaps(dX, xbytes, values, z.values_bytes) || overlaps(dX, xbytes, idx, z.idx_bytes) ||
+      overlaps(dX, xbytes, G, gbytes))
+    return fail(NM_ERR_ALIAS, "dX overlaps an input");
+  nm::TrainArgs a{};
+  a.values = static_cast<const uint16_t*>(values);
+  a.values_bytes = z.values_bytes;
+  a.idx = idx;
+  a.idx_bytes = z.idx_bytes;
+  a.R = R;
+  a.K = K;
+  a.n = n;
+  a.m = m;
+  a.dtype = dtype;
+  a.idx_row_words = z.words;
+  a.G = static_cast<const uint16_t*>(G);
+  a.T = T;
+  a.ldg = ldg;
+  a.out = dX;
+  a.ldo = lddx;
+  a.out_dtype = out_dtype;
+  return hip_status(nm::launch_spmm_dx(a, static_cast<hipStream_t>(stream)), "nm_spmm_dx launch");
+}
+
+nm_status nm_spmm_dw(const uint32_t* idx, int64_t R, int64_t K, int n, int m, int dtype, const void* G, int64_t T,
+                     int64_t ldg, const void* act, int64_t ldx, void* dW, int out_dtype, void* stream) {
+  nm_status st = check_train(R, K, n, m, dtype, T, ldg, out_dtype);
+  if (st != NM_OK) return st;
+  if (ldx < K) return fail(NM_ERR_STRIDE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx > kMaxElems) return fail(NM_ERR_SHAPE, "ldx above 2^40 elements");
+  if (R == 0) return ok();  // no weights, no gradient (T == 0 writes zeros)
+  if (!idx || !dW || (T > 0 && (!G || !act)))
+    return fail(NM_ERR_NULL, "idx, G, act and dW must be non-NULL");
+  if (ldg % 8 || ldx % 8) return fail(NM_ERR_ALIGN, "ldg and ldx must be multiples of 8");
+  if (!aligned16(idx) || !aligned16(G) || !aligned16(act) || !aligned16(dW))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (T * ldg > kMaxElems || T * ldx > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
+  // per-lane byte offsets are 32-bit: every token row of G and act
+  if (T * ldg * 2 >= (int64_t(1) << 32) || T * ldx * 2 >= (int64_t(1) << 32))
+    return fail(NM_ERR_SHAPE, "G or act of 4 GiB or more");
+  Sizes z = sizes_of(R, K, n, m, dtype);
+  if (z.idx_bytes >= (size_t(1) << 32)) return fail(NM_ERR_SHAPE, "index words of 4 GiB or more");
+  const size_t wbytes = size_t(R) * size_t(z.S) * elt_bytes(out_dtype);
+  const size_t gbytes = extent(T, R, ldg, 2), abytes = extent(T, K, ldx, 2);
+  if (overlaps(dW, wbytes, idx, z.idx_bytes) || overlaps(dW, wbytes, G, gbytes) || overlaps(dW, wbytes, act, abytes))
+    return fail(NM_ERR_ALIAS, "dW overlaps an input");
+  nm::TrainArgs a{};
+  a.idx = idx;
+  a.idx_bytes = z.idx_bytes;
+  a.R = R;
+  a.K = K;
+  a.n = n;
+  a.m = m;
+  a.dtype = dtype;
+  a.idx_row_words = z.words;
+  a.G = static_cast<const uint16_t*>(G);
+  a.T = T;
+  a.ldg = ldg;
+  a.act = static_cast<const uint16_t*>(act);
+  a.ldx = ldx;
+  a.out = dW;
+  a.out_dtype = out_dtype;
+  return hip_status(nm::launch_spmm_dw(a, static_cast<hipStream_t>(stream)), "nm_spmm_dw launch");
+}
+
 nm_status nm_hybrid_layout(int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, const uint8_t* flags,
                            int64_t* tile_meta, int64_t* row_meta, int64_t* values_count, int64_t* idx_bytes) {
   nm_status st = check_hybrid_grid(R, K, tile_rows, tile_cols);

@@ -49,6 +49,27 @@ struct SpmmArgs {
 };
 
 hipError_t launch_spmm(const SpmmArgs& a, hipStream_t s);
+// Training-side products (nm_train.hip): dX = G W_nm and the packed dW.
+struct TrainArgs {
+  const uint16_t* values;  // packed W (dX only)
+  size_t values_bytes;
+  const uint32_t* idx;     // index words of the packed W
+  size_t idx_bytes;
+  int64_t R, K;
+  int n, m;
+  int dtype;               // NM_F16 / NM_BF16
+  int64_t idx_row_words;
+  const uint16_t* G;       // [T, R], ldg: gradient of the forward output
+  int64_t T, ldg;
+  const uint16_t* act;     // [T, K], ldx (dW only)
+  int64_t ldx;
+  void* out;               // dX [T, K] (ldo) or dW [R, S] (contiguous)
+  int64_t ldo;
+  int out_dtype;           // NM_F32 or dtype
+};
+hipError_t launch_spmm_dx(const TrainArgs& a, hipStream_t s);
+hipError_t launch_spmm_dw(const TrainArgs& a, hipStream_t s);
+
 // 8-bit 2:4 GEMM (nm_int8.hip): Y int32 for NM_I8, fp32 for NM_FP8.
 hipError_t launch_spmm_i8(const SpmmArgs& a, hipStream_t s);
 

@@ -1,0 +1,553 @@
+// Training-side products of an N:M layer on gfx950.
+//
+// Source: COE-592 lecture 04-2, "M:N sparsity on NVIDIA tensor cores",
+// section "The recipe", step 3 (retrain with the zeros held fixed, so the
+// pattern survives), and the RNM-TD3 abstract of thelatestinai.com's
+// "Structured Sparsity" cards (row-wise N:M kept throughout training).  With
+// G = dL/dYt [T, R] (the forward output's layout):
+//   dX[T, K]  = G W_nm                          (nm_spmm_dx, this file);
+//   dW[R, S]  = sum_t G[t, r] act[t, k(r, s)]   (nm_spmm_dw), the gradient of
+//               each stored survivor, in the packed layout.
+// In dX the reduction runs over R, across the rows of W, so the N:M groups
+// (which run along K) give the instruction nothing to skip: the product is
+// dense on the MFMA and what the packed form saves is the weight bytes read.
+//
+// LDS transpose reads.  ds_read_b64_tr_b16 reads 4 halves per lane like a
+// plain 64-bit read and then exchanges them within each group of 16 lanes:
+// lane 16g + 4a + b receives element b of what lane 16g + 4j + a read, for
+// j = 0..3 (measured on the MI355X with a probe of the instruction).  So
+// when lane 16g + 4j + a points at row 8g + j (plus 4 for a second read),
+// columns 4a..4a+3, of a tile stored reduction-major (rows = reduction),
+// lane 16g + 4a + b gets rows 8g..8g+7 of column 4a + b: the 8 consecutive
+// reduction elements of one column that a v_mfma_f32_16x16x32 operand lane
+// (column 4a + b, quarter g) holds.  Tiles that arrive reduction-major (the
+// decompressed W for dX, G and act for dW) feed the MFMA through two such
+// reads per operand, without a transposing copy.
+#include "nm_device.h"
+#include "nm_internal.h"
+
+namespace nm {
+namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline u32x2 lds_read_tr(const unsigned char* p) {
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// D = C + A x B on v_mfma_f32_16x16x32: lane (i, q) holds A[i][8q..8q+7] and
+// B[8q..8q+7][i]; D rows 4q..4q+3 of column i.
+template <int DT>
+__device__ inline f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (DT == NM_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                  c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c,
+                                                   0, 0, 0);
+  }
+}
+
+constexpr int pat_n(int P) { return P == 0 ? 2 : 1; }
+constexpr int pat_m(int P) { return P == 2 ? 8 : 4; }
+
+// ---------------------------------------------------------------------------
+// dX = G W_nm, computed as dX^T tiles: D[k][t] = sum_r W[r][k] G[t][r].
+//
+// A workgroup (4 waves, 2 x 2) owns 128 k x 128 t; a wave 64 x 64 (4 x 4
+// fragments).  R is walked in chunks of 64 rows:
+//   * G's tile (128 tokens x 64 r, 16 KB) arrives by direct global->LDS loads
+//     through a kNS-deep ring, slot (token, 16-byte chunk c) at token*8 +
+//     (c ^ (token & 7)); a B operand lane (token i, quarter q) reads chunk
+//     4h + q of sub-step h (r 32h + 8q ..) with one 16-byte read;
+//   * W's chunk (64 rows x 128 columns) is decompressed by the workgroup's
+//     256 threads, each one row and 32 columns, from packed values and index
+//     bits it loaded into registers two chunks earlier, into a dense
+//     double-buffered tile [64 r][128 k] (rows padded to 288 bytes); the A
+//     operands (k rows, r reduction) come out of it by transpose reads.
+// One barrier per chunk publishes G's chunk and the W tile decompressed in
+// the previous chunk, and retires the buffers the chunk then refills.
+// ---------------------------------------------------------------------------
+constexpr int kDxBK = 128, kDxBT = 128, kDxRC = 64, kDxNS = 4;
+constexpr int kDxGStage = kDxBT * kDxRC * 2;     // 16 KB
+constexpr int kDxWRow = kDxBK * 2 + 32;          // 288 bytes: padded row of the W tile
+constexpr int kDxWTile = kDxRC * kDxWRow;        // 18 KB
+constexpr int kDxLds = kDxNS * kDxGStage + 2 * kDxWTile;
+
+// One thread's packed share of a chunk: values of 32 columns of one row
+// (2:4 16 values, 1:4 8, 1:8 4) and the two index words holding its bits.
+struct DxPack {
+  u32x4 v0, v1;
+  uint32_t i0, i1;
+};
+
+// Offset that no descriptor here covers: a load from it returns zeros.
+constexpr uint32_t kDeadOff = 0xFFFFFFF0u;
+
+template <int P>
+__device__ inline void dx_load(DxPack& d, __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t ri, uint32_t voff,
+                               uint32_t ioff0, uint32_t ioff1) {
+  if constexpr (P == 0) {
+    d.v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+    // a dead share stays dead: kDeadOff + 16 would wrap to offset 0, and row
+    // 0's values with zero index bits expand (two halves OR'ed into one
+    // position) into arbitrary bits, Inf and NaN among them
+    const uint32_t voff1 = voff == kDeadOff ? kDeadOff : voff + 16u;
+    d.v1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff1, 0, 0));
+  } else if constexpr (P == 1) {
+    d.v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+  } else {
+    const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0));
+    d.v0 = u32x4{t[0], t[1], 0u, 0u};
+  }
+  d.i0 = __builtin_amdgcn_raw_buffer_load_b32(ri, ioff0, 0, 0);
+  d.i1 = __builtin_amdgcn_raw_buffer_load_b32(ri, ioff1, 0, 0);
+}
+
+// The 32 dense halves (16 dwords) of a thread's row segment from its packed
+// share; ishift is the position of its first index bit in word i0.
+template <int P>
+__device__ inline void dx_expand(const DxPack& d, uint32_t ishift, uint32_t (&o)[16]) {
+  const uint64_t bits = (uint64_t(d.i1) << 32 | d.i0) >> ishift;
+  if constexpr (P == 0) {  // 8 groups of 4, two values each
+    const uint32_t v[8] = {d.v0[0], d.v0[1], d.v0[2], d.v0[3], d.v1[0], d.v1[1], d.v1[2], d.v1[3]};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t p0 = uint32_t(bits >> (4 * g)) & 3u, p1 = uint32_t(bits >> (4 * g + 2)) & 3u;
+      const uint64_t w = (uint64_t(v[g] & 0xFFFFu) << (16 * p0)) | (uint64_t(v[g] >> 16) << (16 * p1));
+      o[2 * g] = uint32_t(w);
+      o[2 * g + 1] = uint32_t(w >> 32);
+    }
+  } else if constexpr (P == 1) {  // 8 groups of 4, one value each
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t h = (d.v0[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
+      const uint32_t p = uint32_t(bits >> (2 * g)) & 3u;
+      const uint64_t w = uint64_t(h) << (16 * p);
+      o[2 * g] = uint32_t(w);
+      o[2 * g + 1] = uint32_t(w >> 32);
+    }
+  } else {  // 4 groups of 8, one value each
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t h = (d.v0[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
+      const uint32_t p = uint32_t(bits >> (3 * g)) & 7u;
+      const uint32_t x = h << (16 * (p & 1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * g + e] = (p >> 1) == uint32_t(e) ? x : 0u;
+    }
+  }
+}
+
+template <int P, int DT, int OUT>
+__global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict__ values, uint32_t values_bytes,
+                                                      const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
+                                                      int K, int idx_row_words, const uint16_t* __restrict__ G,
+                                                      int T, int64_t ldg, void* __restrict__ dX, int64_t lddx,
+                                                      int tilesK) {
+  constexpr int N = pat_n(P), M = pat_m(P);
+  constexpr int B = P == 2 ? 3 : 2;  // index bits per survivor
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* gbuf = smem;                          // [kNS][16 KB]
+  unsigned char* wbuf = smem + kDxNS * kDxGStage;      // [2][64][288 B]
+
+  const int tile = blockIdx.x;
+  const int K0 = (tile % tilesK) * kDxBK, T0 = (tile / tilesK) * kDxBT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave >> 1, wt = wave & 1;
+  const int li = lane & 15, lq = lane >> 4;
+  const int nchunks = (R + kDxRC - 1) / kDxRC;
+  const int64_t S = int64_t(K) * N / M;
+
+  // G: descriptor over the tile's token rows (rows past T reread row T - 1;
+  // their outputs are dropped).  R % 8 == 0, so a 16-byte piece of a row lies
+  // wholly before R or wholly past it; pieces past R read zeros, which meet
+  // the zero rows of W's tile past R.
+  const int tlast = min(T0 + kDxBT, T) - 1;
+  const __amdgpu_buffer_rsrc_t rg =
+      make_rsrc(G + int64_t(T0) * ldg, uint32_t((int64_t(tlast - T0) * ldg + R) * 2));
+  uint32_t goff[4];
+  int gcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (wave * 4 + j) * 64 + lane;
+    const int tok = slot >> 3;
+    const int c = (slot & 7) ^ (tok & 7);
+    const int t = min(T0 + tok, T - 1) - T0;
+    goff[j] = uint32_t(t) * uint32_t(ldg) * 2u + uint32_t(c) * 16u;
+    gcol[j] = c * 8;
+  }
+  auto issue_g = [&](int chunk, int slot) {
+    const int r0 = chunk * kDxRC;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // a piece past R (or of a chunk past the last) reads zeros
+      const bool live = chunk < nchunks && r0 + gcol[j] < R;
+      dma16(rg, live ? goff[j] + uint32_t(r0) * 2u : kDeadOff, 0u,
+            gbuf + slot * kDxGStage + (wave * 4 + j) * 1024);
+    }
+  };
+
+  // W: this thread decompresses row (tid >> 2) of the chunk, columns
+  // K0 + 32 (tid & 3) .. +31
+  const int wr = tid >> 2, wc = tid & 3;
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(values, values_bytes);
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(idx, idx_bytes);
+  const int kc = K0 + 32 * wc;                      // first column of the segment
+  const int64_t s0 = int64_t(kc) * N / M;           // its first survivor in the row
+  const int64_t bit0 = s0 * B;                      // its first index bit in the row
+  const uint32_t ishift = uint32_t(bit0 & 31);
+  // the word holding the first bit and the next one, clamped to the row (the
+  // row's last word then holds every bit the segment needs)
+  const int64_t w0 = bit0 >> 5, w1 = min(w0 + 1, int64_t(idx_row_words) - 1);
+  auto pack_offsets = [&](int chunk, uint32_t& voff, uint32_t& ioff0, uint32_t& ioff1) {
+    const int64_t row = int64_t(chunk) * kDxRC + wr;
+    const bool live = chunk < nchunks && row < R && kc < K;
+    voff = live ? uint32_t((row * S + s0) * 2) : kDeadOff;
+    ioff0 = live ? uint32_t((row * idx_row_words + w0) * 4) : kDeadOff;
+    ioff1 = live ? uint32_t((row * idx_row_words + w1) * 4) : kDeadOff;
+  };
+  auto decompress = [&](const DxPack& d, int buf) {
+    uint32_t o[16];
+    dx_expand<P>(d, ishift, o);
+    unsigned char* dst = wbuf + buf * kDxWTile + wr * kDxWRow + wc * 64;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(dst + 16 * q) = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A operand addresses in the W tile: lane L = 16g + 4j + a reads row
+  // 8g + j (+4) of the sub-step, columns 4a.. of fragment kf
+  const int tr_row = 8 * (lane >> 4) + ((lane >> 2) & 3), tr_col = 4 * (lane & 3);
+  auto read_a = [&](int buf, int h, int kf) {
+    const unsigned char* base =
+        wbuf + buf * kDxWTile + (32 * h + tr_row) * kDxWRow + (wk * 64 + kf * 16 + tr_col) * 2;
+    const u32x2 lo = lds_read_tr(base), hi = lds_read_tr(base + 4 * kDxWRow);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto read_b = [&](int slot, int h, int tf) {
+    const int tok = wt * 64 + tf * 16 + li;
+    const int c = 4 * h + lq;
+    return *reinterpret_cast<const u32x4*>(gbuf + slot * kDxGStage + (tok * 8 + (c ^ (tok & 7))) * 16);
+  };
+
+  // ---- prologue: G chunks 0 .. kNS-2 in flight, packed chunks 0 and 1 in
+  // registers, chunk 0 decompressed
+  for (int p = 0; p < kDxNS - 1; ++p) issue_g(p, p);
+  DxPack pk[2];
+  {
+    uint32_t vo, i0, i1;
+    pack_offsets(0, vo, i0, i1);
+    dx_load<P>(pk[0], rv, ri, vo, i0, i1);
+    pack_offsets(1, vo, i0, i1);
+    dx_load<P>(pk[1], rv, ri, vo, i0, i1);
+  }
+  decompress(pk[0], 0);
+  {
+    uint32_t vo, i0, i1;
+    pack_offsets(2, vo, i0, i1);
+    dx_load<P>(pk[0], rv, ri, vo, i0, i1);
+  }
+
+  // Step c: G chunk c (slot c % kNS) and W tile c & 1 are ready after the
+  // barrier; the step refills G slot (c - 1) % kNS with chunk c + kNS - 1,
+  // multiplies, then decompresses chunk c + 1 from register set (c + 1) & 1
+  // into W tile (c + 1) & 1 and loads chunk c + 3's packed share into that
+  // set.  The loop is unrolled by two so the register sets alternate.
+  // Every wave's G loads of chunk c have landed by the time the step starts:
+  // they were issued before the packed loads of chunk c, which the decompress
+  // of chunk c (the previous step, or the prologue) waited for, and loads
+  // complete in issue order.  The barrier then publishes them workgroup-wide.
+  auto step = [&](int c, DxPack& next) {
+    barrier_no_fence();
+    issue_g(c + kDxNS - 1, (c + kDxNS - 1) % kDxNS);
+    const int slot = c % kDxNS, buf = c & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf) a[kf] = read_a(buf, h, kf);
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) b[tf] = read_b(slot, h, tf);
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) acc[kf][tf] = mfma32<DT>(a[kf], b[tf], acc[kf][tf]);
+    }
+    if (c + 1 < nchunks) decompress(next, buf ^ 1);
+    uint32_t vo, i0, i1;
+    pack_offsets(c + 3, vo, i0, i1);
+    dx_load<P>(next, rv, ri, vo, i0, i1);
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, pk[1]);
+    if (c + 1 < nchunks) step(c + 1, pk[0]);
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: lane (t = li, quarter q) holds rows 4q..4q+3 (k) of
+  // column t of each fragment: 16 (fp32) or 8 (half) contiguous bytes of dX
+  const bool vec_ok = OUT == NM_F32 ? (lddx & 3) == 0 : (lddx & 3) == 0;
+#pragma unroll
+  for (int kf = 0; kf < 4; ++kf) {
+    const int k = K0 + wk * 64 + kf * 16 + lq * 4;
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) {
+      const int t = T0 + wt * 64 + tf * 16 + li;
+      if (t >= T || k >= K) continue;
+      const f32x4 v = acc[kf][tf];
+      if constexpr (OUT == NM_F32) {
+        float* y = static_cast<float*>(dX) + int64_t(t) * lddx + k;
+        if (vec_ok && k + 3 < K) {
+          *reinterpret_cast<f32x4*>(y) = v;
+        } else {
+          for (int e = 0; e < 4 && k + e < K; ++e) y[e] = v[e];
+        }
+      } else {
+        uint16_t* y = static_cast<uint16_t*>(dX) + int64_t(t) * lddx + k;
+        const uint32_t p0 = pack_half2<DT>(v[0], v[1]), p1 = pack_half2<DT>(v[2], v[3]);
+        if (vec_ok && k + 3 < K) {
+          *reinterpret_cast<uint2*>(y) = make_uint2(p0, p1);
+        } else {
+          const uint16_t hh[4] = {uint16_t(p0), uint16_t(p0 >> 16), uint16_t(p1), uint16_t(p1 >> 16)};
+          for (int e = 0; e < 4 && k + e < K; ++e) y[e] = hh[e];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dW[r, s] = sum_t G[t, r] act[t, k(r, s)], computed as dense dW^T tiles
+// D[k][r] = sum_t act[t][k] G[t][r] of which each lane keeps the stored
+// entries.  A workgroup (4 waves, 2 x 2) owns 128 k x 128 r; a wave 64 x 64.
+// T is walked in chunks of 64 tokens; both tiles of a chunk, act's [64 t][128
+// k] and G's [64 t][128 r] (16 KB each, token rows of 256 bytes), arrive by
+// direct global->LDS loads through a kNS-deep ring, and both operands come out
+// by transpose reads: an operand lane needs 8 consecutive tokens of one
+// column.  The 16-byte pieces of a row are XOR-swizzled, piece p of row t at
+// p ^ f(t), f(t) = 2 (t & 3) + 8 ((t >> 3) & 1), so the 8-byte transpose
+// reads of 32 lanes (rows 8g + j, g = 0, 1, j = 0..3) fall in distinct banks.
+// A result lane (column r, quarter q) holds rows 4q..4q+3 of D, four
+// consecutive columns k of W's row r: a whole group of four, or half of one
+// of eight, whose stored positions it reads from the index bits and whose
+// survivors it writes to the packed gradient.
+// ---------------------------------------------------------------------------
+constexpr int kDwBK = 128, kDwBR = 128, kDwTC = 64, kDwNS = 4;
+constexpr int kDwTile = kDwTC * 256;                    // 16 KB: 64 token rows of 256 bytes
+constexpr int kDwStage = 2 * kDwTile;                   // act tile, then G tile
+constexpr int kDwLds = kDwNS * kDwStage;                // 128 KB
+
+__device__ inline int dw_swz(int t) { return ((t & 3) << 1) | (((t >> 3) & 1) << 3); }
+
+template <int P, int DT, int OUT>
+__global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
+                                                      int K, int idx_row_words, const uint16_t* __restrict__ G,
+                                                      int T, int64_t ldg, const uint16_t* __restrict__ act,
+                                                      int64_t ldx, void* __restrict__ dW, int tilesK) {
+  constexpr int N = pat_n(P), M = pat_m(P);
+  constexpr int B = P == 2 ? 3 : 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tile = blockIdx.x;
+  const int K0 = (tile % tilesK) * kDwBK, R0 = (tile / tilesK) * kDwBR;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave >> 1, wr = wave & 1;
+  const int li = lane & 15, lq = lane >> 4;
+  const int nchunks = (T + kDwTC - 1) / kDwTC;
+  const int64_t S = int64_t(K) * N / M;
+
+  // Direct loads: instruction j (0..3) of a wave fills token rows
+  // 4 (4 wave + j) .. +3 of a tile, lane l row + l / 16, piece l % 16 (which
+  // holds global piece (l % 16) ^ f(row)).  Tokens past T read zeros, so they
+  // add nothing; columns past K or R are whatever the descriptor allows and
+  // only reach outputs that are dropped.
+  // (with T == 0 nothing is read: the descriptors cover no bytes)
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(act + K0, T > 0 ? uint32_t(((int64_t(T) - 1) * ldx + (K - K0)) * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rg =
+      make_rsrc(G + R0, T > 0 ? uint32_t(((int64_t(T) - 1) * ldg + (R - R0)) * 2) : 0u);
+  int lrow[4];
+  uint32_t aoff[4], goff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * (wave * 4 + j) + (lane >> 4);
+    const int piece = (lane & 15) ^ dw_swz(row);
+    lrow[j] = row;
+    aoff[j] = uint32_t(row) * uint32_t(ldx) * 2u + uint32_t(piece) * 16u;
+    goff[j] = uint32_t(row) * uint32_t(ldg) * 2u + uint32_t(piece) * 16u;
+  }
+  auto issue = [&](int chunk, int slot) {
+    const int t0 = chunk * kDwTC;
+    unsigned char* st = smem + slot * kDwStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool live = t0 + lrow[j] < T;
+      dma16(ra, live ? aoff[j] + uint32_t(t0) * uint32_t(ldx) * 2u : kDeadOff, 0u,
+            st + (wave * 4 + j) * 1024);
+      dma16(rg, live ? goff[j] + uint32_t(t0) * uint32_t(ldg) * 2u : kDeadOff, 0u,
+            st + kDwTile + (wave * 4 + j) * 1024);
+    }
+  };
+
+  // transpose reads: lane L = 16g + 4j + a reads row 8g + j (+ 4) of the
+  // sub-step, columns 4a.. of a 16-column fragment
+  const int tr_row = 8 * (lane >> 4) + ((lane >> 2) & 3), tr_a = lane & 3;
+  auto read_tr = [&](const unsigned char* tileb, int h, int col0) {
+    const int col = col0 + 4 * tr_a;              // first of the 4 columns
+    const int piece = col >> 3, half = (col >> 2) & 1;
+    const int r1 = 32 * h + tr_row, r2 = r1 + 4;
+    const u32x2 lo = lds_read_tr(tileb + r1 * 256 + ((piece ^ dw_swz(r1)) * 16) + half * 8);
+    const u32x2 hi = lds_read_tr(tileb + r2 * 256 + ((piece ^ dw_swz(r2)) * 16) + half * 8);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int p = 0; p < kDwNS - 1; ++p) issue(p, p);
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c has landed once at most the later chunks' loads remain (chunks
+    // past the last issue loads that read zeros, so the count is fixed)
+    wait_vmcnt<(kDwNS - 2) * 8>();
+    barrier_no_fence();
+    issue(c + kDwNS - 1, (c + kDwNS - 1) % kDwNS);
+    const unsigned char* st = smem + (c % kDwNS) * kDwStage;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf) a[kf] = read_tr(st, h, wk * 64 + kf * 16);
+#pragma unroll
+      for (int rf = 0; rf < 4; ++rf) b[rf] = read_tr(st + kDwTile, h, wr * 64 + rf * 16);
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+        for (int rf = 0; rf < 4; ++rf) acc[kf][rf] = mfma32<DT>(a[kf], b[rf], acc[kf][rf]);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: lane (r = li of the fragment, quarter q) holds D rows
+  // 4q..4q+3, columns k..k+3 of W's row r
+#pragma unroll
+  for (int rf = 0; rf < 4; ++rf) {
+    const int r = R0 + wr * 64 + rf * 16 + li;
+#pragma unroll
+    for (int kf = 0; kf < 4; ++kf) {
+      const int k = K0 + wk * 64 + kf * 16 + lq * 4;
+      if (r >= R || k >= K) continue;
+      const f32x4 v = acc[kf][rf];
+      const int g = k / M;                          // the group holding k .. k+3
+      const int64_t sg = int64_t(g) * N;            // its first survivor
+      const int64_t bit = sg * B;
+      const uint32_t* irow = idx + int64_t(r) * idx_row_words;
+      const int64_t w = bit >> 5;
+      const uint64_t pair = uint64_t(irow[w]) |
+                            (w + 1 < idx_row_words ? uint64_t(irow[w + 1]) << 32 : uint64_t(0));
+      const uint32_t bits = uint32_t(pair >> (bit & 31));
+      auto pick = [&](uint32_t p) {   // D value at in-lane column p (0..3)
+        return p == 0 ? v[0] : p == 1 ? v[1] : p == 2 ? v[2] : v[3];
+      };
+      const int64_t o = int64_t(r) * S + sg;
+      if constexpr (P == 0) {
+        const float x0 = pick(bits & 3u), x1 = pick((bits >> 2) & 3u);
+        if constexpr (OUT == NM_F32) {
+          float* y = static_cast<float*>(dW) + o;
+          y[0] = x0;
+          y[1] = x1;
+        } else {
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(dW) + o) = pack_half2<DT>(x0, x1);
+        }
+      } else {
+        const uint32_t pos = bits & (M - 1);
+        // 1:8: the survivor is in this lane's half of the group of eight only
+        // when its position's high bit matches the half
+        const bool mine = P == 1 || int(pos >> 2) == ((k % M) >> 2);
+        if (mine) {
+          const float x = pick(pos & 3u);
+          if constexpr (OUT == NM_F32) {
+            static_cast<float*>(dW)[o] = x;
+          } else {
+            static_cast<uint16_t*>(dW)[o] = uint16_t(pack_half2<DT>(x, 0.f));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int P, int DT, int OUT>
+hipError_t launch_dw_cfg(const TrainArgs& a, hipStream_t s) {
+  const int64_t tilesK = (a.K + kDwBK - 1) / kDwBK, tilesR = (a.R + kDwBR - 1) / kDwBR;
+  if (tilesK * tilesR > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto kern = spmm_dw_kernel<P, DT, OUT>;
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kDwLds); e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(unsigned(tilesK * tilesR)), dim3(256), kDwLds, s, a.idx, uint32_t(a.idx_bytes),
+                     int(a.R), int(a.K), int(a.idx_row_words), a.G, int(a.T), a.ldg, a.act, a.ldx, a.out,
+                     int(tilesK));
+  return hipGetLastError();
+}
+
+template <int P, int DT>
+hipError_t launch_dw_out(const TrainArgs& a, hipStream_t s) {
+  return a.out_dtype == NM_F32 ? launch_dw_cfg<P, DT, NM_F32>(a, s) : launch_dw_cfg<P, DT, DT>(a, s);
+}
+
+template <int P>
+hipError_t launch_dw_dt(const TrainArgs& a, hipStream_t s) {
+  return a.dtype == NM_F16 ? launch_dw_out<P, NM_F16>(a, s) : launch_dw_out<P, NM_BF16>(a, s);
+}
+
+template <int P, int DT, int OUT>
+hipError_t launch_dx_cfg(const TrainArgs& a, hipStream_t s) {
+  const int64_t tilesK = (a.K + kDxBK - 1) / kDxBK, tilesT = (a.T + kDxBT - 1) / kDxBT;
+  if (tilesK * tilesT > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto kern = spmm_dx_kernel<P, DT, OUT>;
+  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kDxLds); e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(unsigned(tilesK * tilesT)), dim3(256), kDxLds, s, a.values,
+                     uint32_t(a.values_bytes), a.idx, uint32_t(a.idx_bytes), int(a.R), int(a.K),
+                     int(a.idx_row_words), a.G, int(a.T), a.ldg, a.out, a.ldo, int(tilesK));
+  return hipGetLastError();
+}
+
+template <int P, int DT>
+hipError_t launch_dx_out(const TrainArgs& a, hipStream_t s) {
+  return a.out_dtype == NM_F32 ? launch_dx_cfg<P, DT, NM_F32>(a, s) : launch_dx_cfg<P, DT, DT>(a, s);
+}
+
+template <int P>
+hipError_t launch_dx_dt(const TrainArgs& a, hipStream_t s) {
+  return a.dtype == NM_F16 ? launch_dx_out<P, NM_F16>(a, s) : launch_dx_out<P, NM_BF16>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_spmm_dw(const TrainArgs& a, hipStream_t s) {
+  if (a.n == 2 && a.m == 4) return launch_dw_dt<0>(a, s);
+  if (a.n == 1 && a.m == 4) return launch_dw_dt<1>(a, s);
+  if (a.n == 1 && a.m == 8) return launch_dw_dt<2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_spmm_dx(const TrainArgs& a, hipStream_t s) {
+  if (a.n == 2 && a.m == 4) return launch_dx_dt<0>(a, s);
+  if (a.n == 1 && a.m == 4) return launch_dx_dt<1>(a, s);
+  if (a.n == 1 && a.m == 8) return launch_dx_dt<2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nm

@@ -365,3 +365,59 @@ def test_hybrid_compress_and_spmm_errors():
     assert mm(Y=F + 256) == 5                  # Y overlaps act
     assert mm(Y=5 * F - 64) == 5               # Y overlaps the tile table
     assert mm(T=0) == 0
+
+
+def test_train_argument_errors():
+    # every call here fails validation (or has nothing to do) before any HIP call
+    L = nm.lib()
+    F = FAKE
+
+    def dx(v=F, i=2 * F, R=256, K=256, n=2, m=4, dt=nm.NM_F16, G=3 * F, T=64, ldg=256, X=4 * F, ldo=256,
+           od=nm.NM_F32):
+        return L.nm_spmm_dx(v, i, R, K, n, m, dt, G, T, ldg, X, ldo, od, None)
+    assert dx(dt=nm.NM_I8) == 3
+    assert dx(od=nm.NM_BF16) == 3
+    assert dx(n=3) == 3
+    assert dx(K=100) == 2
+    assert dx(K=272) == 2                    # K % 32
+    assert dx(R=260) == 2                    # R % 8
+    assert dx(T=-1) == 2
+    assert dx(ldg=128) == 4
+    assert dx(ldo=128) == 4
+    assert dx(T=0) == 0                      # empty dX: nothing enqueued
+    assert dx(G=None) == 1
+    assert dx(X=None) == 1
+    assert dx(ldg=260) == 7                  # G rows must be whole 16-byte pieces
+    assert dx(G=3 * F + 8) == 7
+    assert dx(X=3 * F) == 5                  # dX overlaps G
+
+    def dw(i=F, R=256, K=256, n=2, m=4, dt=nm.NM_BF16, G=2 * F, T=64, ldg=256, a=3 * F, ldx=256, W=4 * F,
+           od=nm.NM_F32):
+        return L.nm_spmm_dw(i, R, K, n, m, dt, G, T, ldg, a, ldx, W, od, None)
+    assert dw(dt=nm.NM_FP8) == 3
+    assert dw(od=nm.NM_F16) == 3
+    assert dw(ldx=200) == 4
+    assert dw(ldg=200) == 4
+    assert dw(R=0) == 0                      # no weights: nothing enqueued
+    assert dw(i=None) == 1
+    assert dw(a=None) == 1
+    assert dw(ldx=260) == 7
+    assert dw(W=3 * F) == 5                  # dW overlaps act
+
+
+def test_train_binding_checks_before_the_device():
+    torch = pytest.importorskip("torch")
+    v = torch.zeros((8, 32), dtype=torch.float16)
+    i = torch.zeros((8, 4), dtype=torch.int32)
+    G = torch.zeros((4, 8), dtype=torch.float16)
+    a = torch.zeros((4, 64), dtype=torch.float16)
+    with pytest.raises((ValueError, TypeError)):
+        nm.nm_spmm_dx(v, i, G[:, :7], 64)               # G's width is not R
+    with pytest.raises(TypeError):
+        nm.nm_spmm_dx(v.to(torch.int8), i, G.to(torch.int8), 64)
+    with pytest.raises(ValueError):
+        nm.nm_spmm_dw(i[:, :3], G, a, 64)               # idx of the wrong width
+    with pytest.raises(TypeError):
+        nm.nm_spmm_dw(i, G, a, 64, out_dtype=torch.bfloat16)
+    with pytest.raises(ValueError):                     # CPU tensors never reach the C ABI
+        nm.nm_spmm_dw(i, G, a, 64)
