@@ -51,8 +51,9 @@ def parse():
                     help="dense-matmul load before the warmup, so the clock has settled "
                          "(an idle GPU takes about a second of load to reach it)")
     ap.add_argument("--workload", type=int, default=2,
-                    help="1..8 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8; "
-                         "8: the same shape in hybrid dense / 2:4 tiles)")
+                    help="1..9 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8; "
+                         "8: the same shape in hybrid dense / 2:4 tiles; 9: its training-side "
+                         "products dX and dW)")
     ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
     ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
@@ -302,6 +303,184 @@ def bench_hybrid(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_train(wl, T, reps):
+    """The training oracle as it stands (dX = G W_nm and the packed dW, fp64) on
+    the first 2048 tokens of G and act (all of them at the workload's size),
+    scaled to all T: both products are linear in the token count."""
+    from oracle import nm_oracle as O
+    from oracle import nm_train as TR
+    n, m = wl.patterns[0]
+    ts = min(T, 2048)
+    vals, idx = O.prune_pack(wl.weights(), n, m)
+    g = wl.gradient(T)[:ts]
+    act = wl.activations(T)[:ts]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        TR.spmm_dx_ref(vals, idx, wl.K, n, m, g, wl.dtype)
+        TR.spmm_dw_ref(idx, wl.K, n, m, g, act, wl.dtype)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times) * T / ts
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"value": 2.0 * 2.0 * wl.R * wl.K * T / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{wl.R}x{wl.K}x{T} {n}:{m} dX and packed dW: fp64 decompress + G W_nm, G^T act "
+                       f"sampled at the stored columns, over the first {ts} of {T} tokens, scaled; "
+                       f"median of {reps} runs")}
+
+
+def bench_train(args, wl):
+    """Training-side products of a fixed-pattern layer: one step = nm_spmm_dx
+    (dX = G W_nm from the packed weight) + nm_spmm_dw (dW at the stored
+    positions, packed), the weight already packed."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_nm_amd as nm
+
+    R, K = wl.R, wl.K
+    T = args.T if args.T is not None else wl.Ts[0]
+    n, m = wl.patterns[0]
+    S = K // m * n
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+    out_dtype = torch.float32 if args.out_dtype == "f32" else tdt
+    out_name = args.out_dtype
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+    W = dev(wl.weights())
+    act = dev(wl.activations(T))
+    G = dev(wl.gradient(T))
+    vals, idx = nm.nm_compress(W, n, m)
+    dX = torch.empty((T, K), dtype=out_dtype, device="cuda")
+    dW = torch.empty((R, S), dtype=out_dtype, device="cuda")
+
+    def dx(_c=0):
+        nm.nm_spmm_dx(vals, idx, G, K, n, m, out_dtype=out_dtype, out=dX)
+
+    def dw(_c=0):
+        nm.nm_spmm_dw(idx, G, act, K, n, m, out_dtype=out_dtype, out=dW)
+
+    settle = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    tw = time.perf_counter()
+    while (time.perf_counter() - tw) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            torch.matmul(settle, settle)
+        torch.cuda.synchronize()
+    del settle
+    for _ in range(args.warmup):
+        dx()
+        dw()
+    torch.cuda.synchronize()
+    # the timed steps run their dX products first, then their dW products, so
+    # each kernel's mean comes from events around its own phase
+    t0 = time.perf_counter()
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    start.record()
+    for _ in range(args.steps):
+        dx()
+    mid.record()
+    for _ in range(args.steps):
+        dw()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    dx_us = start.elapsed_time(mid) * 1e3 / args.steps
+    dw_us = mid.elapsed_time(end) * 1e3 / args.steps
+
+    # dense hipBLASLt products of the same shapes and output dtypes: dX = G W_hat
+    # (W_hat the pruned weight, dense) and the full dense dW = G^T act (G^T
+    # handed over row-major), in alternating blocks with the sparse ones
+    W_hat = nm.nm_decompress(vals, idx, K, n, m).contiguous()
+    Gt = G.t().contiguous()
+    dxh = torch.empty((T, K), dtype=tdt, device="cuda")
+    dwh = torch.empty((R, S), dtype=tdt, device="cuda")
+    loops = {"dx": dx, "dw": dw,
+             "dx_half": lambda c: nm.nm_spmm_dx(vals, idx, G, K, n, m, out_dtype=tdt, out=dxh),
+             "dw_half": lambda c: nm.nm_spmm_dw(idx, G, act, K, n, m, out_dtype=tdt, out=dwh),
+             "dense_dx_half": lambda c: torch.mm(G, W_hat),
+             "dense_dx_f32": lambda c: torch.mm(G, W_hat, out_dtype=torch.float32),
+             "dense_dw_half": lambda c: torch.mm(Gt, act),
+             "dense_dw_f32": lambda c: torch.mm(Gt, act, out_dtype=torch.float32)}
+    iters = max(20, args.steps)
+    for name in list(loops):
+        try:
+            for _ in range(3):
+                loops[name](0)
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"{name} unavailable: {e}", file=sys.stderr)
+            del loops[name]
+    samples = {name: [] for name in loops}
+    for _ in range(5):
+        for name, fn in loops.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                fn(0)
+            b.record()
+            torch.cuda.synchronize()
+            samples[name].append(a.elapsed_time(b) * 1e3 / iters)
+    loop_us = {name: float(np.median(v)) for name, v in samples.items()}
+
+    def ratio(x, y):
+        return loop_us[x] / loop_us[y] if x in loop_us and y in loop_us else None
+
+    # algorithmic FLOP: one MAC per (token, stored weight) in each product; the
+    # MFMA work of both kernels is the dense 2 R K T (neither product can skip
+    # the zeros: in dX they do not lie along the reduction, in dW they are outputs)
+    alg_flop = 2.0 * T * R * S
+    mfma_flop = 2.0 * T * R * K
+    dense_eq_flop = 2.0 * 2.0 * R * K * T
+    ob = 4 if out_name == "f32" else 2
+    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
+               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
+    hsh = source_hash(lib_src)
+    _, ib, _ = nm.nm_packed_sizes(R, K, n, m, nm.NM_BF16 if wl.dtype == "bf16" else nm.NM_F16)
+    per = {"nm_spmm_dx": {"mean_us": dx_us, "flop": alg_flop, "mfma_flop": mfma_flop,
+                          "bytes": R * S * 2 + ib + T * R * 2 + T * K * ob},
+           "nm_spmm_dw": {"mean_us": dw_us, "flop": alg_flop, "mfma_flop": mfma_flop,
+                          "bytes": ib + T * R * 2 + T * K * 2 + R * S * ob}}
+    dom = max(per, key=lambda k: per[k]["mean_us"])
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    achieved = per[dom]["flop"] / (per[dom]["mean_us"] * 1e-6) / 1e12
+    key = "dx" if dom == "nm_spmm_dx" else "dw"
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": traffic_from_profile(f"train_{key}_w{wl.wid}_T{T}_{out_name}", hsh),
+                "kernel": dom, "per_launch": per[dom],
+                "mfma_frac": per[dom]["mfma_flop"] / (per[dom]["mean_us"] * 1e-6) / 1e12 / peak}
+    out = {
+        "metric": METRIC, "value": dense_eq_flop / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,sigma) W, act and G of the workload's shapes)",
+        "config": {"workload": wl.name, "R": R, "K": K, "T": T, "pattern": f"{n}:{m}", "out_dtype": out_name,
+                   "step": "nm_spmm_dx + nm_spmm_dw", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {
+            "nm_spmm_dx_us_in_step": dx_us, "nm_spmm_dw_us_in_step": dw_us,
+            "per_launch": per,
+            "nm_spmm_dx_us_loop": loop_us.get("dx"), "nm_spmm_dw_us_loop": loop_us.get("dw"),
+            "nm_spmm_dx_half_out_us": loop_us.get("dx_half"), "nm_spmm_dw_half_out_us": loop_us.get("dw_half"),
+            "dense_dx_half_out_us": loop_us.get("dense_dx_half"), "dense_dx_f32_out_us": loop_us.get("dense_dx_f32"),
+            "dense_dw_half_out_us": loop_us.get("dense_dw_half"), "dense_dw_f32_out_us": loop_us.get("dense_dw_f32"),
+            "speedup_vs_dense_same_out_dtype": {k: v for k, v in {
+                "dx_f32": ratio("dense_dx_f32", "dx") if out_name == "f32" else None,
+                "dw_f32": ratio("dense_dw_f32", "dw") if out_name == "f32" else None,
+                "dx_half": ratio("dense_dx_half", "dx_half"),
+                "dw_half": ratio("dense_dw_half", "dw_half")}.items() if v is not None},
+        },
+        "wall_s_timed": wall, "source_hash": hsh,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(wl, T, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
 def _hybrid_dense_operand(nm, torch, W, L, flags, tdt):
     """W_hat^T [K, R] row-major for the dense reference GEMM: the weight as the
     hybrid pruning leaves it.  Dense tiles are W itself; a 2:4 tile keeps what
@@ -369,6 +548,9 @@ def main():
     wl = nm_inputs.WORKLOADS[args.workload]
     if wl.hybrid:
         bench_hybrid(args, wl)
+        return
+    if wl.train:
+        bench_train(args, wl)
         return
     T = args.T if args.T is not None else wl.Ts[-1] if args.workload == 3 else wl.Ts[0]
     if args.pattern:

@@ -8,8 +8,8 @@ draw their inputs from here.
 Recipe (the same everywhere):
   * generator: numpy PCG64 seeded with the sequence [workload_id, tensor_id,
     variant]; tensor_id 0 = weight W, 1 = activations, 2 = permutation,
-    3 = hybrid tile flags;
-  * W and activations: float32 standard normal times sigma, then rounded to
+    3 = hybrid tile flags, 4 = output gradient G (training products);
+  * W, activations and G: float32 standard normal times sigma, then rounded to
     the storage type with round-to-nearest-even (fp16 through numpy's cast,
     bf16 through the bit routine below);
   * permutation: a uniform random permutation of 0..K-1 (int32);
@@ -117,6 +117,7 @@ class Workload:
     permuted: bool = False
     note: str = ""
     hybrid: tuple = ()  # (tile_rows, tile_cols, dense fraction) for hybrid dense / 2:4 tiles
+    train: bool = False  # the training-side products (dX, dW) of the layer
 
     def weights(self) -> np.ndarray:
         if self.dtype == I8:
@@ -133,6 +134,11 @@ class Workload:
             return normal_fp8((T, self.K), self.sigma_x, self.wid, 1, T)
         return normal_half((T, self.K), self.sigma_x, self.dtype, self.wid, 1, T)
 
+    def gradient(self, T: int | None = None) -> np.ndarray:
+        """G = dL/dY in the forward output's [T, R] layout, N(0, 1) in the weight type."""
+        T = self.Ts[0] if T is None else T
+        return normal_half((T, self.R), 1.0, self.dtype, self.wid, 4, T)
+
     def permutation(self) -> np.ndarray | None:
         return random_permutation(self.K, self.wid) if self.permuted else None
 
@@ -145,7 +151,8 @@ class Workload:
 # measure: a small 2:4 example, a LLaMA-2-7B projection at prefill and at
 # decode, the general 1:4 / 1:8 forms, a ViT-B/16 MLP fc1 over 64 images of
 # 197 tokens with a learned column permutation, the prefill shape in INT8 and
-# in FP8 E4M3, and the prefill shape with hybrid dense / 2:4 tiles.
+# in FP8 E4M3, the prefill shape with hybrid dense / 2:4 tiles, and the
+# prefill shape's training-side products.
 WORKLOADS = {
     1: Workload(1, "small-2of4-fp16", 256, 256, (64,), ((2, 4),), F16, 1.0,
                 note="2:4 fp16 small case"),
@@ -168,4 +175,8 @@ WORKLOADS = {
     # 128 tiles, half of them (seeded at random) dense, so 25% of W is zero
     8: Workload(8, "llama2-7b-proj-prefill-hybrid-tiles-bf16", 4096, 4096, (2048,), ((2, 4),), BF16, 0.02,
                 note="hybrid dense / 2:4 128x128 tiles, half dense", hybrid=(128, 128, 0.5)),
+    # the training-side products of the prefill projection (retraining with the
+    # 2:4 pattern held): dX = G W_nm and the packed dW, G [2048, 4096] N(0, 1)
+    9: Workload(9, "llama2-7b-proj-backward-2of4-bf16", 4096, 4096, (2048,), ((2, 4),), BF16, 0.02,
+                note="2:4 bf16 dX and packed dW", train=True),
 }

@@ -26,6 +26,8 @@
 #include "nm_device.h"
 #include "nm_internal.h"
 
+#include <type_traits>
+
 namespace nm {
 namespace {
 
@@ -57,24 +59,30 @@ constexpr int pat_m(int P) { return P == 2 ? 8 : 4; }
 // dX = G W_nm, computed as dX^T tiles: D[k][t] = sum_r W[r][k] G[t][r].
 //
 // A workgroup (4 waves, 2 x 2) owns 128 k x 128 t; a wave 64 x 64 (4 x 4
-// fragments).  R is walked in chunks of 64 rows:
-//   * G's tile (128 tokens x 64 r, 16 KB) arrives by direct global->LDS loads
-//     through a kNS-deep ring, slot (token, 16-byte chunk c) at token*8 +
-//     (c ^ (token & 7)); a B operand lane (token i, quarter q) reads chunk
-//     4h + q of sub-step h (r 32h + 8q ..) with one 16-byte read;
+// fragments).  R is walked in chunks of 64 rows, each staged in LDS:
+//   * G's tile (128 tokens x 64 r, 16 KB), 4 16-byte pieces per thread,
+//     loaded into registers two chunks ahead and written to a double-buffered
+//     stage, slot (token, 16-byte chunk c) at token*8 + (c ^ (token & 7)); a
+//     B operand lane (token i, quarter q) reads chunk 4h + q of sub-step h
+//     (r 32h + 8q ..) with one 16-byte read;
 //   * W's chunk (64 rows x 128 columns) is decompressed by the workgroup's
 //     256 threads, each one row and 32 columns, from packed values and index
 //     bits it loaded into registers two chunks earlier, into a dense
 //     double-buffered tile [64 r][128 k] (rows padded to 288 bytes); the A
 //     operands (k rows, r reduction) come out of it by transpose reads.
-// One barrier per chunk publishes G's chunk and the W tile decompressed in
-// the previous chunk, and retires the buffers the chunk then refills.
+// The stages are filled from registers, not by direct global->LDS loads: the
+// compiler cannot tell which LDS bytes a transpose read touches, so after a
+// direct load it would hold every transpose read until that load landed.
+// One barrier per chunk publishes the chunk's stage and tile (written in the
+// previous step) and retires the ones the step then refills.  At 68 KB of
+// LDS two workgroups share a compute unit, each covering the other's barrier
+// and epilogue.
 // ---------------------------------------------------------------------------
-constexpr int kDxBK = 128, kDxBT = 128, kDxRC = 64, kDxNS = 4;
+constexpr int kDxBK = 128, kDxBT = 128, kDxRC = 64;
 constexpr int kDxGStage = kDxBT * kDxRC * 2;     // 16 KB
 constexpr int kDxWRow = kDxBK * 2 + 32;          // 288 bytes: padded row of the W tile
 constexpr int kDxWTile = kDxRC * kDxWRow;        // 18 KB
-constexpr int kDxLds = kDxNS * kDxGStage + 2 * kDxWTile;
+constexpr int kDxLds = 2 * kDxGStage + 2 * kDxWTile;
 
 // One thread's packed share of a chunk: values of 32 columns of one row
 // (2:4 16 values, 1:4 8, 1:8 4) and the two index words holding its bits.
@@ -142,7 +150,7 @@ __device__ inline void dx_expand(const DxPack& d, uint32_t ishift, uint32_t (&o)
 }
 
 template <int P, int DT, int OUT>
-__global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict__ values, uint32_t values_bytes,
+__global__ __launch_bounds__(256, 2) void spmm_dx_kernel(const uint16_t* __restrict__ values, uint32_t values_bytes,
                                                       const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
                                                       int K, int idx_row_words, const uint16_t* __restrict__ G,
                                                       int T, int64_t ldg, void* __restrict__ dX, int64_t lddx,
@@ -150,8 +158,8 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
   constexpr int N = pat_n(P), M = pat_m(P);
   constexpr int B = P == 2 ? 3 : 2;  // index bits per survivor
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* gbuf = smem;                          // [kNS][16 KB]
-  unsigned char* wbuf = smem + kDxNS * kDxGStage;      // [2][64][288 B]
+  unsigned char* gbuf = smem;                          // [2][16 KB]
+  unsigned char* wbuf = smem + 2 * kDxGStage;          // [2][64][288 B]
 
   const int tile = blockIdx.x;
   const int K0 = (tile % tilesK) * kDxBK, T0 = (tile / tilesK) * kDxBT;
@@ -169,6 +177,8 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
   const int tlast = min(T0 + kDxBT, T) - 1;
   const __amdgpu_buffer_rsrc_t rg =
       make_rsrc(G + int64_t(T0) * ldg, uint32_t((int64_t(tlast - T0) * ldg + R) * 2));
+  // this thread's 4 pieces of a chunk: LDS slot gslot[j] = (wave*4 + j)*64 +
+  // lane, holding (token, 16-byte chunk c) of the tile
   uint32_t goff[4];
   int gcol[4];
 #pragma unroll
@@ -180,15 +190,20 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
     goff[j] = uint32_t(t) * uint32_t(ldg) * 2u + uint32_t(c) * 16u;
     gcol[j] = c * 8;
   }
-  auto issue_g = [&](int chunk, int slot) {
+  auto load_g = [&](int chunk, u32x4 (&gr)[4]) {
     const int r0 = chunk * kDxRC;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // a piece past R (or of a chunk past the last) reads zeros
       const bool live = chunk < nchunks && r0 + gcol[j] < R;
-      dma16(rg, live ? goff[j] + uint32_t(r0) * 2u : kDeadOff, 0u,
-            gbuf + slot * kDxGStage + (wave * 4 + j) * 1024);
+      gr[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, live ? goff[j] + uint32_t(r0) * 2u : kDeadOff, 0, 0));
     }
+  };
+  auto write_g = [&](int stage, const u32x4 (&gr)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(gbuf + stage * kDxGStage + ((wave * 4 + j) * 64 + lane) * 16) = gr[j];
   };
 
   // W: this thread decompresses row (tid >> 2) of the chunk, columns
@@ -240,58 +255,66 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
     return *reinterpret_cast<const u32x4*>(gbuf + slot * kDxGStage + (tok * 8 + (c ^ (tok & 7))) * 16);
   };
 
-  // ---- prologue: G chunks 0 .. kNS-2 in flight, packed chunks 0 and 1 in
-  // registers, chunk 0 decompressed
-  for (int p = 0; p < kDxNS - 1; ++p) issue_g(p, p);
+  // ---- prologue: chunks 0 and 1 in registers, chunk 0 staged and
+  // decompressed, chunk 2 in registers
   DxPack pk[2];
-  {
+  u32x4 gs[2][4];
+  auto load_pack = [&](int chunk, DxPack& d) {
     uint32_t vo, i0, i1;
-    pack_offsets(0, vo, i0, i1);
-    dx_load<P>(pk[0], rv, ri, vo, i0, i1);
-    pack_offsets(1, vo, i0, i1);
-    dx_load<P>(pk[1], rv, ri, vo, i0, i1);
-  }
+    pack_offsets(chunk, vo, i0, i1);
+    dx_load<P>(d, rv, ri, vo, i0, i1);
+  };
+  load_g(0, gs[0]);
+  load_pack(0, pk[0]);
+  load_g(1, gs[1]);
+  load_pack(1, pk[1]);
   decompress(pk[0], 0);
-  {
-    uint32_t vo, i0, i1;
-    pack_offsets(2, vo, i0, i1);
-    dx_load<P>(pk[0], rv, ri, vo, i0, i1);
-  }
+  write_g(0, gs[0]);
+  load_g(2, gs[0]);
+  load_pack(2, pk[0]);
 
-  // Step c: G chunk c (slot c % kNS) and W tile c & 1 are ready after the
-  // barrier; the step refills G slot (c - 1) % kNS with chunk c + kNS - 1,
-  // multiplies, then decompresses chunk c + 1 from register set (c + 1) & 1
-  // into W tile (c + 1) & 1 and loads chunk c + 3's packed share into that
-  // set.  The loop is unrolled by two so the register sets alternate.
-  // Every wave's G loads of chunk c have landed by the time the step starts:
-  // they were issued before the packed loads of chunk c, which the decompress
-  // of chunk c (the previous step, or the prologue) waited for, and loads
-  // complete in issue order.  The barrier then publishes them workgroup-wide.
-  auto step = [&](int c, DxPack& next) {
+  // Step c (parity PAR = c & 1, a compile-time constant: the loop is unrolled
+  // by two so the register sets alternate without copies): the barrier
+  // publishes G stage PAR and W tile PAR, written in step c-1 (or the
+  // prologue), and retires stage and tile PAR ^ 1, read in step c-1.  The step
+  // multiplies chunk c, then stages chunk c+1 from register sets (c+1) & 1
+  // into stage and tile PAR ^ 1 and loads chunk c+3 into those sets.  Past the
+  // last chunk the loads read zeros (dead offsets).
+  auto step = [&](auto par_c, int c) {
+    constexpr int PAR = decltype(par_c)::value;
+    DxPack& nextp = pk[PAR ^ 1];
+    u32x4 (&nextg)[4] = gs[PAR ^ 1];
+    wait_lgkm0();
     barrier_no_fence();
-    issue_g(c + kDxNS - 1, (c + kDxNS - 1) % kDxNS);
-    const int slot = c % kDxNS, buf = c & 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 a[4], b[4];
 #pragma unroll
-      for (int kf = 0; kf < 4; ++kf) a[kf] = read_a(buf, h, kf);
+      for (int kf = 0; kf < 4; ++kf) a[kf] = read_a(PAR, h, kf);
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) b[tf] = read_b(slot, h, tf);
+      for (int tf = 0; tf < 4; ++tf) b[tf] = read_b(PAR, h, tf);
 #pragma unroll
       for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf) acc[kf][tf] = mfma32<DT>(a[kf], b[tf], acc[kf][tf]);
     }
-    if (c + 1 < nchunks) decompress(next, buf ^ 1);
-    uint32_t vo, i0, i1;
-    pack_offsets(c + 3, vo, i0, i1);
-    dx_load<P>(next, rv, ri, vo, i0, i1);
+    if (c + 1 < nchunks) {
+      decompress(nextp, PAR ^ 1);
+      write_g(PAR ^ 1, nextg);
+    }
+    load_g(c + 3, nextg);
+    load_pack(c + 3, nextp);
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, pk[1]);
-    if (c + 1 < nchunks) step(c + 1, pk[0]);
+  // whole pairs in the loop and an odd last chunk after it: a pair cut short
+  // inside the loop would give the back edge a path on which the other
+  // register set holds the newest loads, and the compiler's waits before
+  // every later write of a set would then drain both sets
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    step(std::integral_constant<int, 1>{}, c + 1);
   }
+  if (c < nchunks) step(std::integral_constant<int, 0>{}, c);
   wait_vmcnt<0>();
 
   // ---- epilogue: lane (t = li, quarter q) holds rows 4q..4q+3 (k) of
@@ -331,10 +354,14 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
 // D[k][r] = sum_t act[t][k] G[t][r] of which each lane keeps the stored
 // entries.  A workgroup (4 waves, 2 x 2) owns 128 k x 128 r; a wave 64 x 64.
 // T is walked in chunks of 64 tokens; both tiles of a chunk, act's [64 t][128
-// k] and G's [64 t][128 r] (16 KB each, token rows of 256 bytes), arrive by
-// direct global->LDS loads through a kNS-deep ring, and both operands come out
-// by transpose reads: an operand lane needs 8 consecutive tokens of one
-// column.  The 16-byte pieces of a row are XOR-swizzled, piece p of row t at
+// k] and G's [64 t][128 r] (16 KB each, token rows of 256 bytes), are loaded
+// into registers two chunks ahead (8 16-byte pieces per thread) and written to
+// a double-buffered stage after the previous chunk's MFMAs, and both operands
+// come out by transpose reads: an operand lane needs 8 consecutive tokens of
+// one column.  (Staging from registers rather than by direct global->LDS
+// loads keeps the compiler from holding each transpose read until every
+// direct load in flight has landed.)  At 64 KB of LDS two workgroups share a
+// compute unit.  The 16-byte pieces of a row are XOR-swizzled, piece p of row t at
 // p ^ f(t), f(t) = 2 (t & 3) + 8 ((t >> 3) & 1), so the 8-byte transpose
 // reads of 32 lanes (rows 8g + j, g = 0, 1, j = 0..3) fall in distinct banks.
 // A result lane (column r, quarter q) holds rows 4q..4q+3 of D, four
@@ -342,15 +369,15 @@ __global__ __launch_bounds__(256) void spmm_dx_kernel(const uint16_t* __restrict
 // of eight, whose stored positions it reads from the index bits and whose
 // survivors it writes to the packed gradient.
 // ---------------------------------------------------------------------------
-constexpr int kDwBK = 128, kDwBR = 128, kDwTC = 64, kDwNS = 4;
+constexpr int kDwBK = 128, kDwBR = 128, kDwTC = 64;
 constexpr int kDwTile = kDwTC * 256;                    // 16 KB: 64 token rows of 256 bytes
 constexpr int kDwStage = 2 * kDwTile;                   // act tile, then G tile
-constexpr int kDwLds = kDwNS * kDwStage;                // 128 KB
+constexpr int kDwLds = 2 * kDwStage;                    // 64 KB
 
 __device__ inline int dw_swz(int t) { return ((t & 3) << 1) | (((t >> 3) & 1) << 3); }
 
 template <int P, int DT, int OUT>
-__global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
+__global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
                                                       int K, int idx_row_words, const uint16_t* __restrict__ G,
                                                       int T, int64_t ldg, const uint16_t* __restrict__ act,
                                                       int64_t ldx, void* __restrict__ dW, int tilesK) {
@@ -367,9 +394,8 @@ __global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict
   const int nchunks = (T + kDwTC - 1) / kDwTC;
   const int64_t S = int64_t(K) * N / M;
 
-  // Direct loads: instruction j (0..3) of a wave fills token rows
-  // 4 (4 wave + j) .. +3 of a tile, lane l row + l / 16, piece l % 16 (which
-  // holds global piece (l % 16) ^ f(row)).  Tokens past T read zeros, so they
+  // Piece j (0..3) of a lane, in each tile: token row 4 (4 wave + j) + l / 16,
+  // LDS piece l % 16, which holds global piece (l % 16) ^ f(row).  Tokens past T read zeros, so they
   // add nothing; columns past K or R are whatever the descriptor allows and
   // only reach outputs that are dropped.
   // (with T == 0 nothing is read: the descriptors cover no bytes)
@@ -387,16 +413,23 @@ __global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict
     aoff[j] = uint32_t(row) * uint32_t(ldx) * 2u + uint32_t(piece) * 16u;
     goff[j] = uint32_t(row) * uint32_t(ldg) * 2u + uint32_t(piece) * 16u;
   }
-  auto issue = [&](int chunk, int slot) {
+  auto load_chunk = [&](int chunk, u32x4 (&v)[8]) {
     const int t0 = chunk * kDwTC;
-    unsigned char* st = smem + slot * kDwStage;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool live = t0 + lrow[j] < T;
-      dma16(ra, live ? aoff[j] + uint32_t(t0) * uint32_t(ldx) * 2u : kDeadOff, 0u,
-            st + (wave * 4 + j) * 1024);
-      dma16(rg, live ? goff[j] + uint32_t(t0) * uint32_t(ldg) * 2u : kDeadOff, 0u,
-            st + kDwTile + (wave * 4 + j) * 1024);
+      v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ra, live ? aoff[j] + uint32_t(t0) * uint32_t(ldx) * 2u : kDeadOff, 0, 0));
+      v[4 + j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rg, live ? goff[j] + uint32_t(t0) * uint32_t(ldg) * 2u : kDeadOff, 0, 0));
+    }
+  };
+  auto write_chunk = [&](int stage, const u32x4 (&v)[8]) {
+    unsigned char* st = smem + stage * kDwStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(st + (wave * 4 + j) * 1024 + lane * 16) = v[j];
+      *reinterpret_cast<u32x4*>(st + kDwTile + (wave * 4 + j) * 1024 + lane * 16) = v[4 + j];
     }
   };
 
@@ -418,14 +451,21 @@ __global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int p = 0; p < kDwNS - 1; ++p) issue(p, p);
-  for (int c = 0; c < nchunks; ++c) {
-    // chunk c has landed once at most the later chunks' loads remain (chunks
-    // past the last issue loads that read zeros, so the count is fixed)
-    wait_vmcnt<(kDwNS - 2) * 8>();
+  // chunk 0 staged, chunks 1 and 2 in registers; step c (parity PAR, the loop
+  // unrolled by two): the barrier publishes stage PAR and retires stage
+  // PAR ^ 1; the step multiplies chunk c, stages chunk c+1 from register set
+  // PAR ^ 1 and loads chunk c+3 into it (past the last chunk, zeros)
+  u32x4 vs[2][8];
+  load_chunk(0, vs[0]);
+  load_chunk(1, vs[1]);
+  write_chunk(0, vs[0]);
+  load_chunk(2, vs[0]);
+  auto step = [&](auto par_c, int c) {
+    constexpr int PAR = decltype(par_c)::value;
+    u32x4 (&nextv)[8] = vs[PAR ^ 1];
+    wait_lgkm0();
     barrier_no_fence();
-    issue(c + kDwNS - 1, (c + kDwNS - 1) % kDwNS);
-    const unsigned char* st = smem + (c % kDwNS) * kDwStage;
+    const unsigned char* st = smem + PAR * kDwStage;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 a[4], b[4];
@@ -438,7 +478,19 @@ __global__ __launch_bounds__(256) void spmm_dw_kernel(const uint32_t* __restrict
 #pragma unroll
         for (int rf = 0; rf < 4; ++rf) acc[kf][rf] = mfma32<DT>(a[kf], b[rf], acc[kf][rf]);
     }
+    if (c + 1 < nchunks) write_chunk(PAR ^ 1, nextv);
+    load_chunk(c + 3, nextv);
+  };
+  // whole pairs in the loop and an odd last chunk after it: a pair cut short
+  // inside the loop would give the back edge a path on which the other
+  // register set holds the newest loads, and the compiler's waits before
+  // every later write of a set would then drain both sets
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    step(std::integral_constant<int, 1>{}, c + 1);
   }
+  if (c < nchunks) step(std::integral_constant<int, 0>{}, c);
   wait_vmcnt<0>();
 
   // ---- epilogue: lane (r = li of the fragment, quarter q) holds D rows

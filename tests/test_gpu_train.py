@@ -39,7 +39,7 @@ def dw_bound(idx, K, n, m, g, act, dt):
 def case(R, K, T, dt, seed, sw=1.0):
     w = nm_inputs.normal_half((R, K), sw, dt, 70, 0, seed)
     act = nm_inputs.normal_half((T, K), 1.0, dt, 70, 1, seed)
-    g = nm_inputs.normal_half((T, R), 1.0, dt, 70, 3, seed)
+    g = nm_inputs.normal_half((T, R), 1.0, dt, 70, 4, seed)
     return w, act, g
 
 
@@ -90,7 +90,7 @@ def test_exact_on_integers(n, m):
     R, K, T = 200, 256, 150
     w = nm_inputs.integer_half((R, K), -6, 6, "f16", 71, 0, n * m)
     act = nm_inputs.integer_half((T, K), -5, 5, "f16", 71, 1, n * m)
-    g = nm_inputs.integer_half((T, R), -4, 4, "f16", 71, 3, n * m)
+    g = nm_inputs.integer_half((T, R), -4, 4, "f16", 71, 4, n * m)
     vals, idx = O.prune_pack(w, n, m)
     di = torch.from_numpy(idx.view(np.int32)).cuda()
     dx = nm.nm_spmm_dx(to_dev(vals, "f16"), di, to_dev(g, "f16"), K, n, m)
@@ -160,7 +160,7 @@ def test_workload_size_sampled():
     R, K, T, dt = 4096, 4096, 2048, "bf16"
     w = nm_inputs.normal_half((R, K), 0.02, dt, 72, 0)
     act = nm_inputs.normal_half((T, K), 1.0, dt, 72, 1)
-    g = nm_inputs.normal_half((T, R), 1.0, dt, 72, 3)
+    g = nm_inputs.normal_half((T, R), 1.0, dt, 72, 4)
     vals, idx = O.prune_pack(w, 2, 4)
     di = torch.from_numpy(idx.view(np.int32)).cuda()
     dx = nm.nm_spmm_dx(to_dev(vals, dt), di, to_dev(g, dt), K, 2, 4).cpu().numpy()

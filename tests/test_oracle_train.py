@@ -64,7 +64,7 @@ def test_bilinear_identities(n, m, dt):
     R, K, T = 48, 128, 20
     w = nm_inputs.normal_half((R, K), 1.0, dt, 90, 0, n * m)
     act = nm_inputs.normal_half((T, K), 1.0, dt, 90, 1, n * m)
-    g = nm_inputs.normal_half((T, R), 1.0, dt, 90, 3, n * m)
+    g = nm_inputs.normal_half((T, R), 1.0, dt, 90, 4, n * m)
     values, idx = O.prune_pack(w, n, m)
     L = loss(values, idx, K, n, m, act, g, dt)
     dx = TR.spmm_dx_ref(values, idx, K, n, m, g, dt)
