@@ -476,6 +476,12 @@ def bench_train(args, wl):
         },
         "wall_s_timed": wall, "source_hash": hsh,
     }
+    if args.copy_calibration:
+        out["copy_calibration_bytes"] = copy_calibration(torch)
+    if not args.no_peaks:
+        pk = measured_peaks(torch)
+        out["measured_peaks"] = pk
+        roofline["frac_of_measured_dense_matmul"] = roofline["achieved"] / pk["dense_bf16_matmul_tflops"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_train(wl, T, args.cpu_reps)
     print(json.dumps(out), flush=True)
@@ -494,6 +500,16 @@ def _hybrid_dense_operand(nm, torch, W, L, flags, tdt):
     f = torch.from_numpy(np.ascontiguousarray(flags, dtype=np.bool_)).to(W.device)
     mask = f.repeat_interleave(tr, dim=0)[:R].repeat_interleave(tc, dim=1)
     return torch.where(mask, W, pruned).t().contiguous()
+
+
+def copy_calibration(torch):
+    """One plain 256 MiB device copy: the dispatch a counter profile of the
+    same command scales its HBM byte counters against."""
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return src.numel() * 4
 
 
 def measured_peaks(torch):
@@ -832,11 +848,7 @@ def main():
         "source_hash": hsh,
     }
     if args.copy_calibration:
-        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = src.numel() * 4
+        out["copy_calibration_bytes"] = copy_calibration(torch)
     if not args.no_peaks:
         pk = measured_peaks(torch)
         out["measured_peaks"] = pk
