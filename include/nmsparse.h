@@ -83,7 +83,9 @@ typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP
 /* Version of this ABI (major * 100 + minor): 101 adds NM_I8 / NM_I32,
  * 102 adds NM_FP8; 200 replaces the process-wide nm_set_variant by the
  * per-call nm_spmm_variant and gives nm_spmm_perm a caller-owned workspace in
- * place of memory the library allocated. */
+ * place of memory the library allocated; 201 adds the hybrid tiles
+ * (nm_hybrid_*), the training products (nm_spmm_dx, nm_spmm_dw) and the
+ * block / diagonal structures (nm_block_*, nm_diag_*). */
 int nm_version(void);
 
 /* Short fixed text for a status code (never NULL). */
@@ -347,6 +349,65 @@ nm_status nm_hybrid_spmm(const void* values, const uint8_t* idx, const int64_t* 
                          int64_t R, int64_t K, int64_t tile_rows, int64_t tile_cols, int64_t values_count,
                          int64_t idx_bytes, int dtype, const void* act, int64_t T, int64_t ldx, void* Y,
                          int64_t ldy, int out_dtype, void* stream);
+
+/*
+ * The column permutation on two other host structures.  Source: searcharxiv
+ * author page, the SHUFFLESPARSE abstract (one learned permutation applied the
+ * same way to block, N:M and diagonal structures) and the DynaDiag abstract
+ * (a diagonal pattern); gist.science "Technische Samenvatting: SHUFFLESPARSE",
+ * section "2. Methodologie" (y = (W Pi) x, W following a fixed structured
+ * pattern) and the item "Efficiëntie bij Inferentie" (the hardened Pi as a
+ * precomputed index map on the structured kernel's input reads).  The pages
+ * name the structures only; the geometry and storage below are this
+ * library's.  Both products read act through perm the way nm_spmm_perm does,
+ * Y[t, r] = sum_k W[r, k] act[t, perm[k]] (perm NULL: act as it is; an entry
+ * outside [0, K) reads column K - 1), with fp32 accumulation; 16-bit weights
+ * (NM_F16, NM_BF16) and activations of the same type; Y [T, R] row-major,
+ * ldy >= R, out_dtype NM_F32 or the input dtype (RNE).  Every pointer 16-byte
+ * aligned, ldx and ldw multiples of 8, outputs not overlapping inputs
+ * (NM_ERR_ALIAS); stream-ordered, nothing allocated or synchronised.  act of
+ * 4 GiB or more is NM_ERR_SHAPE.
+ *
+ * Block-sparse: W [R, K] (R and K multiples of 32) cut into 32 x 32 blocks,
+ * each kept whole or dropped.  Stored as block-sparse rows:
+ *   row_ptr  int32 [R/32 + 1]: the kept blocks of block-row b are entries
+ *            row_ptr[b] .. row_ptr[b+1]-1;
+ *   col      int32 [nnzb]: their block-columns, ascending within a row;
+ *   values   [nnzb][32][32]: each kept block row-major, bits of W unchanged.
+ * nm_block_structure (host only, no device access) builds row_ptr and col
+ *   from mask[(R/32) * (K/32)] (host uint8, 1 keeps block (b, c) at
+ *   b*(K/32) + c); any output may be NULL (a size query); NM_ERR_SHAPE for a
+ *   bad shape or a mask entry other than 0 or 1.
+ * nm_block_compress copies the kept blocks of W (device, [R, K], ldw >= K)
+ *   into values (device, nnzb*2048 bytes); row_ptr and col on the device.
+ * nm_block_spmm: Y[t, r] = sum over kept blocks (r/32, c) of
+ *   sum_j values[blk][r%32][j] * act[t, perm[32c + j]]; act [T, K], ldx >= K;
+ *   perm int32 [K] or NULL.  Runs the kept blocks on the dense matrix cores.
+ * Entries of row_ptr or col outside their range are clamped on the device: a
+ * malformed structure gives wrong values but no access outside the arrays.
+ *
+ * Diagonal-sparse: W [R, K] non-zero only on D wrap-around diagonals with
+ * distinct offsets o_d in [0, K) (offsets int32 [D], any order; others are
+ * reduced mod K, and a repeated offset adds its diagonal twice): row r of
+ * diagonal d sits at column (r + o_d) mod K.  Stored as values [D][R],
+ * values[d][r] = W[r, (r + o_d) mod K].  K % 8 == 0, K <= 2048, 0 <= D <= K.
+ * nm_diag_compress gathers values from W (device, [R, K], ldw >= K).
+ * nm_diag_spmm: Y[t, r] = sum_d values[d][r] * act[t, perm[(r + o_d) mod K]].
+ *   Every row reads a different activation column per diagonal, so the
+ *   product runs on the vector ALUs (fp32 FMA), not the matrix cores.
+ */
+nm_status nm_block_structure(int64_t R, int64_t K, const uint8_t* mask, int32_t* row_ptr, int32_t* col,
+                             int64_t* nnzb);
+nm_status nm_block_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, const int32_t* row_ptr,
+                            const int32_t* col, int64_t nnzb, void* values, void* stream);
+nm_status nm_block_spmm(const void* values, const int32_t* row_ptr, const int32_t* col, int64_t nnzb, int64_t R,
+                        int64_t K, int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
+                        void* Y, int64_t ldy, int out_dtype, void* stream);
+nm_status nm_diag_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, const int32_t* offsets,
+                           int64_t D, void* values, void* stream);
+nm_status nm_diag_spmm(const void* values, const int32_t* offsets, int64_t D, int64_t R, int64_t K, int dtype,
+                       const void* act, int64_t T, int64_t ldx, const int32_t* perm, void* Y, int64_t ldy,
+                       int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,13 +8,18 @@ draw their inputs from here.
 Recipe (the same everywhere):
   * generator: numpy PCG64 seeded with the sequence [workload_id, tensor_id,
     variant]; tensor_id 0 = weight W, 1 = activations, 2 = permutation,
-    3 = hybrid tile flags, 4 = output gradient G (training products);
+    3 = hybrid tile flags, 4 = output gradient G (training products),
+    5 = kept-block mask, 6 = diagonal offsets;
   * W, activations and G: float32 standard normal times sigma, then rounded to
     the storage type with round-to-nearest-even (fp16 through numpy's cast,
     bf16 through the bit routine below);
   * permutation: a uniform random permutation of 0..K-1 (int32);
   * tile flags: each tile dense (1) when a uniform draw is below the given
-    fraction, else 2:4 (0).
+    fraction, else 2:4 (0);
+  * block mask: each 32 x 32 block kept (1) when a uniform draw is below the
+    kept fraction;
+  * diagonal offsets: D distinct offsets drawn uniformly from 0..K-1 without
+    replacement (int32, in the order drawn).
 
 Half-precision arrays are returned as their raw uint16 bit patterns, the form
 every consumer (oracle, C ABI) takes.
@@ -92,6 +97,18 @@ def normal_fp8(shape, scale: float, workload_id: int, tensor_id: int, variant: i
     return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def block_mask(grid_shape, keep_fraction: float, workload_id: int, variant: int = 0) -> np.ndarray:
+    """uint8 mask over a grid of 32 x 32 weight blocks: 1 (kept) with probability keep_fraction."""
+    rng = rng_for(workload_id, 5, variant)
+    return (rng.random(grid_shape) < keep_fraction).astype(np.uint8)
+
+
+def diag_offsets(K: int, D: int, workload_id: int, variant: int = 0) -> np.ndarray:
+    """D distinct diagonal offsets in [0, K), int32, in the order drawn."""
+    rng = rng_for(workload_id, 6, variant)
+    return rng.choice(int(K), size=int(D), replace=False).astype(np.int32)
+
+
 def tile_flags(tile_grid_shape, dense_fraction: float, workload_id: int, variant: int = 0) -> np.ndarray:
     """uint8 flags over a grid of weight tiles: 1 (dense) with probability dense_fraction."""
     rng = rng_for(workload_id, 3, variant)
@@ -118,6 +135,7 @@ class Workload:
     note: str = ""
     hybrid: tuple = ()  # (tile_rows, tile_cols, dense fraction) for hybrid dense / 2:4 tiles
     train: bool = False  # the training-side products (dX, dW) of the layer
+    host: tuple = ()  # ("block", kept fraction) or ("diag", D): the permutation on another structure
 
     def weights(self) -> np.ndarray:
         if self.dtype == I8:
@@ -142,6 +160,12 @@ class Workload:
     def permutation(self) -> np.ndarray | None:
         return random_permutation(self.K, self.wid) if self.permuted else None
 
+    def block_mask(self) -> np.ndarray:
+        return block_mask((self.R // 32, self.K // 32), self.host[1], self.wid)
+
+    def diag_offsets(self) -> np.ndarray:
+        return diag_offsets(self.K, self.host[1], self.wid)
+
     def tile_flags(self) -> np.ndarray:
         tr, tc, frac = self.hybrid
         return tile_flags((-(-self.R // tr), self.K // tc), frac, self.wid)
@@ -151,8 +175,9 @@ class Workload:
 # measure: a small 2:4 example, a LLaMA-2-7B projection at prefill and at
 # decode, the general 1:4 / 1:8 forms, a ViT-B/16 MLP fc1 over 64 images of
 # 197 tokens with a learned column permutation, the prefill shape in INT8 and
-# in FP8 E4M3, the prefill shape with hybrid dense / 2:4 tiles, and the
-# prefill shape's training-side products.
+# in FP8 E4M3, the prefill shape with hybrid dense / 2:4 tiles, the prefill
+# shape's training-side products, and the permuted ViT layer on a block-sparse
+# and a diagonal-sparse weight at 90% sparsity.
 WORKLOADS = {
     1: Workload(1, "small-2of4-fp16", 256, 256, (64,), ((2, 4),), F16, 1.0,
                 note="2:4 fp16 small case"),
@@ -179,4 +204,13 @@ WORKLOADS = {
     # 2:4 pattern held): dX = G W_nm and the packed dW, G [2048, 4096] N(0, 1)
     9: Workload(9, "llama2-7b-proj-backward-2of4-bf16", 4096, 4096, (2048,), ((2, 4),), BF16, 0.02,
                 note="2:4 bf16 dX and packed dW", train=True),
+    # the permutation on two other host structures (SHUFFLESPARSE's ViT-B/16
+    # setting at 90% sparsity): 10% of the 32 x 32 blocks kept, or 77 of 768
+    # diagonals (10% of each row), activations read through a permutation
+    10: Workload(10, "vit-b16-fc1-perm-block-fp16", 3072, 768, (12608,), ((2, 4),), F16, 0.02,
+                 permuted=True, note="block-sparse 32x32, 10% kept, with column permutation",
+                 host=("block", 0.1)),
+    11: Workload(11, "vit-b16-fc1-perm-diag-fp16", 3072, 768, (12608,), ((2, 4),), F16, 0.02,
+                 permuted=True, note="diagonal-sparse, 77 of 768 diagonals, with column permutation",
+                 host=("diag", 77)),
 }

@@ -17,7 +17,8 @@ import os
 __all__ = ["NM_OK", "NM_F16", "NM_BF16", "NM_F32", "NM_I8", "NM_I32", "NM_FP8", "NMError", "lib", "lib_path",
            "nm_packed_sizes", "nm_compress", "nm_decompress", "nm_spmm", "nm_spmm_perm",
            "nm_spmm_perm_workspace_size", "nm_spmm_perm_static", "nm_check_perm", "nm_spmm_dx", "nm_spmm_dw",
-           "PATTERNS"]
+           "nm_hybrid_layout", "nm_hybrid_compress", "nm_hybrid_spmm", "nm_block_structure", "nm_block_compress",
+           "nm_block_spmm", "nm_diag_compress", "nm_diag_spmm", "PATTERNS"]
 
 NM_OK = 0
 NM_F16, NM_BF16, NM_F32, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
@@ -85,6 +86,16 @@ def lib() -> ctypes.CDLL:
     L.nm_hybrid_compress.argtypes = [vp, i64, i64, i64, i32, i64, i64, vp, vp, i64, i64, vp, vp, vp]
     L.nm_hybrid_spmm.restype = i32
     L.nm_hybrid_spmm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, i64, vp, i64, i32, vp]
+    L.nm_block_structure.restype = i32
+    L.nm_block_structure.argtypes = [i64, i64, vp, vp, vp, ctypes.POINTER(i64)]
+    L.nm_block_compress.restype = i32
+    L.nm_block_compress.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp, vp]
+    L.nm_block_spmm.restype = i32
+    L.nm_block_spmm.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i64, i64, vp, vp, i64, i32, vp]
+    L.nm_diag_compress.restype = i32
+    L.nm_diag_compress.argtypes = [vp, i64, i64, i64, i32, vp, i64, vp, vp]
+    L.nm_diag_spmm.restype = i32
+    L.nm_diag_spmm.argtypes = [vp, vp, i64, i64, i64, i32, vp, i64, i64, vp, vp, i64, i32, vp]
     _lib = L
     return L
 
@@ -456,4 +467,129 @@ def nm_hybrid_spmm(values, idx, layout: HybridLayout, act, out_dtype=None, out=N
                                 layout.tile_rows, layout.tile_cols, layout.values_count, layout.idx_bytes, dt,
                                 act.data_ptr(), T, act.stride(0), out.data_ptr(), out.stride(0), od,
                                 _stream_ptr(act.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The column permutation on block-sparse and diagonal-sparse weights
+# ---------------------------------------------------------------------------
+
+def _out16(torch, dt, out_dtype, what):
+    if dt not in (NM_F16, NM_BF16):
+        raise TypeError(f"{what} take float16 or bfloat16 weights")
+    if out_dtype is None or out_dtype == torch.float32:
+        return NM_F32
+    od = _dtype_code(torch.empty(0, dtype=out_dtype))
+    if od != dt:
+        raise TypeError("out_dtype must be float32 or the weights' dtype")
+    return od
+
+
+def _int32_vector(t, n, name, device):
+    torch = _torch()
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or (n is not None and t.numel() != n) \
+            or t.device != device:
+        size = f"[{n}] " if n is not None else ""
+        raise ValueError(f"{name} must be a contiguous int32 {size}tensor on {device}")
+
+
+def _product_out(torch, out, T, R, od, device):
+    if out is not None:
+        _row_major(out, "out")
+        if out.dtype != _torch_dtype(od) or tuple(out.shape) != (T, R) or out.device != device:
+            raise ValueError(f"out must be a [{T}, {R}] {_torch_dtype(od)} tensor on {device}")
+        return out
+    return torch.empty((T, R), dtype=_torch_dtype(od), device=device)
+
+
+def nm_block_structure(R: int, K: int, mask):
+    """(row_ptr int32 [R/32 + 1], col int32 [nnzb]) as numpy arrays, from a host
+    mask over the 32 x 32 block grid ([R/32, K/32], 1 keeps a block)."""
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8).reshape(-1))
+    if R % 32 == 0 and K % 32 == 0 and m.size != (R // 32) * (K // 32):
+        raise ValueError(f"mask must have {(R // 32) * (K // 32)} entries")
+    n = ctypes.c_int64()
+    _check(lib().nm_block_structure(R, K, m.ctypes.data if m.size else None, None, None, ctypes.byref(n)))
+    row_ptr = np.zeros(R // 32 + 1, dtype=np.int32)
+    col = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(lib().nm_block_structure(R, K, m.ctypes.data if m.size else None, row_ptr.ctypes.data,
+                                    col.ctypes.data, None))
+    return row_ptr, col[:n.value]
+
+
+def nm_block_compress(W, row_ptr, col):
+    """values [nnzb, 32, 32]: the kept blocks of W (row_ptr, col: int32 device tensors)."""
+    torch = _torch()
+    _row_major(W, "W")
+    R, K = W.shape
+    dt = _dtype_code(W)
+    _int32_vector(row_ptr, R // 32 + 1, "row_ptr", W.device)
+    _int32_vector(col, None, "col", W.device)
+    _require_cuda(W, row_ptr, col)
+    nnzb = col.numel()
+    values = torch.empty((nnzb, 32, 32), dtype=W.dtype, device=W.device)
+    _check(lib().nm_block_compress(W.data_ptr(), R, K, W.stride(0), dt, row_ptr.data_ptr(),
+                                   col.data_ptr() or None, nnzb, values.data_ptr() or None, _stream_ptr(W.device)))
+    return values
+
+
+def nm_block_spmm(values, row_ptr, col, act, perm=None, out_dtype=None, out=None):
+    """Y [T, R] = act read through perm times the block-sparse W^T (R = 32 * (row_ptr.numel() - 1))."""
+    torch = _torch()
+    _row_major(act, "act")
+    T, K = act.shape
+    R = 32 * (row_ptr.numel() - 1)
+    dt = _dtype_code(act)
+    od = _out16(torch, dt, out_dtype, "block products")
+    nnzb = col.numel()
+    if values.dtype != act.dtype or tuple(values.shape) != (nnzb, 32, 32) or not values.is_contiguous() \
+            or values.device != act.device:
+        raise ValueError(f"values must be a contiguous [{nnzb}, 32, 32] {act.dtype} tensor on {act.device}")
+    _int32_vector(row_ptr, None, "row_ptr", act.device)
+    _int32_vector(col, None, "col", act.device)
+    if perm is not None:
+        _int32_vector(perm, K, "perm", act.device)
+    out = _product_out(torch, out, T, R, od, act.device)
+    _require_cuda(values, row_ptr, col, act, out, *(t for t in (perm,) if t is not None))
+    _check(lib().nm_block_spmm(values.data_ptr() or None, row_ptr.data_ptr(), col.data_ptr() or None, nnzb, R, K,
+                               dt, act.data_ptr(), T, act.stride(0),
+                               perm.data_ptr() if perm is not None else None, out.data_ptr(), out.stride(0), od,
+                               _stream_ptr(act.device)))
+    return out
+
+
+def nm_diag_compress(W, offsets):
+    """values [D, R]: values[d, r] = W[r, (r + offsets[d]) mod K] (offsets: int32 device tensor)."""
+    torch = _torch()
+    _row_major(W, "W")
+    R, K = W.shape
+    dt = _dtype_code(W)
+    _int32_vector(offsets, None, "offsets", W.device)
+    _require_cuda(W, offsets)
+    D = offsets.numel()
+    values = torch.empty((D, R), dtype=W.dtype, device=W.device)
+    _check(lib().nm_diag_compress(W.data_ptr(), R, K, W.stride(0), dt, offsets.data_ptr() or None, D,
+                                  values.data_ptr() or None, _stream_ptr(W.device)))
+    return values
+
+
+def nm_diag_spmm(values, offsets, act, perm=None, out_dtype=None, out=None):
+    """Y [T, R] = act read through perm times the diagonal-sparse W^T (R = values.shape[1])."""
+    torch = _torch()
+    _row_major(act, "act")
+    T, K = act.shape
+    D, R = values.shape
+    dt = _dtype_code(act)
+    od = _out16(torch, dt, out_dtype, "diagonal products")
+    if values.dtype != act.dtype or not values.is_contiguous() or values.device != act.device:
+        raise ValueError(f"values must be a contiguous [D, R] {act.dtype} tensor on {act.device}")
+    _int32_vector(offsets, D, "offsets", act.device)
+    if perm is not None:
+        _int32_vector(perm, K, "perm", act.device)
+    out = _product_out(torch, out, T, R, od, act.device)
+    _require_cuda(values, offsets, act, out, *(t for t in (perm,) if t is not None))
+    _check(lib().nm_diag_spmm(values.data_ptr() or None, offsets.data_ptr() or None, D, R, K, dt, act.data_ptr(),
+                              T, act.stride(0), perm.data_ptr() if perm is not None else None, out.data_ptr(),
+                              out.stride(0), od, _stream_ptr(act.device)))
     return out

@@ -263,7 +263,7 @@ hipError_t ensure_lds_limit(const void* kern, int bytes) {
 
 extern "C" {
 
-int nm_version(void) { return 200; }
+int nm_version(void) { return 201; }
 
 const char* nm_status_string(int status) {
   switch (status) {
@@ -647,6 +647,191 @@ nm_status nm_hybrid_spmm(const void* values, const uint8_t* idx, const int64_t* 
   a.ldy = ldy;
   a.out_dtype = out_dtype;
   return hip_status(nm::launch_hybrid_spmm(a, static_cast<hipStream_t>(stream)), "nm_hybrid_spmm launch");
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse and diagonal-sparse structures with the column permutation
+// ---------------------------------------------------------------------------
+static nm_status check_block_shape(int64_t R, int64_t K) {
+  if (R < 0 || R > kMaxRT || R % 32)
+    return fail(NM_ERR_SHAPE, "R = %lld must be a multiple of 32 in [0, 2^30]", (long long)R);
+  if (K < 32 || K > kMaxK || K % 32)
+    return fail(NM_ERR_SHAPE, "K = %lld must be a multiple of 32 in [32, 2^24]", (long long)K);
+  return NM_OK;
+}
+
+static nm_status check_host_product(int dtype, int out_dtype, int64_t R, int64_t K, int64_t T, int64_t ldx,
+                                    int64_t ldy) {
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "block / diagonal products take NM_F16 or NM_BF16, not dtype %d", dtype);
+  if (out_dtype != NM_F32 && out_dtype != dtype)
+    return fail(NM_ERR_UNSUPPORTED, "out_dtype %d must be NM_F32 or the input dtype", out_dtype);
+  if (T < 0 || T > kMaxRT) return fail(NM_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (ldx < K) return fail(NM_ERR_STRIDE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldy < R) return fail(NM_ERR_STRIDE, "ldy = %lld < R = %lld", (long long)ldy, (long long)R);
+  if (ldx > kMaxElems || ldy > kMaxElems) return fail(NM_ERR_SHAPE, "leading dimension above 2^40 elements");
+  if (T * ldx > kMaxElems || T * ldy > kMaxElems) return fail(NM_ERR_SHAPE, "T*ld too large");
+  if (int64_t(extent(T, K, ldx, 2)) >= (int64_t(1) << 32))
+    return fail(NM_ERR_SHAPE, "act of 4 GiB or more (its reads use 32-bit offsets)");
+  return NM_OK;
+}
+
+nm_status nm_block_structure(int64_t R, int64_t K, const uint8_t* mask, int32_t* row_ptr, int32_t* col,
+                             int64_t* nnzb) {
+  nm_status st = check_block_shape(R, K);
+  if (st != NM_OK) return st;
+  const int64_t RB = R / 32, KB = K / 32;
+  if (RB * KB > 0 && !mask) return fail(NM_ERR_NULL, "mask must be non-NULL");
+  int64_t n = 0;
+  for (int64_t b = 0; b < RB; ++b) {
+    if (row_ptr) row_ptr[b] = int32_t(n);
+    for (int64_t c = 0; c < KB; ++c) {
+      const uint8_t f = mask[b * KB + c];
+      if (f > 1) return fail(NM_ERR_SHAPE, "mask[%lld] = %d is neither 0 nor 1", (long long)(b * KB + c), f);
+      if (f) {
+        if (col) col[n] = int32_t(c);
+        ++n;
+      }
+    }
+  }
+  if (n > (int64_t(1) << 21)) return fail(NM_ERR_SHAPE, "more than 2^21 kept blocks (values of 4 GiB)");
+  if (row_ptr) row_ptr[RB] = int32_t(n);
+  if (nnzb) *nnzb = n;
+  return ok();
+}
+
+nm_status nm_block_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, const int32_t* row_ptr,
+                            const int32_t* col, int64_t nnzb, void* values, void* stream) {
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "block structures take NM_F16 or NM_BF16 weights, not dtype %d", dtype);
+  nm_status st = check_block_shape(R, K);
+  if (st != NM_OK) return st;
+  if (nnzb < 0 || nnzb > (R / 32) * (K / 32))
+    return fail(NM_ERR_SHAPE, "nnzb = %lld outside [0, blocks of W]", (long long)nnzb);
+  if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw > kMaxElems || R * ldw > kMaxElems) return fail(NM_ERR_SHAPE, "R*ldw too large");
+  if (R == 0 || nnzb == 0) return ok();
+  if (!W || !row_ptr || !col || !values) return fail(NM_ERR_NULL, "W, row_ptr, col and values must be non-NULL");
+  if (ldw % 8) return fail(NM_ERR_ALIGN, "ldw = %lld is not a multiple of 8", (long long)ldw);
+  if (!aligned16(W) || !aligned16(values) || !aligned16(row_ptr) || !aligned16(col))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t vbytes = size_t(nnzb) * 2048;
+  if (overlaps(values, vbytes, W, extent(R, K, ldw, 2)) || overlaps(values, vbytes, row_ptr, size_t(R / 32 + 1) * 4) ||
+      overlaps(values, vbytes, col, size_t(nnzb) * 4))
+    return fail(NM_ERR_ALIAS, "values overlaps an input");
+  return hip_status(nm::launch_block_pack(static_cast<const uint16_t*>(W), ldw, R, K, row_ptr, col, nnzb,
+                                          static_cast<uint16_t*>(values), static_cast<hipStream_t>(stream)),
+                    "nm_block_compress launch");
+}
+
+nm_status nm_block_spmm(const void* values, const int32_t* row_ptr, const int32_t* col, int64_t nnzb, int64_t R,
+                        int64_t K, int dtype, const void* act, int64_t T, int64_t ldx, const int32_t* perm,
+                        void* Y, int64_t ldy, int out_dtype, void* stream) {
+  nm_status st = check_block_shape(R, K);
+  if (st != NM_OK) return st;
+  st = check_host_product(dtype, out_dtype, R, K, T, ldx, ldy);
+  if (st != NM_OK) return st;
+  if (nnzb < 0 || nnzb > (R / 32) * (K / 32))
+    return fail(NM_ERR_SHAPE, "nnzb = %lld outside [0, blocks of W]", (long long)nnzb);
+  if (R == 0 || T == 0) return ok();
+  if (!row_ptr || !act || !Y || (nnzb > 0 && (!values || !col)))
+    return fail(NM_ERR_NULL, "row_ptr, act, Y (and values, col with kept blocks) must be non-NULL");
+  if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of 8", (long long)ldx);
+  if ((values && !aligned16(values)) || !aligned16(row_ptr) || (col && !aligned16(col)) || !aligned16(act) ||
+      !aligned16(Y) || (perm && !aligned16(perm)))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t ybytes = extent(T, R, ldy, elt_bytes(out_dtype)), abytes = extent(T, K, ldx, 2);
+  const size_t vbytes = size_t(nnzb) * 2048;
+  if (overlaps(Y, ybytes, values, vbytes) || overlaps(Y, ybytes, act, abytes) ||
+      overlaps(Y, ybytes, row_ptr, size_t(R / 32 + 1) * 4) || overlaps(Y, ybytes, col, size_t(nnzb) * 4) ||
+      overlaps(Y, ybytes, perm, perm ? size_t(K) * 4 : 0))
+    return fail(NM_ERR_ALIAS, "Y overlaps an input");
+  nm::HostArgs a;
+  a.diagonal = false;
+  a.values = static_cast<const uint16_t*>(values);
+  a.values_bytes = vbytes;
+  a.row_ptr = row_ptr;
+  a.col = col;
+  a.nnz = nnzb;
+  a.R = R;
+  a.K = K;
+  a.dtype = dtype;
+  a.act = static_cast<const uint16_t*>(act);
+  a.act_bytes = abytes;
+  a.ldx = ldx;
+  a.T = T;
+  a.perm = perm;
+  a.out = Y;
+  a.ldy = ldy;
+  a.out_dtype = out_dtype;
+  return hip_status(nm::launch_host_spmm(a, static_cast<hipStream_t>(stream)), "nm_block_spmm launch");
+}
+
+static nm_status check_diag_shape(int64_t R, int64_t K, int64_t D) {
+  if (R < 0 || R > kMaxRT) return fail(NM_ERR_SHAPE, "R = %lld out of range", (long long)R);
+  if (K < 8 || K > nm::kDiagMaxK || K % 8)
+    return fail(NM_ERR_SHAPE, "K = %lld must be a multiple of 8 in [8, %lld]", (long long)K,
+                (long long)nm::kDiagMaxK);
+  if (D < 0 || D > K) return fail(NM_ERR_SHAPE, "D = %lld outside [0, K]", (long long)D);
+  return NM_OK;
+}
+
+nm_status nm_diag_compress(const void* W, int64_t R, int64_t K, int64_t ldw, int dtype, const int32_t* offsets,
+                           int64_t D, void* values, void* stream) {
+  if (dtype != NM_F16 && dtype != NM_BF16)
+    return fail(NM_ERR_UNSUPPORTED, "diagonal structures take NM_F16 or NM_BF16 weights, not dtype %d", dtype);
+  nm_status st = check_diag_shape(R, K, D);
+  if (st != NM_OK) return st;
+  if (ldw < K) return fail(NM_ERR_STRIDE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw > kMaxElems || R * ldw > kMaxElems) return fail(NM_ERR_SHAPE, "R*ldw too large");
+  if (R == 0 || D == 0) return ok();
+  if (!W || !offsets || !values) return fail(NM_ERR_NULL, "W, offsets and values must be non-NULL");
+  if (!aligned16(W) || !aligned16(values) || !aligned16(offsets))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t vbytes = size_t(D) * size_t(R) * 2;
+  if (overlaps(values, vbytes, W, extent(R, K, ldw, 2)) || overlaps(values, vbytes, offsets, size_t(D) * 4))
+    return fail(NM_ERR_ALIAS, "values overlaps an input");
+  return hip_status(nm::launch_diag_pack(static_cast<const uint16_t*>(W), ldw, R, K, offsets, D,
+                                         static_cast<uint16_t*>(values), static_cast<hipStream_t>(stream)),
+                    "nm_diag_compress launch");
+}
+
+nm_status nm_diag_spmm(const void* values, const int32_t* offsets, int64_t D, int64_t R, int64_t K, int dtype,
+                       const void* act, int64_t T, int64_t ldx, const int32_t* perm, void* Y, int64_t ldy,
+                       int out_dtype, void* stream) {
+  nm_status st = check_diag_shape(R, K, D);
+  if (st != NM_OK) return st;
+  st = check_host_product(dtype, out_dtype, R, K, T, ldx, ldy);
+  if (st != NM_OK) return st;
+  if (R == 0 || T == 0) return ok();
+  if (!act || !Y || (D > 0 && (!values || !offsets)))
+    return fail(NM_ERR_NULL, "act, Y (and values, offsets with D > 0) must be non-NULL");
+  if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx = %lld is not a multiple of 8", (long long)ldx);
+  if ((values && !aligned16(values)) || (offsets && !aligned16(offsets)) || !aligned16(act) || !aligned16(Y) ||
+      (perm && !aligned16(perm)))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t ybytes = extent(T, R, ldy, elt_bytes(out_dtype)), abytes = extent(T, K, ldx, 2);
+  if (overlaps(Y, ybytes, values, size_t(D) * size_t(R) * 2) || overlaps(Y, ybytes, act, abytes) ||
+      overlaps(Y, ybytes, offsets, size_t(D) * 4) || overlaps(Y, ybytes, perm, perm ? size_t(K) * 4 : 0))
+    return fail(NM_ERR_ALIAS, "Y overlaps an input");
+  nm::HostArgs a;
+  a.diagonal = true;
+  a.values = static_cast<const uint16_t*>(values);
+  a.values_bytes = size_t(D) * size_t(R) * 2;
+  a.offsets = offsets;
+  a.nnz = D;
+  a.R = R;
+  a.K = K;
+  a.dtype = dtype;
+  a.act = static_cast<const uint16_t*>(act);
+  a.act_bytes = abytes;
+  a.ldx = ldx;
+  a.T = T;
+  a.perm = perm;
+  a.out = Y;
+  a.ldy = ldy;
+  a.out_dtype = out_dtype;
+  return hip_status(nm::launch_host_spmm(a, static_cast<hipStream_t>(stream)), "nm_diag_spmm launch");
 }
 
 }  // extern "C"

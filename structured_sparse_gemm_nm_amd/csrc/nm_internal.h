@@ -131,6 +131,35 @@ constexpr int64_t kHybridMaxTileCols = 8192;  // tile-columns per row the produc
 hipError_t launch_hybrid_pack(const HybridArgs& a, hipStream_t s);
 hipError_t launch_hybrid_spmm(const HybridArgs& a, hipStream_t s);
 
+// The column permutation on block-sparse and diagonal-sparse weights
+// (nm_hosts.hip).  values_bytes and act_bytes bound the weight and activation
+// reads (both below 2^32); row_ptr / col entries are clamped into range on the
+// device, so a malformed structure gives wrong sums but no stray access.
+struct HostArgs {
+  bool diagonal = false;
+  const uint16_t* values = nullptr;
+  uint64_t values_bytes = 0;
+  const int32_t* row_ptr = nullptr;   // block
+  const int32_t* col = nullptr;
+  const int32_t* offsets = nullptr;   // diagonal
+  int64_t nnz = 0;                    // kept blocks, or diagonals
+  int64_t R = 0, K = 0;
+  int dtype = 0;
+  const uint16_t* act = nullptr;
+  uint64_t act_bytes = 0;
+  int64_t ldx = 0, T = 0;
+  const int32_t* perm = nullptr;      // NULL: act read as it is
+  void* out = nullptr;
+  int64_t ldy = 0;
+  int out_dtype = 0;
+};
+constexpr int64_t kDiagMaxK = 2048;   // the diagonal product stages 64 bytes per column in LDS
+hipError_t launch_block_pack(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, const int32_t* row_ptr,
+                             const int32_t* col, int64_t nnzb, uint16_t* values, hipStream_t s);
+hipError_t launch_diag_pack(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, const int32_t* offsets, int64_t D,
+                            uint16_t* values, hipStream_t s);
+hipError_t launch_host_spmm(const HostArgs& a, hipStream_t s);
+
 // Device properties and per-kernel launch set-up, kept per device and safe to
 // call from several host threads (nm_api.cpp).
 int device_cu_count();                 // CUs of the current device (256 if the query fails)

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
     assert {"nm_compress", "nm_spmm", "nm_spmm_perm", "nm_decompress", "nm_packed_sizes"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
-    assert L.nm_version() == 200
+    assert L.nm_version() == 201
     assert not hasattr(L, "nm_set_variant")  # no process-wide kernel state
 
 
@@ -421,3 +421,89 @@ def test_train_binding_checks_before_the_device():
         nm.nm_spmm_dw(i, G, a, 64, out_dtype=torch.bfloat16)
     with pytest.raises(ValueError):                     # CPU tensors never reach the C ABI
         nm.nm_spmm_dw(i, G, a, 64)
+
+
+def test_block_structure_matches_oracle():
+    from oracle import nm_hosts as H
+    rng = np.random.default_rng(4)
+    mask = (rng.random((5, 7)) < 0.4).astype(np.uint8)
+    mask[2] = 0                                   # an empty block-row
+    row_ptr, col = nm.nm_block_structure(160, 224, mask)
+    ref_ptr, ref_col = H.block_structure(mask)
+    assert row_ptr.tolist() == ref_ptr.tolist() and col.tolist() == ref_col.tolist()
+    L = nm.lib()
+    n = ctypes.c_int64()
+    assert L.nm_block_structure(100, 64, None, None, None, ctypes.byref(n)) == 2     # R % 32
+    assert L.nm_block_structure(64, 48, None, None, None, ctypes.byref(n)) == 2      # K % 32
+    assert L.nm_block_structure(64, 64, None, None, None, ctypes.byref(n)) == 1      # mask NULL
+    bad = np.array([1, 2, 0, 0], dtype=np.uint8)
+    assert L.nm_block_structure(64, 64, bad.ctypes.data, None, None, ctypes.byref(n)) == 2
+
+
+def test_block_and_diag_argument_errors():
+    # every call here fails validation (or has nothing to do) before any HIP call
+    L = nm.lib()
+    F = FAKE
+
+    def bs(v=F, rp=2 * F, col=3 * F, nnzb=4, R=64, K=96, dt=nm.NM_F16, act=4 * F, T=16, ldx=96, perm=None,
+           Y=5 * F, ldy=64, od=nm.NM_F32):
+        return L.nm_block_spmm(v, rp, col, nnzb, R, K, dt, act, T, ldx, perm, Y, ldy, od, None)
+    assert bs(dt=nm.NM_I8) == 3
+    assert bs(od=nm.NM_BF16) == 3
+    assert bs(R=48) == 2                                  # R % 32
+    assert bs(K=80, ldx=80) == 2                          # K % 32
+    assert bs(nnzb=7) == 2                                # more blocks than the grid holds
+    assert bs(ldx=64) == 4
+    assert bs(ldy=32) == 4
+    assert bs(T=0) == 0                                   # nothing enqueued
+    assert bs(rp=None) == 1
+    assert bs(v=None) == 1
+    assert bs(ldx=100) == 7
+    assert bs(perm=6 * F + 4) == 7
+    assert bs(Y=4 * F) == 5                               # Y overlaps act
+    assert bs(perm=5 * F + 64) == 5                       # Y overlaps the map
+
+    def bc(W=F, R=64, K=96, ldw=96, dt=nm.NM_BF16, rp=2 * F, col=3 * F, nnzb=4, v=4 * F):
+        return L.nm_block_compress(W, R, K, ldw, dt, rp, col, nnzb, v, None)
+    assert bc(dt=nm.NM_FP8) == 3
+    assert bc(ldw=64) == 4
+    assert bc(nnzb=0) == 0
+    assert bc(col=None) == 1
+    assert bc(ldw=100) == 7
+    assert bc(v=F + 64) == 5                              # values overlaps W
+
+    def ds(v=F, off=2 * F, D=8, R=100, K=64, dt=nm.NM_F16, act=3 * F, T=16, ldx=64, perm=None, Y=4 * F,
+           ldy=100, od=nm.NM_F32):
+        return L.nm_diag_spmm(v, off, D, R, K, dt, act, T, ldx, perm, Y, ldy, od, None)
+    assert ds(K=4096, ldx=4096) == 2                      # K above the staged limit
+    assert ds(K=60, ldx=64) == 2                          # K % 8
+    assert ds(D=65) == 2                                  # more diagonals than columns
+    assert ds(od=nm.NM_F16, dt=nm.NM_BF16) == 3
+    assert ds(ldy=64) == 4
+    assert ds(R=0) == 0
+    assert ds(off=None) == 1
+    assert ds(D=0, v=None, off=None, Y=None) == 1         # Y is still required
+    assert ds(act=3 * F + 8) == 7
+    assert ds(Y=3 * F) == 5
+
+    def dc(W=F, R=100, K=64, ldw=64, dt=nm.NM_F16, off=2 * F, D=8, v=3 * F):
+        return L.nm_diag_compress(W, R, K, ldw, dt, off, D, v, None)
+    assert dc(ldw=32) == 4
+    assert dc(D=0) == 0
+    assert dc(v=None) == 1
+    assert dc(v=F + 32) == 5                              # values overlaps W
+
+
+def test_block_and_diag_binding_checks_before_the_device():
+    torch = pytest.importorskip("torch")
+    act = torch.zeros((4, 64), dtype=torch.float16)
+    rp = torch.zeros(3, dtype=torch.int32)
+    col = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        nm.nm_block_spmm(torch.zeros((2, 32, 16), dtype=torch.float16), rp, col, act)   # block of the wrong shape
+    with pytest.raises(ValueError):
+        nm.nm_block_spmm(torch.zeros((2, 32, 32), dtype=torch.float16), rp.to(torch.int64), col, act)
+    with pytest.raises(ValueError):
+        nm.nm_diag_spmm(torch.zeros((3, 8), dtype=torch.float16), torch.zeros(2, dtype=torch.int32), act)
+    with pytest.raises(ValueError):
+        nm.nm_block_spmm(torch.zeros((2, 32, 32), dtype=torch.float16), rp, col, act)   # CPU tensors
