@@ -40,6 +40,7 @@ METRIC = "2:4 sparse GEMM dense-equivalent TFLOP/s and HBM GB/s; speedup vs dens
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0,
                     "f8e4m3": 5000.0}  # MI355X dense MFMA (int8: TOP/s), published
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (FMA = 2 FLOP), published
 
 
 def parse():
@@ -51,9 +52,10 @@ def parse():
                     help="dense-matmul load before the warmup, so the clock has settled "
                          "(an idle GPU takes about a second of load to reach it)")
     ap.add_argument("--workload", type=int, default=2,
-                    help="1..9 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8; "
+                    help="1..11 (default 2: prefill 4096x4096x2048; 6, 7: the same shape in INT8, FP8; "
                          "8: the same shape in hybrid dense / 2:4 tiles; 9: its training-side "
-                         "products dX and dW)")
+                         "products dX and dW; 10, 11: workload 5's permuted layer on a block-sparse and a "
+                         "diagonal-sparse weight)")
     ap.add_argument("--T", type=int, default=None, help="tokens (decode workload: 1, 8 or 16)")
     ap.add_argument("--pattern", default=None, help="n:m (workload 4: 1:4 or 1:8)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "half"])
@@ -300,6 +302,212 @@ def bench_hybrid(args, wl):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_hybrid(wl, T, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_host(wl, T, reps):
+    """The host-structure oracle as it stands (pack + the dense fp64 product of
+    the stored matrix with act read through perm) on the first 16384 tokens
+    (all of them at the workload's size), scaled to all T (the product is
+    linear in the token count)."""
+    from oracle import nm_hosts as H
+    kind, _ = wl.host
+    w = wl.weights()
+    perm = wl.permutation()
+    ts = min(T, 16384)
+    act = wl.activations(T)[:ts]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        if kind == "block":
+            row_ptr, col = H.block_structure(wl.block_mask())
+            vals = H.block_pack(w, row_ptr, col)
+            H.block_spmm_ref(vals, row_ptr, col, wl.R, wl.K, act, wl.dtype, perm=perm)
+        else:
+            offs = wl.diag_offsets()
+            vals = H.diag_pack(w, offs)
+            H.diag_spmm_ref(vals, offs, wl.R, wl.K, act, wl.dtype, perm=perm)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times) * T / ts
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"value": 2.0 * wl.R * wl.K * T / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{wl.R}x{wl.K}x{T} {kind}: pack, densify and fp64 product through perm over the first "
+                       f"{ts} of {T} tokens, scaled; median of {reps} runs")}
+
+
+def bench_host(args, wl):
+    """The permutation on a block-sparse or diagonal-sparse weight: one step =
+    nm_block_compress + nm_block_spmm (or the diagonal pair) with act read
+    through perm."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_nm_amd as nm
+
+    kind, param = wl.host
+    R, K = wl.R, wl.K
+    T = args.T if args.T is not None else wl.Ts[0]
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+    out_dtype = torch.float32 if args.out_dtype == "f32" else tdt
+    out_name = args.out_dtype
+    ob = 4 if out_name == "f32" else 2
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    W = dev(wl.weights())
+    perm = i32(wl.permutation())
+    if kind == "block":
+        row_ptr, col = nm.nm_block_structure(R, K, wl.block_mask())
+        rp, cl = i32(row_ptr), i32(col)
+        nnz = int(col.size)
+        vals = nm.nm_block_compress(W, rp, cl)
+        stored = nnz * 1024
+        struct_bytes = rp.numel() * 4 + cl.numel() * 4
+    else:
+        offs = i32(wl.diag_offsets())
+        nnz = int(offs.numel())
+        vals = nm.nm_diag_compress(W, offs)
+        stored = nnz * R
+        struct_bytes = nnz * 4
+    step_bytes = stored * 2 + T * K * 2 + T * R * ob
+    rotate = args.rotate if args.rotate is not None else max(1, min(64, -(-320_000_000 // step_bytes)))
+    acts = [dev(wl.activations(T))]
+    for _ in range(rotate - 1):
+        acts.append(acts[0].clone())
+    outs = [torch.empty((T, R), dtype=out_dtype, device="cuda") for _ in range(rotate)]
+    vbuf = torch.empty_like(vals)
+
+    def compress(c=0):
+        if kind == "block":
+            nm.nm_block_compress(W, rp, cl, values=vbuf)
+        else:
+            nm.nm_diag_compress(W, offs, values=vbuf)
+
+    def product(c=0, p=perm, odt=out_dtype, out=None):
+        o = outs[c % rotate] if out is None else out
+        if kind == "block":
+            return nm.nm_block_spmm(vals, rp, cl, acts[c % rotate], perm=p, out_dtype=odt, out=o)
+        return nm.nm_diag_spmm(vals, offs, acts[c % rotate], perm=p, out_dtype=odt, out=o)
+
+    settle = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    tw = time.perf_counter()
+    while (time.perf_counter() - tw) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            torch.matmul(settle, settle)
+        torch.cuda.synchronize()
+    del settle
+    for i in range(args.warmup):
+        compress(i)
+    for i in range(args.warmup):
+        product(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    start.record()
+    for i in range(args.steps):
+        compress(i)
+    mid.record()
+    for i in range(args.steps):
+        product(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    compress_us = start.elapsed_time(mid) * 1e3 / args.steps
+    spmm_us = mid.elapsed_time(end) * 1e3 / args.steps
+
+    # dense hipBLASLt product on the stored matrix densified (act @ W_hat^T),
+    # the same product without the map, and half output, in alternating blocks
+    if kind == "block":
+        W_hat = torch.zeros_like(W)
+        mask = torch.from_numpy(np.kron(wl.block_mask(), np.ones((32, 32), dtype=np.uint8)).astype(bool)).cuda()
+        W_hat[mask] = W[mask]
+    else:
+        cols = (torch.arange(R, device="cuda")[None, :] + offs.long()[:, None]) % K
+        W_hat = torch.zeros_like(W)
+        W_hat[torch.arange(R, device="cuda")[None, :].expand_as(cols), cols] = vals
+    W_hat_t = W_hat.t().contiguous()
+    half_out = torch.empty((T, R), dtype=tdt, device="cuda")
+    loops = {"spmm": lambda c: product(c), "compress": compress,
+             "spmm_no_perm": lambda c: product(c, p=None),
+             "spmm_half": lambda c: product(c, odt=tdt, out=half_out),
+             "dense_half": lambda c: torch.mm(acts[c % rotate], W_hat_t),
+             "dense_f32": lambda c: torch.mm(acts[c % rotate], W_hat_t, out_dtype=torch.float32)}
+    iters = max(20, args.steps)
+    for name in list(loops):
+        try:
+            for i in range(3):
+                loops[name](i)
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"{name} unavailable: {e}", file=sys.stderr)
+            del loops[name]
+    samples = {name: [] for name in loops}
+    for _ in range(5):
+        for name, fn in loops.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(iters):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            samples[name].append(a.elapsed_time(b) * 1e3 / iters)
+    loop_us = {name: float(np.median(v)) for name, v in samples.items()}
+
+    def ratio(x, y):
+        return loop_us[x] / loop_us[y] if x in loop_us and y in loop_us else None
+
+    flop = 2.0 * stored * T                     # one MAC per stored weight and token
+    nbytes = stored * 2 + struct_bytes + T * K * 2 + T * R * ob + K * 4
+    kname = "nm_block_spmm" if kind == "block" else "nm_diag_spmm"
+    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
+               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
+    hsh = source_hash(lib_src)
+    if kind == "block":
+        ach = nbytes / (spmm_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS}
+    else:
+        ach = flop / (spmm_us * 1e-6) / 1e12
+        roofline = {"bound": "alu", "achieved": ach, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": ach / PEAK_FP32_VALU_TFLOPS}
+    roofline.update({"traffic": traffic_from_profile(f"host_{kind}_w{wl.wid}_T{T}_{out_name}", hsh), "kernel": kname,
+                     "per_launch": {"flop": flop, "bytes": nbytes, "mean_us": spmm_us}})
+    out = {
+        "metric": METRIC, "value": 2.0 * R * K * T / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,sigma) W and act, seeded structure and permutation)",
+        "config": {"workload": wl.name, "R": R, "K": K, "T": T, "structure": kind,
+                   ("kept_blocks" if kind == "block" else "diagonals"): nnz,
+                   "density": stored / (R * K), "out_dtype": out_name, "rotate": rotate,
+                   "step": f"{'nm_block_compress' if kind == 'block' else 'nm_diag_compress'} + {kname} (perm)",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {
+            f"{kname}_us_in_step": spmm_us, "compress_us_in_step": compress_us,
+            f"{kname}_us_loop": loop_us.get("spmm"), f"{kname}_no_perm_us": loop_us.get("spmm_no_perm"),
+            f"{kname}_half_out_us": loop_us.get("spmm_half"), "compress_us": loop_us.get("compress"),
+            "dense_half_out_us": loop_us.get("dense_half"), "dense_f32_out_us": loop_us.get("dense_f32"),
+            "perm_overhead": (ratio("spmm", "spmm_no_perm") - 1.0) if ratio("spmm", "spmm_no_perm") else None,
+            "speedup_vs_dense_same_out_dtype": {k: v for k, v in {
+                "f32": ratio("dense_f32", "spmm") if out_name == "f32" else None,
+                "half": ratio("dense_half", "spmm_half")}.items() if v is not None},
+        },
+        "wall_s_timed": wall, "source_hash": hsh,
+    }
+    if args.copy_calibration:
+        out["copy_calibration_bytes"] = copy_calibration(torch)
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks(torch)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_host(wl, T, args.cpu_reps)
     print(json.dumps(out), flush=True)
 
 
@@ -567,6 +775,9 @@ def main():
         return
     if wl.train:
         bench_train(args, wl)
+        return
+    if wl.host:
+        bench_host(args, wl)
         return
     T = args.T if args.T is not None else wl.Ts[-1] if args.workload == 3 else wl.Ts[0]
     if args.pattern:

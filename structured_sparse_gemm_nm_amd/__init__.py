@@ -518,8 +518,9 @@ def nm_block_structure(R: int, K: int, mask):
     return row_ptr, col[:n.value]
 
 
-def nm_block_compress(W, row_ptr, col):
-    """values [nnzb, 32, 32]: the kept blocks of W (row_ptr, col: int32 device tensors)."""
+def nm_block_compress(W, row_ptr, col, values=None):
+    """values [nnzb, 32, 32]: the kept blocks of W (row_ptr, col: int32 device
+    tensors); a caller tensor `values` of that shape is filled in place."""
     torch = _torch()
     _row_major(W, "W")
     R, K = W.shape
@@ -528,7 +529,11 @@ def nm_block_compress(W, row_ptr, col):
     _int32_vector(col, None, "col", W.device)
     _require_cuda(W, row_ptr, col)
     nnzb = col.numel()
-    values = torch.empty((nnzb, 32, 32), dtype=W.dtype, device=W.device)
+    if values is None:
+        values = torch.empty((nnzb, 32, 32), dtype=W.dtype, device=W.device)
+    elif values.dtype != W.dtype or tuple(values.shape) != (nnzb, 32, 32) or not values.is_contiguous() \
+            or values.device != W.device:
+        raise ValueError(f"values must be a contiguous [{nnzb}, 32, 32] {W.dtype} tensor on {W.device}")
     _check(lib().nm_block_compress(W.data_ptr(), R, K, W.stride(0), dt, row_ptr.data_ptr(),
                                    col.data_ptr() or None, nnzb, values.data_ptr() or None, _stream_ptr(W.device)))
     return values
@@ -559,8 +564,9 @@ def nm_block_spmm(values, row_ptr, col, act, perm=None, out_dtype=None, out=None
     return out
 
 
-def nm_diag_compress(W, offsets):
-    """values [D, R]: values[d, r] = W[r, (r + offsets[d]) mod K] (offsets: int32 device tensor)."""
+def nm_diag_compress(W, offsets, values=None):
+    """values [D, R]: values[d, r] = W[r, (r + offsets[d]) mod K] (offsets: int32
+    device tensor); a caller tensor `values` of that shape is filled in place."""
     torch = _torch()
     _row_major(W, "W")
     R, K = W.shape
@@ -568,7 +574,11 @@ def nm_diag_compress(W, offsets):
     _int32_vector(offsets, None, "offsets", W.device)
     _require_cuda(W, offsets)
     D = offsets.numel()
-    values = torch.empty((D, R), dtype=W.dtype, device=W.device)
+    if values is None:
+        values = torch.empty((D, R), dtype=W.dtype, device=W.device)
+    elif values.dtype != W.dtype or tuple(values.shape) != (D, R) or not values.is_contiguous() \
+            or values.device != W.device:
+        raise ValueError(f"values must be a contiguous [{D}, {R}] {W.dtype} tensor on {W.device}")
     _check(lib().nm_diag_compress(W.data_ptr(), R, K, W.stride(0), dt, offsets.data_ptr() or None, D,
                                   values.data_ptr() or None, _stream_ptr(W.device)))
     return values

@@ -44,6 +44,18 @@ __device__ inline float half_to_f32(uint32_t h) {
   }
 }
 
+// c + a.lo * b.lo + a.hi * b.hi on two packed 16-bit values (v_dot2_f32_*).
+template <int DT>
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == NM_F16) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+  }
+}
+
 // XCD-aware order of a 1-D grid: the hardware deals workgroups to the 8 XCDs
 // round robin, so workgroup p runs on XCD p % 8; when the grid is a multiple
 // of 8 each XCD is given a contiguous run of logical tiles instead.
@@ -73,7 +85,8 @@ __global__ __launch_bounds__(256) void block_pack_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Block product.  A workgroup owns one block-row (32 rows) and 256 tokens;
+// Block product, direct (K above 2048, where a token tile's staged row would
+// not fit LDS).  A workgroup owns one block-row (32 rows) and 256 tokens;
 // wave w the tokens 64w .. 64w+63 (2 x 4 fragments of 16 x 16).  For each
 // kept block of the row (block-column c) the wave multiplies the block (K
 // step of 32) with its tokens' 32 activations of the block's columns, on
@@ -188,6 +201,147 @@ __global__ __launch_bounds__(256) void block_spmm_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Block product, staged: one workgroup per 32 tokens and every block-row.
+// The tile's activations are staged once in LDS as read through the map,
+// xs[t][j] = act[T0 + t][perm[j]] (rows of 2K + 16 bytes: the 16-byte B
+// operand reads of 16 consecutive tokens fall in distinct banks when K is a
+// multiple of 128; the map itself is copied to LDS behind the tile first), so
+// a kept block's B operands are plain 16-byte LDS reads
+// whatever the map.  (Gathering per block instead drags every cache line of
+// each token row in for every block, since a block's 32 mapped columns spread
+// over the whole row.)  Wave w then walks block-rows w, w + 4, ...: for each
+// kept block its two 16-row A fragments straight from global memory (the next
+// block's loaded while the current one is multiplied), its two 16-token B
+// fragments from LDS, four MFMAs; the block-row's 32 x 32 outputs go out
+// before the next block-row.  K <= 2048 (LDS); larger K takes the direct
+// kernel above.
+// ---------------------------------------------------------------------------
+constexpr int kStTok = 32;
+constexpr int64_t kBlockStagedMaxK = 2048;
+
+__host__ __device__ constexpr int staged_pitch(int K) { return 2 * K + 16; }
+
+template <int DT, int OUT, bool MAP>
+__global__ __launch_bounds__(256) void block_spmm_staged_kernel(
+    const uint16_t* __restrict__ values, uint32_t values_bytes, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col, int nnzb, int RB, int K, const uint16_t* __restrict__ act, uint32_t act_bytes,
+    int64_t ldx, int T, const int32_t* __restrict__ perm, void* __restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int T0 = blockIdx.x * kStTok;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  const int KB = K / 32, pitch = staged_pitch(K);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(values, values_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, act_bytes);
+
+  // ---- stage: item = 8 columns of one token, consecutive lanes along the
+  // row (one token row's reads stay within its cache lines); tokens past T
+  // are zeros.  The map is first copied to LDS (behind the tile), so an
+  // item's gathers wait on nothing but their own data, and four items' loads
+  // are in flight at a time.
+  const int per_row = K / 8, items = kStTok * per_row;
+  const int32_t* pl = reinterpret_cast<const int32_t*>(smem + kStTok * pitch);
+  if constexpr (MAP) {
+    for (int k = tid * 4; k < K; k += 1024)
+      *reinterpret_cast<u32x4*>(smem + kStTok * pitch + k * 4) = *reinterpret_cast<const u32x4*>(perm + k);
+    __syncthreads();
+  }
+  constexpr int kU = 4;
+  for (int it0 = tid; it0 < items; it0 += 256 * kU) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = min(it0 + 256 * u, items - 1);
+      const int t = it / per_row, j8 = (it - t * per_row) * 8;
+      const bool live = T0 + t < T;
+      const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
+      if constexpr (MAP) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h[e] = live ? __builtin_amdgcn_raw_buffer_load_b16(ra, rowoff + umin(uint32_t(pl[j8 + e]), uint32_t(K - 1)) * 2u, 0, 0)
+                      : 0u;
+        v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      } else {
+        v[u] = live ? __builtin_bit_cast(u32x4,
+                                         __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(j8) * 2u, 0, 0))
+                    : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = it0 + 256 * u;
+      if (it < items) {
+        const int t = it / per_row, j8 = (it - t * per_row) * 8;
+        *reinterpret_cast<u32x4*>(smem + t * pitch + j8 * 2) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool vec_ok = (ldy & 3) == 0;
+  for (int br = wave; br < RB; br += 4) {
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int begin = __builtin_amdgcn_readfirstlane(min(max(row_ptr[br], 0), nnzb));
+    const int end = __builtin_amdgcn_readfirstlane(min(max(row_ptr[br + 1], begin), nnzb));
+    auto load_a = [&](int blk, u32x4 (&a)[2]) {
+#pragma unroll
+      for (int fr = 0; fr < 2; ++fr)
+        a[fr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rv, uint32_t(((blk * 32 + fr * 16 + li) * 32 + 8 * lq) * 2), 0, 0));
+    };
+    u32x4 a[2], an[2];
+    if (begin < end) load_a(begin, a);
+    for (int blk = begin; blk < end; ++blk) {
+      const int c = __builtin_amdgcn_readfirstlane(min(max(col[blk], 0), KB - 1));
+      if (blk + 1 < end) load_a(blk + 1, an);
+      u32x4 b[2];
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft)
+        b[ft] = *reinterpret_cast<const u32x4*>(smem + (ft * 16 + li) * pitch + (32 * c + 8 * lq) * 2);
+#pragma unroll
+      for (int fr = 0; fr < 2; ++fr)
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) acc[fr][ft] = mfma32<DT>(a[fr], b[ft], acc[fr][ft]);
+      a[0] = an[0];
+      a[1] = an[1];
+    }
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const int t = T0 + ft * 16 + li;
+      if (t >= T) continue;
+#pragma unroll
+      for (int fr = 0; fr < 2; ++fr) {
+        const int r = br * 32 + fr * 16 + lq * 4;
+        const f32x4 v = acc[fr][ft];
+        if constexpr (OUT == NM_F32) {
+          float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
+          if (vec_ok) {
+            *reinterpret_cast<f32x4*>(y) = v;
+          } else {
+            for (int e = 0; e < 4; ++e) y[e] = v[e];
+          }
+        } else {
+          uint16_t* y = static_cast<uint16_t*>(Y) + int64_t(t) * ldy + r;
+          const uint32_t p0 = pack_half2<DT>(v[0], v[1]), p1 = pack_half2<DT>(v[2], v[3]);
+          if (vec_ok) {
+            *reinterpret_cast<u32x2*>(y) = u32x2{p0, p1};
+          } else {
+            const uint16_t hh[4] = {uint16_t(p0), uint16_t(p0 >> 16), uint16_t(p1), uint16_t(p1 >> 16)};
+            for (int e = 0; e < 4; ++e) y[e] = hh[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Diagonal pack: values[d][r] = W[r][(r + o_d) mod K], one thread per entry.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void diag_pack_kernel(const uint16_t* __restrict__ W, int64_t ldw, int R, int K,
@@ -204,25 +358,30 @@ __global__ __launch_bounds__(256) void diag_pack_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // Diagonal product.  Each output row needs, for every diagonal, one
 // activation column per token (a different one for every row), so the product
-// is not a tile contraction: it runs on the vector ALUs.  A workgroup owns
-// 256 rows (a thread each) and 32 tokens.  It first stages the 32 tokens'
-// activations in LDS column by column, xs[k][t] = act[T0 + t][perm[k]] (the
-// map is applied here, once per element, so the loop below reads plain
-// columns; 64 bytes per column, K <= 2048), then thread r walks the
-// diagonals: column c = (r + o_d) mod K, its 32 activations in four 16-byte
-// LDS reads, 32 fp32 FMAs with values[d][r].
+// is not a tile contraction: it runs on the vector ALUs.  A workgroup (512
+// threads) owns 32 tokens and every row.  It first stages the 32 tokens' activations in LDS
+// column by column, xs[k][t] = act[T0 + t][perm[k]] (the map is applied here,
+// once per element and token tile, so the loop below reads plain columns; 80
+// bytes per column, K <= 1792), then each thread takes rows tid, tid + 512,
+// ...: per diagonal the column c = (r + o_d) mod K and its 32 activations in
+// four 16-byte LDS reads; two diagonals at a time feed v_dot2_f32 (fp32
+// accumulation of the pair's exact products).
 // ---------------------------------------------------------------------------
 constexpr int kDiagTok = 32;
+// a column of the staged tile: 64 bytes of tokens and 16 of padding, so the
+// 16-byte reads of 16 threads on 16 consecutive columns fall in distinct
+// banks (at 64 bytes every fourth column shares banks: 4-way conflicts)
+constexpr int kDiagPitch = kDiagTok * 2 + 16;
+constexpr int kDiagThreads = 512;   // 8 waves: at two workgroups per CU, 4 waves per SIMD
 
 template <int DT, int OUT, bool MAP>
-__global__ __launch_bounds__(256) void diag_spmm_kernel(const uint16_t* __restrict__ values,
+__global__ __launch_bounds__(kDiagThreads) void diag_spmm_kernel(const uint16_t* __restrict__ values,
                                                         const int32_t* __restrict__ offsets, int D, int R, int K,
                                                         const uint16_t* __restrict__ act, uint32_t act_bytes,
                                                         int64_t ldx, int T, const int32_t* __restrict__ perm,
-                                                        void* __restrict__ Y, int64_t ldy, int tilesR) {
+                                                        void* __restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int R0 = (tile % tilesR) * 256, T0 = (tile / tilesR) * kDiagTok;
+  const int T0 = blockIdx.x * kDiagTok;
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, act_bytes);
 
@@ -230,7 +389,7 @@ __global__ __launch_bounds__(256) void diag_spmm_kernel(const uint16_t* __restri
   // order: token fastest, so the 32 lanes of a column group write its 64
   // contiguous bytes); tokens past T are zeros
   const int groups = kDiagTok * (K / 8);
-  for (int g = tid; g < groups; g += 256) {
+  for (int g = tid; g < groups; g += kDiagThreads) {
     const int t = g % kDiagTok, k8 = (g / kDiagTok) * 8;
     const bool live = T0 + t < T;
     const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
@@ -252,47 +411,96 @@ __global__ __launch_bounds__(256) void diag_spmm_kernel(const uint16_t* __restri
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint16_t*>(smem + (k8 + e) * (kDiagTok * 2) + t * 2) = uint16_t(h[e]);
+      *reinterpret_cast<uint16_t*>(smem + (k8 + e) * kDiagPitch + t * 2) = uint16_t(h[e]);
   }
   __syncthreads();
 
-  const int r = R0 + tid;
-  if (r >= R) return;
-  const int rk = r % K;
-  float acc[kDiagTok];
+  // the offsets, reduced into [0, K), go to LDS behind the tile
+  int32_t* offl = reinterpret_cast<int32_t*>(smem + K * kDiagPitch);
+  for (int d = tid; d < D; d += kDiagThreads) offl[d] = ((offsets[d] % K) + K) % K;
+  __syncthreads();
+
+  constexpr int kDC = 16;   // diagonals whose weights are loaded together
+  for (int r = tid; r < R; r += kDiagThreads) {
+    const int rk = r % K;
+    float acc[kDiagTok];
 #pragma unroll
-  for (int j = 0; j < kDiagTok; ++j) acc[j] = 0.f;
-  for (int d = 0; d < D; ++d) {
-    const int o = __builtin_amdgcn_readfirstlane(((offsets[d] % K) + K) % K);
-    int c = rk + o;
-    c -= c >= K ? K : 0;
-    const float w = half_to_f32<DT>(values[int64_t(d) * R + r]);
-    const u32x4* xs = reinterpret_cast<const u32x4*>(smem + c * (kDiagTok * 2));
+    for (int j = 0; j < kDiagTok; ++j) acc[j] = 0.f;
+    auto column = [&](int d) {
+      const int c = rk + offl[d];
+      return reinterpret_cast<const u32x4*>(smem + (c - (c >= K ? K : 0)) * kDiagPitch);
+    };
+    for (int d0 = 0; d0 < D; d0 += kDC) {
+      // this row's weights of diagonals d0 .. d0 + 15, all loads issued
+      // before the first is used (past D: zero, never read)
+      uint32_t wv[kDC];
 #pragma unroll
-    for (int q = 0; q < kDiagTok / 8; ++q) {
-      const u32x4 x = xs[q];
+      for (int i = 0; i < kDC; ++i) wv[i] = d0 + i < D ? uint32_t(values[int64_t(d0 + i) * R + r]) : 0u;
+      // two diagonals at a time: per token one v_dot2 on (w_d, w_d+1) and the
+      // token's two activations, paired by a byte permute: one VALU operation
+      // per multiply-add instead of a conversion and an FMA
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[8 * q + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[8 * q + 2 * e]);
-        acc[8 * q + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[8 * q + 2 * e + 1]);
+      for (int i = 0; i < kDC; i += 2) {
+        if (d0 + i + 1 < D) {
+          const u32x4* x1 = column(d0 + i);
+          const u32x4* x2 = column(d0 + i + 1);
+          const uint32_t wp = wv[i] | (wv[i + 1] << 16);
+#pragma unroll
+          for (int q = 0; q < kDiagTok / 8; ++q) {
+            const u32x4 a1 = x1[q], a2 = x2[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // v_perm_b32 byte selectors 0-3 take bytes of its second
+              // operand, 4-7 of its first: (low halves of a1, a2), (high halves)
+              const uint32_t lo = __builtin_amdgcn_perm(a2[e], a1[e], 0x05040100u);   // token 2i of both
+              const uint32_t hi = __builtin_amdgcn_perm(a2[e], a1[e], 0x07060302u);   // token 2i + 1
+              acc[8 * q + 2 * e] = dot2<DT>(wp, lo, acc[8 * q + 2 * e]);
+              acc[8 * q + 2 * e + 1] = dot2<DT>(wp, hi, acc[8 * q + 2 * e + 1]);
+            }
+          }
+        } else if (d0 + i < D) {
+          const u32x4* xs = column(d0 + i);
+          const float w = half_to_f32<DT>(wv[i]);
+#pragma unroll
+          for (int q = 0; q < kDiagTok / 8; ++q) {
+            const u32x4 x = xs[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[8 * q + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[8 * q + 2 * e]);
+              acc[8 * q + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[8 * q + 2 * e + 1]);
+            }
+          }
+        }
       }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < kDiagTok; ++j) {
-    const int t = T0 + j;
-    if (t >= T) break;
-    if constexpr (OUT == NM_F32) {
-      static_cast<float*>(Y)[int64_t(t) * ldy + r] = acc[j];
-    } else {
-      static_cast<uint16_t*>(Y)[int64_t(t) * ldy + r] = to_half_bits<DT>(acc[j]);
+    for (int j = 0; j < kDiagTok; ++j) {
+      const int t = T0 + j;
+      if (t >= T) break;
+      if constexpr (OUT == NM_F32) {
+        static_cast<float*>(Y)[int64_t(t) * ldy + r] = acc[j];
+      } else {
+        static_cast<uint16_t*>(Y)[int64_t(t) * ldy + r] = to_half_bits<DT>(acc[j]);
+      }
     }
   }
 }
 
 template <int DT, int OUT, bool MAP>
 hipError_t launch_block_cfg(const HostArgs& a, hipStream_t s) {
-  const int64_t RB = a.R / 32, tilesT = (a.T + kBlkTok - 1) / kBlkTok;
+  const int64_t RB = a.R / 32;
+  if (a.K <= kBlockStagedMaxK) {
+    const int64_t tiles = (a.T + kStTok - 1) / kStTok;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int lds = kStTok * staged_pitch(int(a.K)) + (MAP ? int(a.K) * 4 : 0);
+    auto kern = block_spmm_staged_kernel<DT, OUT, MAP>;
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(unsigned(tiles)), dim3(256), lds, s, a.values, uint32_t(a.values_bytes), a.row_ptr,
+                       a.col, int(a.nnz), int(RB), int(a.K), a.act, uint32_t(a.act_bytes), a.ldx, int(a.T), a.perm,
+                       a.out, a.ldy);
+    return hipGetLastError();
+  }
+  const int64_t tilesT = (a.T + kBlkTok - 1) / kBlkTok;
   if (RB * tilesT > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((block_spmm_kernel<DT, OUT, MAP>), dim3(unsigned(RB * tilesT)), dim3(256), 0, s, a.values,
                      uint32_t(a.values_bytes), a.row_ptr, a.col, int(a.nnz), int(RB), int(a.K), a.act,
@@ -302,14 +510,13 @@ hipError_t launch_block_cfg(const HostArgs& a, hipStream_t s) {
 
 template <int DT, int OUT, bool MAP>
 hipError_t launch_diag_cfg(const HostArgs& a, hipStream_t s) {
-  const int64_t tilesR = (a.R + 255) / 256, tilesT = (a.T + kDiagTok - 1) / kDiagTok;
-  if (tilesR * tilesT > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = size_t(a.K) * kDiagTok * 2;
+  const int64_t tiles = (a.T + kDiagTok - 1) / kDiagTok;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int lds = int(a.K) * kDiagPitch + int(a.nnz) * 4;   // the tile, then the offsets
   auto kern = diag_spmm_kernel<DT, OUT, MAP>;
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(unsigned(tilesR * tilesT)), dim3(256), lds, s, a.values, a.offsets, int(a.nnz),
-                     int(a.R), int(a.K), a.act, uint32_t(a.act_bytes), a.ldx, int(a.T), a.perm, a.out, a.ldy,
-                     int(tilesR));
+  hipLaunchKernelGGL(kern, dim3(unsigned(tiles)), dim3(kDiagThreads), lds, s, a.values, a.offsets, int(a.nnz), int(a.R),
+                     int(a.K), a.act, uint32_t(a.act_bytes), a.ldx, int(a.T), a.perm, a.out, a.ldy);
   return hipGetLastError();
 }
 

@@ -153,7 +153,7 @@ struct HostArgs {
   int64_t ldy = 0;
   int out_dtype = 0;
 };
-constexpr int64_t kDiagMaxK = 2048;   // the diagonal product stages 64 bytes per column in LDS
+constexpr int64_t kDiagMaxK = 1792;   // the diagonal product stages 80 bytes per column (and the offsets) in LDS
 hipError_t launch_block_pack(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, const int32_t* row_ptr,
                              const int32_t* col, int64_t nnzb, uint16_t* values, hipStream_t s);
 hipError_t launch_diag_pack(const uint16_t* W, int64_t ldw, int64_t R, int64_t K, const int32_t* offsets, int64_t D,

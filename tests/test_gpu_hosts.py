@@ -47,8 +47,10 @@ def block_case(R, K, T, keep, dt, seed):
     return w, act, mask, perm
 
 
+# K <= 2048 runs the staged kernel (a token tile staged once in LDS), larger K
+# the direct one
 BLOCK_SHAPES = [(64, 96, 5, 0.5), (256, 768, 300, 0.1), (160, 224, 257, 0.4), (32, 32, 1, 1.0),
-                (96, 512, 513, 1.0), (128, 256, 64, 0.0)]
+                (96, 512, 513, 1.0), (128, 256, 64, 0.0), (64, 2048, 45, 0.3), (96, 2112, 270, 0.2)]
 
 
 @pytest.mark.parametrize("R,K,T,keep", BLOCK_SHAPES)
@@ -156,7 +158,7 @@ def diag_case(R, K, T, D, dt, seed):
     return w, act, offs, perm
 
 
-DIAG_SHAPES = [(100, 64, 5, 8), (1000, 768, 300, 77), (257, 2048, 33, 300), (64, 64, 1, 64), (40, 128, 70, 1),
+DIAG_SHAPES = [(100, 64, 5, 8), (1000, 768, 300, 77), (257, 1792, 33, 300), (64, 64, 1, 64), (40, 128, 70, 1),
                (300, 96, 31, 0)]
 
 
