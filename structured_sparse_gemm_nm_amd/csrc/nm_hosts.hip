@@ -17,6 +17,8 @@
 #include "nm_device.h"
 #include "nm_internal.h"
 
+#include <type_traits>
+
 namespace nm {
 namespace {
 
@@ -218,6 +220,7 @@ __global__ __launch_bounds__(256) void block_spmm_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 constexpr int kStTok = 32;
 constexpr int64_t kBlockStagedMaxK = 2048;
+constexpr int kGatherLdsMaxK = 1024;   // the map applied by gathering within LDS up to this K
 
 __host__ __device__ constexpr int staged_pitch(int K) { return 2 * K + 16; }
 
@@ -237,46 +240,84 @@ __global__ __launch_bounds__(256) void block_spmm_staged_kernel(
 
   // ---- stage: item = 8 columns of one token, consecutive lanes along the
   // row (one token row's reads stay within its cache lines); tokens past T
-  // are zeros.  The map is first copied to LDS (behind the tile), so an
-  // item's gathers wait on nothing but their own data, and four items' loads
-  // are in flight at a time.
+  // are zeros.  With the map, K <= 1024: the rows are staged as they are
+  // (16-byte loads), then every thread gathers its items' mapped columns from
+  // LDS into registers and writes them back after a barrier; larger K gathers
+  // 2-byte pieces from global memory.  The map is copied to LDS (behind the
+  // tile) first, and four items' loads are in flight at a time.
   const int per_row = K / 8, items = kStTok * per_row;
   const int32_t* pl = reinterpret_cast<const int32_t*>(smem + kStTok * pitch);
+  auto stage = [&](auto gather_c) {
+    constexpr bool GATHER = decltype(gather_c)::value;
+    constexpr int kU = 4;
+    for (int it0 = tid; it0 < items; it0 += 256 * kU) {
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int it = min(it0 + 256 * u, items - 1);
+        const int t = it / per_row, j8 = (it - t * per_row) * 8;
+        const bool live = T0 + t < T;
+        const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
+        if constexpr (GATHER) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            h[e] = live ? __builtin_amdgcn_raw_buffer_load_b16(
+                              ra, rowoff + umin(uint32_t(pl[j8 + e]), uint32_t(K - 1)) * 2u, 0, 0)
+                        : 0u;
+          v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        } else {
+          v[u] = live ? __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(j8) * 2u, 0, 0))
+                      : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int it = it0 + 256 * u;
+        if (it < items) {
+          const int t = it / per_row, j8 = (it - t * per_row) * 8;
+          *reinterpret_cast<u32x4*>(smem + t * pitch + j8 * 2) = v[u];
+        }
+      }
+    }
+  };
   if constexpr (MAP) {
     for (int k = tid * 4; k < K; k += 1024)
       *reinterpret_cast<u32x4*>(smem + kStTok * pitch + k * 4) = *reinterpret_cast<const u32x4*>(perm + k);
     __syncthreads();
-  }
-  constexpr int kU = 4;
-  for (int it0 = tid; it0 < items; it0 += 256 * kU) {
-    u32x4 v[kU];
+    if (K <= kGatherLdsMaxK) {
+      stage(std::false_type{});
+      __syncthreads();
+      constexpr int kItems = kStTok * (kGatherLdsMaxK / 8) / 256;   // items per thread, at most
+      u32x4 v[kItems];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int it = min(it0 + 256 * u, items - 1);
-      const int t = it / per_row, j8 = (it - t * per_row) * 8;
-      const bool live = T0 + t < T;
-      const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
-      if constexpr (MAP) {
-        uint32_t h[8];
+      for (int u = 0; u < kItems; ++u) {
+        const int it = tid + 256 * u;
+        if (it < items) {
+          const int t = it / per_row, j8 = (it - t * per_row) * 8;
+          const unsigned char* row = smem + t * pitch;
+          uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          h[e] = live ? __builtin_amdgcn_raw_buffer_load_b16(ra, rowoff + umin(uint32_t(pl[j8 + e]), uint32_t(K - 1)) * 2u, 0, 0)
-                      : 0u;
-        v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-      } else {
-        v[u] = live ? __builtin_bit_cast(u32x4,
-                                         __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(j8) * 2u, 0, 0))
-                    : u32x4{0u, 0u, 0u, 0u};
+          for (int e = 0; e < 8; ++e)
+            h[e] = *reinterpret_cast<const uint16_t*>(row + umin(uint32_t(pl[j8 + e]), uint32_t(K - 1)) * 2u);
+          v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
       }
-    }
+      __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int it = it0 + 256 * u;
-      if (it < items) {
-        const int t = it / per_row, j8 = (it - t * per_row) * 8;
-        *reinterpret_cast<u32x4*>(smem + t * pitch + j8 * 2) = v[u];
+      for (int u = 0; u < kItems; ++u) {
+        const int it = tid + 256 * u;
+        if (it < items) {
+          const int t = it / per_row, j8 = (it - t * per_row) * 8;
+          *reinterpret_cast<u32x4*>(smem + t * pitch + j8 * 2) = v[u];
+        }
       }
+    } else {
+      stage(std::true_type{});
     }
+  } else {
+    stage(std::false_type{});
   }
   __syncthreads();
 
