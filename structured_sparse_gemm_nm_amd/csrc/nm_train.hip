@@ -352,29 +352,37 @@ __global__ __launch_bounds__(256, 2) void spmm_dx_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 // dW[r, s] = sum_t G[t, r] act[t, k(r, s)], computed as dense dW^T tiles
 // D[k][r] = sum_t act[t][k] G[t][r] of which each lane keeps the stored
-// entries.  A workgroup (4 waves, 2 x 2) owns 128 k x 128 r; a wave 64 x 64.
-// T is walked in chunks of 64 tokens; both tiles of a chunk, act's [64 t][128
-// k] and G's [64 t][128 r] (16 KB each, token rows of 256 bytes), are loaded
-// into registers two chunks ahead (8 16-byte pieces per thread) and written to
-// a double-buffered stage after the previous chunk's MFMAs, and both operands
-// come out by transpose reads: an operand lane needs 8 consecutive tokens of
-// one column.  (Staging from registers rather than by direct global->LDS
-// loads keeps the compiler from holding each transpose read until every
-// direct load in flight has landed.)  At 64 KB of LDS two workgroups share a
-// compute unit.  The 16-byte pieces of a row are XOR-swizzled, piece p of row t at
-// p ^ f(t), f(t) = 2 (t & 3) + 8 ((t >> 3) & 1), so the 8-byte transpose
-// reads of 32 lanes (rows 8g + j, g = 0, 1, j = 0..3) fall in distinct banks.
+// entries.  A workgroup (4 waves, 2 x 2) owns 256 k x 128 r; a wave 128 k x
+// 64 r (8 x 4 fragments), so one LDS byte feeds 43 MACs on average against
+// 32 at 64 x 64.  T is walked in chunks of 32 tokens (one MFMA K step): act's
+// [32 t][256 k] and G's [32 t][128 r] tiles are loaded into registers two
+// chunks ahead (6 16-byte pieces per thread) and written to a double-buffered
+// stage after the previous chunk's MFMAs; both operands come out by transpose
+// reads (an operand lane needs 8 consecutive tokens of one column).  Staging
+// from registers rather than by direct global->LDS loads keeps the compiler
+// from holding each transpose read until every direct load in flight has
+// landed.  Token row t of a tile starts at byte P t + 128 (((t >> 3) & 1) + (t
+// >> 4)), P = 544 (act, 512-byte rows) or 288 (G, 256-byte rows): the 8-byte
+// transpose reads of 32 lanes (rows 8g + j, g = 0, 1, j = 0..3) fall in
+// distinct banks (64 banks of 4 bytes), the lanes writing one row write its
+// bytes contiguously, and every fragment's address is a base register plus
+// a constant.  At 2 x 27 KB of LDS two workgroups share a compute unit.
 // A result lane (column r, quarter q) holds rows 4q..4q+3 of D, four
 // consecutive columns k of W's row r: a whole group of four, or half of one
 // of eight, whose stored positions it reads from the index bits and whose
 // survivors it writes to the packed gradient.
 // ---------------------------------------------------------------------------
-constexpr int kDwBK = 128, kDwBR = 128, kDwTC = 64;
-constexpr int kDwTile = kDwTC * 256;                    // 16 KB: 64 token rows of 256 bytes
-constexpr int kDwStage = 2 * kDwTile;                   // act tile, then G tile
-constexpr int kDwLds = 2 * kDwStage;                    // 64 KB
+constexpr int kDwBK = 256, kDwBR = 128, kDwTC = 32;
+constexpr int kDwFK = 8, kDwFR = 4;                    // fragments per wave along k and r
 
-__device__ inline int dw_swz(int t) { return ((t & 3) << 1) | (((t >> 3) & 1) << 3); }
+__host__ __device__ constexpr int dw_row(int t, int pitch) {
+  return t * pitch + (((t >> 3) & 1) + (t >> 4)) * 128;
+}
+constexpr int kDwActTile = dw_row(kDwTC - 1, 544) + 512;   // 17632 bytes
+constexpr int kDwGTile = dw_row(kDwTC - 1, 288) + 256;     // 9440 bytes
+constexpr int kDwStage = kDwActTile + kDwGTile;
+constexpr int kDwLds = 2 * kDwStage;
+static_assert(kDwActTile % 16 == 0 && kDwGTile % 16 == 0, "16-byte aligned tiles");
 
 template <int P, int DT, int OUT>
 __global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
@@ -394,89 +402,92 @@ __global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restr
   const int nchunks = (T + kDwTC - 1) / kDwTC;
   const int64_t S = int64_t(K) * N / M;
 
-  // Piece j (0..3) of a lane, in each tile: token row 4 (4 wave + j) + l / 16,
-  // LDS piece l % 16, which holds global piece (l % 16) ^ f(row).  Tokens past T read zeros, so they
-  // add nothing; columns past K or R are whatever the descriptor allows and
-  // only reach outputs that are dropped.
-  // (with T == 0 nothing is read: the descriptors cover no bytes)
+  // A thread's pieces of a chunk: act rows (tid / 32) + 8 j, piece tid % 32
+  // (j = 0..3), and G rows (tid / 16) + 16 j, piece tid % 16 (j = 0, 1).
+  // Tokens past T read zeros, so they add nothing; columns past K or R are
+  // whatever the descriptor allows and only reach outputs that are dropped
+  // (with T == 0 nothing is read: the descriptors cover no bytes).
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(act + K0, T > 0 ? uint32_t(((int64_t(T) - 1) * ldx + (K - K0)) * 2) : 0u);
   const __amdgpu_buffer_rsrc_t rg =
       make_rsrc(G + R0, T > 0 ? uint32_t(((int64_t(T) - 1) * ldg + (R - R0)) * 2) : 0u);
-  int lrow[4];
-  uint32_t aoff[4], goff[4];
+  int arow[4], grow[2];
+  uint32_t aoff[4], goff[2], aloff[4], gloff[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = 4 * (wave * 4 + j) + (lane >> 4);
-    const int piece = (lane & 15) ^ dw_swz(row);
-    lrow[j] = row;
-    aoff[j] = uint32_t(row) * uint32_t(ldx) * 2u + uint32_t(piece) * 16u;
-    goff[j] = uint32_t(row) * uint32_t(ldg) * 2u + uint32_t(piece) * 16u;
+    arow[j] = (tid >> 5) + 8 * j;
+    aoff[j] = uint32_t(arow[j]) * uint32_t(ldx) * 2u + uint32_t(tid & 31) * 16u;
+    aloff[j] = uint32_t(dw_row(arow[j], 544) + (tid & 31) * 16);
   }
-  auto load_chunk = [&](int chunk, u32x4 (&v)[8]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    grow[j] = (tid >> 4) + 16 * j;
+    goff[j] = uint32_t(grow[j]) * uint32_t(ldg) * 2u + uint32_t(tid & 15) * 16u;
+    gloff[j] = uint32_t(kDwActTile + dw_row(grow[j], 288) + (tid & 15) * 16);
+  }
+  auto load_chunk = [&](int chunk, u32x4 (&v)[6]) {
     const int t0 = chunk * kDwTC;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool live = t0 + lrow[j] < T;
+      const bool live = t0 + arow[j] < T;      // false for every chunk past the last
       v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            ra, live ? aoff[j] + uint32_t(t0) * uint32_t(ldx) * 2u : kDeadOff, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool live = t0 + grow[j] < T;
       v[4 + j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                rg, live ? goff[j] + uint32_t(t0) * uint32_t(ldg) * 2u : kDeadOff, 0, 0));
     }
   };
-  auto write_chunk = [&](int stage, const u32x4 (&v)[8]) {
+  auto write_chunk = [&](int stage, const u32x4 (&v)[6]) {
     unsigned char* st = smem + stage * kDwStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(st + (wave * 4 + j) * 1024 + lane * 16) = v[j];
-      *reinterpret_cast<u32x4*>(st + kDwTile + (wave * 4 + j) * 1024 + lane * 16) = v[4 + j];
-    }
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(st + aloff[j]) = v[j];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(st + gloff[j]) = v[4 + j];
   };
 
-  // transpose reads: lane L = 16g + 4j + a reads row 8g + j (+ 4) of the
-  // sub-step, columns 4a.. of a 16-column fragment
+  // transpose reads: lane L = 16g + 4j + a reads token rows 8g + j and
+  // 8g + j + 4, columns 4a.. of a 16-column fragment
   const int tr_row = 8 * (lane >> 4) + ((lane >> 2) & 3), tr_a = lane & 3;
-  auto read_tr = [&](const unsigned char* tileb, int h, int col0) {
-    const int col = col0 + 4 * tr_a;              // first of the 4 columns
-    const int piece = col >> 3, half = (col >> 2) & 1;
-    const int r1 = 32 * h + tr_row, r2 = r1 + 4;
-    const u32x2 lo = lds_read_tr(tileb + r1 * 256 + ((piece ^ dw_swz(r1)) * 16) + half * 8);
-    const u32x2 hi = lds_read_tr(tileb + r2 * 256 + ((piece ^ dw_swz(r2)) * 16) + half * 8);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  const int a_lo = dw_row(tr_row, 544) + 8 * tr_a, a_hi = dw_row(tr_row + 4, 544) + 8 * tr_a;
+  const int g_lo = kDwActTile + dw_row(tr_row, 288) + 8 * tr_a, g_hi = kDwActTile + dw_row(tr_row + 4, 288) + 8 * tr_a;
+  auto read_tr = [&](const unsigned char* st, int lo, int hi, int col0) {
+    const u32x2 l = lds_read_tr(st + lo + col0 * 2);
+    const u32x2 h = lds_read_tr(st + hi + col0 * 2);
+    return u32x4{l[0], l[1], h[0], h[1]};
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[kDwFK][kDwFR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kDwFK; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kDwFR; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // chunk 0 staged, chunks 1 and 2 in registers; step c (parity PAR, the loop
   // unrolled by two): the barrier publishes stage PAR and retires stage
   // PAR ^ 1; the step multiplies chunk c, stages chunk c+1 from register set
   // PAR ^ 1 and loads chunk c+3 into it (past the last chunk, zeros)
-  u32x4 vs[2][8];
+  u32x4 vs[2][6];
   load_chunk(0, vs[0]);
   load_chunk(1, vs[1]);
   write_chunk(0, vs[0]);
   load_chunk(2, vs[0]);
   auto step = [&](auto par_c, int c) {
     constexpr int PAR = decltype(par_c)::value;
-    u32x4 (&nextv)[8] = vs[PAR ^ 1];
+    u32x4 (&nextv)[6] = vs[PAR ^ 1];
     wait_lgkm0();
     barrier_no_fence();
     const unsigned char* st = smem + PAR * kDwStage;
+    u32x4 a[kDwFK];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 a[4], b[4];
+    for (int kf = 0; kf < kDwFK; ++kf) a[kf] = read_tr(st, a_lo, a_hi, wk * 128 + kf * 16);
 #pragma unroll
-      for (int kf = 0; kf < 4; ++kf) a[kf] = read_tr(st, h, wk * 64 + kf * 16);
+    for (int rf = 0; rf < kDwFR; ++rf) {
+      const u32x4 b = read_tr(st, g_lo, g_hi, wr * 64 + rf * 16);
 #pragma unroll
-      for (int rf = 0; rf < 4; ++rf) b[rf] = read_tr(st + kDwTile, h, wr * 64 + rf * 16);
-#pragma unroll
-      for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-        for (int rf = 0; rf < 4; ++rf) acc[kf][rf] = mfma32<DT>(a[kf], b[rf], acc[kf][rf]);
+      for (int kf = 0; kf < kDwFK; ++kf) acc[kf][rf] = mfma32<DT>(a[kf], b, acc[kf][rf]);
     }
     if (c + 1 < nchunks) write_chunk(PAR ^ 1, nextv);
     load_chunk(c + 3, nextv);
@@ -496,11 +507,11 @@ __global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restr
   // ---- epilogue: lane (r = li of the fragment, quarter q) holds D rows
   // 4q..4q+3, columns k..k+3 of W's row r
 #pragma unroll
-  for (int rf = 0; rf < 4; ++rf) {
+  for (int rf = 0; rf < kDwFR; ++rf) {
     const int r = R0 + wr * 64 + rf * 16 + li;
 #pragma unroll
-    for (int kf = 0; kf < 4; ++kf) {
-      const int k = K0 + wk * 64 + kf * 16 + lq * 4;
+    for (int kf = 0; kf < kDwFK; ++kf) {
+      const int k = K0 + wk * 128 + kf * 16 + lq * 4;
       if (r >= R || k >= K) continue;
       const f32x4 v = acc[kf][rf];
       const int g = k / M;                          // the group holding k .. k+3
