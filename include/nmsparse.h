@@ -390,7 +390,8 @@ nm_status nm_hybrid_spmm(const void* values, const uint8_t* idx, const int64_t* 
  * distinct offsets o_d in [0, K) (offsets int32 [D], any order; others are
  * reduced mod K, and a repeated offset adds its diagonal twice): row r of
  * diagonal d sits at column (r + o_d) mod K.  Stored as values [D][R],
- * values[d][r] = W[r, (r + o_d) mod K].  K % 8 == 0, K <= 1792, 0 <= D <= K.
+ * values[d][r] = W[r, (r + o_d) mod K].  K % 8 == 0, K <= 1792, 0 <= D <= K,
+ * values below 4 GiB.
  * nm_diag_compress gathers values from W (device, [R, K], ldw >= K).
  * nm_diag_spmm: Y[t, r] = sum_d values[d][r] * act[t, perm[(r + o_d) mod K]].
  *   Every row reads a different activation column per diagonal, so the

@@ -773,6 +773,7 @@ static nm_status check_diag_shape(int64_t R, int64_t K, int64_t D) {
     return fail(NM_ERR_SHAPE, "K = %lld must be a multiple of 8 in [8, %lld]", (long long)K,
                 (long long)nm::kDiagMaxK);
   if (D < 0 || D > K) return fail(NM_ERR_SHAPE, "D = %lld outside [0, K]", (long long)D);
+  if (D * R * 2 >= (int64_t(1) << 32)) return fail(NM_ERR_SHAPE, "values of 4 GiB or more (32-bit offsets)");
   return NM_OK;
 }
 

@@ -425,6 +425,7 @@ __global__ __launch_bounds__(kDiagThreads) void diag_spmm_kernel(const uint16_t*
   const int T0 = blockIdx.x * kDiagTok;
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, act_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(values, uint32_t(D) * uint32_t(R) * 2u);   // below 4 GiB
 
   // ---- stage: a thread fills 8 consecutive columns of one token (lane
   // order: token fastest, so the 32 lanes of a column group write its 64
@@ -471,46 +472,51 @@ __global__ __launch_bounds__(kDiagThreads) void diag_spmm_kernel(const uint16_t*
       const int c = rk + offl[d];
       return reinterpret_cast<const u32x4*>(smem + (c - (c >= K ? K : 0)) * kDiagPitch);
     };
-    for (int d0 = 0; d0 < D; d0 += kDC) {
-      // this row's weights of diagonals d0 .. d0 + 15, all loads issued
-      // before the first is used (past D: zero, never read)
+    // two diagonals at a time: per token one v_dot2 on (w_d, w_d+1) and the
+    // token's two activations, paired by a byte permute: one VALU operation
+    // per multiply-add instead of a conversion and an FMA
+    auto pair = [&](int d, uint32_t wp) {
+      const u32x4* x1 = column(d);
+      const u32x4* x2 = column(d + 1);
+#pragma unroll
+      for (int q = 0; q < kDiagTok / 8; ++q) {
+        const u32x4 a1 = x1[q], a2 = x2[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // v_perm_b32 byte selectors 0-3 take bytes of its second operand,
+          // 4-7 of its first: (low halves of a1, a2), then (high halves)
+          const uint32_t lo = __builtin_amdgcn_perm(a2[e], a1[e], 0x05040100u);   // token 2i of both
+          const uint32_t hi = __builtin_amdgcn_perm(a2[e], a1[e], 0x07060302u);   // token 2i + 1
+          acc[8 * q + 2 * e] = dot2<DT>(wp, lo, acc[8 * q + 2 * e]);
+          acc[8 * q + 2 * e + 1] = dot2<DT>(wp, hi, acc[8 * q + 2 * e + 1]);
+        }
+      }
+    };
+    auto weight = [&](int d) {
+      return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rw, uint32_t(d) * uint32_t(R) * 2u + uint32_t(r) * 2u, 0, 0));
+    };
+    // whole batches of kDC diagonals, their weights loaded before the first is
+    // used, then the remaining pairs, then an odd last diagonal: no branch
+    // inside a batch, so every accumulator is updated in place
+    int d = 0;
+    for (; d + kDC <= D; d += kDC) {
       uint32_t wv[kDC];
 #pragma unroll
-      for (int i = 0; i < kDC; ++i) wv[i] = d0 + i < D ? uint32_t(values[int64_t(d0 + i) * R + r]) : 0u;
-      // two diagonals at a time: per token one v_dot2 on (w_d, w_d+1) and the
-      // token's two activations, paired by a byte permute: one VALU operation
-      // per multiply-add instead of a conversion and an FMA
+      for (int i = 0; i < kDC; ++i) wv[i] = weight(d + i);
 #pragma unroll
-      for (int i = 0; i < kDC; i += 2) {
-        if (d0 + i + 1 < D) {
-          const u32x4* x1 = column(d0 + i);
-          const u32x4* x2 = column(d0 + i + 1);
-          const uint32_t wp = wv[i] | (wv[i + 1] << 16);
+      for (int i = 0; i < kDC; i += 2) pair(d + i, wv[i] | (wv[i + 1] << 16));
+    }
+    for (; d + 1 < D; d += 2) pair(d, weight(d) | (weight(d + 1) << 16));
+    if (d < D) {
+      const u32x4* xs = column(d);
+      const float w = half_to_f32<DT>(weight(d));
 #pragma unroll
-          for (int q = 0; q < kDiagTok / 8; ++q) {
-            const u32x4 a1 = x1[q], a2 = x2[q];
+      for (int q = 0; q < kDiagTok / 8; ++q) {
+        const u32x4 x = xs[q];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              // v_perm_b32 byte selectors 0-3 take bytes of its second
-              // operand, 4-7 of its first: (low halves of a1, a2), (high halves)
-              const uint32_t lo = __builtin_amdgcn_perm(a2[e], a1[e], 0x05040100u);   // token 2i of both
-              const uint32_t hi = __builtin_amdgcn_perm(a2[e], a1[e], 0x07060302u);   // token 2i + 1
-              acc[8 * q + 2 * e] = dot2<DT>(wp, lo, acc[8 * q + 2 * e]);
-              acc[8 * q + 2 * e + 1] = dot2<DT>(wp, hi, acc[8 * q + 2 * e + 1]);
-            }
-          }
-        } else if (d0 + i < D) {
-          const u32x4* xs = column(d0 + i);
-          const float w = half_to_f32<DT>(wv[i]);
-#pragma unroll
-          for (int q = 0; q < kDiagTok / 8; ++q) {
-            const u32x4 x = xs[q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[8 * q + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[8 * q + 2 * e]);
-              acc[8 * q + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[8 * q + 2 * e + 1]);
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          acc[8 * q + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[8 * q + 2 * e]);
+          acc[8 * q + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[8 * q + 2 * e + 1]);
         }
       }
     }
