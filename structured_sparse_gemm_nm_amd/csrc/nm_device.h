@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels: operand vector types, the
-// sparse MFMA, output rounding, counted waits and direct global->LDS loads.
+// sparse and dense MFMA, conversions and output rounding, counted waits and
+// direct global->LDS loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,7 @@ typedef __bf16 bf16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
 // D = C + A x B on v_smfmac_f32_16x16x64_{f16,bf16}: A is 16 rows x 64 K in
@@ -30,6 +32,29 @@ __device__ inline f32x4 smfmac(const u32x4& a, const u32x8& b, const f32x4& c, u
   } else {
     return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf8_t, a),
                                                      __builtin_bit_cast(bf16_t, b), c, int(idx), 0, ABID);
+  }
+}
+
+// D = C + A x B on the dense v_mfma_f32_16x16x32_{f16,bf16}: lane (i, q)
+// holds A[i][8q..8q+7] and B[8q..8q+7][i]; D rows 4q..4q+3 of column i.
+template <int DT>
+__device__ inline f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (DT == NM_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                  c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c,
+                                                   0, 0, 0);
+  }
+}
+
+// A 16-bit storage value (low 16 bits of h) as fp32.
+template <int DT>
+__device__ inline float half_to_f32(uint32_t h) {
+  if constexpr (DT == NM_F16) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(h)));
+  } else {
+    return __builtin_bit_cast(float, h << 16);
   }
 }
 

@@ -22,29 +22,6 @@
 namespace nm {
 namespace {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// D = C + A x B on v_mfma_f32_16x16x32: lane (i, q) holds A[i][8q..8q+7] and
-// B[8q..8q+7][i]; D rows 4q..4q+3 of column i.
-template <int DT>
-__device__ inline f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
-                                                  c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c,
-                                                   0, 0, 0);
-  }
-}
-
-template <int DT>
-__device__ inline float half_to_f32(uint32_t h) {
-  if constexpr (DT == NM_F16) {
-    return float(__builtin_bit_cast(_Float16, uint16_t(h)));
-  } else {
-    return __builtin_bit_cast(float, h << 16);
-  }
-}
 
 // c + a.lo * b.lo + a.hi * b.hi on two packed 16-bit values (v_dot2_f32_*).
 template <int DT>

@@ -70,7 +70,6 @@ __global__ __launch_bounds__(256) void hybrid_pack_kernel(
     uint32_t kept[2];
     uint32_t bits = 0;
     select_chunk<2, 4>(ww, kept, bits);
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{kept[0], kept[1]}, rv,
                                           bounded((v0 + rr * Lv + kin / 2) * 2, values_bytes), 0, 0);
     const __amdgpu_buffer_rsrc_t ri = make_rsrc(idx, idx_bytes);

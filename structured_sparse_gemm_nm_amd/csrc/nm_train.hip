@@ -32,24 +32,10 @@ namespace nm {
 namespace {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline u32x2 lds_read_tr(const unsigned char* p) {
   const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
   return __builtin_bit_cast(u32x2, v);
-}
-
-// D = C + A x B on v_mfma_f32_16x16x32: lane (i, q) holds A[i][8q..8q+7] and
-// B[8q..8q+7][i]; D rows 4q..4q+3 of column i.
-template <int DT>
-__device__ inline f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
-  if constexpr (DT == NM_F16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
-                                                  c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c,
-                                                   0, 0, 0);
-  }
 }
 
 constexpr int pat_n(int P) { return P == 0 ? 2 : 1; }
