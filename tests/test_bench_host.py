@@ -71,3 +71,21 @@ def test_committed_traffic_entries_are_well_formed():
         # each part is rounded to whole bytes on its own
         assert abs(e["hbm_bytes_per_launch"] - e["read_bytes"] - e["write_bytes"]) <= 1, key
         assert os.path.exists(os.path.join(ROOT, e["profile"])), key
+
+
+def test_cpu_baseline_train_and_hosts():
+    # the training products and the block / diagonal legs, on a few tokens
+    tr = bench.cpu_baseline_train(nm_inputs.WORKLOADS[9], 64, reps=1)
+    assert tr["kind"] == "oracle" and tr["value"] > 0 and "4096x4096x64" in tr["sample"]
+    for wid, kind in ((10, "block"), (11, "diag")):
+        h = bench.cpu_baseline_host(nm_inputs.WORKLOADS[wid], 64, reps=1)
+        assert h["kind"] == "oracle" and h["value"] > 0 and kind in h["sample"] and "3072x768x64" in h["sample"]
+
+
+def test_host_workload_inputs():
+    # workload 10 keeps about a tenth of its 32 x 32 blocks, workload 11 has 77
+    # distinct offsets in [0, 768)
+    mask = nm_inputs.WORKLOADS[10].block_mask()
+    assert mask.shape == (96, 24) and 0.07 < mask.mean() < 0.13
+    offs = nm_inputs.WORKLOADS[11].diag_offsets()
+    assert len(offs) == 77 and len(set(offs.tolist())) == 77 and offs.min() >= 0 and offs.max() < 768
