@@ -177,3 +177,25 @@ def test_workload_size_sampled():
         ref = (gf[:, r] @ af)[cols[r]]
         err, _ = O.relative_error(dw[r].astype(np.float64)[None], ref[None])
         assert err <= 1e-2, ("dw", r, err)
+
+
+def test_empty_reductions_write_zeros():
+    # R == 0: dX = G W_nm over no rows is all zeros; T == 0: dW over no tokens
+    # is all zeros (both outputs are overwritten, never left as they were)
+    log("dx R=0 / dw T=0")
+    K, T, dt = 256, 40, torch.bfloat16
+    vals = torch.empty((0, K // 2), dtype=dt, device="cuda")
+    idx = torch.empty((0, K // 32), dtype=torch.int32, device="cuda")
+    G = torch.zeros((T, 8), dtype=dt, device="cuda")[:, :0]          # [T, 0] with a row stride of 8
+    out = torch.full((T, K), 5.0, dtype=torch.float32, device="cuda")
+    assert nm.nm_spmm_dx(vals, idx, G, K, 2, 4, out=out) is out
+    R = 64
+    _, ridx = O.prune_pack(nm_inputs.normal_half((R, K), 1.0, "bf16", 73, 0), 2, 4)
+    di = torch.from_numpy(ridx.view(np.int32)).cuda()
+    G0 = torch.empty((0, R), dtype=dt, device="cuda")
+    A0 = torch.empty((0, K), dtype=dt, device="cuda")
+    outw = torch.full((R, K // 2), 5.0, dtype=torch.float32, device="cuda")
+    assert nm.nm_spmm_dw(di, G0, A0, K, 2, 4, out=outw) is outw
+    torch.cuda.synchronize()
+    assert not out.any().item()
+    assert not outw.any().item()
