@@ -124,4 +124,25 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_byte*)lds_dst, 16, int(voff), int(soff), 0, 0);
 }
 
+// XCD-aware order of a 1-D grid: the hardware deals workgroups to the 8 XCDs
+// round robin, so workgroup p runs on XCD p % 8.  Of the largest multiple of 8
+// workgroups each XCD is given a contiguous run of logical tiles instead; the
+// last grid % 8 keep their index.
+__device__ inline int xcd_tile(int p, int grid) {
+  const int full = grid & ~7;
+  return p < full ? (p & 7) * (full >> 3) + (p >> 3) : p;
+}
+
+// Logical tile b of a tilesA x tilesB grid, taken in groups of `group` A tiles
+// that walk every B tile: a run of consecutive b (one XCD's share) covers a
+// rectangle of about group x (run / group) tiles, whose operand bands that
+// XCD's L2 holds for all of them.
+__device__ inline void grouped_tile(int b, int tilesA, int tilesB, int group, int& ta, int& tb) {
+  const int per = group * tilesB;
+  const int grp = b / per, rem = b - grp * per;
+  const int ga = min(group, tilesA - grp * group);
+  ta = grp * group + rem % ga;
+  tb = rem / ga;
+}
+
 }  // namespace nm

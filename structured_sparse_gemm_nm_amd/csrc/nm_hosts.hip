@@ -35,13 +35,6 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
   }
 }
 
-// XCD-aware order of a 1-D grid: the hardware deals workgroups to the 8 XCDs
-// round robin, so workgroup p runs on XCD p % 8; when the grid is a multiple
-// of 8 each XCD is given a contiguous run of logical tiles instead.
-__device__ inline int xcd_tile(int p, int grid) {
-  return (grid & 7) == 0 ? (p & 7) * (grid >> 3) + (p >> 3) : p;
-}
-
 // ---------------------------------------------------------------------------
 // Block pack: the kept blocks of W copied to values[nnzb][32][32].  One
 // workgroup per block-row; each thread copies one 16-byte piece of a block
@@ -376,135 +369,220 @@ __global__ __launch_bounds__(256) void diag_pack_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // Diagonal product.  Each output row needs, for every diagonal, one
 // activation column per token (a different one for every row), so the product
-// is not a tile contraction: it runs on the vector ALUs.  A workgroup (512
-// threads) owns 32 tokens and every row.  It first stages the 32 tokens' activations in LDS
-// column by column, xs[k][t] = act[T0 + t][perm[k]] (the map is applied here,
-// once per element and token tile, so the loop below reads plain columns; 80
-// bytes per column, K <= 1792), then each thread takes rows tid, tid + 512,
-// ...: per diagonal the column c = (r + o_d) mod K and its 32 activations in
-// four 16-byte LDS reads; two diagonals at a time feed v_dot2_f32 (fp32
-// accumulation of the pair's exact products).
+// is not a tile contraction: it runs on the vector ALUs.  A workgroup owns 32
+// tokens and one part of the rows.  It first stages the 32 tokens'
+// activations in LDS column by column, xs[k][t] = act[T0 + t][perm[k]] (the
+// map is applied here, once per element and workgroup, so the loop below reads
+// plain columns; 80 bytes per column, K <= 1792), then each thread takes one
+// unit of G rows: per diagonal the column c = (r + o_d) mod K and its 32
+// activations in four 16-byte LDS reads; two diagonals at a time feed v_dot2_f32 (fp32
+// accumulation of the pair's exact products).  Rows r and r + K lie on the
+// same columns of every diagonal (the diagonals wrap round K), so when R is at
+// least G K a unit is the G rows r, r + K, ..., r + (G - 1) K: the LDS reads
+// and the byte permutes that pair two diagonals' activations are shared by G
+// rows' products (one permute and G v_dot2 per token and diagonal pair).
 // ---------------------------------------------------------------------------
 constexpr int kDiagTok = 32;
 // a column of the staged tile: 64 bytes of tokens and 16 of padding, so the
 // 16-byte reads of 16 threads on 16 consecutive columns fall in distinct
 // banks (at 64 bytes every fourth column shares banks: 4-way conflicts)
 constexpr int kDiagPitch = kDiagTok * 2 + 16;
-constexpr int kDiagThreads = 512;   // 8 waves: at two workgroups per CU, 4 waves per SIMD
+// workgroup size: G == 1, 8 waves (two workgroups per CU, 4 waves per SIMD);
+// G > 1, 4 waves holding G x 32 accumulators each (two workgroups per CU)
+constexpr int diag_threads(int G) { return G == 1 ? 512 : 256; }
+// largest workgroup LDS with the row buffer for the map: two workgroups per CU
+constexpr int kDiagGatherLds = 80 * 1024;
 
-template <int DT, int OUT, bool MAP>
-__global__ __launch_bounds__(kDiagThreads) void diag_spmm_kernel(const uint16_t* __restrict__ values,
+template <int DT, int OUT, bool MAP, int G>
+__global__ __launch_bounds__(diag_threads(G)) void diag_spmm_kernel(const uint16_t* __restrict__ values,
                                                         const int32_t* __restrict__ offsets, int D, int R, int K,
                                                         const uint16_t* __restrict__ act, uint32_t act_bytes,
                                                         int64_t ldx, int T, const int32_t* __restrict__ perm,
-                                                        void* __restrict__ Y, int64_t ldy) {
+                                                        void* __restrict__ Y, int64_t ldy, int parts,
+                                                        int lds_gather) {
+  constexpr int kThreads = diag_threads(G);
   extern __shared__ __align__(16) unsigned char smem[];
-  const int T0 = blockIdx.x * kDiagTok;
+  // workgroup -> (token tile, part): a part is kThreads units of rows, one per
+  // thread; the parts of a token tile are consecutive, on one XCD
+  const int b = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = b / parts, part = b - tile * parts;
+  const int T0 = tile * kDiagTok;
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, act_bytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(values, uint32_t(D) * uint32_t(R) * 2u);   // below 4 GiB
 
-  // ---- stage: a thread fills 8 consecutive columns of one token (lane
-  // order: token fastest, so the 32 lanes of a column group write its 64
-  // contiguous bytes); tokens past T are zeros
-  const int groups = kDiagTok * (K / 8);
-  for (int g = tid; g < groups; g += kDiagThreads) {
-    const int t = g % kDiagTok, k8 = (g / kDiagTok) * 8;
-    const bool live = T0 + t < T;
-    const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
-    uint32_t h[8];
-    if constexpr (MAP) {
+  // ---- stage (tokens past T are zeros)
+  int32_t* offl = reinterpret_cast<int32_t*>(smem + K * kDiagPitch);
+  if constexpr (MAP) {
+    if (lds_gather) {
+      // through the map, 8 tokens at a time: their rows are copied whole
+      // (coalesced 16-byte loads) into a buffer behind the offsets, then each
+      // thread gathers whole columns k from it, 8 tokens into one 16-byte
+      // write of the tile (at the 80-byte pitch 16 consecutive columns cover
+      // all 64 banks once)
+      uint16_t* raw = reinterpret_cast<uint16_t*>(smem + K * kDiagPitch + ((D * 4 + 15) & ~15));
+      const int k8s = K / 8;
+      for (int t0 = 0; t0 < kDiagTok; t0 += 8) {
+        for (int p = tid; p < 8 * k8s; p += kThreads) {
+          const int tt = p / k8s, k8 = (p - tt * k8s) * 8;
+          const int t = T0 + t0 + tt;
+          const uint32_t rowoff = uint32_t(min(t, T - 1)) * uint32_t(ldx) * 2u;
+          *reinterpret_cast<u32x4*>(raw + tt * K + k8) =
+              t < T ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(k8) * 2u, 0, 0))
+                    : u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+        for (int k = tid; k < K; k += kThreads) {
+          const int pk = int(umin(uint32_t(perm[k]), uint32_t(K - 1)));
+          uint32_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        h[e] = live ? __builtin_amdgcn_raw_buffer_load_b16(ra, rowoff + umin(uint32_t(perm[k8 + e]), uint32_t(K - 1)) * 2u, 0, 0)
-                    : 0u;
+          for (int e = 0; e < 8; ++e) h[e] = raw[e * K + pk];
+          *reinterpret_cast<u32x4*>(smem + k * kDiagPitch + 2 * t0) =
+              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+        __syncthreads();   // the buffer is refilled next
+      }
     } else {
-      const u32x4 v = live ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           ra, rowoff + uint32_t(k8) * 2u, 0, 0))
-                           : u32x4{0u, 0u, 0u, 0u};
+      // through the map, gathered from global memory (K too large for the
+      // buffer): a thread takes whole columns k, lanes on consecutive columns
+      // (the 64 gathers of one load fall in a single token row, a few of its
+      // lines), and every token, 8 at a time into one 16-byte write
+      for (int k = tid; k < K; k += kThreads) {
+        const uint32_t col = umin(uint32_t(perm[k]), uint32_t(K - 1)) * 2u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[2 * e] = v[e] & 0xFFFFu;
-        h[2 * e + 1] = v[e] >> 16;
+        for (int i = 0; i < kDiagTok / 8; ++i) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = 8 * i + e;
+            const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
+            h[e] = T0 + t < T ? uint32_t(__builtin_amdgcn_raw_buffer_load_b16(ra, rowoff + col, 0, 0)) : 0u;
+          }
+          *reinterpret_cast<u32x4*>(smem + k * kDiagPitch + 16 * i) =
+              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
       }
     }
+  } else {
+    // a thread fills 8 consecutive columns of one token (lane order: token
+    // fastest, so the 32 lanes of a column group write its 64 contiguous bytes)
+    const int groups = kDiagTok * (K / 8);
+    for (int g = tid; g < groups; g += kThreads) {
+      const int t = g % kDiagTok, k8 = (g / kDiagTok) * 8;
+      const uint32_t rowoff = uint32_t(min(T0 + t, T - 1)) * uint32_t(ldx) * 2u;
+      const u32x4 v = T0 + t < T ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       ra, rowoff + uint32_t(k8) * 2u, 0, 0))
+                                 : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint16_t*>(smem + (k8 + e) * kDiagPitch + t * 2) = uint16_t(h[e]);
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(smem + (k8 + e) * kDiagPitch + t * 2) = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+    }
   }
   __syncthreads();
 
   // the offsets, reduced into [0, K), go to LDS behind the tile
-  int32_t* offl = reinterpret_cast<int32_t*>(smem + K * kDiagPitch);
-  for (int d = tid; d < D; d += kDiagThreads) offl[d] = ((offsets[d] % K) + K) % K;
+  for (int d = tid; d < D; d += kThreads) offl[d] = ((offsets[d] % K) + K) % K;
   __syncthreads();
 
-  constexpr int kDC = 16;   // diagonals whose weights are loaded together
-  for (int r = tid; r < R; r += kDiagThreads) {
-    const int rk = r % K;
-    float acc[kDiagTok];
+  constexpr int kDC = G == 1 ? 16 : 8;   // diagonals whose weights are loaded together
+  // unit u: rows q G K + j K + rk (j < G) with q = u div K, rk = u mod K; with
+  // G == 1 that is row u.  Rows past R (the last q's) are computed from
+  // clamped weight reads and not stored.
+  const int units = G == 1 ? R : ((R + G * K - 1) / (G * K)) * K;
+  if (const int u = part * kThreads + tid; u < units) {
+    const int q = u / K, rk = u - q * K;
+    int row[G];
 #pragma unroll
-    for (int j = 0; j < kDiagTok; ++j) acc[j] = 0.f;
+    for (int j = 0; j < G; ++j) row[j] = q * G * K + j * K + rk;
+    float acc[G][kDiagTok];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int t = 0; t < kDiagTok; ++t) acc[j][t] = 0.f;
     auto column = [&](int d) {
       const int c = rk + offl[d];
       return reinterpret_cast<const u32x4*>(smem + (c - (c >= K ? K : 0)) * kDiagPitch);
     };
-    // two diagonals at a time: per token one v_dot2 on (w_d, w_d+1) and the
-    // token's two activations, paired by a byte permute: one VALU operation
-    // per multiply-add instead of a conversion and an FMA
-    auto pair = [&](int d, uint32_t wp) {
+    // two diagonals at a time: per token one byte permute pairs the token's
+    // activations on the two diagonals, and each of the G rows takes one
+    // v_dot2 on its (w_d, w_d+1): fewer than one VALU operation per
+    // multiply-add
+    auto pair = [&](int d, const uint32_t (&wp)[G]) {
       const u32x4* x1 = column(d);
       const u32x4* x2 = column(d + 1);
 #pragma unroll
-      for (int q = 0; q < kDiagTok / 8; ++q) {
-        const u32x4 a1 = x1[q], a2 = x2[q];
+      for (int c = 0; c < kDiagTok / 8; ++c) {
+        const u32x4 a1 = x1[c], a2 = x2[c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // v_perm_b32 byte selectors 0-3 take bytes of its second operand,
           // 4-7 of its first: (low halves of a1, a2), then (high halves)
           const uint32_t lo = __builtin_amdgcn_perm(a2[e], a1[e], 0x05040100u);   // token 2i of both
           const uint32_t hi = __builtin_amdgcn_perm(a2[e], a1[e], 0x07060302u);   // token 2i + 1
-          acc[8 * q + 2 * e] = dot2<DT>(wp, lo, acc[8 * q + 2 * e]);
-          acc[8 * q + 2 * e + 1] = dot2<DT>(wp, hi, acc[8 * q + 2 * e + 1]);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            acc[j][8 * c + 2 * e] = dot2<DT>(wp[j], lo, acc[j][8 * c + 2 * e]);
+            acc[j][8 * c + 2 * e + 1] = dot2<DT>(wp[j], hi, acc[j][8 * c + 2 * e + 1]);
+          }
         }
       }
     };
-    auto weight = [&](int d) {
-      return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rw, uint32_t(d) * uint32_t(R) * 2u + uint32_t(r) * 2u, 0, 0));
+    auto weight = [&](int d, int j) {
+      const uint32_t r = uint32_t(min(row[j], R - 1));
+      return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rw, uint32_t(d) * uint32_t(R) * 2u + r * 2u, 0, 0));
     };
     // whole batches of kDC diagonals, their weights loaded before the first is
     // used, then the remaining pairs, then an odd last diagonal: no branch
     // inside a batch, so every accumulator is updated in place
     int d = 0;
     for (; d + kDC <= D; d += kDC) {
-      uint32_t wv[kDC];
+      uint32_t wv[G][kDC];
 #pragma unroll
-      for (int i = 0; i < kDC; ++i) wv[i] = weight(d + i);
+      for (int i = 0; i < kDC; ++i)
 #pragma unroll
-      for (int i = 0; i < kDC; i += 2) pair(d + i, wv[i] | (wv[i + 1] << 16));
+        for (int j = 0; j < G; ++j) wv[j][i] = weight(d + i, j);
+#pragma unroll
+      for (int i = 0; i < kDC; i += 2) {
+        uint32_t wp[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) wp[j] = wv[j][i] | (wv[j][i + 1] << 16);
+        pair(d + i, wp);
+      }
     }
-    for (; d + 1 < D; d += 2) pair(d, weight(d) | (weight(d + 1) << 16));
+    for (; d + 1 < D; d += 2) {
+      uint32_t wp[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) wp[j] = weight(d, j) | (weight(d + 1, j) << 16);
+      pair(d, wp);
+    }
     if (d < D) {
       const u32x4* xs = column(d);
-      const float w = half_to_f32<DT>(weight(d));
 #pragma unroll
-      for (int q = 0; q < kDiagTok / 8; ++q) {
-        const u32x4 x = xs[q];
+      for (int j = 0; j < G; ++j) {
+        const float w = half_to_f32<DT>(weight(d, j));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[8 * q + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[8 * q + 2 * e]);
-          acc[8 * q + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[8 * q + 2 * e + 1]);
+        for (int c = 0; c < kDiagTok / 8; ++c) {
+          const u32x4 x = xs[c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[j][8 * c + 2 * e] = __builtin_fmaf(w, half_to_f32<DT>(x[e] & 0xFFFFu), acc[j][8 * c + 2 * e]);
+            acc[j][8 * c + 2 * e + 1] = __builtin_fmaf(w, half_to_f32<DT>(x[e] >> 16), acc[j][8 * c + 2 * e + 1]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < kDiagTok; ++j) {
-      const int t = T0 + j;
-      if (t >= T) break;
-      if constexpr (OUT == NM_F32) {
-        static_cast<float*>(Y)[int64_t(t) * ldy + r] = acc[j];
-      } else {
-        static_cast<uint16_t*>(Y)[int64_t(t) * ldy + r] = to_half_bits<DT>(acc[j]);
+    for (int j = 0; j < G; ++j) {
+      const int r = row[j];
+      if (r >= R) continue;
+#pragma unroll
+      for (int t = 0; t < kDiagTok; ++t) {
+        if (T0 + t >= T) break;
+        if constexpr (OUT == NM_F32) {
+          static_cast<float*>(Y)[int64_t(T0 + t) * ldy + r] = acc[j][t];
+        } else {
+          static_cast<uint16_t*>(Y)[int64_t(T0 + t) * ldy + r] = to_half_bits<DT>(acc[j][t]);
+        }
       }
     }
   }
@@ -536,12 +614,28 @@ template <int DT, int OUT, bool MAP>
 hipError_t launch_diag_cfg(const HostArgs& a, hipStream_t s) {
   const int64_t tiles = (a.T + kDiagTok - 1) / kDiagTok;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int lds = int(a.K) * kDiagPitch + int(a.nnz) * 4;   // the tile, then the offsets
-  auto kern = diag_spmm_kernel<DT, OUT, MAP>;
-  if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(unsigned(tiles)), dim3(kDiagThreads), lds, s, a.values, a.offsets, int(a.nnz), int(a.R),
-                     int(a.K), a.act, uint32_t(a.act_bytes), a.ldx, int(a.T), a.perm, a.out, a.ldy);
-  return hipGetLastError();
+  // the tile, the offsets, and for the map the buffer of 8 token rows when
+  // two workgroups per CU still fit (else the map gathers from global memory)
+  const int base = int(a.K) * kDiagPitch + ((int(a.nnz) * 4 + 15) & ~15);
+  const int lds_gather = MAP && base + 16 * int(a.K) <= kDiagGatherLds ? 1 : 0;
+  const int lds = base + (lds_gather ? 16 * int(a.K) : 0);
+  // rows per unit: G rows share their columns only when R >= G K.  A token
+  // tile's units are split into parts of one unit per thread, each its own
+  // workgroup: several small workgroups per CU balance better than one or two
+  // large ones, at the price of staging each tile once per part.
+  auto launch = [&](auto kern, int G) {
+    const int64_t units = G == 1 ? a.R : ((a.R + G * a.K - 1) / (G * a.K)) * a.K;
+    const int64_t parts = (units + diag_threads(G) - 1) / diag_threads(G);
+    if (tiles * parts > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds); e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(unsigned(tiles * parts)), dim3(diag_threads(G)), lds, s, a.values, a.offsets,
+                       int(a.nnz), int(a.R), int(a.K), a.act, uint32_t(a.act_bytes), a.ldx, int(a.T), a.perm, a.out,
+                       a.ldy, int(parts), lds_gather);
+    return hipGetLastError();
+  };
+  if (a.R >= 4 * a.K) return launch(diag_spmm_kernel<DT, OUT, MAP, 4>, 4);
+  if (a.R >= 2 * a.K) return launch(diag_spmm_kernel<DT, OUT, MAP, 2>, 2);
+  return launch(diag_spmm_kernel<DT, OUT, MAP, 1>, 1);
 }
 
 template <int DT, int OUT>

@@ -26,6 +26,7 @@
 #include "nm_device.h"
 #include "nm_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace nm {
@@ -140,15 +141,16 @@ __global__ __launch_bounds__(256, 2) void spmm_dx_kernel(const uint16_t* __restr
                                                       const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
                                                       int K, int idx_row_words, const uint16_t* __restrict__ G,
                                                       int T, int64_t ldg, void* __restrict__ dX, int64_t lddx,
-                                                      int tilesK) {
+                                                      int tilesK, int tilesT, int group) {
   constexpr int N = pat_n(P), M = pat_m(P);
   constexpr int B = P == 2 ? 3 : 2;  // index bits per survivor
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* gbuf = smem;                          // [2][16 KB]
   unsigned char* wbuf = smem + 2 * kDxGStage;          // [2][64][288 B]
 
-  const int tile = blockIdx.x;
-  const int K0 = (tile % tilesK) * kDxBK, T0 = (tile / tilesK) * kDxBT;
+  int tk, tt;
+  grouped_tile(xcd_tile(blockIdx.x, gridDim.x), tilesK, tilesT, group, tk, tt);
+  const int K0 = tk * kDxBK, T0 = tt * kDxBT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wt = wave & 1;
@@ -374,13 +376,15 @@ template <int P, int DT, int OUT>
 __global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restrict__ idx, uint32_t idx_bytes, int R,
                                                       int K, int idx_row_words, const uint16_t* __restrict__ G,
                                                       int T, int64_t ldg, const uint16_t* __restrict__ act,
-                                                      int64_t ldx, void* __restrict__ dW, int tilesK) {
+                                                      int64_t ldx, void* __restrict__ dW, int tilesK, int tilesR,
+                                                      int group) {
   constexpr int N = pat_n(P), M = pat_m(P);
   constexpr int B = P == 2 ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int tile = blockIdx.x;
-  const int K0 = (tile % tilesK) * kDwBK, R0 = (tile / tilesK) * kDwBR;
+  int tk, tr;
+  grouped_tile(xcd_tile(blockIdx.x, gridDim.x), tilesK, tilesR, group, tk, tr);
+  const int K0 = tk * kDwBK, R0 = tr * kDwBR;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wr = wave & 1;
@@ -539,6 +543,24 @@ __global__ __launch_bounds__(256, 2) void spmm_dw_kernel(const uint32_t* __restr
   }
 }
 
+// Group size for grouped_tile.  An XCD's run of about tiles / 8 tiles covers
+// some bands of the grouped operand (at least min(group, run), more once the
+// run spans several groups) and ceil(run / group) bands of the other, up to
+// their counts; with band bytes in proportion band_a : band_b, the power of two
+// with the fewest bytes is taken, so the XCD's L2 serves the rest.
+int pick_group(int64_t tiles_a, int64_t tiles_b, double band_a, double band_b) {
+  const int64_t run = (tiles_a * tiles_b + 7) / 8;
+  int best = 1;
+  double best_bytes = 0.0;
+  for (int64_t g = 1; g <= tiles_a; g *= 2) {
+    const int64_t na = std::min(tiles_a, std::max(std::min(g, run), (run + tiles_b - 1) / tiles_b));
+    const int64_t nb = std::min(tiles_b, (run + g - 1) / g);
+    const double bytes = double(na) * band_a + double(nb) * band_b;
+    if (g == 1 || bytes < best_bytes) best = int(g), best_bytes = bytes;
+  }
+  return best;
+}
+
 template <int P, int DT, int OUT>
 hipError_t launch_dw_cfg(const TrainArgs& a, hipStream_t s) {
   const int64_t tilesK = (a.K + kDwBK - 1) / kDwBK, tilesR = (a.R + kDwBR - 1) / kDwBR;
@@ -547,7 +569,7 @@ hipError_t launch_dw_cfg(const TrainArgs& a, hipStream_t s) {
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kDwLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(tilesK * tilesR)), dim3(256), kDwLds, s, a.idx, uint32_t(a.idx_bytes),
                      int(a.R), int(a.K), int(a.idx_row_words), a.G, int(a.T), a.ldg, a.act, a.ldx, a.out,
-                     int(tilesK));
+                     int(tilesK), int(tilesR), pick_group(tilesK, tilesR, 2.0, 1.0));
   return hipGetLastError();
 }
 
@@ -569,7 +591,8 @@ hipError_t launch_dx_cfg(const TrainArgs& a, hipStream_t s) {
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), kDxLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(unsigned(tilesK * tilesT)), dim3(256), kDxLds, s, a.values,
                      uint32_t(a.values_bytes), a.idx, uint32_t(a.idx_bytes), int(a.R), int(a.K),
-                     int(a.idx_row_words), a.G, int(a.T), a.ldg, a.out, a.ldo, int(tilesK));
+                     int(a.idx_row_words), a.G, int(a.T), a.ldg, a.out, a.ldo, int(tilesK), int(tilesT),
+                     pick_group(tilesK, tilesT, double(pat_n(P)) / pat_m(P), 1.0));
   return hipGetLastError();
 }
 

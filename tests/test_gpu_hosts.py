@@ -158,8 +158,10 @@ def diag_case(R, K, T, D, dt, seed):
     return w, act, offs, perm
 
 
+# R >= 4K and R >= 2K group 4 / 2 rows that share their columns (rows past R
+# in the last group: 700 x 160, 500 x 128, 300 x 96; R a multiple of 4K: 512 x 128)
 DIAG_SHAPES = [(100, 64, 5, 8), (1000, 768, 300, 77), (257, 1792, 33, 300), (64, 64, 1, 64), (40, 128, 70, 1),
-               (300, 96, 31, 0)]
+               (300, 96, 31, 0), (700, 160, 45, 33), (500, 128, 40, 17), (512, 128, 64, 9), (256, 128, 3, 2)]
 
 
 @pytest.mark.parametrize("R,K,T,D", DIAG_SHAPES)
@@ -187,8 +189,9 @@ def test_diag_against_oracle(R, K, T, D, dt, use_perm):
     assert_close(yh, ref, b, out_half=dt)
 
 
-def test_diag_map_equals_explicit_permutation():
-    R, K, T, dt = 500, 256, 90, "f16"
+@pytest.mark.parametrize("R,K", [(500, 256), (1000, 240)])
+def test_diag_map_equals_explicit_permutation(R, K):
+    T, dt = 90, "f16"
     w, act, offs, perm = diag_case(R, K, T, 40, dt, 5)
     od = dev_i32(offs)
     vals = nm.nm_diag_compress(to_dev(w, dt), od)
@@ -202,8 +205,9 @@ def test_diag_map_equals_explicit_permutation():
     assert torch.equal(y_id, y_plain)
 
 
-def test_diag_exact_on_integers():
-    R, K, T, D = 300, 512, 45, 60
+@pytest.mark.parametrize("R,K,D", [(300, 512, 60), (900, 200, 61), (450, 200, 7)])
+def test_diag_exact_on_integers(R, K, D):
+    T = 45
     w = nm_inputs.integer_half((R, K), -6, 6, "bf16", 85, 0)
     act = nm_inputs.integer_half((T, K), -5, 5, "bf16", 85, 1)
     offs = nm_inputs.diag_offsets(K, D, 85)
