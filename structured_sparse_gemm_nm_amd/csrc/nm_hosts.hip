@@ -392,6 +392,8 @@ constexpr int kDiagPitch = kDiagTok * 2 + 16;
 constexpr int diag_threads(int G) { return G == 1 ? 512 : 256; }
 // largest workgroup LDS with the row buffer for the map: two workgroups per CU
 constexpr int kDiagGatherLds = 80 * 1024;
+// 16-byte pieces of one 8-token row group a thread loads for the row buffer
+constexpr int kGatherPieces = 4;
 
 template <int DT, int OUT, bool MAP, int G>
 __global__ __launch_bounds__(diag_threads(G)) void diag_spmm_kernel(const uint16_t* __restrict__ values,
@@ -419,17 +421,34 @@ __global__ __launch_bounds__(diag_threads(G)) void diag_spmm_kernel(const uint16
       // (coalesced 16-byte loads) into a buffer behind the offsets, then each
       // thread gathers whole columns k from it, 8 tokens into one 16-byte
       // write of the tile (at the 80-byte pitch 16 consecutive columns cover
-      // all 64 banks once)
+      // all 64 banks once).  The loads of all four row groups are issued
+      // first (a thread holds at most kGatherPieces pieces of each: the
+      // launcher takes this path only for K <= kGatherPieces * threads), so
+      // their latency is paid once.
       uint16_t* raw = reinterpret_cast<uint16_t*>(smem + K * kDiagPitch + ((D * 4 + 15) & ~15));
       const int k8s = K / 8;
-      for (int t0 = 0; t0 < kDiagTok; t0 += 8) {
-        for (int p = tid; p < 8 * k8s; p += kThreads) {
+      u32x4 rv[kDiagTok / 8][kGatherPieces];
+#pragma unroll
+      for (int c = 0; c < kDiagTok / 8; ++c)
+#pragma unroll
+        for (int i = 0; i < kGatherPieces; ++i) {
+          const int p = tid + i * kThreads;
           const int tt = p / k8s, k8 = (p - tt * k8s) * 8;
-          const int t = T0 + t0 + tt;
+          const int t = T0 + 8 * c + tt;
           const uint32_t rowoff = uint32_t(min(t, T - 1)) * uint32_t(ldx) * 2u;
-          *reinterpret_cast<u32x4*>(raw + tt * K + k8) =
-              t < T ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(k8) * 2u, 0, 0))
-                    : u32x4{0u, 0u, 0u, 0u};
+          rv[c][i] = p < 8 * k8s && t < T
+                         ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, rowoff + uint32_t(k8) * 2u, 0, 0))
+                         : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int c = 0; c < kDiagTok / 8; ++c) {
+#pragma unroll
+        for (int i = 0; i < kGatherPieces; ++i) {
+          const int p = tid + i * kThreads;
+          if (p < 8 * k8s) {
+            const int tt = p / k8s, k8 = (p - tt * k8s) * 8;
+            *reinterpret_cast<u32x4*>(raw + tt * K + k8) = rv[c][i];
+          }
         }
         __syncthreads();
         for (int k = tid; k < K; k += kThreads) {
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(diag_threads(G)) void diag_spmm_kernel(const uint16
           uint32_t h[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) h[e] = raw[e * K + pk];
-          *reinterpret_cast<u32x4*>(smem + k * kDiagPitch + 2 * t0) =
+          *reinterpret_cast<u32x4*>(smem + k * kDiagPitch + 16 * c) =
               u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
         __syncthreads();   // the buffer is refilled next
@@ -618,6 +637,8 @@ hipError_t launch_diag_cfg(const HostArgs& a, hipStream_t s) {
   // two workgroups per CU still fit (else the map gathers from global memory)
   const int base = int(a.K) * kDiagPitch + ((int(a.nnz) * 4 + 15) & ~15);
   const int lds_gather = MAP && base + 16 * int(a.K) <= kDiagGatherLds ? 1 : 0;
+  // every thread's share of a row group fits its kGatherPieces registers
+  static_assert(kDiagGatherLds / (16 + kDiagPitch) <= kGatherPieces * diag_threads(4), "row group pieces");
   const int lds = base + (lds_gather ? 16 * int(a.K) : 0);
   // rows per unit: G rows share their columns only when R >= G K.  A token
   // tile's units are split into parts of one unit per thread, each its own
