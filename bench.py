@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / matmul peaks")
+    ap.add_argument("--print-source-hash", choices=sorted(KERNEL_SOURCES), default=None,
+                    help="print the source hash of one family of kernels (the key a counter "
+                         "summary is filed under) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy, the reference a counter "
                          "profile of this command scales HBM byte counters against")
@@ -77,6 +80,25 @@ def source_hash(paths):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+CSRC = os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")
+# The sources each family of kernels is built from: its own translation units,
+# plus the shared device and host headers, the C ABI's dispatch and the public
+# header.  Counters taken on one family stay valid while only another changes.
+KERNEL_SOURCES = {
+    "spmm": ["nm_spmm.hip", "nm_spmm_lds.hip", "nm_spmm_lds_nm.hip", "nm_spmm_decode.hip",
+             "nm_spmm_pipe.hip", "nm_spmm_resident.hip", "nm_permute.hip", "nm_int8.hip"],
+    "hybrid": ["nm_hybrid.hip", "nm_select.h"],
+    "host": ["nm_hosts.hip"],
+    "train": ["nm_train.hip"],
+}
+SHARED_SOURCES = ["nm_device.h", "nm_internal.h", "nm_api.cpp"]
+
+
+def kernel_source_hash(family):
+    files = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[family] + SHARED_SOURCES]
+    return source_hash(files + [os.path.join(ROOT, "include", "nmsparse.h")])
 
 
 def traffic_from_profile(kernel_key, hsh):
@@ -266,9 +288,7 @@ def bench_hybrid(args, wl):
     alg_flop = 2.0 * T * L.values_count           # one MAC per stored weight and token
     dense_eq_flop = 2.0 * R * K * T
     achieved = alg_flop / (gemm_mean_us * 1e-6) / 1e12
-    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
-               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
-    hsh = source_hash(lib_src)
+    hsh = kernel_source_hash("hybrid")
     out_name = args.out_dtype
     kernel_key = f"hybrid_w{wl.wid}_{tr}x{tc}_T{T}_{out_name}"
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS[wl.dtype], "unit": "TFLOP/s",
@@ -467,9 +487,7 @@ def bench_host(args, wl):
     flop = 2.0 * stored * T                     # one MAC per stored weight and token
     nbytes = stored * 2 + struct_bytes + T * K * 2 + T * R * ob + K * 4
     kname = "nm_block_spmm" if kind == "block" else "nm_diag_spmm"
-    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
-               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
-    hsh = source_hash(lib_src)
+    hsh = kernel_source_hash("host")
     if kind == "block":
         ach = nbytes / (spmm_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS}
@@ -645,9 +663,7 @@ def bench_train(args, wl):
     mfma_flop = 2.0 * T * R * K
     dense_eq_flop = 2.0 * 2.0 * R * K * T
     ob = 4 if out_name == "f32" else 2
-    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
-               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
-    hsh = source_hash(lib_src)
+    hsh = kernel_source_hash("train")
     _, ib, _ = nm.nm_packed_sizes(R, K, n, m, nm.NM_BF16 if wl.dtype == "bf16" else nm.NM_F16)
     per = {"nm_spmm_dx": {"mean_us": dx_us, "flop": alg_flop, "mfma_flop": mfma_flop,
                           "bytes": R * S * 2 + ib + T * R * 2 + T * K * ob},
@@ -753,6 +769,9 @@ def measured_peaks(torch):
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(kernel_source_hash(args.print_source_hash))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the per-GPU kernel is what --gpus 1 times); run with --gpus 1", file=sys.stderr)
@@ -984,9 +1003,7 @@ def main():
     dense_eq_flop = 2.0 * R * K * T
     alg_flop = 2.0 * R * S * T
     achieved_tflops = alg_flop / (gemm_mean_us * 1e-6) / 1e12
-    lib_src = [os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc", f)
-               for f in sorted(os.listdir(os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")))]
-    hsh = source_hash(lib_src)
+    hsh = kernel_source_hash("spmm")
     kernel_key = f"spmm_w{args.workload}_{n}of{m}_T{T}_{out_name}"
     roofline_bound = "mfma" if args.workload in (1, 2, 4, 6, 7) else "hbm"
     unit = "TOP/s" if i8 else "TFLOP/s"

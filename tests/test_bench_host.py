@@ -89,3 +89,24 @@ def test_host_workload_inputs():
     assert mask.shape == (96, 24) and 0.07 < mask.mean() < 0.13
     offs = nm_inputs.WORKLOADS[11].diag_offsets()
     assert len(offs) == 77 and len(set(offs.tolist())) == 77 and offs.min() >= 0 and offs.max() < 768
+
+
+def test_kernel_source_hash_covers_one_family(monkeypatch, tmp_path):
+    """A family's hash changes with its own sources and the shared ones, not with
+    another family's translation unit."""
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    (tmp_path / "include").mkdir()
+    (tmp_path / "include" / "nmsparse.h").write_text("h")
+    names = {n for fam in bench.KERNEL_SOURCES.values() for n in fam} | set(bench.SHARED_SOURCES)
+    for n in names:
+        (csrc / n).write_text(n)
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    before = {f: bench.kernel_source_hash(f) for f in bench.KERNEL_SOURCES}
+    (csrc / "nm_hosts.hip").write_text("changed")
+    after = {f: bench.kernel_source_hash(f) for f in bench.KERNEL_SOURCES}
+    assert after["host"] != before["host"]
+    assert all(after[f] == before[f] for f in bench.KERNEL_SOURCES if f != "host")
+    (csrc / "nm_device.h").write_text("changed")
+    assert all(bench.kernel_source_hash(f) != after[f] for f in bench.KERNEL_SOURCES)
