@@ -110,3 +110,12 @@ def test_kernel_source_hash_covers_one_family(monkeypatch, tmp_path):
     assert all(after[f] == before[f] for f in bench.KERNEL_SOURCES if f != "host")
     (csrc / "nm_device.h").write_text("changed")
     assert all(bench.kernel_source_hash(f) != after[f] for f in bench.KERNEL_SOURCES)
+
+
+def test_every_kernel_source_belongs_to_a_family():
+    """A new source file cannot escape the hashes that counter summaries are
+    filed under (the prune / pack kernels have no counter summary of their own)."""
+    names = {n for n in os.listdir(bench.CSRC) if n.endswith((".hip", ".cpp", ".h"))}
+    covered = {n for fam in bench.KERNEL_SOURCES.values() for n in fam} | set(bench.SHARED_SOURCES)
+    assert names - covered == {"nm_prune_pack.hip"}
+    assert covered <= names
