@@ -7,7 +7,8 @@
 // its partner slot a zero at the same position, and a 4-group without a
 // survivor two zeros at position 0 (RNM-TD3's ratios run at the 2:4 rate while
 // only their own packed bytes move).  The MFMA operands equal those of
-// nm_spmm_pipe.hip step for step, so the results are bit-identical to it.
+// nm_spmm_pipe.hip step for step; the sums differ from it only in their order
+// (even and odd K steps apart, then added).
 //
 // Packed rows of these patterns are short: per 64-wide K step a row holds 32
 // (1:4) or 16 (1:8) bytes of values and 4 or 3 bytes of index bits.  Loaded
@@ -32,16 +33,22 @@
 //                  bytes loaded 4 at a time, rows contiguous (a 48-byte row
 //                  stride puts a fragment's 16 rows on distinct banks).
 //
-// A workgroup (4 waves stacked along the rows, each 32 rows x 64 tokens = 2 x 4
-// fragments, so every row fragment is widened by one wave only) computes
-// 128 x 64 tiles: a 4096-row layer at 512 tokens then has one tile
-// per compute unit, where 256 x 128 tiles would leave three quarters of the
-// chip idle.  Activation stages form a 4-deep ring (three K steps of loads in
-// flight), a value group is loaded at the first step of the group before it,
-// with counted vmcnt waits and one fence-free barrier per step; every step
-// issues the same loads (past the last step a slot is refilled with that step
-// again, and past the last group the last group is loaded again), so the wait
-// counts are fixed.  Each tile fills its own ring.
+// A workgroup computes 128 x 64 tiles (a 4096-row layer at 512 tokens then
+// has one tile per compute unit, where 256 x 128 tiles would leave three
+// quarters of the chip idle) with 8 waves in two groups of four: the first
+// group multiplies the even K steps, the second the odd ones, each wave 32
+// rows x 64 tokens (2 x 4 fragments, every row fragment widened by one wave of
+// its group).  So each SIMD holds one wave of each group, and one wave's
+// fragment reads, widening and waits run beside the other's MFMAs.  At the
+// end of a tile the odd steps' partial sums reach the even group through LDS
+// and are added once (even + odd, the same order on every run).  Activation
+// stages form a ring of four step pairs (three pairs of loads in flight while
+// one is read), each group loading its own step of a pair; a value group is
+// loaded with the activations of its first pair, three groups buffered; counted
+// vmcnt waits and one fence-free barrier per pair; every pair issues the same
+// loads (past the last step a slot is refilled with that step again, and past
+// the last group the last group is loaded again), so the wait counts are
+// fixed.  Each tile fills its own ring.
 #include "nm_device.h"
 #include "nm_internal.h"
 
@@ -50,10 +57,12 @@ namespace {
 
 constexpr int kBR = 128;
 constexpr int kBT = 64;
-constexpr int kNS = 4;               // one-K-step stages in the ring
+constexpr int kWaves = 8;            // two groups of four waves: even and odd K steps
+constexpr int kNP = 4;               // step pairs in the ring (8 one-step stages)
 constexpr int kStageB = kBT * 128;   // activations, one step
-constexpr int kPerStep = 2;          // activation loads per wave per step
-constexpr int kGroupLoads = 4;       // packed-value loads per wave per group
+constexpr int kPerPair = 2;          // activation loads per wave per step pair (its group's step)
+constexpr int kGroupLoads = 2;       // packed-value loads per wave per group
+constexpr int kNG = 3;               // packed-value group buffers
 constexpr int kSAG = kBR * 128;      // packed values, one group (128 B per row)
 
 // P = 1: 1:4, P = 2: 1:8 (32 or 16 value bytes per row per K step).  GS: steps
@@ -63,16 +72,16 @@ template <int P>
 struct NmPat;
 template <>
 struct NmPat<1> {
-  static constexpr int GS = 4, IBLK = 64, IL = 2;
+  static constexpr int GS = 4, IBLK = 64, IL = 1;
 };
 template <>
 struct NmPat<2> {
-  static constexpr int GS = 8, IBLK = 48, IL = 6;
+  static constexpr int GS = 8, IBLK = 48, IL = 3;
 };
 
 template <int P>
 constexpr int lds_bytes() {
-  return kNS * kStageB + 2 * kSAG + 2 * kBR * NmPat<P>::IBLK;
+  return 2 * kNP * kStageB + kNG * kSAG + 2 * kBR * NmPat<P>::IBLK;
 }
 
 // Tile i of the grid-stride sequence -> (row tile, token tile), token tiles
@@ -132,26 +141,30 @@ __device__ inline void widen_1of8(uint32_t v, uint32_t bits, u32x4& a, uint32_t&
 }
 
 template <int P, int DT, int OUT>
-__global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
+__global__ __launch_bounds__(kWaves * 64, 1) void spmm_lds_nm_kernel(
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ idx, int R, int K, int irow_bytes,
     const uint16_t* __restrict__ act, int T, int64_t ldx, void* __restrict__ Y, int64_t ldy,
     TileMapNM tm) {
   constexpr int FR = 2, FT = 4;
   static_assert(FR == 2, "1:4 index registers hold two row fragments");
-  constexpr int GS = NmPat<P>::GS, IBLK = NmPat<P>::IBLK;
+  constexpr int GS = NmPat<P>::GS, IBLK = NmPat<P>::IBLK, IL = NmPat<P>::IL;
   constexpr int SI = kBR * IBLK;    // index bits, one block
+  constexpr int HG = GS / 2;        // step pairs per value group
+  constexpr int G0 = P == 1 ? 2 : 1;  // value groups loaded before the first pair
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* bbuf = smem;                         // [kNS][kStageB]
-  unsigned char* abuf = smem + kNS * kStageB;         // [2][kSAG]
-  unsigned char* ibuf = smem + kNS * kStageB + 2 * kSAG;  // [2][SI]
+  unsigned char* bbuf = smem;                     // [2 kNP][kStageB]
+  unsigned char* abuf = smem + 2 * kNP * kStageB;  // [kNG][kSAG]
+  unsigned char* ibuf = abuf + kNG * kSAG;         // [2][SI]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // uniform: LDS destinations of the direct loads (M0) are then scalar sums
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
-  const int wr = wave;  // rows wr*32 .. wr*32+31 of the tile, all 64 tokens
+  const int grp = wave >> 2;  // 0: K steps 0, 2, 4, ...; 1: steps 1, 3, 5, ...
+  const int wr = wave & 3;    // rows wr*32 .. wr*32+31 of the tile, all 64 tokens
   const int nsteps = K >> 6;  // a multiple of 4 on this path
+  const int npairs = nsteps >> 1;
   const int S = K / (P == 1 ? 4 : 8);
   const int iwords = irow_bytes >> 2;  // index words per row
   const int ngroups = (nsteps + GS - 1) / GS;
@@ -159,12 +172,12 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   const bool half_last = P == 2 && (nsteps % GS) != 0;
 
   // Per-lane index-block slots, instruction j of a wave.  1:4: 16-byte slots
-  // [(wave*2 + j)*64, +64), slot (row, chunk) at row*4 + (chunk ^ ((row >> 2) & 3));
-  // 1:8: 4-byte slots [(wave*6 + j)*64, +64), slot (row, word d) at row*12 + d.
-  int ipart[NmPat<P>::IL];
+  // [(wave + j)*64, +64), slot (row, chunk) at row*4 + (chunk ^ ((row >> 2) & 3));
+  // 1:8: 4-byte slots [(wave*3 + j)*64, +64), slot (row, word d) at row*12 + d.
+  int ipart[IL];
 #pragma unroll
-  for (int j = 0; j < NmPat<P>::IL; ++j) {
-    const int slot = (wave * NmPat<P>::IL + j) * 64 + lane;
+  for (int j = 0; j < IL; ++j) {
+    const int slot = (wave * IL + j) * 64 + lane;
     ipart[j] = P == 1 ? (slot & 3) ^ ((slot >> 4) & 3) : slot % 12;
   }
 
@@ -182,16 +195,18 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   // Every load is kept inside its row by construction; the index resource
   // also ends with the array.
   __amdgpu_buffer_rsrc_t rb, ra, ri;
-  uint32_t boff[2], aoff[kGroupLoads], ioff[NmPat<P>::IL];
+  uint32_t boff[kPerPair], aoff[kGroupLoads], ioff[IL];
   auto make_src = [&](int R0, int T0) {
     rb = make_rsrc(act + int64_t(T0) * ldx, 0xFFFFFFFFu);
     ra = make_rsrc(values + int64_t(R0) * S, 0xFFFFFFFFu);
     const int64_t ibytes = int64_t(R - R0) * irow_bytes;
     ri = make_rsrc(reinterpret_cast<const unsigned char*>(idx) + int64_t(R0) * irow_bytes,
                    uint32_t(ibytes < 0xFFFFFFFFll ? ibytes : 0xFFFFFFFFll));
+    // activations: the four waves of a group load their group's step, part
+    // (wr*2 + j) of 8 (64 tokens x 128 bytes)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int slot = (wave * 2 + j) * 64 + lane;
+    for (int j = 0; j < kPerPair; ++j) {
+      const int slot = (wr * 2 + j) * 64 + lane;
       const int tok = slot >> 3;
       const int c = (slot & 7) ^ (tok & 7);
       const int t = min(T0 + tok, T - 1) - T0;
@@ -199,13 +214,13 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     }
     // index: the row's start (the part within the block is added per block)
 #pragma unroll
-    for (int j = 0; j < NmPat<P>::IL; ++j) {
-      const int slot = (wave * NmPat<P>::IL + j) * 64 + lane;
+    for (int j = 0; j < IL; ++j) {
+      const int slot = (wave * IL + j) * 64 + lane;
       const int row = P == 1 ? slot >> 2 : slot / 12;
       const int r = min(R0 + row, R - 1) - R0;
       ioff[j] = uint32_t(r) * uint32_t(irow_bytes);
     }
-    // packed values: load j of a wave fills slots [(wave*4 + j)*64, +64) of a
+    // packed values: load j of a wave fills slots [(wave*2 + j)*64, +64) of a
     // group buffer, 8 whole rows; slot (row, chunk c) at row*8 + (c ^ ((row >> 1) & 7))
 #pragma unroll
     for (int j = 0; j < kGroupLoads; ++j) {
@@ -217,11 +232,12 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
     }
   };
 
-  // the activation loads of step src into ring slot buf
+  // this wave's share of the activations of step src (its group's parity)
+  // into ring slot buf
   auto issue_step = [&](int src, int buf) {
 #pragma unroll
-    for (int j = 0; j < kPerStep; ++j)
-      dma16(rb, boff[j], uint32_t(src) * 128u, bbuf + buf * kStageB + (wave * 2 + j) * 1024);
+    for (int j = 0; j < kPerPair; ++j)
+      dma16(rb, boff[j], uint32_t(src) * 128u, bbuf + buf * kStageB + (wr * 2 + j) * 1024);
   };
   // the packed values of group g (clamped to the last group) into buffer gb.
   // Every load stays inside its row: a row is nsteps * VB bytes, whole groups
@@ -242,14 +258,14 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   // reread its last word.  Those slots are never used.
   auto issue_index = [&](int q, int ib) {
 #pragma unroll
-    for (int j = 0; j < NmPat<P>::IL; ++j) {
+    for (int j = 0; j < IL; ++j) {
       if constexpr (P == 1) {
         const int o = q * IBLK + ipart[j] * 16;
         const uint32_t in_row = uint32_t(o + 16 <= irow_bytes ? o : q * IBLK);
-        dma16(ri, ioff[j] + in_row, 0u, ibuf + ib * SI + (wave * 2 + j) * 1024);
+        dma16(ri, ioff[j] + in_row, 0u, ibuf + ib * SI + (wave * IL + j) * 1024);
       } else {
         const int d = min(q * (IBLK / 4) + ipart[j], iwords - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_byte*)(ibuf + ib * SI + (wave * 6 + j) * 256), 4,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_byte*)(ibuf + ib * SI + (wave * IL + j) * 256), 4,
                                                  int(ioff[j] + uint32_t(d) * 4u), 0, 0, 0);
       }
     }
@@ -268,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   // packed values of step u (t = u % GS) of row fragment i: the lane's 8
   // (1:4) or 4 (1:8) bytes, at byte t*VB + lq*(VB/4) of the row's 128-byte run
   auto read_v = [&](int u, int t, int i, uint32_t (&v)[2]) {
-    const unsigned char* sa = abuf + ((u / GS) & 1) * kSAG;
+    const unsigned char* sa = abuf + ((u / GS) % kNG) * kSAG;
     const int row = wr * 32 + i * 16 + li;
     const int f = (row >> 1) & 7;
     if constexpr (P == 1) {
@@ -300,15 +316,16 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       w[3] = 0u;
     }
   };
-  // Widen step t (0..3, a constant at every call) of the current four-step
+  // Widen step t (0..3, a compile-time constant) of the current four-step
   // index group into row operands a[] and index registers k[] (1:4: one
   // register for both fragments, read through the MFMA's abid; 1:8: one each).
   // byte selector: byte lq of fragment 0's word into bits 0..7, of fragment
   // 1's into bits 16..23, zeros elsewhere
   const uint32_t sel14 = uint32_t(lq) | (0x0Cu << 8) | (uint32_t(4 + lq) << 16) | (0x0Cu << 24);
   const uint32_t off6 = uint32_t(6 * lq);  // the lane's 6 bits in a 1:8 step's 24
-  auto widen = [&](int t, const uint32_t (&v)[FR][2], const uint32_t (&w)[FR][4], u32x4 (&a)[FR],
+  auto widen = [&](auto t_c, const uint32_t (&v)[FR][2], const uint32_t (&w)[FR][4], u32x4 (&a)[FR],
                    uint32_t (&k)[FR]) {
+    constexpr int t = decltype(t_c)::value;
     if constexpr (P == 1) {
 #pragma unroll
       for (int i = 0; i < FR; ++i) widen_1of4_values(v[i][0], v[i][1], a[i]);
@@ -326,6 +343,14 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       }
     }
   };
+  using std::integral_constant;
+  // step t0 + grp of the four-step index group: t0 is a constant, grp uniform
+  auto widen_own = [&](auto t0_c, const uint32_t (&v)[FR][2], const uint32_t (&w)[FR][4], u32x4 (&a)[FR],
+                       uint32_t (&k)[FR]) {
+    constexpr int t0 = decltype(t0_c)::value;
+    if (grp) widen(integral_constant<int, t0 + 1>{}, v, w, a, k);
+    else widen(integral_constant<int, t0>{}, v, w, a, k);
+  };
 
   f32x4 acc[FR][FT];
   u32x4 a0[FR], a1[FR];
@@ -334,43 +359,50 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
   uint32_t rv[FR][2];  // raw packed values of the step being read
   uint32_t rw[FR][4];  // raw index words of the current four-step group
 
-  // One step s (position C = s & 3, a compile-time constant: every tile
-  // starts at ring slot 0 and nsteps % 4 == 0): make step s+1 visible,
-  // refill slot C with step s+4, read step s+1, multiply step s, widen s+1.
-  auto body = [&](auto c_, int s, u32x4 (&ca)[FR], uint32_t (&ck)[FR], u32x8 (&cb)[FT],
+  // Value group m is loaded by the body that loads the activations of its
+  // first pair (pair HG*m, body HG*m - 4), into buffer m % kNG; groups below
+  // G0 by the prologue.  Three buffers: the group loaded in body x replaces
+  // the one whose last step was read three groups earlier.
+  auto group_at = [&](int x) { return x >= 0 && ((x + 4) % HG) == 0 && (x + 4) / HG >= G0; };
+
+  // One pair p of K steps (steps 2p and 2p+1; this wave's step s = 2p + grp,
+  // the pair's parity PAR a compile-time constant): make pair p+1 visible,
+  // refill this wave's slot with step s + 8, read step s + 2, multiply step s,
+  // widen s + 2.  The two groups' waves share each SIMD, so one group's
+  // fragment reads and widening run beside the other's MFMAs.
+  auto body = [&](auto par_c, int p, u32x4 (&ca)[FR], uint32_t (&ck)[FR], u32x8 (&cb)[FT],
                   u32x4 (&na)[FR], uint32_t (&nk)[FR], u32x8 (&nb)[FT]) {
-    constexpr int C = decltype(c_)::value;
-    // Step s+1 has landed once at most the loads issued after its activations
-    // remain: the activations of steps s+2, s+3, and a value group if one of
-    // those two steps began a group (groups begin at steps with C == 0, 1:8
-    // every other one; a group issued at step s' precedes that step's
-    // activation loads and is read from step s'+GS on).  An index block
-    // issued in between only makes the wait stricter.
-    bool grp_behind = false;
-    if constexpr (C == 1 || C == 2) grp_behind = P == 1 || ((s >> 2) & 1) == 0;
-    if (grp_behind)
-      wait_vmcnt<2 * kPerStep + kGroupLoads>();
+    constexpr int PAR = decltype(par_c)::value;
+    // Pair p+1 has landed once at most the loads issued after this wave's
+    // share of it remain: its shares of pairs p+2, p+3, and a value group if
+    // body p-2 or p-1 loaded one (an index block loaded in between only
+    // makes the wait stricter).
+    if (group_at(p - 2) || group_at(p - 1))
+      wait_vmcnt<2 * kPerPair + kGroupLoads>();
     else
-      wait_vmcnt<2 * kPerStep>();
+      wait_vmcnt<2 * kPerPair>();
     wait_lgkm0();        // this wave's reads of step s are done
-    barrier_no_fence();  // publishes step s+1; every wave is done reading step s
-    if constexpr (C == 0) {
-      if ((s & 15) == 0 && s + 16 < nsteps) issue_index((s >> 4) + 1, ((s >> 4) + 1) & 1);
-      // the next group's buffer held the previous group, whose last step was
-      // read before this step's barrier
-      if (P == 1 || ((s >> 2) & 1) == 0) issue_group(s / GS + 1, (s / GS + 1) & 1);
+    barrier_no_fence();  // publishes pair p+1; every wave is done reading pair p
+    if constexpr (PAR == 0) {
+      if ((p & 7) == 0 && 2 * p + 16 < nsteps) issue_index((p >> 3) + 1, ((p >> 3) + 1) & 1);
     }
-    issue_step(min(s + kNS, nsteps - 1), C);
-    constexpr int RS = (C + 1) & 3;  // slot and group position of step s+1
+    if (group_at(p)) {
+      const int m = (p + 4) / HG;
+      issue_group(m, m % kNG);
+    }
+    const int s = 2 * p + grp;
+    issue_step(min(s + 2 * kNP, nsteps - 1), s & 7);
+    const int s1 = s + 2;
+    const int rs = s1 & 7;
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      read_b(RS, j, 0, nb[j]);
-      read_b(RS, j, 1, nb[j]);
+      read_b(rs, j, 0, nb[j]);
+      read_b(rs, j, 1, nb[j]);
     }
 #pragma unroll
-    for (int i = 0; i < FR; ++i) read_v(s + 1, P == 1 ? RS : (s + 1) & 7, i, rv[i]);
-    if constexpr (RS == 0) {
-      const int s1 = s + 1;
+    for (int i = 0; i < FR; ++i) read_v(s1, P == 1 ? (s1 & 3) : (s1 & 7), i, rv[i]);
+    if constexpr (PAR == 1) {
+      // step s + 2 opens its four-step index group
 #pragma unroll
       for (int i = 0; i < FR; ++i) read_ix((s1 >> 4) & 1, (s1 >> 2) & 3, i, rw[i]);
     }
@@ -381,13 +413,14 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       acc[1][j] = smfmac<DT, P == 1 ? 1 : 0>(ca[1], cb[j], acc[1][j], ck[1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    widen(RS, rv, rw, na, nk);
+    // step s + 2 sits at position 2 (pair p even) or 0 (p odd), plus grp, of
+    // its four-step index group
+    widen_own(integral_constant<int, PAR == 0 ? 2 : 0>{}, rv, rw, na, nk);
     // keeps the widening here, behind the MFMAs it overlaps, rather than in
     // front of the next step's MFMAs, which need its results
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  using std::integral_constant;
   for (int tile = blockIdx.x; tile < tm.ntiles; tile += tm.grid) {
     int R0, T0;
     tm.rt(tile, R0, T0);
@@ -397,44 +430,65 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
 #pragma unroll
       for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- prologue: index block 0, value group 0 and steps 0 .. kNS-2, then
-    // step kNS-1 into the last slot and step 0 into register set 0
+    // ---- prologue: index block 0, the first value groups and pairs
+    // 0 .. kNP-2, then pair kNP-1 and this wave's step of pair 0 into
+    // register set 0
     issue_index(0, 0);
-    issue_group(0, 0);
 #pragma unroll
-    for (int p = 0; p < kNS - 1; ++p) issue_step(min(p, nsteps - 1), p);
-    wait_vmcnt<2 * kPerStep>();  // index block 0, value group 0 and step 0
+    for (int m = 0; m < G0; ++m) issue_group(m, m);
+#pragma unroll
+    for (int q = 0; q < kNP - 1; ++q) issue_step(min(2 * q + grp, nsteps - 1), (2 * q + grp) & 7);
+    wait_vmcnt<2 * kPerPair>();  // index block 0, the first groups and pair 0
     barrier_no_fence();
-    issue_step(min(kNS - 1, nsteps - 1), kNS - 1);
+    issue_step(min(2 * (kNP - 1) + grp, nsteps - 1), (2 * (kNP - 1) + grp) & 7);
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      read_b(0, j, 0, b0[j]);
-      read_b(0, j, 1, b0[j]);
+      read_b(grp, j, 0, b0[j]);
+      read_b(grp, j, 1, b0[j]);
     }
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
-      read_v(0, 0, i, rv[i]);
+      read_v(grp, grp, i, rv[i]);
       read_ix(0, 0, i, rw[i]);
     }
-    widen(0, rv, rw, a0, k0);
+    widen_own(integral_constant<int, 0>{}, rv, rw, a0, k0);
 
-    for (int s = 0; s < nsteps; s += 4) {
-      body(integral_constant<int, 0>{}, s, a0, k0, b0, a1, k1, b1);
-      body(integral_constant<int, 1>{}, s + 1, a1, k1, b1, a0, k0, b0);
-      body(integral_constant<int, 2>{}, s + 2, a0, k0, b0, a1, k1, b1);
-      body(integral_constant<int, 3>{}, s + 3, a1, k1, b1, a0, k0, b0);
+    for (int p = 0; p < npairs; p += 2) {
+      body(integral_constant<int, 0>{}, p, a0, k0, b0, a1, k1, b1);
+      body(integral_constant<int, 1>{}, p + 1, a1, k1, b1, a0, k0, b0);
     }
 
     // The refills past the last step are still landing and every wave may
-    // still read: drain both before the next tile's prologue reuses the ring
-    // (and before the workgroup ends, so no direct load writes LDS after it).
-    // Stores share the load counter, so this comes before the epilogue's
-    // stores, which then overlap the next tile's first loads.
+    // still read: drain both before the ring is reused.  Stores share the
+    // load counter, so this comes before the epilogue's stores, which then
+    // overlap the next tile's first loads.
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier_no_fence();
 
-    // ---- epilogue
+    // ---- the odd steps' partial sums join the even steps' through LDS (the
+    // ring is idle): sum = even + odd, the same order every run
+    f32x4* red = reinterpret_cast<f32x4*>(bbuf);  // [4 waves][FR * FT][64 lanes]
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FT; ++j) red[(wr * (FR * FT) + i * FT + j) * 64 + lane] = acc[i][j];
+    }
+    wait_lgkm0();
+    barrier_no_fence();
+    f32x4 odd[FR][FT];
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FT; ++j) odd[i][j] = red[(wr * (FR * FT) + i * FT + j) * 64 + lane];
+    }
+    wait_lgkm0();
+    barrier_no_fence();  // the next tile's prologue may refill the ring
+    if (grp != 0) continue;
+
+    // ---- epilogue (the even-step group's waves)
     const bool vec_ok = (ldy & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
@@ -443,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void spmm_lds_nm_kernel(
       for (int j = 0; j < FT; ++j) {
         const int t = T0 + j * 16 + li;
         if (t >= T || r >= R) continue;
-        const f32x4 v = acc[i][j];
+        const f32x4 v = acc[i][j] + odd[i][j];
         if constexpr (OUT == NM_F32) {
           float* y = static_cast<float*>(Y) + int64_t(t) * ldy + r;
           if (vec_ok && r + 3 < R) {
@@ -475,15 +529,15 @@ hipError_t launch_lds_nm(const SpmmArgs& a, hipStream_t s) {
   const int64_t ntiles = int64_t(tilesR) * tilesT;
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int cus = device_cu_count();
-  // two workgroups fit a CU (LDS and registers); more tiles than that are walked
+  // one workgroup (eight waves, two per SIMD) per CU; more tiles are walked
   TileMapNM tm;
   tm.tilesT = tilesT;
   tm.ntiles = int(ntiles);
-  tm.grid = int(ntiles > 2 * cus ? 2 * cus : ntiles);
+  tm.grid = int(ntiles > cus ? cus : ntiles);
   auto kern = spmm_lds_nm_kernel<P, DT, OUT>;
   if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), lds_bytes<P>()); e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(unsigned(tm.grid)), dim3(256), lds_bytes<P>(), s, a.values, a.idx, int(a.R),
-                     int(a.K), int(a.idx_row_words * 4), a.act, int(a.T), a.ldx, a.Y, a.ldy, tm);
+  hipLaunchKernelGGL(kern, dim3(unsigned(tm.grid)), dim3(kWaves * 64), lds_bytes<P>(), s, a.values, a.idx,
+                     int(a.R), int(a.K), int(a.idx_row_words * 4), a.act, int(a.T), a.ldx, a.Y, a.ldy, tm);
   return hipGetLastError();
 }
 

@@ -506,12 +506,19 @@ def test_kernel_families_agree(n, m):
     y_few_ref = nm.nm_spmm(vals, idx, A[:16].contiguous(), K, n, m, variant=1)
     torch.cuda.synchronize()
     # families that add the K steps in order from zero give identical bits
-    # (a family that does not take the shape falls back to the choice by shape)
-    assert torch.equal(outs[1], outs[2]) and torch.equal(outs[1], outs[3])
-    assert torch.equal(outs[1], outs[5]) and torch.equal(outs[1], outs[6])
+    # (a family that does not take the shape falls back to the choice by
+    # shape).  For 1:4 / 1:8 that choice, and families 3, 5 and 6, is the LDS
+    # kernel that sums even and odd K steps apart and then adds the two.
+    assert torch.equal(outs[1], outs[2])
+    if n == 2:
+        assert all(torch.equal(outs[1], outs[v]) for v in (3, 5, 6))
+    else:
+        assert all(torch.equal(outs[6], outs[v]) for v in (3, 5))
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, "bf16")
-    assert_close(outs[1], yref, error_bound(ref_vals, ref_idx, K, n, m, act, "bf16"))
+    bound = error_bound(ref_vals, ref_idx, K, n, m, act, "bf16")
+    assert_close(outs[1], yref, bound)
+    assert_close(outs[6], yref, bound)
     # the few-token family splits K: same product within the summation bound
     assert_close(y_few, yref[:, :16], error_bound(ref_vals, ref_idx, K, n, m, act[:16], "bf16"))
     assert_close(y_few_ref, yref[:, :16])
@@ -565,13 +572,18 @@ def test_lds_nm(R, K, T, dt, out, n, m):
     od = tdt if out == "half" else torch.float32
     y = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od, variant=6)
     y_pipe = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od, variant=2)
+    y_again = nm.nm_spmm(vals, idx, A, K, n, m, out_dtype=od, variant=6)
     torch.cuda.synchronize()
-    # same widened operands, K steps added in the same order
-    assert torch.equal(y, y_pipe)
+    # the same widened operands; the LDS kernel sums even and odd K steps
+    # apart and adds the two, so it matches the pipelined kernel to rounding,
+    # and itself bit for bit
+    assert torch.equal(y, y_again)
     ref_vals, ref_idx = O.prune_pack(w, n, m)
     yref = O.spmm_ref(ref_vals, ref_idx, K, n, m, act, dt)
-    assert_close(y, yref, error_bound(ref_vals, ref_idx, K, n, m, act, dt),
-                 **({"out_half": dt} if out == "half" else {}))
+    bound = error_bound(ref_vals, ref_idx, K, n, m, act, dt)
+    kw = {"out_half": dt} if out == "half" else {}
+    assert_close(y, yref, bound, **kw)
+    assert_close(y_pipe, yref, bound, **kw)
 
 
 # ---------------------------------------------------------------------------
