@@ -236,9 +236,11 @@ nm_status nm_check_perm(const int32_t* perm, int64_t K, void* stream);
  * K % 128 == 0) and, for variant 1 or any other shape, a kernel that loads
  * its operands straight into registers.
  * A named family that does not take the shape falls back to the choice by
- * shape.  Every family computes the same product; all but 4 add the 64-wide
- * K steps in the same order and give the same bits (4 splits K over waves:
- * the same result within the fp32 summation bound).
+ * shape.  Every family computes the same product; all but 4 and 6 add the
+ * 64-wide K steps in the same order and give the same bits (4 splits K over
+ * waves, 6 sums the even and the odd K steps apart and then adds the two:
+ * the same result within the fp32 summation bound, and the same bits on
+ * every run).
  * NM_ERR_UNSUPPORTED outside 0..6.
  */
 nm_status nm_spmm_variant(const void* values, const uint32_t* idx, int64_t R, int64_t K, int n, int m,
