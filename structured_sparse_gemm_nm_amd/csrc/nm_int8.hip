@@ -358,26 +358,69 @@ __global__ __launch_bounds__(256, 1) void spmm_i8_lds_kernel(const uint8_t* __re
     }
   };
 
+  // Load j of a step: 0..3 activations, 4..7 packed values, of step src into
+  // ring slot SL.
+  auto issue_one = [&](int src, auto slot_c, int j) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (j < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte*)(bbuf + SL * kStage8 + (wave * 4 + j) * 1024),
+                                               16, int(boff[j]), int(src * 128), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_byte*)(abuf + SL * kStage8 + (wave * 4 + j - 4) * 1024),
+                                               16, int(aoff[j - 4]), int(src * 64), 0, 0);
+  };
+
   // One step s: make step s+1 visible, refill step s's slot with step s+4,
   // read step s+1's fragments, multiply step s (fragments read one step
-  // earlier, so the reads overlap the MFMAs).
+  // earlier).  The step runs as eight chunks, each: some of step s+1's
+  // fragment reads, the 4 MFMAs of row fragment k of step s, and one load.
+  // The token fragments and index words come first (the next step needs
+  // them from its first chunk on), the row fragments after them, and the last
+  // chunk reads nothing; scheduling barriers keep this order, so no MFMA
+  // waits on a read issued just before it.
   auto step = [&](int s, auto slot_c, const i32x4 (&ca)[8], const i32x8 (&cb)[4], const uint32_t (&cx)[8],
                   i32x4 (&na)[8], i32x8 (&nb)[4], uint32_t (&nx)[8]) {
     constexpr int SL = decltype(slot_c)::value;
+    constexpr int RS = (SL + 1) & 3;  // slot of step s+1
     wait_vmcnt<2 * kPer8>();  // step s+1 has landed (steps s+2, s+3 may remain)
     __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // this wave's reads of step s are done
     __builtin_amdgcn_s_barrier();  // step s+1 visible; every wave is done reading step s
     asm volatile("" ::: "memory");
-    issue(min(s + 4, nsteps - 1), slot_c);
     // at a block's first step every wave is done with the block before it:
     // its buffer takes the next block (first read three steps later)
     if (SL == 0 && s + 4 < nsteps) issue_block((s >> 2) + 1, ((s >> 2) + 1) & 1);
-    read_frags(s + 1, std::integral_constant<int, (SL + 1) & 3>{}, na, nb, nx);
+    const int src = min(s + 4, nsteps - 1);
+    const unsigned char* sb = bbuf + RS * kStage8;
+    const unsigned char* sa = abuf + RS * kStage8;
+    const unsigned char* si = ibuf + (((s + 1) >> 2) & 1) * kBlockI8;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int k = 0; k < 8; ++k) {
+      if (k < 4) {
+        const int tok = wt * 64 + k * 16 + li;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(sb + (tok * 8 + (lq ^ (tok & 7))) * 16);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(sb + (tok * 8 + ((lq + 4) ^ (tok & 7))) * 16);
+        nb[k] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = smfmac8<F8>(ca[i], cb[j], acc[i][j], cx[i]);
+        for (int i = 2 * k; i < 2 * k + 2; ++i) {
+          const int row = wr * 128 + i * 16 + li;
+          nx[i] = *reinterpret_cast<const uint32_t*>(si + (row * 4 + (RS ^ ((row >> 2) & 3))) * 16 + lq * 4);
+        }
+      } else {
+#pragma unroll
+        for (int i = 3 * (k - 4); i < 3 * (k - 4) + 3; ++i) {
+          if (i < 8) {
+            const int row = wr * 128 + i * 16 + li;
+            na[i] = *reinterpret_cast<const i32x4*>(sa + (row * 4 + (lq ^ ((row >> 1) & 3))) * 16);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[k][j] = smfmac8<F8>(ca[k], cb[j], acc[k][j], cx[k]);
+      issue_one(src, slot_c, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   using std::integral_constant;
