@@ -61,28 +61,32 @@ __device__ inline float half_to_f32(uint32_t h) {
 // Unsigned minimum (the map clamp: an entry outside [0, K) reads column K-1).
 __device__ inline uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// fp32 -> the 16-bit storage type DT by the hardware conversions, round to
+// nearest even: v_cvt_f16_f32, and for bf16 v_cvt_pk_bf16_f32, whose bits equal
+// the integer rounding of the fp32 pattern (add 0x7FFF plus the kept lsb, keep
+// the top half; a NaN quieted with its top payload bits) for every input
+// checked: 4M random patterns and the halfway, denormal, overflow and
+// NaN-payload cases.  One instruction per pair of outputs.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// fp32 -> the 16-bit storage type DT (fp16 by the hardware conversion, RNE).
 template <int DT>
 __device__ inline uint16_t to_half_bits(float f) {
   if constexpr (DT == NM_F16) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
   } else {
-    return f32_to_bf16_rne(f);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
   }
 }
 
 // Two rounded outputs packed into one 32-bit word, the first in the low half.
 template <int DT>
 __device__ inline uint32_t pack_half2(float lo, float hi) {
-  return uint32_t(to_half_bits<DT>(lo)) | (uint32_t(to_half_bits<DT>(hi)) << 16);
+  if constexpr (DT == NM_F16) {
+    return uint32_t(to_half_bits<DT>(lo)) | (uint32_t(to_half_bits<DT>(hi)) << 16);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+  }
 }
 
 // s_barrier without the fence __syncthreads() adds (which waits for every
